@@ -1,0 +1,205 @@
+/*
+ * haste.h -- C ABI of the MI355X (gfx950) group-shared fixed fan-in output
+ * layer: a sparse "tail" over many rare labels plus a dense "head" over the
+ * frequent ones, with a fused sigmoid binary cross-entropy over sparse
+ * positives.  One shared library, libhaste.so; HIP kernels only.
+ *
+ * The method (HASTE summary page, gist.science, "HASTE: Hardware-Aware
+ * Dynamic Sparse Training for Large Output Spaces"):
+ *   - section "Method", item 1 (group-shared fixed fan-in): tail labels are
+ *     split into groups of G; every label of group g reads the same F input
+ *     features idx[g][0..F) but owns its weights.  The group's features are
+ *     gathered once into on-chip memory and reused by all G labels through a
+ *     dense matrix-core contraction; indices are stored once per group.
+ *   - section "Method", item 2 (head-tail decomposition): the frequent head
+ *     labels use a standard dense classifier.
+ * The loss and the backward formulas are not printed on the pages; this
+ * library computes the exact gradients of
+ *   z[b][t] = sum_f X[b][idx[t/G][f]] * W[t][f]            (tail)
+ *   zh[b][h] = sum_d X[b][d] * Wh[h][d]                    (head)
+ *   loss = s * sum_{b,label} softplus(z) - y*z,  dz = s * (sigmoid(z) - y)
+ * with y = 1 exactly at the listed positives.
+ *
+ * Conventions shared by every entry point
+ *   - All array arguments are DEVICE pointers (hipMalloc / torch CUDA
+ *     memory) unless a parameter says "host".  The caller owns every buffer,
+ *     including the workspace; the library never allocates, keeps no state
+ *     between calls and is safe to call from several host threads.
+ *   - Every call only enqueues work on `stream` (a hipStream_t, or NULL for
+ *     the default stream) and never synchronises.
+ *   - Layouts are row-major and densely packed:
+ *       X   : B x D                 (dtype)
+ *       idx : N_g x F  int32, N_g = ceil(L/G); each row strictly increasing,
+ *                      values in [0, D)
+ *       W   : (N_g*G) x F           (dtype) label-major: row t = g*G + j is
+ *                      label t's weights over idx[g][0..F).  Rows t >= L
+ *                      (padding of a ragged last group) are never read for
+ *                      a result and their gradient rows are written as 0.
+ *       Z,dZ: B x L                 (dtype), tail label t in column t
+ *       Wh  : H x D                 (dtype)  Zh, dZh: B x H (dtype)
+ *       dX  : B x D  float32
+ *   - dtype HASTE_BF16: inputs are bf16, products accumulate in fp32 on the
+ *     matrix cores (MFMA), dz is rounded to bf16 before it feeds the backward
+ *     contractions, bf16 outputs are rounded to nearest even.
+ *     dtype HASTE_F32: fp32 throughout (VALU kernels; small problems).
+ *   - Errors: arguments are checked on the host before anything is
+ *     enqueued; a failing check returns a status and enqueues nothing.
+ *     Index contents are not checked by the compute calls (an index outside
+ *     [0, D) reads or writes out of bounds); check them once with
+ *     haste_tail_validate.  A failed HIP launch returns HASTE_ERR_HIP.
+ *     haste_last_error() gives a message for the calling thread's last
+ *     failure.
+ */
+#ifndef HASTE_H
+#define HASTE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HASTE_ABI_VERSION 1
+
+typedef enum {
+    HASTE_OK = 0,
+    HASTE_ERR_INVALID = 1,     /* null pointer, bad size, misalignment      */
+    HASTE_ERR_UNSUPPORTED = 2, /* valid, but outside the implemented shapes */
+    HASTE_ERR_WORKSPACE = 3,   /* workspace missing or smaller than needed  */
+    HASTE_ERR_HIP = 4          /* a HIP runtime / launch error               */
+} haste_status;
+
+typedef enum { HASTE_F32 = 0, HASTE_BF16 = 1 } haste_dtype;
+
+/* Tail shape.  Supported: B >= 1, D >= F, F >= 1, L >= 1, G >= 1.
+ * bf16 kernels additionally need G in {16, 32, 64}, F a multiple of 32 with
+ * F <= 256, D <= 1536 and D*B small enough for int32 offsets; other shapes
+ * return HASTE_ERR_UNSUPPORTED.  fp32 accepts any G and F. */
+typedef struct {
+    int32_t B;      /* rows in the batch                    */
+    int32_t D;      /* input feature width                  */
+    int64_t L;      /* live tail labels                     */
+    int32_t G;      /* labels per group                     */
+    int32_t F;      /* fan-in indices per group             */
+    int32_t dtype;  /* haste_dtype of X, W, Z, dZ, dW       */
+} haste_tail_desc;
+
+/* Head shape (dense classifier).  bf16 needs D a multiple of 32. */
+typedef struct {
+    int32_t B;
+    int32_t D;
+    int32_t H;
+    int32_t dtype;
+} haste_head_desc;
+
+/* Sigmoid-BCE over sparse positives, fused into the logit epilogue.
+ * Positives are one row-CSR list for the whole output space in GLOBAL label
+ * ids (head labels [0, H), tail label t has id H + t); each call uses the
+ * ids in [label_offset, label_offset + its label count) and ignores the
+ * rest.  Ids must be unique within a row. */
+typedef struct {
+    const int32_t *row_ptr;   /* device, B+1 entries, row_ptr[0] = 0          */
+    const int32_t *labels;    /* device, nnz entries, global label ids        */
+    int32_t nnz;              /* host copy of row_ptr[B]                      */
+    int32_t reserved0;
+    int64_t label_offset;     /* global id of this branch's label 0           */
+    float grad_scale;         /* s: dz = s*(sigmoid(z) - y); usually 1/B      */
+    int32_t reserved1;
+    float *loss;              /* device fp32 scalar; this call ADDS its loss,
+                                 or NULL for no loss                          */
+    int32_t topk;             /* 0, or K in [1, 8]: per-row top-K logits      */
+    int32_t reserved2;
+    float *topk_val;          /* device B x K, descending                     */
+    int32_t *topk_idx;        /* device B x K global ids; ties -> smaller id  */
+} haste_bce;
+
+int haste_abi_version(void);
+const char *haste_status_string(int status);
+/* Message of the calling thread's last failed call ("" if none). */
+const char *haste_last_error(void);
+
+/* Storage of the tail (Method item 1, "memory efficiency": one index set per
+ * group).  out (host, 4 entries) = { N_g, stored index count N_g*F,
+ * stored weight rows N_g*G, live labels in the last group }. */
+haste_status haste_tail_layout(const haste_tail_desc *d, int64_t *out);
+
+/* Workspace bytes needed by the tail / head calls for this shape and BCE
+ * setup (bce may be NULL).  Pass a 256-byte aligned device buffer at least
+ * this large as `ws`. */
+size_t haste_tail_workspace_bytes(const haste_tail_desc *d, const haste_bce *bce);
+size_t haste_head_workspace_bytes(const haste_head_desc *d, const haste_bce *bce);
+
+/* Tail forward (Method item 1: gather X[:, idx[g]] once per group into LDS,
+ * then a dense per-group contraction).  Writes Z (B x L) if Z != NULL;
+ * adds the BCE loss and writes the top-K if bce asks for them.  At least one
+ * of Z, bce must be given. */
+haste_status haste_tail_fwd(const haste_tail_desc *d, const void *X,
+                            const int32_t *idx, const void *W, void *Z,
+                            const haste_bce *bce, void *ws, size_t ws_bytes,
+                            void *stream);
+
+/* Tail backward: dW (same shape/dtype as W, padded rows zeroed) and dX
+ * (B x D fp32; overwritten, or added to when accumulate_dX != 0).
+ * dZ != NULL: use the given B x L gradient.  dZ == NULL: recompute z and
+ * dz = s*(sigmoid(z)-y) from bce (no B x L buffer; bce->loss is NOT added
+ * here, so a separate forward can own the loss). */
+haste_status haste_tail_bwd(const haste_tail_desc *d, const void *X,
+                            const int32_t *idx, const void *W, const void *dZ,
+                            const haste_bce *bce, void *dW, float *dX,
+                            int accumulate_dX, void *ws, size_t ws_bytes,
+                            void *stream);
+
+/* Fused tail training step: loss (+= into bce->loss), top-K (if asked),
+ * dW and dX in one call, with no B x L buffer anywhere. */
+haste_status haste_tail_step(const haste_tail_desc *d, const void *X,
+                             const int32_t *idx, const void *W,
+                             const haste_bce *bce, void *dW, float *dX,
+                             int accumulate_dX, void *ws, size_t ws_bytes,
+                             void *stream);
+
+/* Head forward (Method item 2: dense classifier).  Zh (B x H) and/or the
+ * fused BCE (loss, top-K). */
+haste_status haste_head_fwd(const haste_head_desc *d, const void *X,
+                            const void *Wh, void *Zh, const haste_bce *bce,
+                            void *ws, size_t ws_bytes, void *stream);
+
+/* Head backward: dWh (H x D, dtype) and dX (B x D fp32, overwritten or
+ * accumulated).  dZh != NULL uses it; NULL recomputes from bce. */
+haste_status haste_head_bwd(const haste_head_desc *d, const void *X,
+                            const void *Wh, const void *dZh,
+                            const haste_bce *bce, void *dWh, float *dX,
+                            int accumulate_dX, void *ws, size_t ws_bytes,
+                            void *stream);
+
+/* Fused head step: loss (+=), top-K (if asked), dWh, dX. */
+haste_status haste_head_step(const haste_head_desc *d, const void *X,
+                             const void *Wh, const haste_bce *bce, void *dWh,
+                             float *dX, int accumulate_dX, void *ws,
+                             size_t ws_bytes, void *stream);
+
+/* Group-major view of the tail positives (the list the fused epilogue
+ * walks): grp_ptr (N_g + 1 entries) and entries (<= nnz), entry = b*G + j,
+ * ordered by group, then row b, then slot j.  Deterministic. */
+haste_status haste_tail_group_positives(const haste_tail_desc *d,
+                                        const haste_bce *bce, int32_t *grp_ptr,
+                                        int32_t *entries, void *ws,
+                                        size_t ws_bytes, void *stream);
+
+/* Index check: writes to *first_bad_group (device int32) the smallest group
+ * whose row of idx is not strictly increasing inside [0, D), or -1. */
+haste_status haste_tail_validate(const haste_tail_desc *d, const int32_t *idx,
+                                 int32_t *first_bad_group, void *stream);
+
+/* Merge two per-row top-K lists (e.g. head and tail) into one: B x K each,
+ * descending, ties broken toward the smaller id (second stage of the
+ * two-stage top-K on the top-K page, with K' = K so the result is exact). */
+haste_status haste_topk_merge(int32_t B, int32_t K, const float *a_val,
+                              const int32_t *a_idx, const float *b_val,
+                              const int32_t *b_idx, float *out_val,
+                              int32_t *out_idx, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HASTE_H */

@@ -1,0 +1,578 @@
+// abi.hip -- the extern "C" entry points of libhaste (declared and
+// documented in include/haste.h): host-side argument checks, workspace
+// layout and kernel dispatch.  Nothing here allocates device memory.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "../../include/haste.h"
+#include "kernels.h"
+
+using namespace haste;
+
+namespace {
+
+thread_local std::string g_err;
+
+haste_status fail(haste_status s, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+haste_status fail(haste_status s, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return s;
+}
+
+haste_status hip_ok(hipError_t e, const char *what) {
+    if (e == hipSuccess) return HASTE_OK;
+    return fail(HASTE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define TRY_HIP(expr, what)                                  \
+    do {                                                     \
+        haste_status _s = hip_ok((expr), (what));            \
+        if (_s != HASTE_OK) return _s;                       \
+    } while (0)
+#define TRY(expr)                                            \
+    do {                                                     \
+        haste_status _s = (expr);                            \
+        if (_s != HASTE_OK) return _s;                       \
+    } while (0)
+
+inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+inline bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+inline int64_t n_groups(const haste_tail_desc *d) { return (d->L + d->G - 1) / d->G; }
+inline int pad_rows(int B) { return (B + 63) / 64 * 64; }
+
+// ----------------------------------------------------------- workspace maps
+struct TailWs {
+    size_t xt, cnt, ptr, ent, dz, total;
+};
+
+TailWs tail_ws(const haste_tail_desc *d, const haste_bce *bce) {
+    TailWs w{};
+    const int64_t ng = n_groups(d);
+    const int nnz = bce ? (bce->nnz > 0 ? bce->nnz : 0) : 0;
+    size_t o = 0;
+    if (d->dtype == HASTE_BF16) {
+        w.xt = o;  o += al256((size_t)d->D * pad_rows(d->B) * 2);
+        w.cnt = o; o += al256((size_t)ng * 4);
+        w.ptr = o; o += al256((size_t)(ng + 1) * 4);
+        w.ent = o; o += al256((size_t)(nnz > 0 ? nnz : 1) * 4);
+    } else {
+        w.cnt = o; o += al256((size_t)ng * 4);
+        w.dz = o;  o += al256((size_t)d->B * d->L * 4);
+    }
+    w.total = o;
+    return w;
+}
+
+struct HeadWs {
+    size_t bm, dz, total;
+    int words;
+};
+
+HeadWs head_ws(const haste_head_desc *d) {
+    HeadWs w{};
+    size_t o = 0;
+    w.words = (d->H + 31) / 32;
+    w.bm = o; o += al256((size_t)d->B * w.words * 4);
+    w.dz = o; o += al256((size_t)d->B * d->H * (d->dtype == HASTE_BF16 ? 2 : 4));
+    w.total = o;
+    return w;
+}
+
+// ------------------------------------------------------------- validation
+haste_status check_tail(const haste_tail_desc *d) {
+    if (!d) return fail(HASTE_ERR_INVALID, "tail descriptor is NULL");
+    if (d->B < 1 || d->D < 1 || d->L < 1 || d->G < 1 || d->F < 1)
+        return fail(HASTE_ERR_INVALID, "tail sizes must be >= 1 (B=%d D=%d L=%lld G=%d F=%d)",
+                    d->B, d->D, (long long)d->L, d->G, d->F);
+    if (d->F > d->D) return fail(HASTE_ERR_INVALID, "F=%d exceeds D=%d", d->F, d->D);
+    if (d->dtype != HASTE_F32 && d->dtype != HASTE_BF16)
+        return fail(HASTE_ERR_INVALID, "unknown dtype %d", d->dtype);
+    if (d->dtype == HASTE_BF16) {
+        if (!tail_bf16_supported(d->G, d->F, d->D))
+            return fail(HASTE_ERR_UNSUPPORTED,
+                        "bf16 tail supports G in {16,32,64}, F in {32,64,128}, F <= D <= 1536 "
+                        "(got G=%d F=%d D=%d)", d->G, d->F, d->D);
+        if ((int64_t)d->B * d->G > (1 << 30))
+            return fail(HASTE_ERR_UNSUPPORTED, "B*G too large");
+    }
+    if (d->L > ((int64_t)1 << 40)) return fail(HASTE_ERR_UNSUPPORTED, "L too large");
+    return HASTE_OK;
+}
+
+haste_status check_head(const haste_head_desc *d) {
+    if (!d) return fail(HASTE_ERR_INVALID, "head descriptor is NULL");
+    if (d->B < 1 || d->D < 1 || d->H < 1)
+        return fail(HASTE_ERR_INVALID, "head sizes must be >= 1 (B=%d D=%d H=%d)", d->B, d->D, d->H);
+    if (d->dtype != HASTE_F32 && d->dtype != HASTE_BF16)
+        return fail(HASTE_ERR_INVALID, "unknown dtype %d", d->dtype);
+    if (d->dtype == HASTE_BF16 && (d->D % 8 != 0 || d->H % 8 != 0))
+        return fail(HASTE_ERR_UNSUPPORTED, "bf16 head needs D and H multiples of 8 (D=%d H=%d)",
+                    d->D, d->H);
+    return HASTE_OK;
+}
+
+haste_status check_bce(const haste_bce *b, int B, bool need_loss_ok) {
+    (void)need_loss_ok;
+    if (!b) return HASTE_OK;
+    if (b->nnz < 0) return fail(HASTE_ERR_INVALID, "bce.nnz < 0");
+    if (!b->row_ptr) return fail(HASTE_ERR_INVALID, "bce.row_ptr is NULL");
+    if (b->nnz > 0 && !b->labels) return fail(HASTE_ERR_INVALID, "bce.labels is NULL");
+    if (b->label_offset < 0) return fail(HASTE_ERR_INVALID, "bce.label_offset < 0");
+    if (b->topk != 0) return fail(HASTE_ERR_UNSUPPORTED, "bce.topk is not supported by this call");
+    (void)B;
+    return HASTE_OK;
+}
+
+haste_status need(const void *p, const char *name) {
+    if (!p) return fail(HASTE_ERR_INVALID, "%s is NULL", name);
+    return HASTE_OK;
+}
+
+haste_status need_al(const void *p, size_t a, const char *name) {
+    if (!p) return fail(HASTE_ERR_INVALID, "%s is NULL", name);
+    if (!aligned(p, a)) return fail(HASTE_ERR_INVALID, "%s is not %zu-byte aligned", name, a);
+    return HASTE_OK;
+}
+
+haste_status check_ws(void *ws, size_t ws_bytes, size_t need_bytes) {
+    if (need_bytes == 0) return HASTE_OK;
+    if (!ws) return fail(HASTE_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need_bytes);
+    if (!aligned(ws, 256)) return fail(HASTE_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+    if (ws_bytes < need_bytes)
+        return fail(HASTE_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, need_bytes);
+    return HASTE_OK;
+}
+
+hipStream_t S(void *st) { return (hipStream_t)st; }
+char *B8(void *p, size_t off) { return (char *)p + off; }
+
+// ---------------------------------------------------------- bf16 tail core
+TailArgs tail_args(const haste_tail_desc *d, const void *X, const int32_t *idx, const void *W,
+                   void *ws, const TailWs &m) {
+    (void)X;
+    TailArgs a{};
+    a.XT = (const unsigned short *)B8(ws, m.xt);
+    a.idx = idx;
+    a.W = (const unsigned short *)W;
+    a.grp_ptr = (const int32_t *)B8(ws, m.ptr);
+    a.grp_ent = (const int32_t *)B8(ws, m.ent);
+    a.B = d->B;
+    a.D = d->D;
+    a.Bp = pad_rows(d->B);
+    a.F = d->F;
+    a.L = d->L;
+    a.Ng = n_groups(d);
+    return a;
+}
+
+haste_status bf16_prep(const haste_tail_desc *d, const void *X, const haste_bce *bce, void *ws,
+                       const TailWs &m, hipStream_t st) {
+    TRY_HIP(launch_transpose_x((const unsigned short *)X, (unsigned short *)B8(ws, m.xt), d->B,
+                               d->D, pad_rows(d->B), st), "transpose X");
+    if (bce) {
+        TRY_HIP(launch_group_positives(bce->row_ptr, bce->labels, bce->nnz, d->B, bce->label_offset,
+                                       d->L, d->G, n_groups(d), (int32_t *)B8(ws, m.cnt),
+                                       (int32_t *)B8(ws, m.ptr), (int32_t *)B8(ws, m.ent), st),
+                "group positives");
+    }
+    return HASTE_OK;
+}
+
+F32Args f32_tail_args(const haste_tail_desc *d, const void *X, const int32_t *idx, const void *W,
+                      const haste_bce *bce) {
+    F32Args a{};
+    a.X = (const float *)X;
+    a.idx = idx;
+    a.W = (const float *)W;
+    a.B = d->B;
+    a.D = d->D;
+    a.G = d->G;
+    a.F = d->F;
+    a.L = d->L;
+    a.Ng = n_groups(d);
+    if (bce) {
+        a.row_ptr = bce->row_ptr;
+        a.labels = bce->labels;
+        a.label_offset = bce->label_offset;
+        a.s = bce->grad_scale;
+        a.loss = bce->loss;
+    }
+    return a;
+}
+
+haste_status zero_dx(float *dX, int B, int D, int accumulate, hipStream_t st) {
+    if (!accumulate) TRY_HIP(launch_fill_u32(dX, 0u, (size_t)B * D, st), "zero dX");
+    return HASTE_OK;
+}
+
+// common argument checks of tail compute calls
+haste_status tail_common(const haste_tail_desc *d, const void *X, const int32_t *idx,
+                         const void *W) {
+    TRY(check_tail(d));
+    const size_t al = d->dtype == HASTE_BF16 ? 16 : 4;
+    TRY(need_al(X, al, "X"));
+    TRY(need_al(idx, 4, "idx"));
+    TRY(need_al(W, al, "W"));
+    return HASTE_OK;
+}
+
+}  // namespace
+
+// =================================================================== C ABI
+extern "C" {
+
+int haste_abi_version(void) { return HASTE_ABI_VERSION; }
+
+const char *haste_status_string(int s) {
+    switch (s) {
+    case HASTE_OK: return "ok";
+    case HASTE_ERR_INVALID: return "invalid argument";
+    case HASTE_ERR_UNSUPPORTED: return "unsupported shape or option";
+    case HASTE_ERR_WORKSPACE: return "workspace missing or too small";
+    case HASTE_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char *haste_last_error(void) { return g_err.c_str(); }
+
+haste_status haste_tail_layout(const haste_tail_desc *d, int64_t *out) {
+    g_err.clear();
+    if (!d) return fail(HASTE_ERR_INVALID, "tail descriptor is NULL");
+    if (!out) return fail(HASTE_ERR_INVALID, "out is NULL");
+    if (d->L < 1 || d->G < 1 || d->F < 1) return fail(HASTE_ERR_INVALID, "L, G, F must be >= 1");
+    const int64_t ng = n_groups(d);
+    out[0] = ng;
+    out[1] = ng * d->F;
+    out[2] = ng * d->G;
+    out[3] = d->L - (ng - 1) * d->G;
+    return HASTE_OK;
+}
+
+size_t haste_tail_workspace_bytes(const haste_tail_desc *d, const haste_bce *bce) {
+    if (check_tail(d) != HASTE_OK) return 0;
+    return tail_ws(d, bce).total;
+}
+
+size_t haste_head_workspace_bytes(const haste_head_desc *d, const haste_bce *bce) {
+    (void)bce;
+    if (check_head(d) != HASTE_OK) return 0;
+    return head_ws(d).total;
+}
+
+haste_status haste_tail_fwd(const haste_tail_desc *d, const void *X, const int32_t *idx,
+                            const void *W, void *Z, const haste_bce *bce, void *ws,
+                            size_t ws_bytes, void *stream) {
+    g_err.clear();
+    TRY(tail_common(d, X, idx, W));
+    TRY(check_bce(bce, d->B, true));
+    if (!Z && !bce) return fail(HASTE_ERR_INVALID, "nothing to compute: Z and bce are both NULL");
+    if (Z && !aligned(Z, d->dtype == HASTE_BF16 ? 2 : 4)) return fail(HASTE_ERR_INVALID, "Z misaligned");
+    const TailWs m = tail_ws(d, bce);
+    TRY(check_ws(ws, ws_bytes, m.total));
+    hipStream_t st = S(stream);
+    if (d->dtype == HASTE_BF16) {
+        TRY(bf16_prep(d, X, bce, ws, m, st));
+        TailArgs a = tail_args(d, X, idx, W, ws, m);
+        a.Z = (unsigned short *)Z;
+        if (bce) {
+            a.loss = bce->loss;
+            a.s = bce->grad_scale;
+        }
+        TRY_HIP(launch_tail_t1(T1_FWD, d->G, a, Z != nullptr, bce && bce->loss, st), "tail fwd");
+    } else {
+        F32Args a = f32_tail_args(d, X, idx, W, bce);
+        a.Z = (float *)Z;
+        TRY_HIP(launch_f32_tail_logits(a, Z != nullptr, bce != nullptr, bce && bce->loss, st),
+                "tail fwd f32");
+    }
+    return HASTE_OK;
+}
+
+haste_status haste_tail_bwd(const haste_tail_desc *d, const void *X, const int32_t *idx,
+                            const void *W, const void *dZ, const haste_bce *bce, void *dW,
+                            float *dX, int accumulate_dX, void *ws, size_t ws_bytes,
+                            void *stream) {
+    g_err.clear();
+    TRY(tail_common(d, X, idx, W));
+    if (!dZ && !bce) return fail(HASTE_ERR_INVALID, "need dZ or bce to form the gradient");
+    if (!dZ) TRY(check_bce(bce, d->B, false));
+    TRY(need_al(dW, d->dtype == HASTE_BF16 ? 8 : 4, "dW"));
+    TRY(need_al(dX, 4, "dX"));
+    if (dZ && !aligned(dZ, d->dtype == HASTE_BF16 ? 2 : 4)) return fail(HASTE_ERR_INVALID, "dZ misaligned");
+    const haste_bce *b = dZ ? nullptr : bce;
+    const TailWs m = tail_ws(d, b);
+    TRY(check_ws(ws, ws_bytes, m.total));
+    hipStream_t st = S(stream);
+    TRY(zero_dx(dX, d->B, d->D, accumulate_dX, st));
+    if (d->dtype == HASTE_BF16) {
+        TRY(bf16_prep(d, X, b, ws, m, st));
+        TailArgs a = tail_args(d, X, idx, W, ws, m);
+        a.dW = (unsigned short *)dW;
+        a.dX = dX;
+        a.dZ = (const unsigned short *)dZ;
+        if (b) a.s = b->grad_scale;
+        TRY_HIP(launch_tail_t1(dZ ? T1_DW_MEM : T1_DW_BCE, d->G, a, false, false, st), "tail dW");
+        TRY_HIP(launch_tail_t2(d->G, dZ != nullptr, a, st), "tail dX");
+    } else {
+        F32Args a = f32_tail_args(d, X, idx, W, b);
+        a.loss = nullptr;
+        a.dW = (float *)dW;
+        a.dX = dX;
+        if (dZ) {
+            a.dZ = (float *)dZ;
+        } else {
+            a.dZ = (float *)B8(ws, m.dz);
+            TRY_HIP(launch_f32_tail_logits(a, false, true, false, st), "tail dz f32");
+        }
+        TRY_HIP(launch_f32_tail_dw(a, st), "tail dW f32");
+        TRY_HIP(launch_f32_tail_dx(a, st), "tail dX f32");
+    }
+    return HASTE_OK;
+}
+
+haste_status haste_tail_step(const haste_tail_desc *d, const void *X, const int32_t *idx,
+                             const void *W, const haste_bce *bce, void *dW, float *dX,
+                             int accumulate_dX, void *ws, size_t ws_bytes, void *stream) {
+    g_err.clear();
+    TRY(tail_common(d, X, idx, W));
+    TRY(need(bce, "bce"));
+    TRY(check_bce(bce, d->B, true));
+    TRY(need_al(dW, d->dtype == HASTE_BF16 ? 8 : 4, "dW"));
+    TRY(need_al(dX, 4, "dX"));
+    const TailWs m = tail_ws(d, bce);
+    TRY(check_ws(ws, ws_bytes, m.total));
+    hipStream_t st = S(stream);
+    TRY(zero_dx(dX, d->B, d->D, accumulate_dX, st));
+    if (d->dtype == HASTE_BF16) {
+        TRY(bf16_prep(d, X, bce, ws, m, st));
+        TailArgs a = tail_args(d, X, idx, W, ws, m);
+        a.dW = (unsigned short *)dW;
+        a.dX = dX;
+        a.s = bce->grad_scale;
+        a.loss = bce->loss;
+        TRY_HIP(launch_tail_t1(T1_DW_BCE, d->G, a, false, bce->loss != nullptr, st), "tail step dW");
+        TRY_HIP(launch_tail_t2(d->G, false, a, st), "tail step dX");
+    } else {
+        F32Args a = f32_tail_args(d, X, idx, W, bce);
+        a.dW = (float *)dW;
+        a.dX = dX;
+        a.dZ = (float *)B8(ws, m.dz);
+        TRY_HIP(launch_f32_tail_logits(a, false, true, bce->loss != nullptr, st), "tail step f32");
+        TRY_HIP(launch_f32_tail_dw(a, st), "tail dW f32");
+        TRY_HIP(launch_f32_tail_dx(a, st), "tail dX f32");
+    }
+    return HASTE_OK;
+}
+
+// ------------------------------------------------------------------- head
+namespace {
+
+haste_status head_common(const haste_head_desc *d, const void *X, const void *Wh) {
+    TRY(check_head(d));
+    const size_t al = d->dtype == HASTE_BF16 ? 16 : 4;
+    TRY(need_al(X, al, "X"));
+    TRY(need_al(Wh, al, "Wh"));
+    return HASTE_OK;
+}
+
+// logits + (optional) BCE.  dz_out: where dz goes (NULL: nowhere).
+haste_status head_logits(const haste_head_desc *d, const void *X, const void *Wh, void *Zh,
+                         const haste_bce *bce, bool want_loss, void *dz_out, void *ws,
+                         const HeadWs &m, hipStream_t st) {
+    if (d->dtype == HASTE_BF16) {
+        GemmArgs g{};
+        g.A = (const unsigned short *)X;
+        g.Bm = (const unsigned short *)Wh;
+        g.M = d->B;
+        g.N = d->H;
+        g.K = d->D;
+        g.lda = d->D;
+        g.ldb = d->D;
+        g.k_split = d->D;
+        g.Zout = (unsigned short *)Zh;
+        if (bce) {
+            TRY_HIP(launch_head_bitmap(bce->row_ptr, bce->labels, bce->nnz, d->B, bce->label_offset,
+                                       d->H, (uint32_t *)B8(ws, m.bm), m.words, st), "head bitmap");
+            g.bitmap = (const uint32_t *)B8(ws, m.bm);
+            g.bm_words = m.words;
+            g.s = bce->grad_scale;
+            g.loss = want_loss ? bce->loss : nullptr;
+            g.dZout = (unsigned short *)dz_out;
+        }
+        TRY_HIP(launch_gemm(true, true, EPI_BCE, g, st), "head logits");
+    } else {
+        F32Args a{};
+        a.X = (const float *)X;
+        a.W = (const float *)Wh;
+        a.Z = (float *)Zh;
+        a.B = d->B;
+        a.D = d->D;
+        a.L = d->H;
+        if (bce) {
+            a.row_ptr = bce->row_ptr;
+            a.labels = bce->labels;
+            a.label_offset = bce->label_offset;
+            a.s = bce->grad_scale;
+            a.loss = want_loss ? bce->loss : nullptr;
+            a.dZ = (float *)dz_out;
+        }
+        TRY_HIP(launch_f32_head_logits(a, Zh != nullptr, bce != nullptr, want_loss, st),
+                "head logits f32");
+    }
+    return HASTE_OK;
+}
+
+haste_status head_grads(const haste_head_desc *d, const void *X, const void *Wh, const void *dz,
+                        void *dWh, float *dX, hipStream_t st) {
+    if (d->dtype == HASTE_BF16) {
+        GemmArgs g{};  // dWh[h][d] = sum_b dz[b][h] X[b][d]
+        g.A = (const unsigned short *)dz;
+        g.Bm = (const unsigned short *)X;
+        g.M = d->H;
+        g.N = d->D;
+        g.K = d->B;
+        g.lda = d->H;
+        g.ldb = d->D;
+        g.k_split = d->B;
+        g.C16 = (unsigned short *)dWh;
+        TRY_HIP(launch_gemm(false, false, EPI_STORE16, g, st), "head dW");
+        GemmArgs x{};  // dX[b][d] += sum_h dz[b][h] Wh[h][d]
+        x.A = (const unsigned short *)dz;
+        x.Bm = (const unsigned short *)Wh;
+        x.M = d->B;
+        x.N = d->D;
+        x.K = d->H;
+        x.lda = d->H;
+        x.ldb = d->D;
+        x.C32 = dX;
+        const int tiles = ((d->B + 127) / 128) * ((d->D + 127) / 128);
+        int splits = (512 + tiles - 1) / tiles;
+        int ks = (d->H + splits - 1) / splits;
+        ks = (ks + 31) / 32 * 32;
+        if (ks < 256) ks = 256;
+        x.k_split = ks;
+        TRY_HIP(launch_gemm(true, false, EPI_ATOMIC32, x, st), "head dX");
+    } else {
+        F32Args a{};
+        a.X = (const float *)X;
+        a.W = (const float *)Wh;
+        a.dZ = (float *)dz;
+        a.dW = (float *)dWh;
+        a.dX = dX;
+        a.B = d->B;
+        a.D = d->D;
+        a.L = d->H;
+        TRY_HIP(launch_f32_head_dw(a, st), "head dW f32");
+        TRY_HIP(launch_f32_head_dx(a, st), "head dX f32");
+    }
+    return HASTE_OK;
+}
+
+}  // namespace
+
+haste_status haste_head_fwd(const haste_head_desc *d, const void *X, const void *Wh, void *Zh,
+                            const haste_bce *bce, void *ws, size_t ws_bytes, void *stream) {
+    g_err.clear();
+    TRY(head_common(d, X, Wh));
+    TRY(check_bce(bce, d->B, true));
+    if (!Zh && !bce) return fail(HASTE_ERR_INVALID, "nothing to compute: Zh and bce are both NULL");
+    const HeadWs m = head_ws(d);
+    TRY(check_ws(ws, ws_bytes, bce ? m.total : 0));
+    return head_logits(d, X, Wh, Zh, bce, bce && bce->loss, nullptr, ws, m, S(stream));
+}
+
+haste_status haste_head_bwd(const haste_head_desc *d, const void *X, const void *Wh,
+                            const void *dZh, const haste_bce *bce, void *dWh, float *dX,
+                            int accumulate_dX, void *ws, size_t ws_bytes, void *stream) {
+    g_err.clear();
+    TRY(head_common(d, X, Wh));
+    if (!dZh && !bce) return fail(HASTE_ERR_INVALID, "need dZh or bce to form the gradient");
+    if (!dZh) TRY(check_bce(bce, d->B, false));
+    TRY(need_al(dWh, d->dtype == HASTE_BF16 ? 2 : 4, "dWh"));
+    TRY(need_al(dX, 4, "dX"));
+    if (dZh && !aligned(dZh, 16)) return fail(HASTE_ERR_INVALID, "dZh is not 16-byte aligned");
+    const HeadWs m = head_ws(d);
+    TRY(check_ws(ws, ws_bytes, dZh ? 0 : m.total));
+    hipStream_t st = S(stream);
+    TRY(zero_dx(dX, d->B, d->D, accumulate_dX, st));
+    const void *dz = dZh;
+    if (!dz) {
+        TRY(head_logits(d, X, Wh, nullptr, bce, false, B8(ws, m.dz), ws, m, st));
+        dz = B8(ws, m.dz);
+    }
+    return head_grads(d, X, Wh, dz, dWh, dX, st);
+}
+
+haste_status haste_head_step(const haste_head_desc *d, const void *X, const void *Wh,
+                             const haste_bce *bce, void *dWh, float *dX, int accumulate_dX,
+                             void *ws, size_t ws_bytes, void *stream) {
+    g_err.clear();
+    TRY(head_common(d, X, Wh));
+    TRY(need(bce, "bce"));
+    TRY(check_bce(bce, d->B, true));
+    TRY(need_al(dWh, d->dtype == HASTE_BF16 ? 2 : 4, "dWh"));
+    TRY(need_al(dX, 4, "dX"));
+    const HeadWs m = head_ws(d);
+    TRY(check_ws(ws, ws_bytes, m.total));
+    hipStream_t st = S(stream);
+    TRY(zero_dx(dX, d->B, d->D, accumulate_dX, st));
+    TRY(head_logits(d, X, Wh, nullptr, bce, bce->loss != nullptr, B8(ws, m.dz), ws, m, st));
+    return head_grads(d, X, Wh, B8(ws, m.dz), dWh, dX, st);
+}
+
+// -------------------------------------------------------------- utilities
+haste_status haste_tail_group_positives(const haste_tail_desc *d, const haste_bce *bce,
+                                        int32_t *grp_ptr, int32_t *entries, void *ws,
+                                        size_t ws_bytes, void *stream) {
+    g_err.clear();
+    TRY(check_tail(d));
+    TRY(need(bce, "bce"));
+    TRY(check_bce(bce, d->B, false));
+    TRY(need_al(grp_ptr, 4, "grp_ptr"));
+    if (bce->nnz > 0) TRY(need_al(entries, 4, "entries"));
+    const TailWs m = tail_ws(d, bce);
+    TRY(check_ws(ws, ws_bytes, m.total));
+    TRY_HIP(launch_group_positives(bce->row_ptr, bce->labels, bce->nnz, d->B, bce->label_offset,
+                                   d->L, d->G, n_groups(d), (int32_t *)B8(ws, m.cnt), grp_ptr,
+                                   entries, S(stream)),
+            "group positives");
+    return HASTE_OK;
+}
+
+haste_status haste_tail_validate(const haste_tail_desc *d, const int32_t *idx,
+                                 int32_t *first_bad_group, void *stream) {
+    g_err.clear();
+    if (!d) return fail(HASTE_ERR_INVALID, "tail descriptor is NULL");
+    if (d->L < 1 || d->G < 1 || d->F < 1 || d->D < 1) return fail(HASTE_ERR_INVALID, "bad sizes");
+    TRY(need_al(idx, 4, "idx"));
+    TRY(need_al(first_bad_group, 4, "first_bad_group"));
+    TRY_HIP(launch_validate(idx, n_groups(d), d->F, d->D, first_bad_group, S(stream)), "validate");
+    return HASTE_OK;
+}
+
+haste_status haste_topk_merge(int32_t B, int32_t K, const float *a_val, const int32_t *a_idx,
+                              const float *b_val, const int32_t *b_idx, float *out_val,
+                              int32_t *out_idx, void *stream) {
+    g_err.clear();
+    if (B < 0 || K < 1 || K > 64) return fail(HASTE_ERR_INVALID, "need B >= 0 and 1 <= K <= 64");
+    TRY(need(a_val, "a_val"));
+    TRY(need(a_idx, "a_idx"));
+    TRY(need(b_val, "b_val"));
+    TRY(need(b_idx, "b_idx"));
+    TRY(need(out_val, "out_val"));
+    TRY(need(out_idx, "out_idx"));
+    TRY_HIP(launch_topk_merge(B, K, a_val, a_idx, b_val, b_idx, out_val, out_idx, S(stream)),
+            "topk merge");
+    return HASTE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,82 @@
+// common.h -- device helpers shared by the gfx950 kernels of libhaste.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace haste {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+
+#define HASTE_LDS(T, p) ((__attribute__((address_space(3))) T *)(p))
+
+// 16x16 output, K = 32 bf16 per instruction.  Operand lane layout (both A
+// and B): lane l holds row/col (l % 16) and K slots 8*(l/16) .. +7.
+// Output: lane l holds rows 4*(l/16)+i (i = 0..3) of column l % 16.
+__device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// 16x16 output, K = 16: lane l holds K slots 4*(l/16) .. +3.
+__device__ __forceinline__ f32x4 mfma16(i16x4 a, i16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each block of 16
+// lanes, lane i receives, for k = 0..3, element (i % 4) of the 4-element
+// run addressed by lane 4*k + i/4 of its block.
+__device__ __forceinline__ i16x4 lds_read_tr(const void *lds_ptr) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(HASTE_LDS(i16x4, lds_ptr));
+}
+
+__device__ __forceinline__ float bf16_to_f32(unsigned short b) {
+    return __uint_as_float(((unsigned)b) << 16);
+}
+
+// Round to nearest even (hardware conversion on gfx950).
+__device__ __forceinline__ unsigned short f32_to_bf16(float x) {
+    __bf16 h = (__bf16)x;
+    return __builtin_bit_cast(unsigned short, h);
+}
+
+__device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
+    return (unsigned)f32_to_bf16(lo) | ((unsigned)f32_to_bf16(hi) << 16);
+}
+
+// Sigmoid-BCE on one logit, fp32, scaled by s.  e = exp(-|z|) is shared by
+// the sigmoid and the softplus.  Hardware exp/log/rcp via the device math
+// intrinsics (__expf, __logf).
+struct BceOut {
+    float dz;
+    float loss;
+};
+
+__device__ __forceinline__ float bce_dz(float z, float y, float s) {
+    float e = __expf(-fabsf(z));
+    float r = __frcp_rn(1.0f + e);
+    float sig = z >= 0.f ? r : e * r;
+    return s * (sig - y);
+}
+
+__device__ __forceinline__ BceOut bce_both(float z, float y, float s) {
+    float e = __expf(-fabsf(z));
+    float r = __frcp_rn(1.0f + e);
+    float sig = z >= 0.f ? r : e * r;
+    float lin = fmaxf(z, 0.f) - y * z;
+    // log(1+e) for e in (0, 1]: use log1p-accurate form for small e
+    float l1p = (e < 1e-4f) ? e * (1.0f - 0.5f * e) : __logf(1.0f + e);
+    BceOut o;
+    o.dz = s * (sig - y);
+    o.loss = s * (lin + l1p);
+    return o;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+}  // namespace haste

@@ -1,0 +1,103 @@
+// kernels.h -- launchers of the gfx950 kernels (internal C++ interface of
+// libhaste; the public interface is include/haste.h).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace haste {
+
+// Everything a tail kernel may read or write.  Pointers not used by a
+// given launch may be null.
+struct TailArgs {
+    const unsigned short *XT;    // D x Bp bf16, zero beyond column B
+    const int32_t *idx;          // Ng x F
+    const unsigned short *W;     // (Ng*G) x F bf16
+    unsigned short *Z;           // B x L bf16 (forward output)
+    const unsigned short *dZ;    // B x L bf16 (given gradient)
+    unsigned short *dW;          // (Ng*G) x F bf16
+    float *dX;                   // B x D fp32 (atomically accumulated)
+    const int32_t *grp_ptr;      // Ng + 1 group-major positives
+    const int32_t *grp_ent;      // entries b*G + j
+    float *loss;                 // fp32 scalar (+=)
+    float s;                     // gradient scale
+    int B, D, Bp, F;
+    int64_t L, Ng;
+};
+
+enum T1Mode { T1_FWD = 0, T1_DW_BCE = 1, T1_DW_MEM = 2 };
+
+// Launch helpers return hipSuccess or the launch error.
+hipError_t launch_transpose_x(const unsigned short *X, unsigned short *XT,
+                              int B, int D, int Bp, hipStream_t st);
+hipError_t launch_fill_u32(void *p, uint32_t v, size_t n, hipStream_t st);
+hipError_t launch_group_positives(const int32_t *row_ptr, const int32_t *labels,
+                                  int nnz, int B, int64_t label_offset,
+                                  int64_t L, int G, int64_t Ng, int32_t *cnt,
+                                  int32_t *grp_ptr, int32_t *ent,
+                                  hipStream_t st);
+hipError_t launch_tail_t1(int mode, int G, const TailArgs &a, bool store_z,
+                          bool do_loss, hipStream_t st);
+hipError_t launch_tail_t2(int G, bool dz_mem, const TailArgs &a,
+                          hipStream_t st);
+bool tail_bf16_supported(int G, int F, int D);
+
+// Head (dense classifier) GEMMs.
+struct GemmArgs {
+    const unsigned short *A;
+    const unsigned short *Bm;
+    int M, N, K;
+    int lda, ldb;              // row strides (elements)
+    // epilogue
+    unsigned short *C16;       // bf16 output, ldc = N
+    float *C32;                // fp32 output (atomic add), ldc = N
+    unsigned short *Zout;      // BCE: optional logits (bf16), ld N
+    unsigned short *dZout;     // BCE: optional dz (bf16), ld N
+    const uint32_t *bitmap;    // BCE: positives bitmap, row stride bm_words
+    int bm_words;
+    float *loss;
+    float s;
+    int k_split;               // K elements per split (multiple of 32)
+};
+enum GemmEpi { EPI_BCE = 0, EPI_STORE16 = 1, EPI_ATOMIC32 = 2 };
+// a_kmaj: A stored [m][k]; else [k][m].  b_kmaj: B stored [n][k]; else [k][n].
+hipError_t launch_gemm(bool a_kmaj, bool b_kmaj, int epi, const GemmArgs &g,
+                       hipStream_t st);
+hipError_t launch_head_bitmap(const int32_t *row_ptr, const int32_t *labels,
+                              int nnz, int B, int64_t label_offset, int H,
+                              uint32_t *bm, int bm_words, hipStream_t st);
+
+// fp32 (VALU) path.
+struct F32Args {
+    const float *X;
+    const int32_t *idx;
+    const float *W;
+    float *Z;
+    float *dZ;                 // given or workspace
+    float *dW;
+    float *dX;
+    const int32_t *row_ptr;
+    const int32_t *labels;
+    int64_t label_offset;
+    float *loss;
+    float s;
+    int B, D, G, F;
+    int64_t L, Ng;
+};
+hipError_t launch_f32_tail_logits(const F32Args &a, bool store_z, bool bce,
+                                  bool loss, hipStream_t st);
+hipError_t launch_f32_tail_dw(const F32Args &a, hipStream_t st);
+hipError_t launch_f32_tail_dx(const F32Args &a, hipStream_t st);
+hipError_t launch_f32_head_logits(const F32Args &a, bool store_z, bool bce,
+                                  bool loss, hipStream_t st);
+hipError_t launch_f32_head_dw(const F32Args &a, hipStream_t st);
+hipError_t launch_f32_head_dx(const F32Args &a, hipStream_t st);
+
+// utilities
+hipError_t launch_validate(const int32_t *idx, int64_t Ng, int F, int D,
+                           int32_t *first_bad, hipStream_t st);
+hipError_t launch_topk_merge(int B, int K, const float *av, const int32_t *ai,
+                             const float *bv, const int32_t *bi, float *ov,
+                             int32_t *oi, hipStream_t st);
+
+}  // namespace haste

@@ -1,0 +1,318 @@
+"""Thin Python binding of libhaste (include/haste.h), same names as the C ABI.
+
+Argument marshalling only: shapes and dtypes are read from torch tensors,
+device pointers and the current HIP stream are passed to the C entry points,
+and a workspace tensor is allocated when the caller does not bring one.
+Every step of the layer runs in the library's HIP kernels; if the library is
+missing, importing this module fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhaste.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "haste.h")
+
+HASTE_OK, HASTE_ERR_INVALID, HASTE_ERR_UNSUPPORTED, HASTE_ERR_WORKSPACE, HASTE_ERR_HIP = range(5)
+HASTE_F32, HASTE_BF16 = 0, 1
+
+
+class HasteError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"haste status {status}: {msg}")
+        self.status = status
+
+
+class TailDesc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("D", ctypes.c_int32), ("L", ctypes.c_int64),
+                ("G", ctypes.c_int32), ("F", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class HeadDesc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("D", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+class BceStruct(ctypes.Structure):
+    _fields_ = [("row_ptr", ctypes.c_void_p), ("labels", ctypes.c_void_p),
+                ("nnz", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+                ("label_offset", ctypes.c_int64), ("grad_scale", ctypes.c_float),
+                ("reserved1", ctypes.c_int32), ("loss", ctypes.c_void_p),
+                ("topk", ctypes.c_int32), ("reserved2", ctypes.c_int32),
+                ("topk_val", ctypes.c_void_p), ("topk_idx", ctypes.c_void_p)]
+
+
+_lib = None
+_vp, _sz, _i32, _i64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64
+_PD = ctypes.POINTER(TailDesc)
+_PH = ctypes.POINTER(HeadDesc)
+_PB = ctypes.POINTER(BceStruct)
+
+_SIGS = {
+    "haste_abi_version": (ctypes.c_int, []),
+    "haste_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "haste_last_error": (ctypes.c_char_p, []),
+    "haste_tail_layout": (ctypes.c_int, [_PD, ctypes.POINTER(ctypes.c_int64)]),
+    "haste_tail_workspace_bytes": (_sz, [_PD, _PB]),
+    "haste_head_workspace_bytes": (_sz, [_PH, _PB]),
+    "haste_tail_fwd": (ctypes.c_int, [_PD, _vp, _vp, _vp, _vp, _PB, _vp, _sz, _vp]),
+    "haste_tail_bwd": (ctypes.c_int, [_PD, _vp, _vp, _vp, _vp, _PB, _vp, _vp, ctypes.c_int,
+                                      _vp, _sz, _vp]),
+    "haste_tail_step": (ctypes.c_int, [_PD, _vp, _vp, _vp, _PB, _vp, _vp, ctypes.c_int, _vp,
+                                       _sz, _vp]),
+    "haste_head_fwd": (ctypes.c_int, [_PH, _vp, _vp, _vp, _PB, _vp, _sz, _vp]),
+    "haste_head_bwd": (ctypes.c_int, [_PH, _vp, _vp, _vp, _PB, _vp, _vp, ctypes.c_int, _vp,
+                                      _sz, _vp]),
+    "haste_head_step": (ctypes.c_int, [_PH, _vp, _vp, _PB, _vp, _vp, ctypes.c_int, _vp, _sz,
+                                       _vp]),
+    "haste_tail_group_positives": (ctypes.c_int, [_PD, _PB, _vp, _vp, _vp, _sz, _vp]),
+    "haste_tail_validate": (ctypes.c_int, [_PD, _vp, _vp, _vp]),
+    "haste_topk_merge": (ctypes.c_int, [_i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+}
+
+
+def lib():
+    """Load libhaste.so (built in-tree by sparse_output_layer_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m sparse_output_layer_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def header_functions() -> list[str]:
+    """Entry-point names declared in include/haste.h."""
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(haste_[a-z_0-9]+)\s*\(", txt)))
+
+
+def _check(status: int):
+    if status != HASTE_OK:
+        raise HasteError(status, lib().haste_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return HASTE_BF16
+    if t.dtype == torch.float32:
+        return HASTE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _need(t: torch.Tensor, name: str, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+@dataclass
+class Bce:
+    """Positives (row-CSR, global label ids) and BCE options for one call."""
+    row_ptr: torch.Tensor            # int32, B+1, device
+    labels: torch.Tensor             # int32, nnz, device
+    label_offset: int = 0
+    grad_scale: float = 1.0
+    loss: Optional[torch.Tensor] = None   # float32 scalar (1 element), device
+
+    def struct(self) -> BceStruct:
+        _need(self.row_ptr, "row_ptr", torch.int32)
+        _need(self.labels, "labels", torch.int32)
+        if self.loss is not None:
+            _need(self.loss, "loss", torch.float32)
+        s = BceStruct()
+        s.row_ptr = self.row_ptr.data_ptr()
+        s.labels = self.labels.data_ptr() if self.labels.numel() else None
+        s.nnz = int(self.labels.numel())
+        s.label_offset = int(self.label_offset)
+        s.grad_scale = float(self.grad_scale)
+        s.loss = self.loss.data_ptr() if self.loss is not None else None
+        s.topk = 0
+        return s
+
+
+def _bref(bce: Optional[Bce]):
+    return None if bce is None else ctypes.pointer(bce.struct())
+
+
+def tail_desc(X: torch.Tensor, idx: torch.Tensor, L: int, G: int) -> TailDesc:
+    B, D = X.shape
+    return TailDesc(B=B, D=D, L=int(L), G=int(G), F=int(idx.shape[1]), dtype=_dtype_code(X))
+
+
+def head_desc(X: torch.Tensor, Wh: torch.Tensor) -> HeadDesc:
+    B, D = X.shape
+    return HeadDesc(B=B, D=D, H=int(Wh.shape[0]), dtype=_dtype_code(X))
+
+
+def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]):
+    if nbytes == 0:
+        return None, 0
+    if ws is not None and ws.numel() >= nbytes:
+        return ws, ws.numel()
+    t = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return t, nbytes
+
+
+# ----------------------------------------------------------- entry points
+def haste_abi_version() -> int:
+    return lib().haste_abi_version()
+
+
+def haste_tail_layout(L: int, G: int, F: int, B: int = 1, D: int = 1) -> dict:
+    d = TailDesc(B=B, D=max(D, F), L=L, G=G, F=F, dtype=HASTE_BF16)
+    out = (ctypes.c_int64 * 4)()
+    _check(lib().haste_tail_layout(ctypes.byref(d), out))
+    return {"n_groups": out[0], "index_count": out[1], "weight_rows": out[2],
+            "last_group_live": out[3]}
+
+
+def haste_tail_workspace_bytes(X, idx, L, G, bce: Optional[Bce] = None) -> int:
+    return lib().haste_tail_workspace_bytes(ctypes.byref(tail_desc(X, idx, L, G)), _bref(bce))
+
+
+def haste_head_workspace_bytes(X, Wh, bce: Optional[Bce] = None) -> int:
+    return lib().haste_head_workspace_bytes(ctypes.byref(head_desc(X, Wh)), _bref(bce))
+
+
+def _tail_in(X, idx, W):
+    _need(X, "X")
+    _need(idx, "idx", torch.int32)
+    _need(W, "W", X.dtype)
+
+
+def haste_tail_fwd(X, idx, W, L, G, Z=None, bce: Optional[Bce] = None, workspace=None):
+    _tail_in(X, idx, W)
+    if Z is not None:
+        _need(Z, "Z", X.dtype)
+    d = tail_desc(X, idx, L, G)
+    b = _bref(bce)
+    ws, nb = _workspace(lib().haste_tail_workspace_bytes(ctypes.byref(d), b), X.device, workspace)
+    _check(lib().haste_tail_fwd(ctypes.byref(d), _ptr(X), _ptr(idx), _ptr(W), _ptr(Z), b,
+                                _ptr(ws), nb, _stream()))
+    return Z
+
+
+def haste_tail_bwd(X, idx, W, L, G, dW, dX, dZ=None, bce: Optional[Bce] = None,
+                   accumulate_dX=False, workspace=None):
+    _tail_in(X, idx, W)
+    _need(dW, "dW", X.dtype)
+    _need(dX, "dX", torch.float32)
+    if dZ is not None:
+        _need(dZ, "dZ", X.dtype)
+    d = tail_desc(X, idx, L, G)
+    b = None if dZ is not None else _bref(bce)
+    ws, nb = _workspace(lib().haste_tail_workspace_bytes(ctypes.byref(d), b), X.device, workspace)
+    _check(lib().haste_tail_bwd(ctypes.byref(d), _ptr(X), _ptr(idx), _ptr(W), _ptr(dZ), b,
+                                _ptr(dW), _ptr(dX), int(bool(accumulate_dX)), _ptr(ws), nb,
+                                _stream()))
+
+
+def haste_tail_step(X, idx, W, L, G, bce: Bce, dW, dX, accumulate_dX=False, workspace=None):
+    _tail_in(X, idx, W)
+    _need(dW, "dW", X.dtype)
+    _need(dX, "dX", torch.float32)
+    d = tail_desc(X, idx, L, G)
+    b = _bref(bce)
+    ws, nb = _workspace(lib().haste_tail_workspace_bytes(ctypes.byref(d), b), X.device, workspace)
+    _check(lib().haste_tail_step(ctypes.byref(d), _ptr(X), _ptr(idx), _ptr(W), b, _ptr(dW),
+                                 _ptr(dX), int(bool(accumulate_dX)), _ptr(ws), nb, _stream()))
+
+
+def haste_head_fwd(X, Wh, Zh=None, bce: Optional[Bce] = None, workspace=None):
+    _need(X, "X")
+    _need(Wh, "Wh", X.dtype)
+    if Zh is not None:
+        _need(Zh, "Zh", X.dtype)
+    d = head_desc(X, Wh)
+    b = _bref(bce)
+    ws, nb = _workspace(lib().haste_head_workspace_bytes(ctypes.byref(d), b), X.device, workspace)
+    _check(lib().haste_head_fwd(ctypes.byref(d), _ptr(X), _ptr(Wh), _ptr(Zh), b, _ptr(ws), nb,
+                                _stream()))
+    return Zh
+
+
+def haste_head_bwd(X, Wh, dWh, dX, dZh=None, bce: Optional[Bce] = None, accumulate_dX=False,
+                   workspace=None):
+    _need(X, "X")
+    _need(Wh, "Wh", X.dtype)
+    _need(dWh, "dWh", X.dtype)
+    _need(dX, "dX", torch.float32)
+    if dZh is not None:
+        _need(dZh, "dZh", X.dtype)
+    d = head_desc(X, Wh)
+    b = None if dZh is not None else _bref(bce)
+    ws, nb = _workspace(lib().haste_head_workspace_bytes(ctypes.byref(d), b), X.device, workspace)
+    _check(lib().haste_head_bwd(ctypes.byref(d), _ptr(X), _ptr(Wh), _ptr(dZh), b, _ptr(dWh),
+                                _ptr(dX), int(bool(accumulate_dX)), _ptr(ws), nb, _stream()))
+
+
+def haste_head_step(X, Wh, bce: Bce, dWh, dX, accumulate_dX=False, workspace=None):
+    _need(X, "X")
+    _need(Wh, "Wh", X.dtype)
+    _need(dWh, "dWh", X.dtype)
+    _need(dX, "dX", torch.float32)
+    d = head_desc(X, Wh)
+    b = _bref(bce)
+    ws, nb = _workspace(lib().haste_head_workspace_bytes(ctypes.byref(d), b), X.device, workspace)
+    _check(lib().haste_head_step(ctypes.byref(d), _ptr(X), _ptr(Wh), b, _ptr(dWh), _ptr(dX),
+                                 int(bool(accumulate_dX)), _ptr(ws), nb, _stream()))
+
+
+def haste_tail_group_positives(B, D, L, G, F, bce: Bce, dtype=torch.bfloat16, workspace=None):
+    d = TailDesc(B=B, D=D, L=L, G=G, F=F,
+                 dtype=HASTE_BF16 if dtype == torch.bfloat16 else HASTE_F32)
+    b = _bref(bce)
+    dev = bce.row_ptr.device
+    ng = (L + G - 1) // G
+    grp_ptr = torch.empty(ng + 1, dtype=torch.int32, device=dev)
+    ent = torch.empty(max(1, bce.labels.numel()), dtype=torch.int32, device=dev)
+    ws, nb = _workspace(lib().haste_tail_workspace_bytes(ctypes.byref(d), b), dev, workspace)
+    _check(lib().haste_tail_group_positives(ctypes.byref(d), b, _ptr(grp_ptr), _ptr(ent),
+                                            _ptr(ws), nb, _stream()))
+    return grp_ptr, ent
+
+
+def haste_tail_validate(idx, D, L, G) -> torch.Tensor:
+    _need(idx, "idx", torch.int32)
+    d = TailDesc(B=1, D=D, L=L, G=G, F=int(idx.shape[1]), dtype=HASTE_BF16)
+    out = torch.empty(1, dtype=torch.int32, device=idx.device)
+    _check(lib().haste_tail_validate(ctypes.byref(d), _ptr(idx), _ptr(out), _stream()))
+    return out
+
+
+def haste_topk_merge(a_val, a_idx, b_val, b_idx):
+    B, K = a_val.shape
+    for t, n in ((a_val, "a_val"), (b_val, "b_val")):
+        _need(t, n, torch.float32)
+    for t, n in ((a_idx, "a_idx"), (b_idx, "b_idx")):
+        _need(t, n, torch.int32)
+    ov = torch.empty_like(a_val)
+    oi = torch.empty_like(a_idx)
+    _check(lib().haste_topk_merge(B, K, _ptr(a_val), _ptr(a_idx), _ptr(b_val), _ptr(b_idx),
+                                  _ptr(ov), _ptr(oi), _stream()))
+    return ov, oi

@@ -1,0 +1,98 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every entry point include/haste.h declares, reports the storage layout the
+oracle defines, sizes workspaces, and rejects bad arguments before anything
+is enqueued (no compute call runs here)."""
+import ctypes
+
+import pytest
+
+import oracle
+from sparse_output_layer_amd import haste as H
+
+
+@pytest.fixture(scope="module")
+def L():
+    return H.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = H.header_functions()
+    assert "haste_tail_fwd" in names and "haste_tail_step" in names
+    missing = [n for n in names if not hasattr(L, n)]
+    assert missing == []
+    assert L.haste_abi_version() == 1
+    for s in range(5):
+        assert L.haste_status_string(s)
+
+
+@pytest.mark.parametrize("Lb,G,F", [(1024, 16, 16), (662000, 16, 128), (662000, 64, 128),
+                                    (2984000, 32, 128), (8600000, 64, 64), (7, 3, 5),
+                                    (1, 64, 32)])
+def test_layout_matches_oracle_bit_exact(Lb, G, F):
+    got = H.haste_tail_layout(Lb, G, F)
+    assert got == oracle.layout(Lb, G, F)
+
+
+def _desc(**kw):
+    d = dict(B=8, D=64, L=1024, G=16, F=32, dtype=H.HASTE_BF16)
+    d.update(kw)
+    return H.TailDesc(**d)
+
+
+def test_workspace_sizes(L):
+    d = _desc()
+    n0 = L.haste_tail_workspace_bytes(ctypes.byref(d), None)
+    b = H.BceStruct(nnz=10000)
+    n1 = L.haste_tail_workspace_bytes(ctypes.byref(d), ctypes.byref(b))
+    assert n0 > 0 and n1 >= n0 + 10000 * 4 - 256
+    # unsupported shape -> 0
+    assert L.haste_tail_workspace_bytes(ctypes.byref(_desc(G=8)), None) == 0
+    h = H.HeadDesc(B=8, D=64, H=128, dtype=H.HASTE_BF16)
+    assert L.haste_head_workspace_bytes(ctypes.byref(h), None) >= 8 * 128 * 2
+
+
+def _status(L, d, X=0x1000, idx=0x1000, W=0x1000, Z=0x1000, bce=None, ws=None, nb=0):
+    return L.haste_tail_fwd(ctypes.byref(d) if d is not None else None, X, idx, W, Z, bce,
+                            ws, nb, None)
+
+
+def test_argument_errors_fail_before_launch(L):
+    assert _status(L, None) == H.HASTE_ERR_INVALID
+    assert b"NULL" in L.haste_last_error()
+    assert _status(L, _desc(B=0)) == H.HASTE_ERR_INVALID
+    assert _status(L, _desc(F=128, D=64)) == H.HASTE_ERR_INVALID      # F > D
+    assert _status(L, _desc(dtype=7)) == H.HASTE_ERR_INVALID
+    assert _status(L, _desc(G=8)) == H.HASTE_ERR_UNSUPPORTED
+    assert _status(L, _desc(F=48)) == H.HASTE_ERR_UNSUPPORTED
+    assert _status(L, _desc(D=4096, F=128)) == H.HASTE_ERR_UNSUPPORTED
+    assert _status(L, _desc(), X=0) == H.HASTE_ERR_INVALID
+    assert _status(L, _desc(), X=0x1002) == H.HASTE_ERR_INVALID      # misaligned bf16
+    assert _status(L, _desc(), Z=0, bce=None) == H.HASTE_ERR_INVALID  # nothing to do
+    # workspace: needed but missing / too small / misaligned
+    assert _status(L, _desc()) == H.HASTE_ERR_WORKSPACE
+    assert _status(L, _desc(), ws=0x1000, nb=16) == H.HASTE_ERR_WORKSPACE
+    assert _status(L, _desc(), ws=0x1010, nb=1 << 30) == H.HASTE_ERR_WORKSPACE
+    # bce checks
+    b = H.BceStruct(nnz=-1, row_ptr=0x1000)
+    assert _status(L, _desc(), bce=ctypes.byref(b)) == H.HASTE_ERR_INVALID
+    b = H.BceStruct(nnz=5, row_ptr=0x1000, labels=None)
+    assert _status(L, _desc(), bce=ctypes.byref(b)) == H.HASTE_ERR_INVALID
+    b = H.BceStruct(nnz=5, row_ptr=0x1000, labels=0x1000, topk=5)
+    assert _status(L, _desc(), bce=ctypes.byref(b)) == H.HASTE_ERR_UNSUPPORTED
+    # fp32 accepts any G / F
+    d = _desc(dtype=H.HASTE_F32, G=3, F=7)
+    assert _status(L, d) == H.HASTE_ERR_WORKSPACE
+
+
+def test_head_and_step_argument_errors(L):
+    h = H.HeadDesc(B=8, D=60, H=128, dtype=H.HASTE_BF16)       # D % 8 != 0
+    assert L.haste_head_fwd(ctypes.byref(h), 0x1000, 0x1000, 0x1000, None, None, 0, None) == \
+        H.HASTE_ERR_UNSUPPORTED
+    h = H.HeadDesc(B=0, D=64, H=128, dtype=H.HASTE_BF16)
+    assert L.haste_head_fwd(ctypes.byref(h), 0x1000, 0x1000, 0x1000, None, None, 0, None) == \
+        H.HASTE_ERR_INVALID
+    d = _desc()
+    assert L.haste_tail_step(ctypes.byref(d), 0x1000, 0x1000, 0x1000, None, 0x1000, 0x1000, 0,
+                             None, 0, None) == H.HASTE_ERR_INVALID       # bce required
+    assert L.haste_topk_merge(4, 0, 1, 1, 1, 1, 1, 1, None) == H.HASTE_ERR_INVALID
+    assert L.haste_tail_validate(None, 0x1000, 0x1000, None) == H.HASTE_ERR_INVALID

@@ -1,0 +1,218 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Small shapes are compared element by element; they span several MFMA tiles,
+several 64-row chunks and ragged tails (rows, labels, features).  Integer
+outputs (group-major positives, index validation, merged top-K ids) must be
+bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from _gpu import DEV, Dev, check, check_loss, dev_array, to_f64
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    dict(B=40, D=96, H=48, L=200, G=16, F=32),
+    dict(B=64, D=128, H=64, L=512, G=32, F=64),
+    dict(B=70, D=200, H=56, L=300, G=64, F=128),
+    dict(B=128, D=768, H=256, L=2000, G=16, F=128),
+    dict(B=33, D=1024, H=96, L=700, G=64, F=64, idx_dist="skew10"),
+    dict(B=65, D=768, H=128, L=1000, G=64, F=128, pos_per_row=7),
+    dict(B=130, D=768, H=136, L=1500, G=32, F=128),
+]
+
+
+def _ids(c):
+    return "B{B}-D{D}-L{L}-G{G}-F{F}".format(**c)
+
+
+@pytest.fixture(scope="module")
+def H():
+    from sparse_output_layer_amd import haste
+    haste.lib()
+    return haste
+
+
+def _ref(inp):
+    c = inp.cfg
+    return oracle.step(inp.X_f64(), inp.Wh_f64(), inp.idx, inp.W_f64(), inp.row_ptr,
+                       inp.labels, c.L, c.G, 1.0 / c.B)
+
+
+@pytest.mark.parametrize("case", CASES, ids=[_ids(c) for c in CASES])
+def test_bf16_tail_and_head(H, case):
+    print("case", case, flush=True)
+    inp = wl.make_inputs(wl.tiny("par", **case))
+    c = inp.cfg
+    s = 1.0 / c.B
+    r = _ref(inp)
+    d = Dev(inp)
+    bf = torch.bfloat16
+
+    # tail forward: logits and loss
+    Z = torch.empty(c.B, c.L, dtype=bf, device=DEV)
+    b = d.bce(c.H, s)
+    H.haste_tail_fwd(d.X, d.idx, d.W, c.L, c.G, Z=Z, bce=b)
+    torch.cuda.synchronize()
+    check("tail Z", to_f64(Z), r.Zt, r.Zt_abs, "bf16", nterms=c.F)
+    check_loss("tail fwd loss", b.loss.item(), r.loss_tail, "bf16")
+
+    # fused tail step
+    dW = torch.full_like(d.W, 7.0)
+    dX = torch.full((c.B, c.D), 3.0, dtype=torch.float32, device=DEV)
+    b = d.bce(c.H, s)
+    H.haste_tail_step(d.X, d.idx, d.W, c.L, c.G, b, dW, dX)
+    torch.cuda.synchronize()
+    check_loss("tail step loss", b.loss.item(), r.loss_tail, "bf16")
+    check("tail dW", to_f64(dW[:c.L]), r.dWt, r.dWt_abs, "bf16", nterms=c.B)
+    assert torch.all(dW[c.L:] == 0), "padded label rows of dW must be exactly zero"
+    ng = c.n_groups
+    check("tail dX", to_f64(dX), r.dX_tail, r.dX_tail_abs, "bf16", nterms=ng * c.G)
+    # deterministic weight gradient (no atomics on dW)
+    dW2 = torch.empty_like(d.W)
+    dX2 = torch.empty_like(dX)
+    H.haste_tail_step(d.X, d.idx, d.W, c.L, c.G, d.bce(c.H, s, loss=False), dW2, dX2)
+    torch.cuda.synchronize()
+    assert torch.equal(dW, dW2)
+
+    # tail backward, recomputing dz from the positives (no loss added)
+    dW3 = torch.empty_like(d.W)
+    dX3 = torch.zeros_like(dX)
+    b3 = d.bce(c.H, s)
+    H.haste_tail_bwd(d.X, d.idx, d.W, c.L, c.G, dW3, dX3, bce=b3)
+    torch.cuda.synchronize()
+    assert b3.loss.item() == 0.0
+    assert torch.equal(dW3, dW)
+    check("tail bwd dX", to_f64(dX3), r.dX_tail, r.dX_tail_abs, "bf16", nterms=ng * c.G)
+
+    # tail backward with a given dZ (bf16), accumulating into dX
+    dZ_bits = wl.bf16_bits_from_f32(r.dZt.astype(np.float32))
+    dZ64 = wl.f64_from_bf16_bits(dZ_bits)
+    dZt = dev_array(dZ_bits, "bf16")
+    dW4 = torch.empty_like(d.W)
+    dX4 = torch.ones_like(dX)
+    H.haste_tail_bwd(d.X, d.idx, d.W, c.L, c.G, dW4, dX4, dZ=dZt, accumulate_dX=True)
+    torch.cuda.synchronize()
+    rW, rWa = oracle.tail_dW(inp.X_f64(), inp.idx, dZ64, c.L, c.G)
+    rX, rXa = oracle.tail_dX(inp.idx, inp.W_f64(), dZ64, c.D, c.L, c.G)
+    check("tail bwd(dZ) dW", to_f64(dW4[:c.L]), rW, rWa, "bf16", nterms=c.B)
+    check("tail bwd(dZ) dX", to_f64(dX4) - 1.0, rX, rXa, "bf16", nterms=ng * c.G)
+
+    # head: forward logits + loss, fused step accumulating into the tail's dX
+    Zh = torch.empty(c.B, c.H, dtype=bf, device=DEV)
+    bh = d.bce(0, s)
+    H.haste_head_fwd(d.X, d.Wh, Zh=Zh, bce=bh)
+    torch.cuda.synchronize()
+    check("head Z", to_f64(Zh), r.Zh, r.Zh_abs, "bf16", nterms=c.D)
+    check_loss("head loss", bh.loss.item(), r.loss_head, "bf16")
+    dWh = torch.empty_like(d.Wh)
+    bh = d.bce(0, s)
+    H.haste_head_step(d.X, d.Wh, bh, dWh, dX, accumulate_dX=True)
+    torch.cuda.synchronize()
+    check_loss("head step loss", bh.loss.item(), r.loss_head, "bf16")
+    check("head dW", to_f64(dWh), r.dWh, r.dWh_abs, "bf16", nterms=c.B)
+    check("step dX (head+tail)", to_f64(dX), r.dX, r.dX_abs, "bf16", nterms=ng * c.G + c.H)
+    # head backward with a given dZh
+    dZh_bits = wl.bf16_bits_from_f32(r.dZh.astype(np.float32))
+    dZh64 = wl.f64_from_bf16_bits(dZh_bits)
+    dWh2 = torch.empty_like(d.Wh)
+    dXh = torch.empty_like(dX)
+    H.haste_head_bwd(d.X, d.Wh, dWh2, dXh, dZh=dev_array(dZh_bits, "bf16"))
+    torch.cuda.synchronize()
+    rWh, rWha = oracle.head_dW(inp.X_f64(), dZh64)
+    rXh, rXha = oracle.head_dX(inp.Wh_f64(), dZh64)
+    check("head bwd(dZ) dW", to_f64(dWh2), rWh, rWha, "bf16", nterms=c.B)
+    check("head bwd(dZ) dX", to_f64(dXh), rXh, rXha, "bf16", nterms=c.H)
+
+    # integers: group-major positives, bit-exact
+    gp, ent = H.haste_tail_group_positives(c.B, c.D, c.L, c.G, c.F, d.bce(c.H, s))
+    rp, re_ = oracle.group_positives(inp.row_ptr, inp.labels, c.H, c.L, c.G)
+    torch.cuda.synchronize()
+    assert np.array_equal(gp.cpu().numpy(), rp)
+    assert np.array_equal(ent.cpu().numpy()[:re_.size], re_)
+
+
+def test_fp32_c1_full(H):
+    """The tiny fp32 workload, every output, at the fp32 tolerance."""
+    inp = wl.make_inputs("c1")
+    c = inp.cfg
+    s = 1.0 / c.B
+    r = _ref(inp)
+    d = Dev(inp)
+    f = torch.float32
+    Z = torch.empty(c.B, c.L, dtype=f, device=DEV)
+    b = d.bce(c.H, s)
+    H.haste_tail_fwd(d.X, d.idx, d.W, c.L, c.G, Z=Z, bce=b)
+    dW = torch.empty_like(d.W)
+    dX = torch.empty(c.B, c.D, dtype=f, device=DEV)
+    b2 = d.bce(c.H, s)
+    H.haste_tail_step(d.X, d.idx, d.W, c.L, c.G, b2, dW, dX)
+    Zh = torch.empty(c.B, c.H, dtype=f, device=DEV)
+    bh = d.bce(0, s)
+    H.haste_head_fwd(d.X, d.Wh, Zh=Zh, bce=bh)
+    dWh = torch.empty_like(d.Wh)
+    bh2 = d.bce(0, s)
+    H.haste_head_step(d.X, d.Wh, bh2, dWh, dX, accumulate_dX=True)
+    torch.cuda.synchronize()
+    check("Z", to_f64(Z), r.Zt, r.Zt_abs, "f32")
+    check_loss("tail loss", b.loss.item(), r.loss_tail, "f32")
+    check_loss("tail step loss", b2.loss.item(), r.loss_tail, "f32")
+    check("dW", to_f64(dW), r.dWt, r.dWt_abs, "f32")
+    check("Zh", to_f64(Zh), r.Zh, r.Zh_abs, "f32")
+    check_loss("head loss", bh.loss.item(), r.loss_head, "f32")
+    check("dWh", to_f64(dWh), r.dWh, r.dWh_abs, "f32")
+    check("dX", to_f64(dX), r.dX, r.dX_abs, "f32")
+
+
+def test_fp32_ragged_groups_of_three(H):
+    inp = wl.make_inputs("c1", L=203, G=3, F=7)
+    c = inp.cfg
+    s = 0.37
+    r = oracle.step(inp.X_f64(), inp.Wh_f64(), inp.idx, inp.W_f64(), inp.row_ptr, inp.labels,
+                    c.L, c.G, s)
+    d = Dev(inp)
+    dW = torch.empty_like(d.W)
+    dX = torch.empty(c.B, c.D, dtype=torch.float32, device=DEV)
+    b = d.bce(c.H, s)
+    H.haste_tail_step(d.X, d.idx, d.W, c.L, c.G, b, dW, dX)
+    torch.cuda.synchronize()
+    check("dW", to_f64(dW[:c.L]), r.dWt, r.dWt_abs, "f32")
+    assert torch.all(dW[c.L:] == 0)
+    check("dX", to_f64(dX), r.dX_tail, r.dX_tail_abs, "f32")
+    check_loss("loss", b.loss.item(), r.loss_tail, "f32")
+
+
+def test_validate_indices(H):
+    inp = wl.make_inputs(wl.tiny("v", L=640, G=16, F=32, D=96))
+    idx = inp.idx.copy()
+    t = torch.from_numpy(idx).to(DEV)
+    assert H.haste_tail_validate(t, 96, 640, 16).item() == -1
+    bad = idx.copy()
+    bad[17, 3], bad[17, 4] = bad[17, 4], bad[17, 3]      # unsorted row
+    bad[30, 0] = 96                                      # out of range
+    t = torch.from_numpy(bad).to(DEV)
+    assert H.haste_tail_validate(t, 96, 640, 16).item() == 17
+    bad[17] = idx[17]
+    t = torch.from_numpy(bad).to(DEV)
+    assert H.haste_tail_validate(t, 96, 640, 16).item() == 30
+
+
+def test_topk_merge_exact(H):
+    rng = np.random.default_rng(4)
+    B, K = 37, 5
+    va = np.round(rng.standard_normal((B, 40)) * 2) / 2
+    ids = np.arange(80).reshape(2, 40)
+    # each side's own top-K (oracle order), then merge both on the GPU
+    av, ai = oracle.topk(va, K, id_offset=0)
+    vb = np.round(rng.standard_normal((B, 40)) * 2) / 2
+    bv, bi = oracle.topk(vb, K, id_offset=40)
+    ov, oi = H.haste_topk_merge(*(torch.tensor(x, dtype=dt, device=DEV) for x, dt in
+                                  ((av, torch.float32), (ai, torch.int32),
+                                   (bv, torch.float32), (bi, torch.int32))))
+    full = np.concatenate([va, vb], 1)
+    rv, ri = oracle.topk(full, K, ids=ids.reshape(-1))
+    assert np.array_equal(oi.cpu().numpy(), ri)
+    assert np.array_equal(ov.cpu().numpy(), rv.astype(np.float32))
