@@ -1,0 +1,246 @@
+#!/usr/bin/env python3
+"""Training-step throughput of the group-shared fixed fan-in output layer on
+one MI355X: head (dense classifier) + tail (group-shared sparse layer),
+forward, fused sigmoid-BCE over sparse positives, and every gradient.
+
+Workload (default): the 670K-label shape with groups of 16 -- B=512 rows,
+D=768 bf16 features, H=8,192 head labels, L=662,000 tail labels in groups of
+G=16 sharing F=128 fan-in indices, W ~ N(0, 0.02), 5 Zipf(1.1) positives per
+row; synthetic, seeded, resident in HBM before timing starts.
+
+One step = haste_head_step + haste_tail_prepare + haste_tail_step_dw +
+haste_tail_step_dx (the split form of haste_tail_step), all on one stream.
+W warm-up steps, then K timed steps between device synchronisations; HIP
+events around every call give each kernel's average duration inside the
+timed region.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+METRIC = "tail+head fwd+bwd samples/sec at 670K labels; % of HBM/MFMA roofline"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--config", default="c2", help="workload name in workloads.CONFIGS")
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="target CPU time of the oracle baseline sample (0 = skip)")
+    return p.parse_args()
+
+
+def algorithmic(cfg):
+    """Algorithmic flops and HBM bytes the method itself needs, per call."""
+    B, D, H, L, G, F = cfg.B, cfg.D, cfg.H, cfg.L, cfg.G, cfg.F
+    ng = (L + G - 1) // G
+    wbytes = ng * G * F * 2          # W (bf16, padded rows included)
+    idxb = ng * F * 4
+    xb, dxb = B * D * 2, B * D * 4
+    return {
+        "head_step": {"flops": 6 * B * D * H, "bytes": 2 * H * D * 2 + xb + dxb},
+        "tail_prepare": {"flops": 0, "bytes": 2 * xb},
+        # logits + weight gradient contractions; W read, dW written, idx, X
+        "tail_step_dw": {"flops": 4 * B * F * L, "bytes": 2 * wbytes + idxb + xb},
+        # input-gradient contraction; W read, idx, X, dX written
+        "tail_step_dx": {"flops": 2 * B * F * L, "bytes": wbytes + idxb + xb + dxb},
+    }
+
+
+def cpu_baseline(inp, seconds):
+    """The fp64 oracle, as it stands, on the host's cores: a full training
+    step over the first n tail groups and the first h head labels, timed and
+    scaled to the whole step."""
+    import numpy as np
+
+    import oracle
+    cfg = inp.cfg
+    G, B = cfg.G, cfg.B
+    nth = oracle.threads()
+    X = inp.X_f64()
+    s = 1.0 / B
+
+    def tail_time(n):
+        W = oracle_w(n)
+        t0 = time.perf_counter()
+        oracle.tail_step(X, inp.idx[:n], W, inp.row_ptr, inp.labels, cfg.H, n * G, G, s)
+        return time.perf_counter() - t0
+
+    def oracle_w(n):
+        import workloads as wl
+        return wl.f64_from_bf16_bits(inp.W[:n * G]) if cfg.dtype == "bf16" \
+            else inp.W[:n * G].astype(np.float64)
+
+    def head_time(h):
+        import workloads as wl
+        Wh = wl.f64_from_bf16_bits(inp.Wh[:h]) if cfg.dtype == "bf16" \
+            else inp.Wh[:h].astype(np.float64)
+        t0 = time.perf_counter()
+        Z, _ = oracle.head_logits(X, Wh, want_abs=False)
+        Y = oracle.positive_mask(inp.row_ptr, inp.labels, 0, h)
+        dz, lt = oracle.bce(Z, Y, s)
+        oracle.head_dW(X, dz, want_abs=False)
+        oracle.head_dX(Wh, dz, want_abs=False)
+        return time.perf_counter() - t0
+
+    ng = cfg.n_groups
+    n0 = min(ng, 8)
+    t0 = tail_time(n0)
+    n = int(min(ng, max(n0, n0 * (0.8 * seconds) / max(t0, 1e-6))))
+    tt = tail_time(n)
+    if tt < 0.4 * seconds and n < ng:   # first estimate was overhead-bound
+        n = int(min(ng, n * (0.8 * seconds) / max(tt, 1e-6)))
+        tt = tail_time(n)
+    h0 = min(cfg.H, 64)
+    th0 = head_time(h0)
+    h = int(min(cfg.H, max(h0, h0 * (0.2 * seconds) / max(th0, 1e-6))))
+    th = head_time(h)
+    full = tt * ng / n + th * cfg.H / h
+    return {"value": B / full, "unit": "samples/s", "cores": nth, "kind": "oracle",
+            "sample": f"fp64 oracle training step on the first {n} of {ng} tail groups "
+                      f"({tt:.1f} s) and the first {h} of {cfg.H} head labels ({th:.1f} s), "
+                      f"scaled by group/label count to the full step ({full:.1f} s per step)"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
+              "the layer's multi-GPU sharding is described in DESIGN.md, not launched.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import workloads as wl
+    from sparse_output_layer_amd import haste as H
+
+    cfg = wl.CONFIGS[args.config]
+    t_gen = time.perf_counter()
+    inp = wl.make_inputs(cfg)
+    t_gen = time.perf_counter() - t_gen
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    assert cfg.dtype == "bf16"
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    X, Wh, W = bf(inp.X), bf(inp.Wh), bf(inp.W)
+    idx = torch.from_numpy(inp.idx).to(dev)
+    rp = torch.from_numpy(inp.row_ptr).to(dev)
+    lab = torch.from_numpy(inp.labels).to(dev)
+    B, D, L, G = cfg.B, cfg.D, cfg.L, cfg.G
+    s = 1.0 / B
+    loss = torch.zeros(1, dtype=torch.float32, device=dev)
+    bce_h = H.Bce(rp, lab, 0, s, loss)
+    bce_t = H.Bce(rp, lab, cfg.H, s, loss)
+    dX = torch.empty(B, D, dtype=torch.float32, device=dev)
+    dWh = torch.empty_like(Wh)
+    dW = torch.empty_like(W)
+    ws_t = torch.empty(H.haste_tail_workspace_bytes(X, idx, L, G, bce_t), dtype=torch.uint8,
+                       device=dev)
+    ws_h = torch.empty(max(256, H.haste_head_workspace_bytes(X, Wh, bce_h)), dtype=torch.uint8,
+                       device=dev)
+    names = ["head_step", "tail_prepare", "tail_step_dw", "tail_step_dx"]
+
+    def step(ev=None):
+        loss.zero_()
+        if ev is not None:
+            ev[0].record()
+        H.haste_head_step(X, Wh, bce_h, dWh, dX, workspace=ws_h)
+        if ev is not None:
+            ev[1].record()
+        H.haste_tail_prepare(X, idx, L, G, bce_t, ws_t)
+        if ev is not None:
+            ev[2].record()
+        H.haste_tail_step_dw(X, idx, W, L, G, bce_t, dW, ws_t)
+        if ev is not None:
+            ev[3].record()
+        H.haste_tail_step_dx(X, idx, W, L, G, bce_t, dX, ws_t, accumulate_dX=True)
+        if ev is not None:
+            ev[4].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record()
+    for k in range(args.steps):
+        step(evs[k])
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = t0.elapsed_time(t1) / args.steps
+    per = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) * 1e3
+           for i, n in enumerate(names)}          # microseconds
+    step_loss = loss.item()
+
+    alg = algorithmic(cfg)
+    tot_flops = sum(v["flops"] for v in alg.values())
+    tot_bytes = sum(v["bytes"] for v in alg.values())
+    tail_kernels = ["tail_step_dw", "tail_step_dx"]
+    dom = max(tail_kernels, key=lambda n: per[n])
+    a_tf = alg[dom]["flops"] / (per[dom] * 1e-6) / 1e12
+    kernels = {n: {"avg_us": round(per[n], 2),
+                   "tflops": round(alg[n]["flops"] / (per[n] * 1e-6) / 1e12, 1),
+                   "gbs": round(alg[n]["bytes"] / (per[n] * 1e-6) / 1e9, 1)} for n in names}
+    tail_us = per["tail_prepare"] + per["tail_step_dw"] + per["tail_step_dx"]
+    tail_tf = (alg["tail_step_dw"]["flops"] + alg["tail_step_dx"]["flops"]) / (tail_us * 1e-6) / 1e12
+    step_tf = tot_flops / (ms * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(B / (ms * 1e-3), 1),
+        "unit": "samples/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {cfg.note}; B={B} D={D} H={cfg.H} L={L} G={G} "
+                               f"F={cfg.F}, positives/row={cfg.pos_per_row} Zipf({cfg.zipf_s})",
+                   "global_batch": B, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(a_tf, 1),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(a_tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "algorithmic_flops_per_launch": alg[dom]["flops"],
+                     "avg_launch_us": round(per[dom], 2)},
+        "step_roofline": {"algorithmic_tflop": round(tot_flops / 1e12, 4),
+                          "algorithmic_gb": round(tot_bytes / 1e9, 4),
+                          "achieved_tflops": round(step_tf, 1),
+                          "frac_mfma": round(step_tf / PEAK_BF16_TFLOPS, 4),
+                          "tail_tflops": round(tail_tf, 1),
+                          "tail_frac_mfma": round(tail_tf / PEAK_BF16_TFLOPS, 4)},
+        "kernels": kernels,
+        "loss": step_loss,
+        "wall_s": round(wall, 3),
+        "gen_s": round(t_gen, 2),
+    }
+    if args.cpu_seconds > 0:
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

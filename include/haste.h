@@ -74,7 +74,7 @@ typedef enum { HASTE_F32 = 0, HASTE_BF16 = 1 } haste_dtype;
 
 /* Tail shape.  Supported: B >= 1, D >= F, F >= 1, L >= 1, G >= 1.
  * bf16 kernels additionally need G in {16, 32, 64}, F a multiple of 32 with
- * F <= 256, D <= 1536 and D*B small enough for int32 offsets; other shapes
+ * F <= 128 (F in {32, 64, 128}), D <= 1024; other shapes
  * return HASTE_ERR_UNSUPPORTED.  fp32 accepts any G and F. */
 typedef struct {
     int32_t B;      /* rows in the batch                    */
@@ -157,6 +157,28 @@ haste_status haste_tail_step(const haste_tail_desc *d, const void *X,
                              const haste_bce *bce, void *dW, float *dX,
                              int accumulate_dX, void *ws, size_t ws_bytes,
                              void *stream);
+
+/* Split form of haste_tail_step, for callers that time or overlap its
+ * parts.  haste_tail_prepare writes into ws the transposed X and the
+ * group-major positives.  haste_tail_step_dw (one kernel) then adds the
+ * loss and writes dW (gather + contraction + fused BCE + weight gradient);
+ * haste_tail_step_dx (one kernel, plus a fill of dX unless accumulating)
+ * adds the tail's dX.  Both read what haste_tail_prepare left in ws: call
+ * the three on one stream, prepare first, with the same descriptor, X, idx,
+ * W, bce and workspace; together they produce what haste_tail_step
+ * produces.  ws must not be reused by another call in between. */
+haste_status haste_tail_prepare(const haste_tail_desc *d, const void *X,
+                                const haste_bce *bce, void *ws,
+                                size_t ws_bytes, void *stream);
+haste_status haste_tail_step_dw(const haste_tail_desc *d, const void *X,
+                                const int32_t *idx, const void *W,
+                                const haste_bce *bce, void *dW, void *ws,
+                                size_t ws_bytes, void *stream);
+haste_status haste_tail_step_dx(const haste_tail_desc *d, const void *X,
+                                const int32_t *idx, const void *W,
+                                const haste_bce *bce, float *dX,
+                                int accumulate_dX, void *ws, size_t ws_bytes,
+                                void *stream);
 
 /* Head forward (Method item 2: dense classifier).  Zh (B x H) and/or the
  * fused BCE (loss, top-K). */

@@ -60,8 +60,8 @@ TailWs tail_ws(const haste_tail_desc *d, const haste_bce *bce) {
     size_t o = 0;
     if (d->dtype == HASTE_BF16) {
         w.xt = o;  o += al256((size_t)d->D * pad_rows(d->B) * 2);
-        w.cnt = o; o += al256((size_t)ng * 4);
-        w.ptr = o; o += al256((size_t)(ng + 1) * 4);
+        w.cnt = o; o += al256((size_t)(nnz > 0 ? nnz : 1) * 8 + 8);   // keys + count
+        w.ptr = o; o += al256((size_t)(ng + 4) * 4);   // +3: 16-byte reads of a pair
         w.ent = o; o += al256((size_t)(nnz > 0 ? nnz : 1) * 4);
     } else {
         w.cnt = o; o += al256((size_t)ng * 4);
@@ -98,7 +98,7 @@ haste_status check_tail(const haste_tail_desc *d) {
     if (d->dtype == HASTE_BF16) {
         if (!tail_bf16_supported(d->G, d->F, d->D))
             return fail(HASTE_ERR_UNSUPPORTED,
-                        "bf16 tail supports G in {16,32,64}, F in {32,64,128}, F <= D <= 1536 "
+                        "bf16 tail supports G in {16,32,64}, F in {32,64,128}, F <= D <= 1024 "
                         "(got G=%d F=%d D=%d)", d->G, d->F, d->D);
         if ((int64_t)d->B * d->G > (1 << 30))
             return fail(HASTE_ERR_UNSUPPORTED, "B*G too large");
@@ -179,7 +179,7 @@ haste_status bf16_prep(const haste_tail_desc *d, const void *X, const haste_bce 
                                d->D, pad_rows(d->B), st), "transpose X");
     if (bce) {
         TRY_HIP(launch_group_positives(bce->row_ptr, bce->labels, bce->nnz, d->B, bce->label_offset,
-                                       d->L, d->G, n_groups(d), (int32_t *)B8(ws, m.cnt),
+                                       d->L, d->G, n_groups(d), (long long *)B8(ws, m.cnt),
                                        (int32_t *)B8(ws, m.ptr), (int32_t *)B8(ws, m.ent), st),
                 "group positives");
     }
@@ -373,6 +373,73 @@ haste_status haste_tail_step(const haste_tail_desc *d, const void *X, const int3
     return HASTE_OK;
 }
 
+haste_status haste_tail_prepare(const haste_tail_desc *d, const void *X, const haste_bce *bce,
+                                void *ws, size_t ws_bytes, void *stream) {
+    g_err.clear();
+    TRY(check_tail(d));
+    TRY(need_al(X, d->dtype == HASTE_BF16 ? 16 : 4, "X"));
+    TRY(need(bce, "bce"));
+    TRY(check_bce(bce, d->B, true));
+    const TailWs m = tail_ws(d, bce);
+    TRY(check_ws(ws, ws_bytes, m.total));
+    if (d->dtype == HASTE_BF16) TRY(bf16_prep(d, X, bce, ws, m, S(stream)));
+    return HASTE_OK;  // the fp32 path needs no preparation
+}
+
+haste_status haste_tail_step_dw(const haste_tail_desc *d, const void *X, const int32_t *idx,
+                                const void *W, const haste_bce *bce, void *dW, void *ws,
+                                size_t ws_bytes, void *stream) {
+    g_err.clear();
+    TRY(tail_common(d, X, idx, W));
+    TRY(need(bce, "bce"));
+    TRY(check_bce(bce, d->B, true));
+    TRY(need_al(dW, d->dtype == HASTE_BF16 ? 8 : 4, "dW"));
+    const TailWs m = tail_ws(d, bce);
+    TRY(check_ws(ws, ws_bytes, m.total));
+    hipStream_t st = S(stream);
+    if (d->dtype == HASTE_BF16) {
+        TailArgs a = tail_args(d, X, idx, W, ws, m);
+        a.dW = (unsigned short *)dW;
+        a.s = bce->grad_scale;
+        a.loss = bce->loss;
+        TRY_HIP(launch_tail_t1(T1_DW_BCE, d->G, a, false, bce->loss != nullptr, st), "tail step dW");
+    } else {
+        F32Args a = f32_tail_args(d, X, idx, W, bce);
+        a.dW = (float *)dW;
+        a.dZ = (float *)B8(ws, m.dz);
+        TRY_HIP(launch_f32_tail_logits(a, false, true, bce->loss != nullptr, st), "tail step f32");
+        TRY_HIP(launch_f32_tail_dw(a, st), "tail dW f32");
+    }
+    return HASTE_OK;
+}
+
+haste_status haste_tail_step_dx(const haste_tail_desc *d, const void *X, const int32_t *idx,
+                                const void *W, const haste_bce *bce, float *dX,
+                                int accumulate_dX, void *ws, size_t ws_bytes, void *stream) {
+    g_err.clear();
+    TRY(tail_common(d, X, idx, W));
+    TRY(need(bce, "bce"));
+    TRY(check_bce(bce, d->B, true));
+    TRY(need_al(dX, 4, "dX"));
+    const TailWs m = tail_ws(d, bce);
+    TRY(check_ws(ws, ws_bytes, m.total));
+    hipStream_t st = S(stream);
+    TRY(zero_dx(dX, d->B, d->D, accumulate_dX, st));
+    if (d->dtype == HASTE_BF16) {
+        TailArgs a = tail_args(d, X, idx, W, ws, m);
+        a.dX = dX;
+        a.s = bce->grad_scale;
+        TRY_HIP(launch_tail_t2(d->G, false, a, st), "tail step dX");
+    } else {
+        F32Args a = f32_tail_args(d, X, idx, W, bce);
+        a.loss = nullptr;
+        a.dX = dX;
+        a.dZ = (float *)B8(ws, m.dz);
+        TRY_HIP(launch_f32_tail_dx(a, st), "tail dX f32");
+    }
+    return HASTE_OK;
+}
+
 // ------------------------------------------------------------------- head
 namespace {
 
@@ -542,7 +609,7 @@ haste_status haste_tail_group_positives(const haste_tail_desc *d, const haste_bc
     const TailWs m = tail_ws(d, bce);
     TRY(check_ws(ws, ws_bytes, m.total));
     TRY_HIP(launch_group_positives(bce->row_ptr, bce->labels, bce->nnz, d->B, bce->label_offset,
-                                   d->L, d->G, n_groups(d), (int32_t *)B8(ws, m.cnt), grp_ptr,
+                                   d->L, d->G, n_groups(d), (long long *)B8(ws, m.cnt), grp_ptr,
                                    entries, S(stream)),
             "group positives");
     return HASTE_OK;

@@ -8,6 +8,7 @@ namespace haste {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) short i16x4;
 typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
@@ -19,6 +20,12 @@ typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 // Output: lane l holds rows 4*(l/16)+i (i = 0..3) of column l % 16.
 __device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// 32x32 output, K = 16 bf16 per instruction.  A / B: lane l holds row / col
+// (l % 32) and K slots 8*(l/32) .. +7.  Output: register r of lane l holds
+// row 8*(r/4) + 4*(l/32) + r%4 of column l % 32.
+__device__ __forceinline__ f32x16 mfma32x32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 // 16x16 output, K = 16: lane l holds K slots 4*(l/16) .. +3.
 __device__ __forceinline__ f32x4 mfma16(i16x4 a, i16x4 b, f32x4 c) {
@@ -72,6 +79,33 @@ __device__ __forceinline__ BceOut bce_both(float z, float y, float s) {
     o.dz = s * (sig - y);
     o.loss = s * (lin + l1p);
     return o;
+}
+
+// Fast forms for the fused epilogue (hardware v_exp_f32 / v_rcp_f32 /
+// v_log_f32, about 1 ulp each).  sigmoid(z) from e = exp(-|z|):
+// r = 1/(1+e) is sigmoid(|z|); sigmoid(z) = r for z >= 0, 1 - r otherwise.
+// softplus(z) = max(z,0) + log(1+e); the log of a product of (1+e) factors
+// (each in [1, 2]) replaces one log per logit.
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float fast_exp_neg_abs(float z) {
+    return __builtin_amdgcn_exp2f(fabsf(z) * -kLog2e);
+}
+__device__ __forceinline__ float fast_sigmoid(float z, float e, float &den) {
+    den = 1.0f + e;
+    const float r = __builtin_amdgcn_rcpf(den);
+    return z >= 0.f ? r : 1.0f - r;
+}
+__device__ __forceinline__ float fast_log(float x) {
+    return __builtin_amdgcn_logf(x) * kLn2;
+}
+
+// Workgroup barrier that waits only for this wave's LDS operations.  Global
+// loads, including global->LDS copies, stay in flight (__syncthreads would
+// wait for those copies too).  Also a compiler memory barrier.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 __device__ __forceinline__ float wave_sum(float v) {

@@ -33,7 +33,7 @@ hipError_t launch_transpose_x(const unsigned short *X, unsigned short *XT,
 hipError_t launch_fill_u32(void *p, uint32_t v, size_t n, hipStream_t st);
 hipError_t launch_group_positives(const int32_t *row_ptr, const int32_t *labels,
                                   int nnz, int B, int64_t label_offset,
-                                  int64_t L, int G, int64_t Ng, int32_t *cnt,
+                                  int64_t L, int G, int64_t Ng, long long *keys,
                                   int32_t *grp_ptr, int32_t *ent,
                                   hipStream_t st);
 hipError_t launch_tail_t1(int mode, int G, const TailArgs &a, bool store_z,

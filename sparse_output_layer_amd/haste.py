@@ -67,6 +67,10 @@ _SIGS = {
                                       _vp, _sz, _vp]),
     "haste_tail_step": (ctypes.c_int, [_PD, _vp, _vp, _vp, _PB, _vp, _vp, ctypes.c_int, _vp,
                                        _sz, _vp]),
+    "haste_tail_prepare": (ctypes.c_int, [_PD, _vp, _PB, _vp, _sz, _vp]),
+    "haste_tail_step_dw": (ctypes.c_int, [_PD, _vp, _vp, _vp, _PB, _vp, _vp, _sz, _vp]),
+    "haste_tail_step_dx": (ctypes.c_int, [_PD, _vp, _vp, _vp, _PB, _vp, ctypes.c_int, _vp,
+                                          _sz, _vp]),
     "haste_head_fwd": (ctypes.c_int, [_PH, _vp, _vp, _vp, _PB, _vp, _sz, _vp]),
     "haste_head_bwd": (ctypes.c_int, [_PH, _vp, _vp, _vp, _PB, _vp, _vp, ctypes.c_int, _vp,
                                       _sz, _vp]),
@@ -241,6 +245,37 @@ def haste_tail_step(X, idx, W, L, G, bce: Bce, dW, dX, accumulate_dX=False, work
     ws, nb = _workspace(lib().haste_tail_workspace_bytes(ctypes.byref(d), b), X.device, workspace)
     _check(lib().haste_tail_step(ctypes.byref(d), _ptr(X), _ptr(idx), _ptr(W), b, _ptr(dW),
                                  _ptr(dX), int(bool(accumulate_dX)), _ptr(ws), nb, _stream()))
+
+
+def haste_tail_prepare(X, idx, L, G, bce: Bce, workspace: torch.Tensor):
+    """Split step, part 1: transposed X and group-major positives into
+    `workspace` (keep it for haste_tail_step_dw / haste_tail_step_dx)."""
+    _need(X, "X")
+    d = tail_desc(X, idx, L, G)
+    _check(lib().haste_tail_prepare(ctypes.byref(d), _ptr(X), _bref(bce), _ptr(workspace),
+                                    workspace.numel(), _stream()))
+
+
+def haste_tail_step_dw(X, idx, W, L, G, bce: Bce, dW, workspace: torch.Tensor):
+    """Split step, part 2: loss and dW (one kernel)."""
+    _tail_in(X, idx, W)
+    _need(dW, "dW", X.dtype)
+    d = tail_desc(X, idx, L, G)
+    b = _bref(bce)
+    _check(lib().haste_tail_step_dw(ctypes.byref(d), _ptr(X), _ptr(idx), _ptr(W), b, _ptr(dW),
+                                    _ptr(workspace), workspace.numel(), _stream()))
+
+
+def haste_tail_step_dx(X, idx, W, L, G, bce: Bce, dX, workspace: torch.Tensor,
+                       accumulate_dX=False):
+    """Second half of haste_tail_step (dX), using what _dw left in `workspace`."""
+    _tail_in(X, idx, W)
+    _need(dX, "dX", torch.float32)
+    d = tail_desc(X, idx, L, G)
+    b = _bref(bce)
+    _check(lib().haste_tail_step_dx(ctypes.byref(d), _ptr(X), _ptr(idx), _ptr(W), b, _ptr(dX),
+                                    int(bool(accumulate_dX)), _ptr(workspace), workspace.numel(),
+                                    _stream()))
 
 
 def haste_head_fwd(X, Wh, Zh=None, bce: Optional[Bce] = None, workspace=None):
