@@ -539,307 +539,406 @@ hipError_t launch_tail_t1(int mode, int G, const TailArgs &a, bool store_z, bool
 }
 
 // ------------------------------------------------------------------- T2
-// Workgroup = (row chunk of BC2 rows) x (range of groups), 8 waves.  Each
-// wave owns NTW32 tiles of 32 features of the dX accumulator (32x32 MFMA
-// tiles, rows x features).
+// Workgroup = (row chunk of BC2 rows) x (range of groups), 16 waves in three
+// roles, each SIMD hosting two consumers, one Z^T wave and one builder:
+//   consumers (8): own all BC2 rows x NTW32 32-feature tiles of the dX
+//     accumulator, in 32x32 MFMA accumulators for the whole group range, and
+//     run only the dense product;
+//   Z^T waves (4): recompute Z^T and dz for the next step;
+//   builders (4): build W^T and the inverse index for the next step.
+// The consumers keep the matrix cores busy while the other two roles run
+// their latency-bound chains for the next step.
 //
-// Per group g, the dense product dX_chunk += dz_g (rows x G) * W~_g (G x D)
+// Per group g the dense product dX_chunk += dz_g (rows x G) * W~_g (G x D)
 // runs on v_mfma_f32_32x32x16_bf16 (K = 16 labels per instruction), where
 // W~_g is W_g^T scattered to the rows idx_g and zero elsewhere: the B
-// operand of feature d is row f of W_g^T when idx_g[f] = d, else a zero row.
+// operand of feature d is row f of W_g^T when idx_g[f] = d, else a zero row
+// (the inverse index d -> f is rebuilt per group).
 //
-// Software pipeline, one barrier per group.  W_g and idx_g arrive in an LDS
-// ring of R slots through asynchronous direct global->LDS loads issued R-1
-// groups ahead (no registers held).  Iteration g:
-//   issue the loads of group g+R,
-//   (1) recompute Z^T of group g+1 for the chunk (A operand from the raw
-//       W_{g+1} rows, B operand gathered from the chunk with transposing
-//       reads at rows idx_{g+1}), sigmoid-BCE -> dz, published in LDS in the
-//       A-operand layout of the 32x32x16 product,
-//   (2) build W_{g+1}^T ([f][j]) and the inverse index feature -> f,
-//   (3) dense product of group g,
-//   wait for the loads of group g+2, barrier.
-constexpr int T2_NW = 8;
+// Groups are processed GPI at a time ("steps"), so that the recompute of
+// Z^T has at least eight 16x16 tiles per step for the eight waves.
+// Software pipeline, one barrier per step.  W_g and idx_g (and the pair
+// grp_ptr[g], grp_ptr[g+1]) arrive in an LDS ring of T2_R slots through
+// asynchronous direct global->LDS copies, issued T2_R steps ahead.
+// Iteration k:
+//   Z^T waves and builders issue the copies of step k+T2_R into the slot of
+//   step k,
+//   (1) Z^T waves: recompute Z^T of step k+1 (A operand: raw W rows; B
+//       operand: the chunk gathered at rows idx with transposing reads),
+//       sigmoid-BCE -> dz, published in LDS in the A-operand layout of the
+//       32x32x16 product,
+//   (2) builders: W^T ([f][j]) and the inverse index of step k+1,
+//   (3) consumers: dense product of step k,
+//   all: clear the inverse index of step k-1, wait for the copies of step
+//   k+2, barrier.
+//
+// Bank spreading: the chunk's 16-byte units are rotated by the row index,
+// the raw W rows' 16-byte units are XOR-swizzled (applied by choosing each
+// lane's source address of the direct copy, whose LDS destination is fixed
+// per lane), and W^T rows are padded by 8 bytes.
+constexpr int T2_R = 3;
+constexpr int T2_NC = 8, T2_NZ = 4, T2_NB = 4;   // consumer, Z^T and W^T waves
+constexpr int T2_NW = T2_NC + T2_NZ + T2_NB;
 
-struct T2Lds {  // byte offsets of the LDS regions (host and device agree)
-    int ring, ring_slot, ring_idx, wts, wts_slot, inv, exch, total;
+template <int N>
+__device__ __forceinline__ void vm_wait_c() {
+    static_assert(N >= 0 && N < 16, "vmcnt immediate");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | N);  // vmcnt(N); expcnt, lgkmcnt untouched
+}
+
+__host__ __device__ constexpr int t2_gpi(int G, int BC2) {
+    return (G / 16) * (BC2 / 16) * 2 <= 8 ? 2 : 1;
+}
+// direct copies per copying wave (Z^T waves and builders) per step, 1 KB
+// each, for F up to 128
+__host__ __device__ constexpr int t2_nbmax(int G, int BC2) {
+    return (t2_gpi(G, BC2) * (G / 4 + 1) + T2_NZ + T2_NB - 1) / (T2_NZ + T2_NB);
+}
+
+struct T2Lds {  // byte offsets and sizes of the LDS regions (host and device agree)
+    int ring, wsz, slot, wts, wts_grp, inv, ndp, exch, exch_grp, total;
 };
 
-__host__ __device__ inline T2Lds t2_layout(int D, int F, int G, int BC2, int NTW32, int R) {
+__host__ __device__ inline T2Lds t2_layout(int D, int F, int G, int BC2, int NTW32) {
     T2Lds L;
-    const int BCP = BC2 + 8, RT = BC2 / 32, JT = G / 16;
-    const int wbytes = G * F * 2;                  // multiple of 1 KB
-    int o = ((D * BCP * 2) + 1023) / 1024 * 1024;  // X^T chunk
+    const int GPI = t2_gpi(G, BC2);
+    L.ndp = T2_NC * NTW32 * 32;
+    int o = (D * BC2 * 2 + 1023) & ~1023;       // X^T chunk, rows of BC2 bf16
     L.ring = o;
-    L.ring_idx = wbytes;                           // idx_g, then grp_ptr[g], grp_ptr[g+1]
-    L.ring_slot = wbytes + 1024;                   // both fit in one 1 KB block (F <= 128)
-    o += R * L.ring_slot;
+    L.wsz = G * F * 2;                          // raw W_g (a multiple of 1 KB)
+    L.slot = GPI * (L.wsz + 1024);              // + idx_g and the pointer pair
+    o += T2_R * L.slot;
     L.wts = o;
-    L.wts_slot = (F + 1) * G * 2;                  // row F = zeros
-    o += 2 * L.wts_slot;
+    L.wts_grp = ((F + 1) * (G * 2 + 8) + 15) & ~15;   // W_g^T (padded rows) + zero row F
+    o += 2 * GPI * L.wts_grp;
     L.inv = o;
-    o += 2 * (T2_NW * NTW32 * 32) * 2;
-    o = (o + 15) / 16 * 16;
+    o += (3 * GPI * L.ndp + 15) & ~15;          // u8 inverse index, 3 buffers
     L.exch = o;
-    o += 2 * RT * JT * 64 * 16;
-    o = (o + 1023) / 1024 * 1024;                  // + one scratch block for dummy copies
-    L.total = o + 1024;
+    L.exch_grp = BC2 * G * 2;                   // dz of one group, MFMA A layout
+    o += 2 * GPI * L.exch_grp;
+    L.total = o + 1024;                         // + target of the padding copies
     return L;
 }
 
-__device__ __forceinline__ void vm_wait(int n) {
-    // s_waitcnt vmcnt(n), other counters untouched (gfx9 encoding)
-    switch (n) {
-    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-    case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
-    case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
-    case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
-    case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
-    case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
-    case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
-    case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;
-    case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
-    default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-    }
-}
-
 template <int G, int BC2, int NTW32>
-__global__ __launch_bounds__(64 * T2_NW, 1) void k_tail_t2(TailArgs a, int dz_mem, int n_granges,
-                                                           int R) {
-    constexpr int NW = T2_NW, NT = 64 * NW;
-    constexpr int JT = G / 16, BT = BC2 / 16, RT = BC2 / 32, BCP = BC2 + 8;
-    constexpr int NDP = NW * NTW32 * 32;
-    const int F = a.F, KS = F / 32;
-    const T2Lds LY = t2_layout(a.D, F, G, BC2, NTW32, R);
-    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-    unsigned short *tile = (unsigned short *)lds;
+__global__ __launch_bounds__(64 * T2_NW, 1) void k_tail_t2(TailArgs a, int dz_mem, int n_granges) {
+    constexpr int NW = T2_NW, NT = 64 * NW, R = T2_R;
+    constexpr int GPI = t2_gpi(G, BC2), NBMAX = t2_nbmax(G, BC2);
+    constexpr int JT = G / 16, BT = BC2 / 16, RT = BC2 / 32;
+    constexpr int NU = BC2 / 8;                // 16-byte units per chunk row
+    constexpr int GPR = G / 4, LGPR = G == 16 ? 2 : G == 32 ? 3 : 4;
+    constexpr int WTS = G * 2 + 8;             // W^T row stride, bytes
+    constexpr int NDP = T2_NC * NTW32 * 32;    // features covered by the consumer waves
+    constexpr int LROW = BC2 == 64 ? 7 : 6;    // log2 of a chunk row in bytes
+    constexpr int NTILE = GPI * JT * BT;       // 16x16 Z^T tiles per step
+    constexpr int TPW = NTILE / T2_NZ;         // tiles per Z^T wave (same group and label tile)
+    static_assert(NTILE % T2_NZ == 0 && BT % TPW == 0, "Z^T tile split");
+    constexpr int NB_T = T2_NB * 64;           // threads that build W^T
+    const int F = a.F, KS = F / 32, UPR = F / 8;
+    const int lupr = F == 128 ? 4 : F == 64 ? 3 : 2;       // log2(F/8)
+    const int swsh = UPR >= 8 ? 0 : 1;
+    const T2Lds LY = t2_layout(a.D, F, G, BC2, NTW32);
+    extern __shared__ __attribute__((aligned(1024))) unsigned char lds[];
+    unsigned char *tile = lds;
     unsigned char *ring = lds + LY.ring;
-    unsigned short *wts0 = (unsigned short *)(lds + LY.wts);
-    short *inv0 = (short *)(lds + LY.inv);
+    unsigned char *wts0 = lds + LY.wts;
+    unsigned char *inv0 = lds + LY.inv;
     unsigned char *exch0 = lds + LY.exch;
-    unsigned char *scratch = lds + LY.total - 1024;
+    unsigned char *pad = lds + LY.total - 1024;
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int q = lane >> 4, m = lane & 15;
+    const int hq = lane >> 4, m = lane & 15;
     const int gr = blockIdx.x % n_granges, bch = blockIdx.x / n_granges;
     const int64_t gA = (int64_t)gr * a.Ng / n_granges, gB = (int64_t)(gr + 1) * a.Ng / n_granges;
     const int ng = (int)(gB - gA);
+    const int nsteps = (ng + GPI - 1) / GPI;
     const int r0 = bch * BC2;
-    const int nq = (G / 4) * (F / 4);
-    const int dbase = w * NTW32 * 32;
-    const int wblk = G * F * 2 / 1024;               // 1 KB blocks of raw W per group
-    const int nblk = wblk + 1;                       // + idx
-    const int NB = (nblk + NW - 1) / NW;             // copies per wave per group
+    const int wblk = LY.wsz >> 10;
+    const int gstride = LY.wsz + 1024;
+    // wave roles (uniform): consumers 0..7, Z^T waves 8..11, W^T builders 12..15
+    const int role = w < T2_NC ? 0 : w < T2_NC + T2_NZ ? 1 : 2;
+    const int dbase = w * NTW32 * 32;          // consumer's first feature
 
-    // Asynchronous copy of W_g, idx_g (and grp_ptr[g], grp_ptr[g+1] after it)
-    // into ring slot (g - gA) % R.  The pointer read covers 4 entries; the
-    // workspace holds 3 spare entries past grp_ptr[Ng].
-    auto issue = [&](int k) {  // k = g - gA
-        unsigned char *slot = ring + (k % R) * LY.ring_slot;
-        const int64_t g = gA + k;
-        for (int i = 0; i < NB; ++i) {
-            const int blk = w + NW * i;
-            if (blk < wblk) {
-                const unsigned short *src = a.W + g * G * (int64_t)F + blk * 512 + lane * 8;
-                __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)(
-                                                          slot + blk * 1024), 16, 0, 0);
-            } else if (blk == wblk) {
-                const int32_t *src = a.idx + g * (int64_t)F + (lane < F / 4 ? lane * 4 : 0);
-                if (lane == F / 4 && !dz_mem) src = a.grp_ptr + g;
-                __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)(
-                                                          slot + LY.ring_idx), 16, 0, 0);
-            } else {  // keep the per-wave copy count uniform
-                __builtin_amdgcn_global_load_lds(a.W + lane * 8, (__attribute__((address_space(3))) void *)(
-                                                          scratch), 16, 0, 0);
+    // Copy plan of a copying wave (loop invariant): block b = (w - T2_NC) +
+    // (T2_NZ + T2_NB) * i of a step is group q's W block `sub`, or its index
+    // block when sub == wblk.
+    int cp_q[NBMAX], cp_sub[NBMAX], cp_off[NBMAX];
+#pragma unroll
+    for (int i = 0; i < NBMAX; ++i) {
+        const int b = (w - T2_NC) + (T2_NZ + T2_NB) * i;
+        cp_q[i] = b / (wblk + 1);
+        cp_sub[i] = b - cp_q[i] * (wblk + 1);
+        const int p = cp_sub[i] * 64 + lane, r = p >> lupr, pc = p & (UPR - 1);
+        cp_off[i] = r * F + ((pc ^ ((r >> swsh) & (UPR - 1))) << 3);   // elements of W_g
+    }
+    auto issue = [&](int k, unsigned char *slot) {
+#pragma unroll
+        for (int i = 0; i < NBMAX; ++i) {
+            const int q = cp_q[i];
+            const int64_t g = gA + (int64_t)k * GPI + q;
+            const void *src = a.W + lane * 8;
+            unsigned char *dst = pad;
+            if (q < GPI && g < gB) {
+                unsigned char *gb = slot + q * gstride;
+                if (cp_sub[i] < wblk) {
+                    src = a.W + g * G * (int64_t)F + cp_off[i];
+                    dst = gb + cp_sub[i] * 1024;
+                } else {
+                    const int32_t *s = a.idx + g * (int64_t)F + (lane < F / 4 ? lane * 4 : 0);
+                    if (lane == F / 4 && !dz_mem) s = a.grp_ptr + g;
+                    src = s;
+                    dst = gb + LY.wsz;
+                }
             }
+            __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
         }
     };
 
-    {   // stage the chunk, reset the inverse maps, zero rows
-        constexpr int SEG = BC2 / 8;
+    {   // stage the chunk (units rotated by row), reset the inverse maps, zero rows
         const unsigned short *src = a.XT + r0;
-        for (int i = tid; i < a.D * SEG; i += NT) {
-            const int d = i / SEG, sg = i % SEG;
-            *(u32x4 *)(tile + d * BCP + sg * 8) = *(const u32x4 *)(src + (int64_t)d * a.Bp + sg * 8);
+        for (int i = tid; i < a.D * NU; i += NT) {
+            const int d = i / NU, u = i % NU;
+            *(u32x4 *)(tile + (d << LROW) + (((u + d) & (NU - 1)) << 4)) =
+                *(const u32x4 *)(src + (int64_t)d * a.Bp + u * 8);
         }
-        for (int i = tid; i < 2 * NDP; i += NT) inv0[i] = (short)F;
-        for (int i = tid; i < 2 * G; i += NT)
-            wts0[(i / G) * (LY.wts_slot / 2) + F * G + i % G] = 0;
+        const unsigned fill = (unsigned)F * 0x01010101u;
+        for (int i = tid; i < 3 * GPI * NDP / 4; i += NT) ((unsigned *)inv0)[i] = fill;
+        for (int i = tid; i < 2 * GPI * (G / 2); i += NT)
+            ((unsigned *)(wts0 + (i / (G / 2)) * LY.wts_grp + F * WTS))[i % (G / 2)] = 0u;
     }
-    f32x16 acc[RT][NTW32];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int nt = 0; nt < NTW32; ++nt) acc[rt][nt] = (f32x16){};
-
-    // (1) Z^T of group k -> dz -> exch slot k & 1
-    auto zt = [&](int k) {
-        const unsigned char *slot = ring + (k % R) * LY.ring_slot;
-        const unsigned short *rw = (const unsigned short *)slot;
-        const int *ri = (const int *)(slot + LY.ring_idx);
-        unsigned char *exch = exch0 + (k & 1) * (RT * JT * 64 * 16);
-        const int64_t g = gA + k;
-        int gp0 = 0, gp1 = 0;
+    // (1) Z^T of step k -> dz -> exch.  Z^T wave p takes tiles p*TPW .. +TPW-1:
+    // one group and label tile, TPW consecutive 16-row tiles, so the raw W rows
+    // and the index reads serve all of them.
+    auto zt = [&](int k, const unsigned char *slot, unsigned char *exch) {
+        const int tl0 = (w - T2_NC) * TPW;
+        const int q = tl0 / (JT * BT), jt = (tl0 % (JT * BT)) / BT, bt0 = tl0 % BT;
+        const int64_t g = gA + (int64_t)k * GPI + q;
+        if (g >= gB) return;
+        const unsigned char *gb = slot + q * gstride;
+        const int *ri = (const int *)(gb + LY.wsz);
+        float dzv[TPW][4];
         if (!dz_mem) {
-            gp0 = ri[F];
-            gp1 = ri[F + 1];
-        }
-        for (int tl = w; tl < JT * BT; tl += NW) {   // label tile jt, row tile bt
-            const int jt = tl / BT, bt = tl % BT;
-            float dzv[4];
-            const int row = r0 + 16 * bt + m;
-            if (!dz_mem) {
-                f32x4 z = {0.f, 0.f, 0.f, 0.f};
-                const int col = 16 * bt + 4 * (m & 3);
-                for (int s = 0; s < KS; ++s) {
-                    const bf16x8 Av = *(const bf16x8 *)(rw + (16 * jt + m) * F + 32 * s + 8 * q);
-                    const int fa = 32 * s + 8 * q + (m >> 2);
-                    i16x4 b0 = lds_read_tr(tile + ri[fa] * BCP + col);
-                    i16x4 b1 = lds_read_tr(tile + ri[fa + 4] * BCP + col);
-                    bf16x8 Bv = __builtin_bit_cast(
-                        bf16x8, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
-                    z = mfma32(Av, Bv, z);
-                }
-                // positives of this group inside the tile (lane owns slots 16jt+4q+i of row)
-                unsigned ymask = 0;
-                bool has_pos = false;            // wave-uniform
-                for (int e = gp0; e < gp1; ++e) {
-                    const int v = a.grp_ent[e];
-                    const int lb = v / G - (r0 + 16 * bt), j = v % G;
-                    if (lb < 0 || lb >= 16 || (j >> 4) != jt) continue;
-                    has_pos = true;
-                    if (lb == m && ((j >> 2) & 3) == q) ymask |= 1u << (j & 3);
-                }
-                if (!has_pos && r0 + 16 * bt + 16 <= a.B && (g + 1) * G <= a.L) {
+            const int arow = 16 * jt + m;
+            const unsigned char *ab = gb + arow * F * 2;
+            const int asw = (arow >> swsh) & (UPR - 1);
+            const int ch = (m & 1) * 8;
+            const int *rl = ri + 8 * hq + (m >> 2);
+            f32x4 z[TPW];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        float den;
-                        dzv[i] = a.s * fast_sigmoid(z[i], fast_exp_neg_abs(z[i]), den);
-                    }
-                } else {
+            for (int t = 0; t < TPW; ++t) z[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int64_t t = g * G + 16 * jt + 4 * q + i;
-                        const bool live = row < a.B && t < a.L;
-                        float den;
-                        dzv[i] = live ? a.s * (fast_sigmoid(z[i], fast_exp_neg_abs(z[i]), den) -
-                                               (float)((ymask >> i) & 1u))
-                                      : 0.f;
-                    }
+            for (int s = 0; s < 4; ++s) {   // K steps of 32 features, F <= 128
+                if (s >= KS) break;
+                const bf16x8 Av = *(const bf16x8 *)(ab + (((4 * s + hq) ^ asw) << 4));
+                const int d0 = rl[32 * s], d1 = rl[32 * s + 4];
+#pragma unroll
+                for (int t = 0; t < TPW; ++t) {
+                    // chunk address of (row d, columns 16bt + 4(m%4) .. +3)
+                    const int cu16 = (2 * (bt0 + t) + ((m & 3) >> 1)) << 4;
+                    const i16x4 b0 = lds_read_tr(tile + ((d0 << LROW) | ((((d0 << 4) + cu16) & ((NU - 1) << 4)) | ch)));
+                    const i16x4 b1 = lds_read_tr(tile + ((d1 << LROW) | ((((d1 << 4) + cu16) & ((NU - 1) << 4)) | ch)));
+                    const bf16x8 Bv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
+                    z[t] = mfma32(Av, Bv, z[t]);
                 }
+            }
+            // positives of this group inside the wave's rows (lane owns labels 16jt+4hq+i)
+            const int gp0 = __builtin_amdgcn_readfirstlane(ri[F]);
+            const int gp1 = __builtin_amdgcn_readfirstlane(ri[F + 1]);
+            unsigned ymask[TPW];
+            bool has_pos = false;                // wave-uniform
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) ymask[t] = 0;
+            for (int e = gp0; e < gp1; ++e) {
+                const int v = a.grp_ent[e];
+                const int lb = v / G - (r0 + 16 * bt0), j = v % G;
+                if (lb < 0 || lb >= 16 * TPW || (j >> 4) != jt) continue;
+                has_pos = true;
+#pragma unroll
+                for (int t = 0; t < TPW; ++t)
+                    if (lb == 16 * t + m && ((j >> 2) & 3) == hq) ymask[t] |= 1u << (j & 3);
+            }
+            // sigmoid(z) = 1 / (1 + 2^(-z log2 e)); saturates cleanly at both ends
+            if (!has_pos && r0 + 16 * (bt0 + TPW) <= a.B && (g + 1) * G <= a.L) {
+#pragma unroll
+                for (int t = 0; t < TPW; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        dzv[t][i] = a.s * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z[t][i] * -kLog2e));
             } else {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int64_t t = g * G + 16 * jt + 4 * q + i;
-                    const bool live = row < a.B && t < a.L;
-                    dzv[i] = live ? bf16_to_f32(a.dZ[(int64_t)row * a.L + t]) : 0.f;
-                }
+                for (int t = 0; t < TPW; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int64_t lt = g * G + 16 * jt + 4 * hq + i;
+                        const bool live = r0 + 16 * (bt0 + t) + m < a.B && lt < a.L;
+                        const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z[t][i] * -kLog2e));
+                        dzv[t][i] = live ? a.s * (sg - (float)((ymask[t] >> i) & 1u)) : 0.f;
+                    }
             }
-            // element (row 16bt+m, label 16jt+4q+i) -> 32x32x16 A operand of row tile bt/2:
-            // lane 16(bt%2)+m+32(q/2), K slots 4(q%2)+i
-            const int lane2 = 16 * (bt & 1) + m + 32 * (q >> 1);
-            *(u32x2 *)(exch + (((bt >> 1) * JT + jt) * 64 + lane2) * 16 + 8 * (q & 1)) =
-                (u32x2){pack_bf16x2(dzv[0], dzv[1]), pack_bf16x2(dzv[2], dzv[3])};
+        } else {
+#pragma unroll
+            for (int t = 0; t < TPW; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = r0 + 16 * (bt0 + t) + m;
+                    const int64_t lt = g * G + 16 * jt + 4 * hq + i;
+                    const bool live = row < a.B && lt < a.L;
+                    dzv[t][i] = live ? bf16_to_f32(a.dZ[(int64_t)row * a.L + lt]) : 0.f;
+                }
+        }
+        // (row 16bt+m, label 16jt+4hq+i) -> A operand of the 32-row block bt/2:
+        // lane 16(bt%2)+m+32(hq/2), K slots 4(hq%2)+i
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            const int bt = bt0 + t;
+            const int lane2 = 16 * (bt & 1) + m + 32 * (hq >> 1);
+            *(u32x2 *)(exch + q * LY.exch_grp + (((bt >> 1) * JT + jt) * 64 + lane2) * 16 + 8 * (hq & 1)) =
+                (u32x2){pack_bf16x2(dzv[t][0], dzv[t][1]), pack_bf16x2(dzv[t][2], dzv[t][3])};
         }
     };
 
-    // (2) W_g^T ([f][j]) and the inverse index, for group k
-    auto build = [&](int k) {
-        const unsigned char *slot = ring + (k % R) * LY.ring_slot;
-        const unsigned short *rw = (const unsigned short *)slot;
-        const int *ri = (const int *)(slot + LY.ring_idx);
-        unsigned short *wts = wts0 + (k & 1) * (LY.wts_slot / 2);
-        short *inv = inv0 + (k & 1) * NDP;
-        for (int u = tid; u < nq; u += NT) {
-            const int ja = u % (G / 4), fc = u / (G / 4);
+    // (2) W^T ([f][j], rows of WTS bytes) and the inverse index of step k, on
+    // the builder waves.  Thread = 4 labels x 4 features.  Four consecutive
+    // lanes take consecutive feature quads, then the label quads, then the
+    // next features: with the 8-byte row padding the writes of 16 lanes hit
+    // distinct banks.
+    const int lf4 = lupr + 1;                 // log2(F/4)
+    const int lnq = LGPR + lf4;               // log2(units per group)
+    const int bth = tid - (T2_NC + T2_NZ) * 64;
+    auto build = [&](int k, const unsigned char *slot, unsigned char *wts, unsigned char *inv) {
+        for (int u = bth; u < (GPI << lnq); u += NB_T) {
+            const int q = u >> lnq, rest = u & ((1 << lnq) - 1);
+            const int r2 = rest >> 2, ja = r2 & (GPR - 1), fc = ((r2 >> LGPR) << 2) | (rest & 3);
+            if (gA + (int64_t)k * GPI + q >= gB) continue;
+            const unsigned char *wq = slot + q * gstride;
             u32x2 rr[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) rr[e] = *(const u32x2 *)(rw + (4 * ja + e) * F + 4 * fc);
+            for (int e = 0; e < 4; ++e) {
+                const int row = 4 * ja + e;
+                rr[e] = *(const u32x2 *)(wq + row * F * 2 + (((fc >> 1) ^ ((row >> swsh) & (UPR - 1))) << 4) +
+                                         (fc & 1) * 8);
+            }
+            unsigned char *wt = wts + q * LY.wts_grp + (4 * fc) * WTS + 8 * ja;
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const int word = kk >> 1, sh = (kk & 1) * 16;
-                const unsigned v0 = (rr[0][word] >> sh) & 0xffffu, v1 = (rr[1][word] >> sh) & 0xffffu;
-                const unsigned v2 = (rr[2][word] >> sh) & 0xffffu, v3 = (rr[3][word] >> sh) & 0xffffu;
-                *(u32x2 *)(wts + (4 * fc + kk) * G + 4 * ja) = (u32x2){v0 | (v1 << 16), v2 | (v3 << 16)};
+            for (int kk = 0; kk < 4; ++kk) {   // feature 4fc+kk: element kk of each row
+                const unsigned sel = (kk & 1) ? 0x07060302u : 0x05040100u;
+                const int wd = kk >> 1;
+                const u32x2 o = {__builtin_amdgcn_perm(rr[1][wd], rr[0][wd], sel),
+                                 __builtin_amdgcn_perm(rr[3][wd], rr[2][wd], sel)};
+                *(u32x2 *)(wt + kk * WTS) = o;
             }
         }
-        if (tid < F) inv[ri[tid]] = (short)tid;
+        for (int i = bth; i < GPI * F; i += NB_T) {
+            const int q = i / F, f = i - q * F;
+            if (gA + (int64_t)k * GPI + q >= gB) continue;
+            const int *ri = (const int *)(slot + q * gstride + LY.wsz);
+            inv[q * NDP + ri[f]] = (unsigned char)f;
+        }
     };
 
-    // (3) dense product of group k
-    auto dense = [&](int k) {
-        const unsigned short *wts = wts0 + (k & 1) * (LY.wts_slot / 2) + 8 * (lane >> 5);
-        short *inv = inv0 + (k & 1) * NDP;
-        const unsigned char *exch = exch0 + (k & 1) * (RT * JT * 64 * 16);
-        const unsigned short *brow[NTW32];
+    // (3) dense product of step k on the consumer waves: all BC2 rows x the
+    // wave's NTW32 feature tiles; each B fetch feeds RT row blocks.
+    auto dense = [&](f32x16 (&acc)[RT][NTW32], int k, const unsigned char *wts, const unsigned char *inv,
+                     const unsigned char *exch) {
 #pragma unroll
-        for (int nt = 0; nt < NTW32; ++nt) brow[nt] = wts + inv[dbase + 32 * nt + (lane & 31)] * G;
+        for (int q = 0; q < GPI; ++q) {
+            if (gA + (int64_t)k * GPI + q >= gB) break;
+            const unsigned char *wt = wts + q * LY.wts_grp + 16 * (lane >> 5);
+            const unsigned char *iv = inv + q * NDP + dbase + (lane & 31);
+            const unsigned char *brow[NTW32];
 #pragma unroll
-        for (int jt = 0; jt < JT; ++jt) {
-            bf16x8 Am[RT];
+            for (int nt = 0; nt < NTW32; ++nt) brow[nt] = wt + iv[32 * nt] * WTS;
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
-                Am[rt] = *(const bf16x8 *)(exch + ((rt * JT + jt) * 64 + lane) * 16);
+            for (int jt = 0; jt < JT; ++jt) {
+                bf16x8 Am[RT];
 #pragma unroll
-            for (int nt = 0; nt < NTW32; ++nt) {
-                const bf16x8 Bv = *(const bf16x8 *)(brow[nt] + 16 * jt);
+                for (int rt = 0; rt < RT; ++rt)
+                    Am[rt] = *(const bf16x8 *)(exch + q * LY.exch_grp + ((rt * JT + jt) * 64 + lane) * 16);
 #pragma unroll
-                for (int rt = 0; rt < RT; ++rt) acc[rt][nt] = mfma32x32(Am[rt], Bv, acc[rt][nt]);
+                for (int nt = 0; nt < NTW32; ++nt) {   // labels 16jt + 8(lane/32) .. +7 of row f
+                    const u32x2 lo = *(const u32x2 *)(brow[nt] + 32 * jt);
+                    const u32x2 hi = *(const u32x2 *)(brow[nt] + 32 * jt + 8);
+                    const bf16x8 Bv = __builtin_bit_cast(bf16x8, (u32x4){lo[0], lo[1], hi[0], hi[1]});
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt) acc[rt][nt] = mfma32x32(Am[rt], Bv, acc[rt][nt]);
+                }
             }
         }
-        // reset this wave's slice of the inverse map (only this wave reads it)
-        for (int i = lane; i < NTW32 * 32; i += 64) inv[dbase + i] = (short)F;
     };
 
-    // Ring: groups 0..R-1 are loaded up front; iteration k refills the slot of
-    // group k (last read by zt/build of group k in iteration k-1, before the
-    // barrier that closed it) with group k+R.
+    // Ring: steps 0..R-1 are loaded up front; iteration k refills the slot of
+    // step k (last read by the Z^T and W^T work of step k in iteration k-1,
+    // before the barrier that closed it) with step k+R.
     __syncthreads();
-    for (int k = 0; k < R && k < ng; ++k) issue(k);
+    if (role != 0)
+        for (int k = 0; k < R; ++k) issue(k, ring + k * LY.slot);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (ng > 0) {
-        zt(0);
-        build(0);
+    if (nsteps > 0) {
+        if (role == 1) zt(0, ring, exch0);
+        if (role == 2) build(0, ring, wts0, inv0);
     }
     __syncthreads();
-    for (int k = 0; k < ng; ++k) {
-        if (k + R < ng) issue(k + R);
-        if (k + 1 < ng) {
-            zt(k + 1);
-            build(k + 1);
-        }
-        dense(k);
-        // iteration k+1 reads group k+2: wait for its loads (vector-memory
-        // results return in issue order), leaving the later groups in flight
-        const int last = k + R < ng ? k + R : ng - 1;
-        const int after = (k + 2 < ng) ? last - (k + 2) : 0;
-        vm_wait(after > 0 ? after * NB : 0);
+    // Per-iteration tail shared by all roles: clear the inverse index of step
+    // k-1 (no longer read), wait for the copies of step k+2 (vector-memory
+    // results return in issue order), barrier.  Consumers run their own loop
+    // so that their accumulators are not live in the other roles' code.
+    const unsigned fill = (unsigned)F * 0x01010101u;
+    auto close_step = [&](int ic) {
+        const int ip = ic == 0 ? 2 : ic - 1;
+        unsigned *ivp = (unsigned *)(inv0 + ip * GPI * NDP);
+        for (int i = tid; i < GPI * NDP / 4; i += NT) ivp[i] = fill;
+        vm_wait_c<NBMAX>();
         lds_barrier();
-    }
-
-    // flush: reg r of tile (rt, nt) = row 32rt+8(r/4)+4(lane/32)+r%4, feature dbase+32nt+lane%32
+    };
+    if (role == 0) {
+        f32x16 acc[RT][NTW32];
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+        for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int nt = 0; nt < NTW32; ++nt) {
-            const int d = dbase + 32 * nt + (lane & 31);
-            if (d >= a.D) continue;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = r0 + 32 * rt + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                if (row < a.B) atomicAdd(a.dX + (int64_t)row * a.D + d, acc[rt][nt][r]);
-            }
+            for (int nt = 0; nt < NTW32; ++nt) acc[rt][nt] = (f32x16){};
+        int ic = 0;   // inverse-index buffer of step k
+        for (int k = 0; k < nsteps; ++k) {
+            const int bc = k & 1;
+            dense(acc, k, wts0 + bc * GPI * LY.wts_grp, inv0 + ic * GPI * NDP, exch0 + bc * GPI * LY.exch_grp);
+            close_step(ic);
+            ic = ic == 2 ? 0 : ic + 1;
         }
-}
-
-static T2Lds t2_plan(int D, int F, int G, int BC2, int NTW32, int &R) {
-    for (R = 4; R >= 2; --R) {
-        T2Lds L = t2_layout(D, F, G, BC2, NTW32, R);
-        if (L.total <= 160 * 1024) return L;
+        // flush: reg r of tile (rt, nt) = row 32rt+8(r/4)+4(lane/32)+r%4, feature dbase+32nt+lane%32
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int nt = 0; nt < NTW32; ++nt) {
+                const int d = dbase + 32 * nt + (lane & 31);
+                if (d >= a.D) continue;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = r0 + 32 * rt + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                    if (row < a.B) atomicAdd(a.dX + (int64_t)row * a.D + d, acc[rt][nt][r]);
+                }
+            }
+    } else {
+        int sc = 0, ic = 0;
+        for (int k = 0; k < nsteps; ++k) {
+            issue(k + R, ring + sc * LY.slot);
+            const int sn = sc == R - 1 ? 0 : sc + 1;
+            const int in = ic == 2 ? 0 : ic + 1;
+            const int bn = (k + 1) & 1;
+            if (k + 1 < nsteps) {
+                if (role == 1) {
+                    __builtin_amdgcn_s_setprio(2);   // short latency chain: issue ahead of the MFMA stream
+                    zt(k + 1, ring + sn * LY.slot, exch0 + bn * GPI * LY.exch_grp);
+                    __builtin_amdgcn_s_setprio(0);
+                } else {
+                    build(k + 1, ring + sn * LY.slot, wts0 + bn * GPI * LY.wts_grp, inv0 + in * GPI * NDP);
+                }
+            }
+            close_step(ic);
+            sc = sn;
+            ic = in;
+        }
+        __builtin_amdgcn_s_waitcnt(0);   // padding copies still in flight
     }
-    R = 0;
-    return t2_layout(D, F, G, BC2, NTW32, 2);
 }
 
 static int64_t t2_granges(int nbch, int64_t Ng) {
@@ -854,39 +953,51 @@ static int64_t t2_granges(int nbch, int64_t Ng) {
     return ngr;
 }
 
+static bool t2_fits(int D, int F, int G, int BC2, int NTW32) {
+    return t2_layout(D, F, G, BC2, NTW32).total <= 160 * 1024;
+}
+
+static int t2_ntw(int D, int BC2) {   // 32-feature tiles per consumer wave
+    (void)BC2;
+    return ((D + 31) / 32 + T2_NC - 1) / T2_NC;
+}
+
 template <int G, int BC2, int NTW32>
 static hipError_t t2_go(bool dz_mem, const TailArgs &a, hipStream_t st) {
     const int nbch = a.Bp / BC2;
     const int64_t ngr = t2_granges(nbch, a.Ng);
     if (ngr < 1) return hipSuccess;
-    int R = 0;
-    const T2Lds L = t2_plan(a.D, a.F, G, BC2, NTW32, R);
-    if (R < 2) return hipErrorInvalidValue;
+    const T2Lds L = t2_layout(a.D, a.F, G, BC2, NTW32);
+    if (L.total > 160 * 1024) return hipErrorInvalidValue;
     allow_lds((const void *)k_tail_t2<G, BC2, NTW32>, L.total);
     hipLaunchKernelGGL((k_tail_t2<G, BC2, NTW32>), dim3((unsigned)(ngr * nbch)), dim3(64 * T2_NW),
-                       L.total, st, a, (int)dz_mem, (int)ngr, R);
+                       L.total, st, a, (int)dz_mem, (int)ngr);
     return hipGetLastError();
 }
 
-static bool t2_fits(int D, int F, int G, int BC2, int NTW32) {
-    int R = 0;
-    t2_plan(D, F, G, BC2, NTW32, R);
-    return R >= 2;
+template <int G, int BC2>
+static hipError_t t2_pick_ntw(bool dz_mem, const TailArgs &a, hipStream_t st) {
+    switch (t2_ntw(a.D, BC2)) {
+    case 1: return t2_go<G, BC2, 1>(dz_mem, a, st);
+    case 2: return t2_go<G, BC2, 2>(dz_mem, a, st);
+    case 3: return t2_go<G, BC2, 3>(dz_mem, a, st);
+    }
+    if constexpr (BC2 == 32)
+        if (t2_ntw(a.D, BC2) == 4) return t2_go<G, BC2, 4>(dz_mem, a, st);
+    return hipErrorInvalidValue;
 }
 
-template <int G, int NTW32>
-static hipError_t t2_pick_bc(bool dz_mem, const TailArgs &a, hipStream_t st) {
-    if (t2_fits(a.D, a.F, G, 64, NTW32)) return t2_go<G, 64, NTW32>(dz_mem, a, st);
-    return t2_go<G, 32, NTW32>(dz_mem, a, st);
+// 64-row chunks when they fit in LDS, the batch is larger than 32 rows and
+// the accumulator (2 x NTW32 32x32 tiles per consumer) stays within 96 registers
+static int t2_bc(int G, int F, int D, int B) {
+    if (B > 32 && t2_ntw(D, 64) <= 3 && t2_fits(D, F, G, 64, t2_ntw(D, 64))) return 64;
+    return 32;
 }
 
 template <int G>
 static hipError_t t2_pick(bool dz_mem, const TailArgs &a, hipStream_t st) {
-    const int nd = (a.D + 31) / 32, need = (nd + T2_NW - 1) / T2_NW;
-    if (need <= 1) return t2_pick_bc<G, 1>(dz_mem, a, st);
-    if (need <= 2) return t2_pick_bc<G, 2>(dz_mem, a, st);
-    if (need <= 3) return t2_pick_bc<G, 3>(dz_mem, a, st);
-    return t2_pick_bc<G, 4>(dz_mem, a, st);
+    if (t2_bc(G, a.F, a.D, a.B) == 64) return t2_pick_ntw<G, 64>(dz_mem, a, st);
+    return t2_pick_ntw<G, 32>(dz_mem, a, st);
 }
 
 hipError_t launch_tail_t2(int G, bool dz_mem, const TailArgs &a, hipStream_t st) {
@@ -902,11 +1013,9 @@ bool tail_bf16_supported(int G, int F, int D) {
     if (!(G == 16 || G == 32 || G == 64)) return false;
     if (!(F == 32 || F == 64 || F == 128)) return false;
     if (D < F || D > 1024) return false;
-    // T1: two chunk buffers; T2: chunk + pipeline buffers with BC2 = 32 at least
+    // T1: two chunk buffers; T2: chunk + pipeline buffers with 32-row chunks at least
     if (t1_buf_bytes(D, 8) * 2 > 160 * 1024 || t1_buf_bytes(D, 4) * 2 > 160 * 1024) return false;
-    const int nd = (D + 31) / 32, need = (nd + T2_NW - 1) / T2_NW;
-    const int ntw = need <= 1 ? 1 : need <= 2 ? 2 : need <= 3 ? 3 : 4;
-    if (t2_layout(D, F, G, 32, ntw, 2).total > 160 * 1024) return false;
+    if (!t2_fits(D, F, G, 32, t2_ntw(D, 32))) return false;
     return true;
 }
 
