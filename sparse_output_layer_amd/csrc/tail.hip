@@ -544,10 +544,8 @@ hipError_t launch_tail_t1(int mode, int G, const TailArgs &a, bool store_z, bool
 //   consumers (8): own all BC2 rows x NTW32 32-feature tiles of the dX
 //     accumulator, in 32x32 MFMA accumulators for the whole group range, and
 //     run only the dense product;
-//   Z^T waves (4): recompute Z^T and dz for the next step;
-//   builders (4): build W^T and the inverse index for the next step.
-// The consumers keep the matrix cores busy while the other two roles run
-// their latency-bound chains for the next step.
+//   Z^T waves (4): recompute Z^T and dz;
+//   builders (4): build W^T and the inverse index.
 //
 // Per group g the dense product dX_chunk += dz_g (rows x G) * W~_g (G x D)
 // runs on v_mfma_f32_32x32x16_bf16 (K = 16 labels per instruction), where
@@ -556,74 +554,54 @@ hipError_t launch_tail_t1(int mode, int G, const TailArgs &a, bool store_z, bool
 // (the inverse index d -> f is rebuilt per group).
 //
 // Groups are processed GPI at a time ("steps"), so that the recompute of
-// Z^T has at least eight 16x16 tiles per step for the eight waves.
-// Software pipeline, one barrier per step.  W_g and idx_g (and the pair
-// grp_ptr[g], grp_ptr[g+1]) arrive in an LDS ring of T2_R slots through
-// asynchronous direct global->LDS copies, issued T2_R steps ahead.
-// Iteration k:
-//   Z^T waves and builders issue the copies of step k+T2_R into the slot of
-//   step k,
-//   (1) Z^T waves: recompute Z^T of step k+1 (A operand: raw W rows; B
-//       operand: the chunk gathered at rows idx with transposing reads),
-//       sigmoid-BCE -> dz, published in LDS in the A-operand layout of the
-//       32x32x16 product,
-//   (2) builders: W^T ([f][j]) and the inverse index of step k+1,
-//   (3) consumers: dense product of step k,
-//   all: clear the inverse index of step k-1, wait for the copies of step
-//   k+2, barrier.
+// Z^T has at least eight 16x16 tiles per step.  One barrier per step.  The
+// Z^T waves and builders load their operands (idx_g, W_g rows, the pointer
+// pair of the group-major positives) straight from global memory into
+// registers, four steps ahead of use, and work two steps ahead of the
+// consumers, so that none of their memory or MFMA latencies is on the path
+// of a step.  Iteration k:
+//   consumers: dense product of step k;
+//   Z^T waves: sigmoid-BCE epilogue of step k+1 (from the Z^T accumulators
+//     of the previous iteration) -> dz, stored in LDS in the A-operand layout
+//     of the 32x32x16 product; gather (transposing reads of the chunk at rows
+//     idx) and MFMAs of step k+2; load the operands of step k+4;
+//   builders: W^T ([f][j]) and the inverse index of step k+2; load step k+4;
+//   all: clear the inverse index of step k-1, barrier.
 //
 // Bank spreading: the chunk's 16-byte units are rotated by the row index,
-// the raw W rows' 16-byte units are XOR-swizzled (applied by choosing each
-// lane's source address of the direct copy, whose LDS destination is fixed
-// per lane), and W^T rows are padded by 8 bytes.
-constexpr int T2_R = 3;
+// W^T rows are padded by 8 bytes.
 constexpr int T2_NC = 8, T2_NZ = 4, T2_NB = 4;   // consumer, Z^T and W^T waves
 constexpr int T2_NW = T2_NC + T2_NZ + T2_NB;
-
-template <int N>
-__device__ __forceinline__ void vm_wait_c() {
-    static_assert(N >= 0 && N < 16, "vmcnt immediate");
-    __builtin_amdgcn_s_waitcnt(0x0F70 | N);  // vmcnt(N); expcnt, lgkmcnt untouched
-}
 
 __host__ __device__ constexpr int t2_gpi(int G, int BC2) {
     return (G / 16) * (BC2 / 16) * 2 <= 8 ? 2 : 1;
 }
-// direct copies per copying wave (Z^T waves and builders) per step, 1 KB
-// each, for F up to 128
-__host__ __device__ constexpr int t2_nbmax(int G, int BC2) {
-    return (t2_gpi(G, BC2) * (G / 4 + 1) + T2_NZ + T2_NB - 1) / (T2_NZ + T2_NB);
-}
 
 struct T2Lds {  // byte offsets and sizes of the LDS regions (host and device agree)
-    int ring, wsz, slot, wts, wts_grp, inv, ndp, exch, exch_grp, total;
+    int wts, wts_grp, inv, ndp, exch, exch_grp, total;
 };
 
 __host__ __device__ inline T2Lds t2_layout(int D, int F, int G, int BC2, int NTW32) {
     T2Lds L;
     const int GPI = t2_gpi(G, BC2);
     L.ndp = T2_NC * NTW32 * 32;
-    int o = (D * BC2 * 2 + 1023) & ~1023;       // X^T chunk, rows of BC2 bf16
-    L.ring = o;
-    L.wsz = G * F * 2;                          // raw W_g (a multiple of 1 KB)
-    L.slot = GPI * (L.wsz + 1024);              // + idx_g and the pointer pair
-    o += T2_R * L.slot;
+    int o = (D * BC2 * 2 + 15) & ~15;            // X^T chunk, rows of BC2 bf16
     L.wts = o;
     L.wts_grp = ((F + 1) * (G * 2 + 8) + 15) & ~15;   // W_g^T (padded rows) + zero row F
-    o += 2 * GPI * L.wts_grp;
+    o += 3 * GPI * L.wts_grp;                    // three steps
     L.inv = o;
-    o += (3 * GPI * L.ndp + 15) & ~15;          // u8 inverse index, 3 buffers
+    o += (4 * GPI * L.ndp + 15) & ~15;           // u8 inverse index, four steps
     L.exch = o;
-    L.exch_grp = BC2 * G * 2;                   // dz of one group, MFMA A layout
+    L.exch_grp = BC2 * G * 2;                    // dz of one group, MFMA A layout
     o += 2 * GPI * L.exch_grp;
-    L.total = o + 1024;                         // + target of the padding copies
+    L.total = o;
     return L;
 }
 
 template <int G, int BC2, int NTW32>
 __global__ __launch_bounds__(64 * T2_NW, 1) void k_tail_t2(TailArgs a, int dz_mem, int n_granges) {
-    constexpr int NW = T2_NW, NT = 64 * NW, R = T2_R;
-    constexpr int GPI = t2_gpi(G, BC2), NBMAX = t2_nbmax(G, BC2);
+    constexpr int NT = 64 * T2_NW;
+    constexpr int GPI = t2_gpi(G, BC2);
     constexpr int JT = G / 16, BT = BC2 / 16, RT = BC2 / 32;
     constexpr int NU = BC2 / 8;                // 16-byte units per chunk row
     constexpr int GPR = G / 4, LGPR = G == 16 ? 2 : G == 32 ? 3 : 4;
@@ -633,18 +611,17 @@ __global__ __launch_bounds__(64 * T2_NW, 1) void k_tail_t2(TailArgs a, int dz_me
     constexpr int NTILE = GPI * JT * BT;       // 16x16 Z^T tiles per step
     constexpr int TPW = NTILE / T2_NZ;         // tiles per Z^T wave (same group and label tile)
     static_assert(NTILE % T2_NZ == 0 && BT % TPW == 0, "Z^T tile split");
-    constexpr int NB_T = T2_NB * 64;           // threads that build W^T
-    const int F = a.F, KS = F / 32, UPR = F / 8;
-    const int lupr = F == 128 ? 4 : F == 64 ? 3 : 2;       // log2(F/8)
-    const int swsh = UPR >= 8 ? 0 : 1;
+    constexpr int NB_T = T2_NB * 64;           // builder threads
+    constexpr int UPT = (GPI * GPR * 32 + NB_T - 1) / NB_T;   // W^T units per builder thread (F <= 128)
+    const int F = a.F, KS = F / 32;
+    const int lf4 = F == 128 ? 5 : F == 64 ? 4 : 3;        // log2(F/4)
+    const int lnq = LGPR + lf4;                             // log2(W^T units per group)
     const T2Lds LY = t2_layout(a.D, F, G, BC2, NTW32);
-    extern __shared__ __attribute__((aligned(1024))) unsigned char lds[];
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     unsigned char *tile = lds;
-    unsigned char *ring = lds + LY.ring;
     unsigned char *wts0 = lds + LY.wts;
     unsigned char *inv0 = lds + LY.inv;
     unsigned char *exch0 = lds + LY.exch;
-    unsigned char *pad = lds + LY.total - 1024;
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int hq = lane >> 4, m = lane & 15;
@@ -653,46 +630,9 @@ __global__ __launch_bounds__(64 * T2_NW, 1) void k_tail_t2(TailArgs a, int dz_me
     const int ng = (int)(gB - gA);
     const int nsteps = (ng + GPI - 1) / GPI;
     const int r0 = bch * BC2;
-    const int wblk = LY.wsz >> 10;
-    const int gstride = LY.wsz + 1024;
-    // wave roles (uniform): consumers 0..7, Z^T waves 8..11, W^T builders 12..15
+    // wave roles (uniform): consumers 0..7, Z^T waves 8..11, builders 12..15
     const int role = w < T2_NC ? 0 : w < T2_NC + T2_NZ ? 1 : 2;
-    const int dbase = w * NTW32 * 32;          // consumer's first feature
-
-    // Copy plan of a copying wave (loop invariant): block b = (w - T2_NC) +
-    // (T2_NZ + T2_NB) * i of a step is group q's W block `sub`, or its index
-    // block when sub == wblk.
-    int cp_q[NBMAX], cp_sub[NBMAX], cp_off[NBMAX];
-#pragma unroll
-    for (int i = 0; i < NBMAX; ++i) {
-        const int b = (w - T2_NC) + (T2_NZ + T2_NB) * i;
-        cp_q[i] = b / (wblk + 1);
-        cp_sub[i] = b - cp_q[i] * (wblk + 1);
-        const int p = cp_sub[i] * 64 + lane, r = p >> lupr, pc = p & (UPR - 1);
-        cp_off[i] = r * F + ((pc ^ ((r >> swsh) & (UPR - 1))) << 3);   // elements of W_g
-    }
-    auto issue = [&](int k, unsigned char *slot) {
-#pragma unroll
-        for (int i = 0; i < NBMAX; ++i) {
-            const int q = cp_q[i];
-            const int64_t g = gA + (int64_t)k * GPI + q;
-            const void *src = a.W + lane * 8;
-            unsigned char *dst = pad;
-            if (q < GPI && g < gB) {
-                unsigned char *gb = slot + q * gstride;
-                if (cp_sub[i] < wblk) {
-                    src = a.W + g * G * (int64_t)F + cp_off[i];
-                    dst = gb + cp_sub[i] * 1024;
-                } else {
-                    const int32_t *s = a.idx + g * (int64_t)F + (lane < F / 4 ? lane * 4 : 0);
-                    if (lane == F / 4 && !dz_mem) s = a.grp_ptr + g;
-                    src = s;
-                    dst = gb + LY.wsz;
-                }
-            }
-            __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
-        }
-    };
+    auto live = [&](int k, int q) { return gA + (int64_t)k * GPI + q < gB; };
 
     {   // stage the chunk (units rotated by row), reset the inverse maps, zero rows
         const unsigned short *src = a.XT + r0;
@@ -702,207 +642,63 @@ __global__ __launch_bounds__(64 * T2_NW, 1) void k_tail_t2(TailArgs a, int dz_me
                 *(const u32x4 *)(src + (int64_t)d * a.Bp + u * 8);
         }
         const unsigned fill = (unsigned)F * 0x01010101u;
-        for (int i = tid; i < 3 * GPI * NDP / 4; i += NT) ((unsigned *)inv0)[i] = fill;
-        for (int i = tid; i < 2 * GPI * (G / 2); i += NT)
+        for (int i = tid; i < 4 * GPI * NDP / 4; i += NT) ((unsigned *)inv0)[i] = fill;
+        for (int i = tid; i < 3 * GPI * (G / 2); i += NT)
             ((unsigned *)(wts0 + (i / (G / 2)) * LY.wts_grp + F * WTS))[i % (G / 2)] = 0u;
     }
-    // (1) Z^T of step k -> dz -> exch.  Z^T wave p takes tiles p*TPW .. +TPW-1:
-    // one group and label tile, TPW consecutive 16-row tiles, so the raw W rows
-    // and the index reads serve all of them.
-    auto zt = [&](int k, const unsigned char *slot, unsigned char *exch) {
-        const int tl0 = (w - T2_NC) * TPW;
-        const int q = tl0 / (JT * BT), jt = (tl0 % (JT * BT)) / BT, bt0 = tl0 % BT;
-        const int64_t g = gA + (int64_t)k * GPI + q;
-        if (g >= gB) return;
-        const unsigned char *gb = slot + q * gstride;
-        const int *ri = (const int *)(gb + LY.wsz);
-        float dzv[TPW][4];
-        if (!dz_mem) {
-            const int arow = 16 * jt + m;
-            const unsigned char *ab = gb + arow * F * 2;
-            const int asw = (arow >> swsh) & (UPR - 1);
-            const int ch = (m & 1) * 8;
-            const int *rl = ri + 8 * hq + (m >> 2);
-            f32x4 z[TPW];
-#pragma unroll
-            for (int t = 0; t < TPW; ++t) z[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {   // K steps of 32 features, F <= 128
-                if (s >= KS) break;
-                const bf16x8 Av = *(const bf16x8 *)(ab + (((4 * s + hq) ^ asw) << 4));
-                const int d0 = rl[32 * s], d1 = rl[32 * s + 4];
-#pragma unroll
-                for (int t = 0; t < TPW; ++t) {
-                    // chunk address of (row d, columns 16bt + 4(m%4) .. +3)
-                    const int cu16 = (2 * (bt0 + t) + ((m & 3) >> 1)) << 4;
-                    const i16x4 b0 = lds_read_tr(tile + ((d0 << LROW) | ((((d0 << 4) + cu16) & ((NU - 1) << 4)) | ch)));
-                    const i16x4 b1 = lds_read_tr(tile + ((d1 << LROW) | ((((d1 << 4) + cu16) & ((NU - 1) << 4)) | ch)));
-                    const bf16x8 Bv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
-                    z[t] = mfma32(Av, Bv, z[t]);
-                }
-            }
-            // positives of this group inside the wave's rows (lane owns labels 16jt+4hq+i)
-            const int gp0 = __builtin_amdgcn_readfirstlane(ri[F]);
-            const int gp1 = __builtin_amdgcn_readfirstlane(ri[F + 1]);
-            unsigned ymask[TPW];
-            bool has_pos = false;                // wave-uniform
-#pragma unroll
-            for (int t = 0; t < TPW; ++t) ymask[t] = 0;
-            for (int e = gp0; e < gp1; ++e) {
-                const int v = a.grp_ent[e];
-                const int lb = v / G - (r0 + 16 * bt0), j = v % G;
-                if (lb < 0 || lb >= 16 * TPW || (j >> 4) != jt) continue;
-                has_pos = true;
-#pragma unroll
-                for (int t = 0; t < TPW; ++t)
-                    if (lb == 16 * t + m && ((j >> 2) & 3) == hq) ymask[t] |= 1u << (j & 3);
-            }
-            // sigmoid(z) = 1 / (1 + 2^(-z log2 e)); saturates cleanly at both ends
-            if (!has_pos && r0 + 16 * (bt0 + TPW) <= a.B && (g + 1) * G <= a.L) {
-#pragma unroll
-                for (int t = 0; t < TPW; ++t)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        dzv[t][i] = a.s * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z[t][i] * -kLog2e));
-            } else {
-#pragma unroll
-                for (int t = 0; t < TPW; ++t)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int64_t lt = g * G + 16 * jt + 4 * hq + i;
-                        const bool live = r0 + 16 * (bt0 + t) + m < a.B && lt < a.L;
-                        const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z[t][i] * -kLog2e));
-                        dzv[t][i] = live ? a.s * (sg - (float)((ymask[t] >> i) & 1u)) : 0.f;
-                    }
-            }
-        } else {
-#pragma unroll
-            for (int t = 0; t < TPW; ++t)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = r0 + 16 * (bt0 + t) + m;
-                    const int64_t lt = g * G + 16 * jt + 4 * hq + i;
-                    const bool live = row < a.B && lt < a.L;
-                    dzv[t][i] = live ? bf16_to_f32(a.dZ[(int64_t)row * a.L + lt]) : 0.f;
-                }
-        }
-        // (row 16bt+m, label 16jt+4hq+i) -> A operand of the 32-row block bt/2:
-        // lane 16(bt%2)+m+32(hq/2), K slots 4(hq%2)+i
-#pragma unroll
-        for (int t = 0; t < TPW; ++t) {
-            const int bt = bt0 + t;
-            const int lane2 = 16 * (bt & 1) + m + 32 * (hq >> 1);
-            *(u32x2 *)(exch + q * LY.exch_grp + (((bt >> 1) * JT + jt) * 64 + lane2) * 16 + 8 * (hq & 1)) =
-                (u32x2){pack_bf16x2(dzv[t][0], dzv[t][1]), pack_bf16x2(dzv[t][2], dzv[t][3])};
-        }
-    };
-
-    // (2) W^T ([f][j], rows of WTS bytes) and the inverse index of step k, on
-    // the builder waves.  Thread = 4 labels x 4 features.  Four consecutive
-    // lanes take consecutive feature quads, then the label quads, then the
-    // next features: with the 8-byte row padding the writes of 16 lanes hit
-    // distinct banks.
-    const int lf4 = lupr + 1;                 // log2(F/4)
-    const int lnq = LGPR + lf4;               // log2(units per group)
-    const int bth = tid - (T2_NC + T2_NZ) * 64;
-    auto build = [&](int k, const unsigned char *slot, unsigned char *wts, unsigned char *inv) {
-        for (int u = bth; u < (GPI << lnq); u += NB_T) {
-            const int q = u >> lnq, rest = u & ((1 << lnq) - 1);
-            const int r2 = rest >> 2, ja = r2 & (GPR - 1), fc = ((r2 >> LGPR) << 2) | (rest & 3);
-            if (gA + (int64_t)k * GPI + q >= gB) continue;
-            const unsigned char *wq = slot + q * gstride;
-            u32x2 rr[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int row = 4 * ja + e;
-                rr[e] = *(const u32x2 *)(wq + row * F * 2 + (((fc >> 1) ^ ((row >> swsh) & (UPR - 1))) << 4) +
-                                         (fc & 1) * 8);
-            }
-            unsigned char *wt = wts + q * LY.wts_grp + (4 * fc) * WTS + 8 * ja;
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {   // feature 4fc+kk: element kk of each row
-                const unsigned sel = (kk & 1) ? 0x07060302u : 0x05040100u;
-                const int wd = kk >> 1;
-                const u32x2 o = {__builtin_amdgcn_perm(rr[1][wd], rr[0][wd], sel),
-                                 __builtin_amdgcn_perm(rr[3][wd], rr[2][wd], sel)};
-                *(u32x2 *)(wt + kk * WTS) = o;
-            }
-        }
-        for (int i = bth; i < GPI * F; i += NB_T) {
-            const int q = i / F, f = i - q * F;
-            if (gA + (int64_t)k * GPI + q >= gB) continue;
-            const int *ri = (const int *)(slot + q * gstride + LY.wsz);
-            inv[q * NDP + ri[f]] = (unsigned char)f;
-        }
-    };
-
-    // (3) dense product of step k on the consumer waves: all BC2 rows x the
-    // wave's NTW32 feature tiles; each B fetch feeds RT row blocks.
-    auto dense = [&](f32x16 (&acc)[RT][NTW32], int k, const unsigned char *wts, const unsigned char *inv,
-                     const unsigned char *exch) {
-#pragma unroll
-        for (int q = 0; q < GPI; ++q) {
-            if (gA + (int64_t)k * GPI + q >= gB) break;
-            const unsigned char *wt = wts + q * LY.wts_grp + 16 * (lane >> 5);
-            const unsigned char *iv = inv + q * NDP + dbase + (lane & 31);
-            const unsigned char *brow[NTW32];
-#pragma unroll
-            for (int nt = 0; nt < NTW32; ++nt) brow[nt] = wt + iv[32 * nt] * WTS;
-#pragma unroll
-            for (int jt = 0; jt < JT; ++jt) {
-                bf16x8 Am[RT];
-#pragma unroll
-                for (int rt = 0; rt < RT; ++rt)
-                    Am[rt] = *(const bf16x8 *)(exch + q * LY.exch_grp + ((rt * JT + jt) * 64 + lane) * 16);
-#pragma unroll
-                for (int nt = 0; nt < NTW32; ++nt) {   // labels 16jt + 8(lane/32) .. +7 of row f
-                    const u32x2 lo = *(const u32x2 *)(brow[nt] + 32 * jt);
-                    const u32x2 hi = *(const u32x2 *)(brow[nt] + 32 * jt + 8);
-                    const bf16x8 Bv = __builtin_bit_cast(bf16x8, (u32x4){lo[0], lo[1], hi[0], hi[1]});
-#pragma unroll
-                    for (int rt = 0; rt < RT; ++rt) acc[rt][nt] = mfma32x32(Am[rt], Bv, acc[rt][nt]);
-                }
-            }
-        }
-    };
-
-    // Ring: steps 0..R-1 are loaded up front; iteration k refills the slot of
-    // step k (last read by the Z^T and W^T work of step k in iteration k-1,
-    // before the barrier that closed it) with step k+R.
     __syncthreads();
-    if (role != 0)
-        for (int k = 0; k < R; ++k) issue(k, ring + k * LY.slot);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (nsteps > 0) {
-        if (role == 1) zt(0, ring, exch0);
-        if (role == 2) build(0, ring, wts0, inv0);
-    }
-    __syncthreads();
+
     // Per-iteration tail shared by all roles: clear the inverse index of step
-    // k-1 (no longer read), wait for the copies of step k+2 (vector-memory
-    // results return in issue order), barrier.  Consumers run their own loop
-    // so that their accumulators are not live in the other roles' code.
+    // k-1 (no longer read), barrier.  Each role runs its own loop so that its
+    // registers are not live in the other roles' code; every loop passes the
+    // same number of barriers.
     const unsigned fill = (unsigned)F * 0x01010101u;
-    auto close_step = [&](int ic) {
-        const int ip = ic == 0 ? 2 : ic - 1;
-        unsigned *ivp = (unsigned *)(inv0 + ip * GPI * NDP);
+    auto close_step = [&](int k) {
+        unsigned *ivp = (unsigned *)(inv0 + ((k + 3) & 3) * GPI * NDP);
         for (int i = tid; i < GPI * NDP / 4; i += NT) ivp[i] = fill;
-        vm_wait_c<NBMAX>();
         lds_barrier();
     };
+
     if (role == 0) {
+        // ---------------------------------------------------------- consumers
+        const int dbase = w * NTW32 * 32;      // first feature of this wave
         f32x16 acc[RT][NTW32];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int nt = 0; nt < NTW32; ++nt) acc[rt][nt] = (f32x16){};
-        int ic = 0;   // inverse-index buffer of step k
+        __syncthreads();                       // prologue of the other roles
+        int sw = 0;                            // W^T buffer of step k (k mod 3)
         for (int k = 0; k < nsteps; ++k) {
-            const int bc = k & 1;
-            dense(acc, k, wts0 + bc * GPI * LY.wts_grp, inv0 + ic * GPI * NDP, exch0 + bc * GPI * LY.exch_grp);
-            close_step(ic);
-            ic = ic == 2 ? 0 : ic + 1;
+            const unsigned char *wts = wts0 + sw * GPI * LY.wts_grp;
+            const unsigned char *inv = inv0 + (k & 3) * GPI * NDP;
+            const unsigned char *exch = exch0 + (k & 1) * GPI * LY.exch_grp;
+#pragma unroll
+            for (int q = 0; q < GPI; ++q) {
+                if (!live(k, q)) break;
+                const unsigned char *wt = wts + q * LY.wts_grp + 16 * (lane >> 5);
+                const unsigned char *iv = inv + q * NDP + dbase + (lane & 31);
+                const unsigned char *brow[NTW32];
+#pragma unroll
+                for (int nt = 0; nt < NTW32; ++nt) brow[nt] = wt + iv[32 * nt] * WTS;
+#pragma unroll
+                for (int jt = 0; jt < JT; ++jt) {
+                    bf16x8 Am[RT];
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt)
+                        Am[rt] = *(const bf16x8 *)(exch + q * LY.exch_grp + ((rt * JT + jt) * 64 + lane) * 16);
+#pragma unroll
+                    for (int nt = 0; nt < NTW32; ++nt) {   // labels 16jt + 8(lane/32) .. +7 of row f
+                        const u32x2 lo = *(const u32x2 *)(brow[nt] + 32 * jt);
+                        const u32x2 hi = *(const u32x2 *)(brow[nt] + 32 * jt + 8);
+                        const bf16x8 Bv = __builtin_bit_cast(bf16x8, (u32x4){lo[0], lo[1], hi[0], hi[1]});
+#pragma unroll
+                        for (int rt = 0; rt < RT; ++rt) acc[rt][nt] = mfma32x32(Am[rt], Bv, acc[rt][nt]);
+                    }
+                }
+            }
+            close_step(k);
+            sw = sw == 2 ? 0 : sw + 1;
         }
         // flush: reg r of tile (rt, nt) = row 32rt+8(r/4)+4(lane/32)+r%4, feature dbase+32nt+lane%32
 #pragma unroll
@@ -917,27 +713,227 @@ __global__ __launch_bounds__(64 * T2_NW, 1) void k_tail_t2(TailArgs a, int dz_me
                     if (row < a.B) atomicAdd(a.dX + (int64_t)row * a.D + d, acc[rt][nt][r]);
                 }
             }
-    } else {
-        int sc = 0, ic = 0;
-        for (int k = 0; k < nsteps; ++k) {
-            issue(k + R, ring + sc * LY.slot);
-            const int sn = sc == R - 1 ? 0 : sc + 1;
-            const int in = ic == 2 ? 0 : ic + 1;
-            const int bn = (k + 1) & 1;
-            if (k + 1 < nsteps) {
-                if (role == 1) {
-                    __builtin_amdgcn_s_setprio(2);   // short latency chain: issue ahead of the MFMA stream
-                    zt(k + 1, ring + sn * LY.slot, exch0 + bn * GPI * LY.exch_grp);
-                    __builtin_amdgcn_s_setprio(0);
-                } else {
-                    build(k + 1, ring + sn * LY.slot, wts0 + bn * GPI * LY.wts_grp, inv0 + in * GPI * NDP);
+    } else if (role == 1) {
+        // ------------------------------------------------------------ Z^T waves
+        // Wave p takes tiles p*TPW .. +TPW-1 of a step: one group q and label
+        // tile jt, TPW consecutive 16-row tiles bt0.. (lane (hq, m) owns labels
+        // 16jt + 4hq .. +3 of row 16bt + m in each).
+        const int tl0 = (w - T2_NC) * TPW;
+        const int q = tl0 / (JT * BT), jt = (tl0 % (JT * BT)) / BT, bt0 = tl0 % BT;
+        const int ch = (m & 1) * 8;
+        struct Ops {            // operands of one step, loaded four steps ahead
+            int d[8];           // idx[32s + 8hq + m/4] and idx[.. + 4], s < KS
+            u32x4 A[4];         // W row 16jt+m, features 32s + 8hq .. +7
+            int gp0, gp1;       // group-major positives of the group
+        };
+        auto fetch = [&](int k, Ops &o) {
+            if (!live(k, q)) return;
+            const int64_t g = gA + (int64_t)k * GPI + q;
+            if (!dz_mem) {
+                const int32_t *ix = a.idx + g * F + 8 * hq + (m >> 2);
+                const unsigned short *wr = a.W + (g * G + 16 * jt + m) * (int64_t)F + 8 * hq;
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    if (s >= KS) break;
+                    o.d[2 * s] = ix[32 * s];
+                    o.d[2 * s + 1] = ix[32 * s + 4];
+                    o.A[s] = *(const u32x4 *)(wr + 32 * s);
+                }
+                o.gp0 = a.grp_ptr[g];
+                o.gp1 = a.grp_ptr[g + 1];
+            }
+        };
+        f32x4 z[TPW];
+        int zg0 = 0, zg1 = 0;   // pointer pair of the step whose Z^T is in z
+        // gather + MFMAs of step k into z
+        auto part1 = [&](int k, const Ops &o) {
+            if (!live(k, q) || dz_mem) return;
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) z[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+            i16x4 b[4][TPW][2];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                if (s >= KS) break;
+#pragma unroll
+                for (int t = 0; t < TPW; ++t) {
+                    // chunk address of (row d, columns 16bt + 4(m%4) .. +3)
+                    const int cu16 = (2 * (bt0 + t) + ((m & 3) >> 1)) << 4;
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const int d = o.d[2 * s + h];
+                        b[s][t][h] = lds_read_tr(tile + ((d << LROW) | ((((d << 4) + cu16) & ((NU - 1) << 4)) | ch)));
+                    }
                 }
             }
-            close_step(ic);
-            sc = sn;
-            ic = in;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                if (s >= KS) break;
+                const bf16x8 Av = __builtin_bit_cast(bf16x8, o.A[s]);
+#pragma unroll
+                for (int t = 0; t < TPW; ++t) {
+                    const bf16x8 Bv = __builtin_bit_cast(
+                        bf16x8, __builtin_shufflevector(b[s][t][0], b[s][t][1], 0, 1, 2, 3, 4, 5, 6, 7));
+                    z[t] = mfma32(Av, Bv, z[t]);
+                }
+            }
+            zg0 = __builtin_amdgcn_readfirstlane(o.gp0);
+            zg1 = __builtin_amdgcn_readfirstlane(o.gp1);
+        };
+        // sigmoid-BCE of step k (Z^T in z) -> dz -> exch
+        auto epilogue = [&](int k) {
+            if (!live(k, q)) return;
+            const int64_t g = gA + (int64_t)k * GPI + q;
+            float dzv[TPW][4];
+            if (!dz_mem) {
+                // positives of this group inside the wave's rows
+                unsigned ymask[TPW];
+                bool has_pos = false;                // wave-uniform
+#pragma unroll
+                for (int t = 0; t < TPW; ++t) ymask[t] = 0;
+                for (int e = zg0; e < zg1; ++e) {
+                    const int v = a.grp_ent[e];
+                    const int lb = v / G - (r0 + 16 * bt0), j = v % G;
+                    if (lb < 0 || lb >= 16 * TPW || (j >> 4) != jt) continue;
+                    has_pos = true;
+#pragma unroll
+                    for (int t = 0; t < TPW; ++t)
+                        if (lb == 16 * t + m && ((j >> 2) & 3) == hq) ymask[t] |= 1u << (j & 3);
+                }
+                // sigmoid(z) = 1 / (1 + 2^(-z log2 e)); saturates cleanly at both ends
+                if (!has_pos && r0 + 16 * (bt0 + TPW) <= a.B && (g + 1) * G <= a.L) {
+#pragma unroll
+                    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            dzv[t][i] = a.s * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z[t][i] * -kLog2e));
+                } else {
+#pragma unroll
+                    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int64_t lt = g * G + 16 * jt + 4 * hq + i;
+                            const bool on = r0 + 16 * (bt0 + t) + m < a.B && lt < a.L;
+                            const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z[t][i] * -kLog2e));
+                            dzv[t][i] = on ? a.s * (sg - (float)((ymask[t] >> i) & 1u)) : 0.f;
+                        }
+                }
+            } else {
+#pragma unroll
+                for (int t = 0; t < TPW; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int row = r0 + 16 * (bt0 + t) + m;
+                        const int64_t lt = g * G + 16 * jt + 4 * hq + i;
+                        const bool on = row < a.B && lt < a.L;
+                        dzv[t][i] = on ? bf16_to_f32(a.dZ[(int64_t)row * a.L + lt]) : 0.f;
+                    }
+            }
+            // (row 16bt+m, label 16jt+4hq+i) -> A operand of the 32-row block bt/2:
+            // lane 16(bt%2)+m+32(hq/2), K slots 4(hq%2)+i
+            unsigned char *ex = exch0 + (k & 1) * GPI * LY.exch_grp + q * LY.exch_grp;
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+                const int bt = bt0 + t;
+                const int lane2 = 16 * (bt & 1) + m + 32 * (hq >> 1);
+                *(u32x2 *)(ex + (((bt >> 1) * JT + jt) * 64 + lane2) * 16 + 8 * (hq & 1)) =
+                    (u32x2){pack_bf16x2(dzv[t][0], dzv[t][1]), pack_bf16x2(dzv[t][2], dzv[t][3])};
+            }
+        };
+        Ops oA, oB;
+        fetch(0, oA);
+        fetch(1, oB);
+        part1(0, oA);
+        epilogue(0);
+        fetch(2, oA);
+        part1(1, oB);
+        fetch(3, oB);
+        __syncthreads();
+        // iteration k: oA (k even) / oB (k odd) holds step k+2 and then receives step k+4
+        auto iter = [&](int k, Ops &o) {
+            __builtin_amdgcn_s_setprio(2);     // short chain: issue ahead of the MFMA stream
+            epilogue(k + 1);
+            part1(k + 2, o);
+            __builtin_amdgcn_s_setprio(0);
+            fetch(k + 4, o);
+            close_step(k);
+        };
+        for (int k = 0; k < nsteps; k += 2) {   // unrolled by two: the operand sets alternate
+            iter(k, oA);
+            if (k + 1 < nsteps) iter(k + 1, oB);
         }
-        __builtin_amdgcn_s_waitcnt(0);   // padding copies still in flight
+    } else {
+        // ------------------------------------------------------------- builders
+        // Thread = 4 labels x 4 features of W_g.  Four consecutive lanes take
+        // consecutive feature quads, then the label quads, then the next
+        // features: with the 8-byte row padding the W^T writes of 16 lanes
+        // hit distinct banks.
+        const int bth = tid - (T2_NC + T2_NZ) * 64;
+        struct Ops {
+            u32x2 r[UPT][4];    // rows 4ja+e, features 4fc .. +3, per unit
+            int fi;             // idx[f] of the inverse-index entry of this thread
+        };
+        auto unit = [&](int i, int &q, int &fc, int &ja) {
+            const int u = bth + NB_T * i;
+            q = u >> lnq;
+            const int rest = u & ((1 << lnq) - 1), r2 = rest >> 2;
+            ja = r2 & (GPR - 1);
+            fc = ((r2 >> LGPR) << 2) | (rest & 3);
+        };
+        auto fetch = [&](int k, Ops &o) {
+#pragma unroll
+            for (int i = 0; i < UPT; ++i) {
+                int q, fc, ja;
+                unit(i, q, fc, ja);
+                if (bth + NB_T * i >= (GPI << lnq) || !live(k, q)) continue;
+                const int64_t g = gA + (int64_t)k * GPI + q;
+                const unsigned short *wr = a.W + (g * G + 4 * ja) * (int64_t)F + 4 * fc;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o.r[i][e] = *(const u32x2 *)(wr + e * F);
+            }
+            if (bth < GPI * F) {
+                const int q = bth / F;
+                if (live(k, q)) o.fi = a.idx[(gA + (int64_t)k * GPI + q) * F + (bth - q * F)];
+            }
+        };
+        auto build = [&](int k, const Ops &o) {
+            unsigned char *wts = wts0 + (k % 3) * GPI * LY.wts_grp;
+#pragma unroll
+            for (int i = 0; i < UPT; ++i) {
+                int q, fc, ja;
+                unit(i, q, fc, ja);
+                if (bth + NB_T * i >= (GPI << lnq) || !live(k, q)) continue;
+                unsigned char *wt = wts + q * LY.wts_grp + (4 * fc) * WTS + 8 * ja;
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {   // feature 4fc+kk: element kk of each row
+                    const unsigned sel = (kk & 1) ? 0x07060302u : 0x05040100u;
+                    const int wd = kk >> 1;
+                    const u32x2 v = {__builtin_amdgcn_perm(o.r[i][1][wd], o.r[i][0][wd], sel),
+                                     __builtin_amdgcn_perm(o.r[i][3][wd], o.r[i][2][wd], sel)};
+                    *(u32x2 *)(wt + kk * WTS) = v;
+                }
+            }
+            if (bth < GPI * F) {
+                const int q = bth / F;
+                if (live(k, q)) inv0[((k & 3) * GPI + q) * NDP + o.fi] = (unsigned char)(bth - q * F);
+            }
+        };
+        Ops oA, oB;
+        fetch(0, oA);
+        fetch(1, oB);
+        build(0, oA);
+        build(1, oB);
+        fetch(2, oA);
+        fetch(3, oB);
+        __syncthreads();
+        auto iter = [&](int k, Ops &o) {
+            build(k + 2, o);
+            fetch(k + 4, o);
+            close_step(k);
+        };
+        for (int k = 0; k < nsteps; k += 2) {
+            iter(k, oA);
+            if (k + 1 < nsteps) iter(k + 1, oB);
+        }
     }
 }
 
@@ -990,13 +986,14 @@ static hipError_t t2_pick_ntw(bool dz_mem, const TailArgs &a, hipStream_t st) {
 // 64-row chunks when they fit in LDS, the batch is larger than 32 rows and
 // the accumulator (2 x NTW32 32x32 tiles per consumer) stays within 96 registers
 static int t2_bc(int G, int F, int D, int B) {
-    if (B > 32 && t2_ntw(D, 64) <= 3 && t2_fits(D, F, G, 64, t2_ntw(D, 64))) return 64;
+    if (G < 64 && B > 32 && t2_ntw(D, 64) <= 3 && t2_fits(D, F, G, 64, t2_ntw(D, 64))) return 64;
     return 32;
 }
 
 template <int G>
 static hipError_t t2_pick(bool dz_mem, const TailArgs &a, hipStream_t st) {
-    if (t2_bc(G, a.F, a.D, a.B) == 64) return t2_pick_ntw<G, 64>(dz_mem, a, st);
+    if constexpr (G < 64)   // G = 64 always takes 32-row chunks (16 Z^T tiles per 64 rows)
+        if (t2_bc(G, a.F, a.D, a.B) == 64) return t2_pick_ntw<G, 64>(dz_mem, a, st);
     return t2_pick_ntw<G, 32>(dz_mem, a, st);
 }
 
