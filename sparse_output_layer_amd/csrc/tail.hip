@@ -564,7 +564,8 @@ hipError_t launch_tail_t1(int mode, int G, const TailArgs &a, bool store_z, bool
 //   Z^T waves: sigmoid-BCE epilogue of step k+1 (from the Z^T accumulators
 //     of the previous iteration) -> dz, stored in LDS in the A-operand layout
 //     of the 32x32x16 product; gather (transposing reads of the chunk at rows
-//     idx) and MFMAs of step k+2; load the operands of step k+4;
+//     idx) and MFMAs of step k+2 and the load of its positives; load the
+//     operands of step k+4;
 //   builders: W^T ([f][j]) and the inverse index of step k+2; load step k+4;
 //   all: clear the inverse index of step k-1, barrier.
 //
@@ -727,29 +728,27 @@ __global__ __launch_bounds__(64 * T2_NW, 1) void k_tail_t2(TailArgs a, int dz_me
             int gp0, gp1;       // group-major positives of the group
         };
         auto fetch = [&](int k, Ops &o) {
-            if (!live(k, q)) return;
+            if (!live(k, q) || dz_mem) return;
             const int64_t g = gA + (int64_t)k * GPI + q;
-            if (!dz_mem) {
-                const int32_t *ix = a.idx + g * F + 8 * hq + (m >> 2);
-                const unsigned short *wr = a.W + (g * G + 16 * jt + m) * (int64_t)F + 8 * hq;
+            const int32_t *ix = a.idx + g * F + 8 * hq + (m >> 2);
+            const unsigned short *wr = a.W + (g * G + 16 * jt + m) * (int64_t)F + 8 * hq;
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    if (s >= KS) break;
-                    o.d[2 * s] = ix[32 * s];
-                    o.d[2 * s + 1] = ix[32 * s + 4];
-                    o.A[s] = *(const u32x4 *)(wr + 32 * s);
-                }
-                o.gp0 = a.grp_ptr[g];
-                o.gp1 = a.grp_ptr[g + 1];
+            for (int s = 0; s < 4; ++s) {
+                if (s >= KS) break;
+                o.d[2 * s] = ix[32 * s];
+                o.d[2 * s + 1] = ix[32 * s + 4];
+                o.A[s] = *(const u32x4 *)(wr + 32 * s);
             }
+            o.gp0 = a.grp_ptr[g];
+            o.gp1 = a.grp_ptr[g + 1];
         };
-        f32x4 z[TPW];
-        int zg0 = 0, zg1 = 0;   // pointer pair of the step whose Z^T is in z
-        // gather + MFMAs of step k into z
+        f32x4 z[TPW];           // Z^T of the step in flight (from the MFMAs of the previous iteration)
+        int zg0 = 0, zn = 0;    // its positives: first entry and count (uniform)
+        int pe = 0;             // entry zg0 + lane, lane < min(zn, 64)
+        // transposing reads of the chunk at rows idx, then the MFMAs, of step
+        // k into z; and the load of its positives
         auto part1 = [&](int k, const Ops &o) {
             if (!live(k, q) || dz_mem) return;
-#pragma unroll
-            for (int t = 0; t < TPW; ++t) z[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
             i16x4 b[4][TPW][2];
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
@@ -766,6 +765,8 @@ __global__ __launch_bounds__(64 * T2_NW, 1) void k_tail_t2(TailArgs a, int dz_me
                 }
             }
 #pragma unroll
+            for (int t = 0; t < TPW; ++t) z[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
             for (int s = 0; s < 4; ++s) {
                 if (s >= KS) break;
                 const bf16x8 Av = __builtin_bit_cast(bf16x8, o.A[s]);
@@ -777,7 +778,8 @@ __global__ __launch_bounds__(64 * T2_NW, 1) void k_tail_t2(TailArgs a, int dz_me
                 }
             }
             zg0 = __builtin_amdgcn_readfirstlane(o.gp0);
-            zg1 = __builtin_amdgcn_readfirstlane(o.gp1);
+            zn = __builtin_amdgcn_readfirstlane(o.gp1) - zg0;
+            pe = lane < zn ? a.grp_ent[zg0 + lane] : 0;
         };
         // sigmoid-BCE of step k (Z^T in z) -> dz -> exch
         auto epilogue = [&](int k) {
@@ -790,8 +792,8 @@ __global__ __launch_bounds__(64 * T2_NW, 1) void k_tail_t2(TailArgs a, int dz_me
                 bool has_pos = false;                // wave-uniform
 #pragma unroll
                 for (int t = 0; t < TPW; ++t) ymask[t] = 0;
-                for (int e = zg0; e < zg1; ++e) {
-                    const int v = a.grp_ent[e];
+                for (int e = 0; e < zn; ++e) {
+                    const int v = e < 64 ? __builtin_amdgcn_readlane(pe, e) : a.grp_ent[zg0 + e];
                     const int lb = v / G - (r0 + 16 * bt0), j = v % G;
                     if (lb < 0 || lb >= 16 * TPW || (j >> 4) != jt) continue;
                     has_pos = true;
@@ -848,7 +850,8 @@ __global__ __launch_bounds__(64 * T2_NW, 1) void k_tail_t2(TailArgs a, int dz_me
         part1(1, oB);
         fetch(3, oB);
         __syncthreads();
-        // iteration k: oA (k even) / oB (k odd) holds step k+2 and then receives step k+4
+        // iteration k: z holds step k+1; oA (k even) / oB (k odd) holds step k+2
+        // and then receives step k+4
         auto iter = [&](int k, Ops &o) {
             __builtin_amdgcn_s_setprio(2);     // short chain: issue ahead of the MFMA stream
             epilogue(k + 1);
