@@ -38,7 +38,35 @@ def parse():
     p.add_argument("--config", default="c2", help="workload name in workloads.CONFIGS")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target CPU time of the oracle baseline sample (0 = skip)")
+    p.add_argument("--calib-mib", type=int, default=0,
+                   help="after timing, one device-to-device copy of this many MiB: the "
+                        "known-size reference for the FETCH_SIZE / WRITE_SIZE counters")
     return p.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def source_digest(path):
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(kernel, launch_key):
+    """HBM bytes per launch of `kernel` from the committed counter runs
+    (profiles/traffic.json), or None when there are none for this workload or
+    when the kernel's source changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)[kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    src = os.path.join(ROOT, rec["source"])
+    if rec.get("workload") != launch_key or not os.path.exists(src) \
+            or source_digest(src) != rec["source_sha256"]:
+        return None
+    return rec["fetch_bytes"] + rec["write_bytes"]
 
 
 def algorithmic(cfg):
@@ -223,7 +251,8 @@ def main():
                    "global_batch": B, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(a_tf, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(a_tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(a_tf / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(dom, cfg.name),
                      "algorithmic_flops_per_launch": alg[dom]["flops"],
                      "avg_launch_us": round(per[dom], 2)},
         "step_roofline": {"algorithmic_tflop": round(tot_flops / 1e12, 4),
@@ -237,6 +266,14 @@ def main():
         "wall_s": round(wall, 3),
         "gen_s": round(t_gen, 2),
     }
+    if args.calib_mib > 0:
+        n = args.calib_mib << 20
+        src_t = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst_t = torch.empty(n, dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        dst_t.copy_(src_t)
+        torch.cuda.synchronize()
+        del src_t, dst_t
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     print(json.dumps(out), flush=True)

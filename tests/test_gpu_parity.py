@@ -78,6 +78,20 @@ def test_bf16_tail_and_head(H, case):
     torch.cuda.synchronize()
     assert torch.equal(dW, dW2)
 
+    # split form of the step (prepare, dW, dX), as the benchmark runs it
+    b5 = d.bce(c.H, s)
+    ws = torch.empty(H.haste_tail_workspace_bytes(d.X, d.idx, c.L, c.G, b5), dtype=torch.uint8,
+                     device=DEV)
+    dW5 = torch.empty_like(d.W)
+    dX5 = torch.full_like(dX, 2.0)
+    H.haste_tail_prepare(d.X, d.idx, c.L, c.G, b5, ws)
+    H.haste_tail_step_dw(d.X, d.idx, d.W, c.L, c.G, b5, dW5, ws)
+    H.haste_tail_step_dx(d.X, d.idx, d.W, c.L, c.G, b5, dX5, ws, accumulate_dX=True)
+    torch.cuda.synchronize()
+    check_loss("split step loss", b5.loss.item(), r.loss_tail, "bf16")
+    assert torch.equal(dW5, dW)
+    check("split step dX", to_f64(dX5) - 2.0, r.dX_tail, r.dX_tail_abs, "bf16", nterms=ng * c.G)
+
     # tail backward, recomputing dz from the positives (no loss added)
     dW3 = torch.empty_like(d.W)
     dX3 = torch.zeros_like(dX)
