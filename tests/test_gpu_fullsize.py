@@ -1,0 +1,116 @@
+"""Parity at the workloads' full sizes, in the launch configuration that
+bench.py times (haste_head_step, then haste_tail_prepare, haste_tail_step_dw
+and haste_tail_step_dx on one stream, head and tail accumulating into one
+dX).  The oracle cannot evaluate these steps whole in test time, so the
+checks are on outputs it computes one by one:
+
+  - dW of sampled tail groups (all rows), including the ragged last group;
+  - dWh of sampled head labels (all rows);
+  - dX of sampled rows (all head and tail labels);
+  - the total loss, streamed over chunks of groups.
+
+The top-K of the 8.6M-label workload is not built; that workload is checked
+without it."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from _gpu import DEV, Dev, check, check_loss, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def H():
+    from sparse_output_layer_amd import haste
+    haste.lib()
+    return haste
+
+
+def _sample(n, fixed, extra, rng):
+    pick = [i for i in fixed if 0 <= i < n] + list(rng.integers(0, n, size=extra))
+    return np.array(sorted(set(int(i) for i in pick)), dtype=np.int32)
+
+
+@pytest.mark.parametrize("name", ["c2", "c3", "c4", "c5"])
+def test_full_size_step(H, name):
+    print("full-size step", name, flush=True)
+    cfg = wl.CONFIGS[name].replace(topk=0)
+    inp = wl.make_inputs(cfg)
+    c = inp.cfg
+    B, D, L, G, Hn = c.B, c.D, c.L, c.G, c.H
+    ng = c.n_groups
+    s = 1.0 / B
+    d = Dev(inp)
+
+    # the benchmark's step
+    loss = torch.zeros(1, dtype=torch.float32, device=DEV)
+    bh = H.Bce(d.row_ptr, d.labels, 0, s, loss)
+    bt = H.Bce(d.row_ptr, d.labels, Hn, s, loss)
+    dX = torch.empty(B, D, dtype=torch.float32, device=DEV)
+    dWh = torch.empty_like(d.Wh)
+    dW = torch.empty_like(d.W)
+    ws_t = torch.empty(H.haste_tail_workspace_bytes(d.X, d.idx, L, G, bt), dtype=torch.uint8,
+                       device=DEV)
+    ws_h = torch.empty(max(256, H.haste_head_workspace_bytes(d.X, d.Wh, bh)), dtype=torch.uint8,
+                       device=DEV)
+    H.haste_head_step(d.X, d.Wh, bh, dWh, dX, workspace=ws_h)
+    H.haste_tail_prepare(d.X, d.idx, L, G, bt, ws_t)
+    H.haste_tail_step_dw(d.X, d.idx, d.W, L, G, bt, dW, ws_t)
+    H.haste_tail_step_dx(d.X, d.idx, d.W, L, G, bt, dX, ws_t, accumulate_dX=True)
+    torch.cuda.synchronize()
+    print("  GPU step done", flush=True)
+
+    X = inp.X_f64()
+    Wt = inp.W_f64()
+    Wh = inp.Wh_f64()
+    rng = np.random.default_rng(12345)
+    gp, _ = oracle.group_positives(inp.row_ptr, inp.labels, Hn, L, G)
+    with_pos = np.nonzero(np.diff(gp) > 0)[0]
+
+    # dW of sampled groups (all rows); padded label rows must be zero
+    groups = _sample(ng, [0, 1, ng // 2, ng - 1] + list(with_pos[:3]), 3, rng)
+    dW_h = dW.view(torch.int16).cpu().numpy().view(np.uint16)
+    for g in groups:
+        g = int(g)
+        Z, _ = oracle.tail_logits(X, inp.idx, Wt, L, G, g0=g, g1=g + 1, want_abs=False)
+        nl = Z.shape[1]
+        Y = oracle.positive_mask(inp.row_ptr, inp.labels, Hn + g * G, nl)
+        dz, _ = oracle.bce(Z, Y, s)
+        rW, rWa = oracle.tail_dW(X, inp.idx, dz, L, G, g0=g, g1=g + 1)
+        got = wl.f64_from_bf16_bits(dW_h[g * G:g * G + nl])
+        check(f"dW group {g}", got, rW, rWa, "bf16", nterms=B)
+        assert np.all(dW_h[g * G + nl:(g + 1) * G] == 0), f"padded rows of group {g}"
+
+    # head: logits of all rows (small), dWh of sampled labels
+    Zh, _ = oracle.head_logits(X, Wh, want_abs=False)
+    Yh = oracle.positive_mask(inp.row_ptr, inp.labels, 0, Hn)
+    dzh, lth = oracle.bce(Zh, Yh, s)
+    labs = _sample(Hn, [0, 1, Hn // 2, Hn - 1], 4, rng)
+    rWh, rWha = oracle.head_dW(X, dzh[:, labs])
+    got = to_f64(dWh[torch.from_numpy(labs).long().to(DEV)])
+    check("dWh sampled labels", got, rWh, rWha, "bf16", nterms=B)
+
+    # dX of sampled rows over every head and tail label
+    rows = _sample(B, [0, 1, B // 2, B - 1], 2, rng)
+    Zr, _ = oracle.tail_logits(X, inp.idx, Wt, L, G, rows=rows, want_abs=False)
+    Yr = oracle.positive_mask(inp.row_ptr, inp.labels, Hn, L, rows=rows)
+    dzr, _ = oracle.bce(Zr, Yr, s)
+    rXt, rXta = oracle.tail_dX(inp.idx, Wt, dzr, D, L, G)
+    rXh, rXha = oracle.head_dX(Wh, dzh[rows])
+    got = to_f64(dX[torch.from_numpy(rows).long().to(DEV)])
+    check("dX sampled rows", got, rXt + rXh, rXta + rXha, "bf16", nterms=ng * G + Hn)
+    print("  sampled outputs match", flush=True)
+
+    # total loss: head from the full head logits, tail streamed over groups
+    ref_loss = float(lth.sum())
+    chunk = max(1, (1 << 24) // (B * G))
+    for g0 in range(0, ng, chunk):
+        g1 = min(ng, g0 + chunk)
+        Z, _ = oracle.tail_logits(X, inp.idx, Wt, L, G, g0=g0, g1=g1, want_abs=False)
+        Y = oracle.positive_mask(inp.row_ptr, inp.labels, Hn + g0 * G, Z.shape[1])
+        _, lt = oracle.bce(Z, Y, s)
+        ref_loss += float(lt.sum())
+    check_loss("step loss", loss.item(), ref_loss, "bf16")
