@@ -298,7 +298,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, int store_z,
         bf16x8 wreg[RW][KS][JT];
         unsigned zrow[RW][KS];            // tr-gather rows: lo16 = h 0, hi16 = h 1
         unsigned frow[RW][FT / 2];        // dW rows, two f-tiles per word
-        int gp0[RW], gp1[RW];             // positives range per group
+        int gp0[RW], pn[RW], pe[RW];      // positives per group: first, count, entry per lane
         f32x4 dwacc[RW][FT][JT];
 #pragma unroll
         for (int r = 0; r < RW; ++r) {
@@ -322,10 +322,11 @@ __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, int store_z,
 #pragma unroll
             for (int p = 0; p < FT / 2; ++p)
                 frow[r][p] = (unsigned)ix[32 * p + m] | ((unsigned)ix[32 * p + 16 + m] << 16);
-            gp0[r] = gp1[r] = 0;
+            gp0[r] = pn[r] = pe[r] = 0;
             if (need_pos && ok) {
-                gp0[r] = a.grp_ptr[g];
-                gp1[r] = a.grp_ptr[g + 1];
+                gp0[r] = __builtin_amdgcn_readfirstlane(a.grp_ptr[g]);
+                pn[r] = __builtin_amdgcn_readfirstlane(a.grp_ptr[g + 1]) - gp0[r];
+                pe[r] = lane < pn[r] ? a.grp_ent[gp0[r] + lane] : 0;
             }
 #pragma unroll
             for (int ft = 0; ft < FT; ++ft)
@@ -350,8 +351,8 @@ __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, int store_z,
                 // positives of group g in rows [r0, r0+32): lane owns rows r0+16h2+4q+i, slot 16jt+m
                 uint64_t ymask = 0;
                 bool has_pos = false;             // wave-uniform
-                for (int e = gp0[r]; e < gp1[r]; ++e) {
-                    const int v = a.grp_ent[e];
+                for (int e = 0; e < pn[r]; ++e) {
+                    const int v = e < 64 ? __builtin_amdgcn_readlane(pe[r], e) : a.grp_ent[gp0[r] + e];
                     const int lb = v / G - r0, j = v % G;
                     if (lb < 0 || lb >= BC) continue;
                     has_pos = true;
