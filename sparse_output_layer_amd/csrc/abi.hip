@@ -60,11 +60,13 @@ TailWs tail_ws(const haste_tail_desc *d, const haste_bce *bce) {
     size_t o = 0;
     if (d->dtype == HASTE_BF16) {
         w.xt = o;  o += al256((size_t)d->D * pad_rows(d->B) * 2);
-        w.cnt = o; o += al256((size_t)(nnz > 0 ? nnz : 1) * 8 + 8);   // keys + count
+        w.cnt = o; o += al256((size_t)(nnz > 0 ? nnz : 1) * 20 + 8);  // keys, sorted, ranks, count
         w.ptr = o; o += al256((size_t)(ng + 4) * 4);   // +3: 16-byte reads of a pair
         w.ent = o; o += al256((size_t)(nnz > 0 ? nnz : 1) * 4);
     } else {
-        w.cnt = o; o += al256((size_t)ng * 4);
+        // per-group counts; also the key space of haste_tail_group_positives
+        const size_t keys = (size_t)(nnz > 0 ? nnz : 1) * 20 + 8;
+        w.cnt = o; o += al256((size_t)ng * 4 > keys ? (size_t)ng * 4 : keys);
         w.dz = o;  o += al256((size_t)d->B * d->L * 4);
     }
     w.total = o;

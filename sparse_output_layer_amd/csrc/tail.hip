@@ -74,11 +74,14 @@ hipError_t launch_fill_u32(void *p, uint32_t v, size_t n, hipStream_t st) {
 
 // ---------------------------------------------------- group-major positives
 // The fused epilogue walks, per group, the list of (row b, slot j) pairs
-// whose label is a positive.  Built deterministically without atomics or
-// scans: every tail positive gets the key (g << 32) | (b*G + j); the entry
-// of a positive lands at the number of keys smaller than its own, and
-// grp_ptr[g] is the number of keys smaller than (g << 32).  The keys are
-// few (one per positive), so each workgroup keeps them all in LDS.
+// whose label is a positive.  Built deterministically without a sort network:
+// every tail positive gets the key (g << 32) | (b*G + j); a key's rank (the
+// valid keys below it, plus equal keys at smaller input positions, so a label
+// listed twice in a row keeps both entries in input order) is its place in
+// the group-major order, and the list is written directly (sorted[rank] =
+// key).  grp_ptr[g] is a binary search for (g << 32); entries are the keys'
+// low words.  Ranking is nnz^2 comparisons, spread over a 2-D grid of
+// 256 x 256 key tiles.
 __device__ __forceinline__ int row_of(const int32_t *row_ptr, int B, int k) {
     int lo = 0, hi = B;  // row_ptr[lo] <= k < row_ptr[hi]
     while (hi - lo > 1) {
@@ -88,81 +91,56 @@ __device__ __forceinline__ int row_of(const int32_t *row_ptr, int B, int k) {
     return lo;
 }
 
+// Invalid key: all ones (compares above every valid key as unsigned).
 __global__ void k_gpos_keys(const int32_t *row_ptr, const int32_t *labels, int nnz, int B,
-                            int64_t off, int64_t L, int G, long long *keys) {
+                            int64_t off, int64_t L, int G, unsigned long long *keys, int *rank,
+                            int *nvalid) {
     const int k = blockIdx.x * blockDim.x + threadIdx.x;
+    if (k == 0) *nvalid = 0;
     if (k >= nnz) return;
     const int64_t t = (int64_t)labels[k] - off;
-    long long key = -1;
+    unsigned long long key = ~0ull;
     if (t >= 0 && t < L)
-        key = ((long long)(t / G) << 32) | (long long)(row_of(row_ptr, B, k) * G + (int)(t % G));
+        key = ((unsigned long long)(t / G) << 32) |
+              (unsigned long long)(unsigned)(row_of(row_ptr, B, k) * G + (int)(t % G));
     keys[k] = key;
+    rank[k] = 0;
 }
 
-__global__ __launch_bounds__(256) void k_gpos_place(const long long *keys, int nnz, int64_t Ng,
-                                                    int32_t *grp_ptr, int32_t *ent) {
-    constexpr int CH = 2048;
-    __shared__ long long sk[CH];
-    const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-    const bool roleA = t <= Ng;                      // grp_ptr[t]
-    const long long thrA = roleA ? (long long)(t << 32) : 0;
-    long long thrB = -1;                             // own key (role B)
-    if (t < nnz) thrB = keys[t];
-    int cA = 0, cB = 0;
-    for (int c0 = 0; c0 < nnz; c0 += CH) {
-        __syncthreads();
-        for (int i = threadIdx.x; i < CH; i += blockDim.x)
-            sk[i] = c0 + i < nnz ? keys[c0 + i] : -1;
-        __syncthreads();
-        const int lim = nnz - c0 < CH ? nnz - c0 : CH;
-        for (int i = 0; i < lim; ++i) {
-            const long long v = sk[i];
-            cA += (v >= 0 && v < thrA) ? 1 : 0;
-            cB += (v >= 0 && v < thrB) ? 1 : 0;
-        }
-    }
-    if (roleA) grp_ptr[t] = cA;
-    if (thrB >= 0) ent[cB] = (int32_t)(thrB & 0xffffffffLL);
-}
+constexpr int GPOS_TILE = 256;
 
-// Up to 16384 positives: one workgroup sorts the keys in LDS (bitonic), then
-// grp_ptr[g] is a binary search for (g << 32) and the entries are the low
-// words of the sorted keys.  Non-tail positives carry the largest key.
-constexpr int GPOS_SORT_MAX = 16384;
-
-__global__ __launch_bounds__(1024) void k_gpos_sort(long long *keys, int nnz, int *nvalid) {
-    extern __shared__ unsigned long long sk[];
-    int N = 2;
-    while (N < nnz) N <<= 1;
-    const int tid = threadIdx.x;
-    for (int i = tid; i < N; i += 1024)
-        sk[i] = (i < nnz && keys[i] >= 0) ? (unsigned long long)keys[i] : ~0ull;
+// Block (x, y): keys of tile x counted against the keys of tile y.
+__global__ __launch_bounds__(GPOS_TILE) void k_gpos_rank(const unsigned long long *keys, int nnz,
+                                                          int *rank, int *nvalid) {
+    __shared__ unsigned long long sk[GPOS_TILE];
+    const int k = blockIdx.x * GPOS_TILE + threadIdx.x;
+    const int j0 = blockIdx.y * GPOS_TILE;
+    const int jj = j0 + threadIdx.x;
+    sk[threadIdx.x] = jj < nnz ? keys[jj] : ~0ull;
+    const unsigned long long own = k < nnz ? keys[k] : ~0ull;
     __syncthreads();
-    for (int k = 2; k <= N; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int i = tid; i < N; i += 1024) {
-                const int p = i ^ j;
-                if (p > i) {
-                    const unsigned long long x = sk[i], y = sk[p];
-                    const bool up = (i & k) == 0;
-                    if ((x > y) == up) {
-                        sk[i] = y;
-                        sk[p] = x;
-                    }
-                }
-            }
-            __syncthreads();
-        }
+    if (own == ~0ull) return;
+    // equal keys count only at positions before k
+    const int before = k - j0 < 0 ? 0 : (k - j0 > GPOS_TILE ? GPOS_TILE : k - j0);
+    int r = 0;
+#pragma unroll 16
+    for (int i = 0; i < GPOS_TILE; ++i) {
+        const unsigned long long v = sk[i];
+        r += (v < own || (v == own && i < before)) ? 1 : 0;
     }
-    for (int i = tid; i < nnz; i += 1024) {
-        keys[i] = (long long)sk[i];
-        const bool last = sk[i] != ~0ull && (i + 1 == N || sk[i + 1] == ~0ull);
-        if (last) *nvalid = i + 1;
-    }
-    if (tid == 0 && sk[0] == ~0ull) *nvalid = 0;
+    if (r) atomicAdd(rank + k, r);
+    if (blockIdx.y == 0) atomicAdd(nvalid, 1);
 }
 
-__global__ void k_gpos_index(const long long *sorted, const int *nvalid, int64_t Ng,
+__global__ void k_gpos_scatter(const unsigned long long *keys, const int *rank, int nnz,
+                               unsigned long long *sorted) {
+    const int k = blockIdx.x * blockDim.x + threadIdx.x;
+    if (k >= nnz) return;
+    const unsigned long long key = keys[k];
+    if (key != ~0ull) sorted[rank[k]] = key;
+}
+
+__global__ void k_gpos_index(const unsigned long long *sorted, const int *nvalid, int64_t Ng,
                              int32_t *grp_ptr, int32_t *ent) {
     const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
     const int n = *nvalid;
@@ -171,39 +149,37 @@ __global__ void k_gpos_index(const long long *sorted, const int *nvalid, int64_t
         int lo = 0, hi = n;  // first index with sorted >= thr
         while (lo < hi) {
             const int mid = (lo + hi) >> 1;
-            if ((unsigned long long)sorted[mid] < thr) lo = mid + 1; else hi = mid;
+            if (sorted[mid] < thr) lo = mid + 1; else hi = mid;
         }
         grp_ptr[t] = lo;
     }
-    if (t < n) ent[t] = (int32_t)(sorted[t] & 0xffffffffLL);
+    if (t < n) ent[t] = (int32_t)(sorted[t] & 0xffffffffull);
 }
 
+// keys: workspace of 20*max(nnz,1) + 8 bytes, 8-byte aligned (keys, sorted
+// keys, ranks, count)
 hipError_t launch_group_positives(const int32_t *row_ptr, const int32_t *labels, int nnz,
                                   int B, int64_t off, int64_t L, int G, int64_t Ng,
-                                  long long *keys, int32_t *grp_ptr, int32_t *ent,
+                                  long long *keys_ws, int32_t *grp_ptr, int32_t *ent,
                                   hipStream_t st) {
     hipError_t e;
-    if (nnz > 0) {
-        hipLaunchKernelGGL(k_gpos_keys, dim3((nnz + 255) / 256), dim3(256), 0, st, row_ptr,
-                           labels, nnz, B, off, L, G, keys);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
-    const int64_t n = (Ng + 1 > nnz ? Ng + 1 : nnz);
-    if (nnz <= GPOS_SORT_MAX) {
-        int N = 2;
-        while (N < nnz) N <<= 1;
-        int *nvalid = (int *)(keys + (nnz > 0 ? nnz : 1));
-        const size_t lds = (size_t)N * 8;
-        (void)hipFuncSetAttribute((const void *)k_gpos_sort,
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        hipLaunchKernelGGL(k_gpos_sort, dim3(1), dim3(1024), lds, st, keys, nnz, nvalid);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipLaunchKernelGGL(k_gpos_index, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                           keys, nvalid, Ng, grp_ptr, ent);
-        return hipGetLastError();
-    }
-    hipLaunchKernelGGL(k_gpos_place, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, keys,
-                       nnz, Ng, grp_ptr, ent);
+    if (nnz <= 0) return launch_fill_u32(grp_ptr, 0u, (size_t)(Ng + 1), st);
+    unsigned long long *keys = (unsigned long long *)keys_ws;
+    unsigned long long *sorted = keys + nnz;
+    int *rank = (int *)(sorted + nnz);
+    int *nvalid = rank + nnz;
+    const unsigned nt = (unsigned)((nnz + GPOS_TILE - 1) / GPOS_TILE);
+    hipLaunchKernelGGL(k_gpos_keys, dim3(nt), dim3(GPOS_TILE), 0, st, row_ptr, labels, nnz, B,
+                       off, L, G, keys, rank, nvalid);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(k_gpos_rank, dim3(nt, nt), dim3(GPOS_TILE), 0, st, keys, nnz, rank,
+                       nvalid);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(k_gpos_scatter, dim3(nt), dim3(GPOS_TILE), 0, st, keys, rank, nnz, sorted);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int64_t n = Ng + 1 > nnz ? Ng + 1 : nnz;
+    hipLaunchKernelGGL(k_gpos_index, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, sorted,
+                       nvalid, Ng, grp_ptr, ent);
     return hipGetLastError();
 }
 

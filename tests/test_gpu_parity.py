@@ -230,3 +230,37 @@ def test_topk_merge_exact(H):
     rv, ri = oracle.topk(full, K, ids=ids.reshape(-1))
     assert np.array_equal(oi.cpu().numpy(), ri)
     assert np.array_equal(ov.cpu().numpy(), rv.astype(np.float32))
+
+
+@pytest.mark.parametrize("B,L,G,per_row,dup,dtype", [
+    (3, 40, 16, 0, False, torch.bfloat16),       # no positives at all
+    (70, 300, 64, 4, True, torch.bfloat16),      # duplicates, ragged last group
+    (1100, 5000, 16, 5, True, torch.bfloat16),   # more keys than one LDS chunk
+    (600, 777, 3, 7, True, torch.float32),       # fp32 desc, groups of three
+])
+def test_group_positives_edges(H, B, L, G, per_row, dup, dtype):
+    """Group-major positives, bit-exact against the oracle: labels below and
+    above the tail range, empty rows, a label listed twice in a row (both
+    entries kept, in input order), and key counts spanning several chunks."""
+    print("group positives", B, L, G, per_row, dup, flush=True)
+    rng = np.random.default_rng(B * 7 + L)
+    off = 50
+    counts = rng.integers(0, per_row + 1, size=B) if per_row else np.zeros(B, np.int64)
+    labels = []
+    for b in range(B):
+        row = list(rng.integers(0, off + L + 30, size=int(counts[b])))
+        if dup and row:
+            row.append(row[0])
+        labels += row
+    row_ptr = np.zeros(B + 1, np.int32)
+    for b in range(B):
+        n = int(counts[b]) + (1 if dup and counts[b] else 0)
+        row_ptr[b + 1] = row_ptr[b] + n
+    labels = np.array(labels, np.int32)
+    assert labels.size == row_ptr[-1]
+    rp, re_ = oracle.group_positives(row_ptr, labels, off, L, G)
+    bce = H.Bce(torch.from_numpy(row_ptr).to(DEV), torch.from_numpy(labels).to(DEV), off, 1.0)
+    gp, ent = H.haste_tail_group_positives(B, 128, L, G, 32, bce, dtype=dtype)
+    torch.cuda.synchronize()
+    assert np.array_equal(gp.cpu().numpy(), rp)
+    assert np.array_equal(ent.cpu().numpy()[:re_.size], re_)
