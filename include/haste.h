@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define HASTE_ABI_VERSION 1
+#define HASTE_ABI_VERSION 2
 
 typedef enum {
     HASTE_OK = 0,
@@ -83,7 +83,17 @@ typedef struct {
     int32_t G;      /* labels per group                     */
     int32_t F;      /* fan-in indices per group             */
     int32_t dtype;  /* haste_dtype of X, W, Z, dZ, dW       */
+    int32_t flags;  /* 0 or HASTE_TAIL_LEAN                 */
 } haste_tail_desc;
+
+/* Tail flag.  By default the bf16 training calls that form dz from the
+ * positives (haste_tail_step, its split form, haste_tail_bwd with dZ NULL)
+ * keep dz of the dW pass in the workspace as bf16 tiles, B_pad x (N_g*G)
+ * x 2 bytes (B_pad = B rounded up to 64), and the dX pass reads them back.
+ * HASTE_TAIL_LEAN drops that buffer: the dX pass recomputes Z and dz from X,
+ * W and the positives, and nothing of size B x L is stored.  Both forms give
+ * the same results up to the summation order of Z. */
+#define HASTE_TAIL_LEAN 1
 
 /* Head shape (dense classifier).  bf16 needs D a multiple of 32. */
 typedef struct {
@@ -142,16 +152,18 @@ haste_status haste_tail_fwd(const haste_tail_desc *d, const void *X,
 /* Tail backward: dW (same shape/dtype as W, padded rows zeroed) and dX
  * (B x D fp32; overwritten, or added to when accumulate_dX != 0).
  * dZ != NULL: use the given B x L gradient.  dZ == NULL: recompute z and
- * dz = s*(sigmoid(z)-y) from bce (no B x L buffer; bce->loss is NOT added
- * here, so a separate forward can own the loss). */
+ * dz = s*(sigmoid(z)-y) from bce (dz kept in ws between the dW and dX
+ * passes unless HASTE_TAIL_LEAN; bce->loss is NOT added here, so a separate
+ * forward can own the loss). */
 haste_status haste_tail_bwd(const haste_tail_desc *d, const void *X,
                             const int32_t *idx, const void *W, const void *dZ,
                             const haste_bce *bce, void *dW, float *dX,
                             int accumulate_dX, void *ws, size_t ws_bytes,
                             void *stream);
 
-/* Fused tail training step: loss (+= into bce->loss), top-K (if asked),
- * dW and dX in one call, with no B x L buffer anywhere. */
+/* Fused tail training step: loss (+= into bce->loss), dW and dX in one
+ * call; no logits are stored, and with HASTE_TAIL_LEAN no B x L buffer of
+ * any kind (see HASTE_TAIL_LEAN). */
 haste_status haste_tail_step(const haste_tail_desc *d, const void *X,
                              const int32_t *idx, const void *W,
                              const haste_bce *bce, void *dW, float *dX,
@@ -163,10 +175,12 @@ haste_status haste_tail_step(const haste_tail_desc *d, const void *X,
  * group-major positives.  haste_tail_step_dw (one kernel) then adds the
  * loss and writes dW (gather + contraction + fused BCE + weight gradient);
  * haste_tail_step_dx (one kernel, plus a fill of dX unless accumulating)
- * adds the tail's dX.  Both read what haste_tail_prepare left in ws: call
- * the three on one stream, prepare first, with the same descriptor, X, idx,
- * W, bce and workspace; together they produce what haste_tail_step
- * produces.  ws must not be reused by another call in between. */
+ * adds the tail's dX.  Both read what haste_tail_prepare left in ws, and
+ * unless HASTE_TAIL_LEAN haste_tail_step_dx also reads the dz tiles that
+ * haste_tail_step_dw left there: call the three on one stream, in this
+ * order, with the same descriptor, X, idx, W, bce and workspace; together
+ * they produce what haste_tail_step produces.  ws must not be reused by
+ * another call in between. */
 haste_status haste_tail_prepare(const haste_tail_desc *d, const void *X,
                                 const haste_bce *bce, void *ws,
                                 size_t ws_bytes, void *stream);

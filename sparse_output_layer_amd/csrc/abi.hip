@@ -50,7 +50,8 @@ inline int pad_rows(int B) { return (B + 63) / 64 * 64; }
 
 // ----------------------------------------------------------- workspace maps
 struct TailWs {
-    size_t xt, cnt, ptr, ent, dz, total;
+    size_t xt, cnt, ptr, ent, dz, dzt, total;
+    bool has_dzt;
 };
 
 TailWs tail_ws(const haste_tail_desc *d, const haste_bce *bce) {
@@ -63,6 +64,10 @@ TailWs tail_ws(const haste_tail_desc *d, const haste_bce *bce) {
         w.cnt = o; o += al256((size_t)(nnz > 0 ? nnz : 1) * 20 + 8);  // keys, sorted, ranks, count
         w.ptr = o; o += al256((size_t)(ng + 4) * 4);   // +3: 16-byte reads of a pair
         w.ent = o; o += al256((size_t)(nnz > 0 ? nnz : 1) * 4);
+        // dz of the dW pass, kept for the dX pass unless the caller asks for
+        // the lean form (which recomputes it): Bp x (Ng*G) bf16 in 1 KB tiles
+        w.has_dzt = bce && !(d->flags & HASTE_TAIL_LEAN);
+        if (w.has_dzt) { w.dzt = o; o += al256((size_t)ng * d->G * pad_rows(d->B) * 2); }
     } else {
         // per-group counts; also the key space of haste_tail_group_positives
         const size_t keys = (size_t)(nnz > 0 ? nnz : 1) * 20 + 8;
@@ -97,6 +102,7 @@ haste_status check_tail(const haste_tail_desc *d) {
     if (d->F > d->D) return fail(HASTE_ERR_INVALID, "F=%d exceeds D=%d", d->F, d->D);
     if (d->dtype != HASTE_F32 && d->dtype != HASTE_BF16)
         return fail(HASTE_ERR_INVALID, "unknown dtype %d", d->dtype);
+    if (d->flags & ~HASTE_TAIL_LEAN) return fail(HASTE_ERR_INVALID, "unknown tail flags 0x%x", d->flags);
     if (d->dtype == HASTE_BF16) {
         if (!tail_bf16_supported(d->G, d->F, d->D))
             return fail(HASTE_ERR_UNSUPPORTED,
@@ -166,6 +172,7 @@ TailArgs tail_args(const haste_tail_desc *d, const void *X, const int32_t *idx, 
     a.W = (const unsigned short *)W;
     a.grp_ptr = (const int32_t *)B8(ws, m.ptr);
     a.grp_ent = (const int32_t *)B8(ws, m.ent);
+    a.dzt = m.has_dzt ? (unsigned short *)B8(ws, m.dzt) : nullptr;
     a.B = d->B;
     a.D = d->D;
     a.Bp = pad_rows(d->B);
@@ -323,7 +330,7 @@ haste_status haste_tail_bwd(const haste_tail_desc *d, const void *X, const int32
         a.dZ = (const unsigned short *)dZ;
         if (b) a.s = b->grad_scale;
         TRY_HIP(launch_tail_t1(dZ ? T1_DW_MEM : T1_DW_BCE, d->G, a, false, false, st), "tail dW");
-        TRY_HIP(launch_tail_t2(d->G, dZ != nullptr, a, st), "tail dX");
+        TRY_HIP(launch_tail_t2(d->G, dZ ? 1 : a.dzt ? 2 : 0, a, st), "tail dX");
     } else {
         F32Args a = f32_tail_args(d, X, idx, W, b);
         a.loss = nullptr;
@@ -362,7 +369,7 @@ haste_status haste_tail_step(const haste_tail_desc *d, const void *X, const int3
         a.s = bce->grad_scale;
         a.loss = bce->loss;
         TRY_HIP(launch_tail_t1(T1_DW_BCE, d->G, a, false, bce->loss != nullptr, st), "tail step dW");
-        TRY_HIP(launch_tail_t2(d->G, false, a, st), "tail step dX");
+        TRY_HIP(launch_tail_t2(d->G, a.dzt ? 2 : 0, a, st), "tail step dX");
     } else {
         F32Args a = f32_tail_args(d, X, idx, W, bce);
         a.dW = (float *)dW;
@@ -431,7 +438,7 @@ haste_status haste_tail_step_dx(const haste_tail_desc *d, const void *X, const i
         TailArgs a = tail_args(d, X, idx, W, ws, m);
         a.dX = dX;
         a.s = bce->grad_scale;
-        TRY_HIP(launch_tail_t2(d->G, false, a, st), "tail step dX");
+        TRY_HIP(launch_tail_t2(d->G, a.dzt ? 2 : 0, a, st), "tail step dX");
     } else {
         F32Args a = f32_tail_args(d, X, idx, W, bce);
         a.loss = nullptr;

@@ -15,6 +15,8 @@ struct TailArgs {
     const unsigned short *W;     // (Ng*G) x F bf16
     unsigned short *Z;           // B x L bf16 (forward output)
     const unsigned short *dZ;    // B x L bf16 (given gradient)
+    unsigned short *dzt;         // dz tiles of the dW pass for the dX pass, or null:
+                                 // Ng x (Bp/32) x (G/16) tiles of 1 KB (32 rows x 16 labels)
     unsigned short *dW;          // (Ng*G) x F bf16
     float *dX;                   // B x D fp32 (atomically accumulated)
     const int32_t *grp_ptr;      // Ng + 1 group-major positives
@@ -38,7 +40,9 @@ hipError_t launch_group_positives(const int32_t *row_ptr, const int32_t *labels,
                                   hipStream_t st);
 hipError_t launch_tail_t1(int mode, int G, const TailArgs &a, bool store_z,
                           bool do_loss, hipStream_t st);
-hipError_t launch_tail_t2(int G, bool dz_mem, const TailArgs &a,
+// dz_mode: 0 recompute dz from the positives, 1 read the B x L dZ,
+// 2 read the dz tiles (dzt) that the dW pass (T1_DW_BCE) stored
+hipError_t launch_tail_t2(int G, int dz_mode, const TailArgs &a,
                           hipStream_t st);
 bool tail_bf16_supported(int G, int F, int D);
 

@@ -422,6 +422,10 @@ __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, int store_z,
                     for (int jt = 0; jt < JT; ++jt) {
                         u32x4 v = {dzp[0][jt][0], dzp[0][jt][1], dzp[1][jt][0], dzp[1][jt][1]};
                         Bj[jt] = __builtin_bit_cast(bf16x8, v);
+                        // dz tile (g, chunk, jt) for the dX pass, in this register layout:
+                        // lane (q, m) holds rows 4q+i and 16+4q+i (i = 0..3) of label 16jt+m
+                        if (MODE == T1_DW_BCE && a.dzt)
+                            *(u32x4 *)(a.dzt + ((((int64_t)g * nch + ch) * JT + jt) << 9) + lane * 8) = v;
                     }
 #pragma unroll
                     for (int ft = 0; ft < FT; ++ft) {
@@ -577,7 +581,7 @@ __host__ __device__ inline T2Lds t2_layout(int D, int F, int G, int BC2, int NTW
 }
 
 template <int G, int BC2, int NTW32>
-__global__ __launch_bounds__(64 * T2_NW, 1) void k_tail_t2(TailArgs a, int dz_mem, int n_granges) {
+__global__ __launch_bounds__(64 * T2_NW, 1) void k_tail_t2(TailArgs a, int dz_mode, int n_granges) {
     constexpr int NT = 64 * T2_NW;
     constexpr int GPI = t2_gpi(G, BC2);
     constexpr int JT = G / 16, BT = BC2 / 16, RT = BC2 / 32;
@@ -612,9 +616,10 @@ __global__ __launch_bounds__(64 * T2_NW, 1) void k_tail_t2(TailArgs a, int dz_me
     const int role = w < T2_NC ? 0 : w < T2_NC + T2_NZ ? 1 : 2;
     auto live = [&](int k, int q) { return gA + (int64_t)k * GPI + q < gB; };
 
+    const int dz_mem = dz_mode;             // dz not recomputed (modes 1, 2)
     {   // stage the chunk (units rotated by row), reset the inverse maps, zero rows
         const unsigned short *src = a.XT + r0;
-        for (int i = tid; i < a.D * NU; i += NT) {
+        for (int i = tid; i < (dz_mode == 0 ? a.D * NU : 0); i += NT) {
             const int d = i / NU, u = i % NU;
             *(u32x4 *)(tile + (d << LROW) + (((u + d) & (NU - 1)) << 4)) =
                 *(const u32x4 *)(src + (int64_t)d * a.Bp + u * 8);
@@ -691,6 +696,57 @@ __global__ __launch_bounds__(64 * T2_NW, 1) void k_tail_t2(TailArgs a, int dz_me
                     if (row < a.B) atomicAdd(a.dX + (int64_t)row * a.D + d, acc[rt][nt][r]);
                 }
             }
+    } else if (role == 1 && dz_mode == 2) {
+        // --------------------------------------------------- dz tile loaders
+        // dz comes from the tiles of the dW pass: wave p copies tile p of a
+        // step (group q, 32-row block rt, label tile jt; at most four per
+        // step) into exch, transposed from the dW pass's layout (lane (qq, mm):
+        // rows 4qq+i and 16+4qq+i of label mm) into the A-operand layout
+        // (lane: one row, eight consecutive labels).  Loads run four steps
+        // ahead.
+        constexpr int NBLK = GPI * RT * JT;
+        static_assert(NBLK <= T2_NZ, "one dz tile per loader wave");
+        const int blk = w - T2_NC;
+        const bool act = blk < NBLK;
+        const int q = blk / (RT * JT), rt = (blk / JT) % RT, jt = blk % JT;
+        const int64_t nch32 = a.Bp / 32;
+        const int mm = lane & 15, qq = lane >> 4;
+        auto fetch = [&](int k, u32x4 &v) {
+            if (!act || !live(k, q)) return;
+            const int64_t g = gA + (int64_t)k * GPI + q;
+            v = *(const u32x4 *)(a.dzt + (((g * nch32 + (r0 >> 5) + rt) * JT + jt) << 9) + lane * 8);
+        };
+        auto put = [&](int k, const u32x4 &v) {
+            if (!act || !live(k, q)) return;
+            unsigned char *ex = exch0 + ((k & 1) * GPI + q) * LY.exch_grp + (rt * JT + jt) * 1024 +
+                                (32 * (mm >> 3)) * 16 + 2 * (mm & 7);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int rho = 16 * (e >> 2) + 4 * qq + (e & 3);
+                const unsigned wv = v[e >> 1];
+                *(unsigned short *)(ex + rho * 16) = (unsigned short)((e & 1) ? (wv >> 16) : (wv & 0xffffu));
+            }
+        };
+        u32x4 s0 = {}, s1 = {}, s2 = {}, s3 = {};
+        fetch(0, s0);
+        fetch(1, s1);
+        fetch(2, s2);
+        fetch(3, s3);
+        put(0, s0);
+        fetch(4, s0);
+        __syncthreads();
+        // iteration k: step k+1 is in set (k+1) mod 4; it then receives step k+5
+        auto iter = [&](int k, u32x4 &v) {
+            put(k + 1, v);
+            fetch(k + 5, v);
+            close_step(k);
+        };
+        for (int k = 0; k < nsteps; k += 4) {
+            iter(k, s1);
+            if (k + 1 < nsteps) iter(k + 1, s2);
+            if (k + 2 < nsteps) iter(k + 2, s3);
+            if (k + 3 < nsteps) iter(k + 3, s0);
+        }
     } else if (role == 1) {
         // ------------------------------------------------------------ Z^T waves
         // Wave p takes tiles p*TPW .. +TPW-1 of a step: one group q and label
@@ -939,7 +995,7 @@ static int t2_ntw(int D, int BC2) {   // 32-feature tiles per consumer wave
 }
 
 template <int G, int BC2, int NTW32>
-static hipError_t t2_go(bool dz_mem, const TailArgs &a, hipStream_t st) {
+static hipError_t t2_go(int dz_mode, const TailArgs &a, hipStream_t st) {
     const int nbch = a.Bp / BC2;
     const int64_t ngr = t2_granges(nbch, a.Ng);
     if (ngr < 1) return hipSuccess;
@@ -947,19 +1003,19 @@ static hipError_t t2_go(bool dz_mem, const TailArgs &a, hipStream_t st) {
     if (L.total > 160 * 1024) return hipErrorInvalidValue;
     allow_lds((const void *)k_tail_t2<G, BC2, NTW32>, L.total);
     hipLaunchKernelGGL((k_tail_t2<G, BC2, NTW32>), dim3((unsigned)(ngr * nbch)), dim3(64 * T2_NW),
-                       L.total, st, a, (int)dz_mem, (int)ngr);
+                       L.total, st, a, dz_mode, (int)ngr);
     return hipGetLastError();
 }
 
 template <int G, int BC2>
-static hipError_t t2_pick_ntw(bool dz_mem, const TailArgs &a, hipStream_t st) {
+static hipError_t t2_pick_ntw(int dz_mode, const TailArgs &a, hipStream_t st) {
     switch (t2_ntw(a.D, BC2)) {
-    case 1: return t2_go<G, BC2, 1>(dz_mem, a, st);
-    case 2: return t2_go<G, BC2, 2>(dz_mem, a, st);
-    case 3: return t2_go<G, BC2, 3>(dz_mem, a, st);
+    case 1: return t2_go<G, BC2, 1>(dz_mode, a, st);
+    case 2: return t2_go<G, BC2, 2>(dz_mode, a, st);
+    case 3: return t2_go<G, BC2, 3>(dz_mode, a, st);
     }
     if constexpr (BC2 == 32)
-        if (t2_ntw(a.D, BC2) == 4) return t2_go<G, BC2, 4>(dz_mem, a, st);
+        if (t2_ntw(a.D, BC2) == 4) return t2_go<G, BC2, 4>(dz_mode, a, st);
     return hipErrorInvalidValue;
 }
 
@@ -971,17 +1027,19 @@ static int t2_bc(int G, int F, int D, int B) {
 }
 
 template <int G>
-static hipError_t t2_pick(bool dz_mem, const TailArgs &a, hipStream_t st) {
+static hipError_t t2_pick(int dz_mode, const TailArgs &a, hipStream_t st) {
     if constexpr (G < 64)   // G = 64 always takes 32-row chunks (16 Z^T tiles per 64 rows)
-        if (t2_bc(G, a.F, a.D, a.B) == 64) return t2_pick_ntw<G, 64>(dz_mem, a, st);
-    return t2_pick_ntw<G, 32>(dz_mem, a, st);
+        if (t2_bc(G, a.F, a.D, a.B) == 64) return t2_pick_ntw<G, 64>(dz_mode, a, st);
+    return t2_pick_ntw<G, 32>(dz_mode, a, st);
 }
 
-hipError_t launch_tail_t2(int G, bool dz_mem, const TailArgs &a, hipStream_t st) {
+hipError_t launch_tail_t2(int G, int dz_mode, const TailArgs &a, hipStream_t st) {
+    if (dz_mode < 0 || dz_mode > 2 || (dz_mode == 1 && !a.dZ) || (dz_mode == 2 && !a.dzt))
+        return hipErrorInvalidValue;
     switch (G) {
-    case 16: return t2_pick<16>(dz_mem, a, st);
-    case 32: return t2_pick<32>(dz_mem, a, st);
-    case 64: return t2_pick<64>(dz_mem, a, st);
+    case 16: return t2_pick<16>(dz_mode, a, st);
+    case 32: return t2_pick<32>(dz_mode, a, st);
+    case 64: return t2_pick<64>(dz_mode, a, st);
     }
     return hipErrorInvalidValue;
 }

@@ -22,6 +22,7 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "haste.h")
 
 HASTE_OK, HASTE_ERR_INVALID, HASTE_ERR_UNSUPPORTED, HASTE_ERR_WORKSPACE, HASTE_ERR_HIP = range(5)
 HASTE_F32, HASTE_BF16 = 0, 1
+HASTE_TAIL_LEAN = 1   # tail flag: recompute dz in the dX pass instead of keeping it in ws
 
 
 class HasteError(RuntimeError):
@@ -32,7 +33,8 @@ class HasteError(RuntimeError):
 
 class TailDesc(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("D", ctypes.c_int32), ("L", ctypes.c_int64),
-                ("G", ctypes.c_int32), ("F", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("G", ctypes.c_int32), ("F", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("flags", ctypes.c_int32)]
 
 
 class HeadDesc(ctypes.Structure):
@@ -163,9 +165,10 @@ def _bref(bce: Optional[Bce]):
     return None if bce is None else ctypes.pointer(bce.struct())
 
 
-def tail_desc(X: torch.Tensor, idx: torch.Tensor, L: int, G: int) -> TailDesc:
+def tail_desc(X: torch.Tensor, idx: torch.Tensor, L: int, G: int, lean: bool = False) -> TailDesc:
     B, D = X.shape
-    return TailDesc(B=B, D=D, L=int(L), G=int(G), F=int(idx.shape[1]), dtype=_dtype_code(X))
+    return TailDesc(B=B, D=D, L=int(L), G=int(G), F=int(idx.shape[1]), dtype=_dtype_code(X),
+                    flags=HASTE_TAIL_LEAN if lean else 0)
 
 
 def head_desc(X: torch.Tensor, Wh: torch.Tensor) -> HeadDesc:
@@ -195,8 +198,8 @@ def haste_tail_layout(L: int, G: int, F: int, B: int = 1, D: int = 1) -> dict:
             "last_group_live": out[3]}
 
 
-def haste_tail_workspace_bytes(X, idx, L, G, bce: Optional[Bce] = None) -> int:
-    return lib().haste_tail_workspace_bytes(ctypes.byref(tail_desc(X, idx, L, G)), _bref(bce))
+def haste_tail_workspace_bytes(X, idx, L, G, bce: Optional[Bce] = None, lean=False) -> int:
+    return lib().haste_tail_workspace_bytes(ctypes.byref(tail_desc(X, idx, L, G, lean)), _bref(bce))
 
 
 def haste_head_workspace_bytes(X, Wh, bce: Optional[Bce] = None) -> int:
@@ -209,11 +212,11 @@ def _tail_in(X, idx, W):
     _need(W, "W", X.dtype)
 
 
-def haste_tail_fwd(X, idx, W, L, G, Z=None, bce: Optional[Bce] = None, workspace=None):
+def haste_tail_fwd(X, idx, W, L, G, Z=None, bce: Optional[Bce] = None, workspace=None, lean=False):
     _tail_in(X, idx, W)
     if Z is not None:
         _need(Z, "Z", X.dtype)
-    d = tail_desc(X, idx, L, G)
+    d = tail_desc(X, idx, L, G, lean)
     b = _bref(bce)
     ws, nb = _workspace(lib().haste_tail_workspace_bytes(ctypes.byref(d), b), X.device, workspace)
     _check(lib().haste_tail_fwd(ctypes.byref(d), _ptr(X), _ptr(idx), _ptr(W), _ptr(Z), b,
@@ -222,13 +225,13 @@ def haste_tail_fwd(X, idx, W, L, G, Z=None, bce: Optional[Bce] = None, workspace
 
 
 def haste_tail_bwd(X, idx, W, L, G, dW, dX, dZ=None, bce: Optional[Bce] = None,
-                   accumulate_dX=False, workspace=None):
+                   accumulate_dX=False, workspace=None, lean=False):
     _tail_in(X, idx, W)
     _need(dW, "dW", X.dtype)
     _need(dX, "dX", torch.float32)
     if dZ is not None:
         _need(dZ, "dZ", X.dtype)
-    d = tail_desc(X, idx, L, G)
+    d = tail_desc(X, idx, L, G, lean)
     b = None if dZ is not None else _bref(bce)
     ws, nb = _workspace(lib().haste_tail_workspace_bytes(ctypes.byref(d), b), X.device, workspace)
     _check(lib().haste_tail_bwd(ctypes.byref(d), _ptr(X), _ptr(idx), _ptr(W), _ptr(dZ), b,
@@ -236,42 +239,43 @@ def haste_tail_bwd(X, idx, W, L, G, dW, dX, dZ=None, bce: Optional[Bce] = None,
                                 _stream()))
 
 
-def haste_tail_step(X, idx, W, L, G, bce: Bce, dW, dX, accumulate_dX=False, workspace=None):
+def haste_tail_step(X, idx, W, L, G, bce: Bce, dW, dX, accumulate_dX=False, workspace=None,
+                    lean=False):
     _tail_in(X, idx, W)
     _need(dW, "dW", X.dtype)
     _need(dX, "dX", torch.float32)
-    d = tail_desc(X, idx, L, G)
+    d = tail_desc(X, idx, L, G, lean)
     b = _bref(bce)
     ws, nb = _workspace(lib().haste_tail_workspace_bytes(ctypes.byref(d), b), X.device, workspace)
     _check(lib().haste_tail_step(ctypes.byref(d), _ptr(X), _ptr(idx), _ptr(W), b, _ptr(dW),
                                  _ptr(dX), int(bool(accumulate_dX)), _ptr(ws), nb, _stream()))
 
 
-def haste_tail_prepare(X, idx, L, G, bce: Bce, workspace: torch.Tensor):
+def haste_tail_prepare(X, idx, L, G, bce: Bce, workspace: torch.Tensor, lean=False):
     """Split step, part 1: transposed X and group-major positives into
     `workspace` (keep it for haste_tail_step_dw / haste_tail_step_dx)."""
     _need(X, "X")
-    d = tail_desc(X, idx, L, G)
+    d = tail_desc(X, idx, L, G, lean)
     _check(lib().haste_tail_prepare(ctypes.byref(d), _ptr(X), _bref(bce), _ptr(workspace),
                                     workspace.numel(), _stream()))
 
 
-def haste_tail_step_dw(X, idx, W, L, G, bce: Bce, dW, workspace: torch.Tensor):
+def haste_tail_step_dw(X, idx, W, L, G, bce: Bce, dW, workspace: torch.Tensor, lean=False):
     """Split step, part 2: loss and dW (one kernel)."""
     _tail_in(X, idx, W)
     _need(dW, "dW", X.dtype)
-    d = tail_desc(X, idx, L, G)
+    d = tail_desc(X, idx, L, G, lean)
     b = _bref(bce)
     _check(lib().haste_tail_step_dw(ctypes.byref(d), _ptr(X), _ptr(idx), _ptr(W), b, _ptr(dW),
                                     _ptr(workspace), workspace.numel(), _stream()))
 
 
 def haste_tail_step_dx(X, idx, W, L, G, bce: Bce, dX, workspace: torch.Tensor,
-                       accumulate_dX=False):
+                       accumulate_dX=False, lean=False):
     """Second half of haste_tail_step (dX), using what _dw left in `workspace`."""
     _tail_in(X, idx, W)
     _need(dX, "dX", torch.float32)
-    d = tail_desc(X, idx, L, G)
+    d = tail_desc(X, idx, L, G, lean)
     b = _bref(bce)
     _check(lib().haste_tail_step_dx(ctypes.byref(d), _ptr(X), _ptr(idx), _ptr(W), b, _ptr(dX),
                                     int(bool(accumulate_dX)), _ptr(workspace), workspace.numel(),

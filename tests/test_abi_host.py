@@ -20,7 +20,7 @@ def test_exports_every_declared_symbol(L):
     assert "haste_tail_fwd" in names and "haste_tail_step" in names
     missing = [n for n in names if not hasattr(L, n)]
     assert missing == []
-    assert L.haste_abi_version() == 1
+    assert L.haste_abi_version() == 2
     for s in range(5):
         assert L.haste_status_string(s)
 
@@ -45,6 +45,11 @@ def test_workspace_sizes(L):
     b = H.BceStruct(nnz=10000)
     n1 = L.haste_tail_workspace_bytes(ctypes.byref(d), ctypes.byref(b))
     assert n0 > 0 and n1 >= n0 + 10000 * 4 - 256
+    # with positives, the default form also keeps the dz tiles: B_pad x N_g*G bf16
+    nl = L.haste_tail_workspace_bytes(ctypes.byref(_desc(flags=H.HASTE_TAIL_LEAN)), ctypes.byref(b))
+    assert n1 - nl >= 64 * 1024 * 2 and nl >= n0 + 10000 * 4 - 256
+    # unknown flags -> 0
+    assert L.haste_tail_workspace_bytes(ctypes.byref(_desc(flags=2)), None) == 0
     # unsupported shape -> 0
     assert L.haste_tail_workspace_bytes(ctypes.byref(_desc(G=8)), None) == 0
     h = H.HeadDesc(B=8, D=64, H=128, dtype=H.HASTE_BF16)
@@ -62,6 +67,7 @@ def test_argument_errors_fail_before_launch(L):
     assert _status(L, _desc(B=0)) == H.HASTE_ERR_INVALID
     assert _status(L, _desc(F=128, D=64)) == H.HASTE_ERR_INVALID      # F > D
     assert _status(L, _desc(dtype=7)) == H.HASTE_ERR_INVALID
+    assert _status(L, _desc(flags=4)) == H.HASTE_ERR_INVALID
     assert _status(L, _desc(G=8)) == H.HASTE_ERR_UNSUPPORTED
     assert _status(L, _desc(F=48)) == H.HASTE_ERR_UNSUPPORTED
     assert _status(L, _desc(D=4096, F=128)) == H.HASTE_ERR_UNSUPPORTED

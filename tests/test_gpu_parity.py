@@ -78,19 +78,31 @@ def test_bf16_tail_and_head(H, case):
     torch.cuda.synchronize()
     assert torch.equal(dW, dW2)
 
-    # split form of the step (prepare, dW, dX), as the benchmark runs it
-    b5 = d.bce(c.H, s)
-    ws = torch.empty(H.haste_tail_workspace_bytes(d.X, d.idx, c.L, c.G, b5), dtype=torch.uint8,
-                     device=DEV)
-    dW5 = torch.empty_like(d.W)
-    dX5 = torch.full_like(dX, 2.0)
-    H.haste_tail_prepare(d.X, d.idx, c.L, c.G, b5, ws)
-    H.haste_tail_step_dw(d.X, d.idx, d.W, c.L, c.G, b5, dW5, ws)
-    H.haste_tail_step_dx(d.X, d.idx, d.W, c.L, c.G, b5, dX5, ws, accumulate_dX=True)
+    # lean form: the dX pass recomputes dz instead of reading the dW pass's tiles
+    dW6 = torch.empty_like(d.W)
+    dX6 = torch.empty_like(dX)
+    b6 = d.bce(c.H, s)
+    H.haste_tail_step(d.X, d.idx, d.W, c.L, c.G, b6, dW6, dX6, lean=True)
     torch.cuda.synchronize()
-    check_loss("split step loss", b5.loss.item(), r.loss_tail, "bf16")
-    assert torch.equal(dW5, dW)
-    check("split step dX", to_f64(dX5) - 2.0, r.dX_tail, r.dX_tail_abs, "bf16", nterms=ng * c.G)
+    check_loss("lean step loss", b6.loss.item(), r.loss_tail, "bf16")
+    assert torch.equal(dW6, dW)
+    check("lean step dX", to_f64(dX6), r.dX_tail, r.dX_tail_abs, "bf16", nterms=ng * c.G)
+
+    # split form of the step (prepare, dW, dX), as the benchmark runs it, both forms
+    for lean in (False, True):
+        b5 = d.bce(c.H, s)
+        ws = torch.empty(H.haste_tail_workspace_bytes(d.X, d.idx, c.L, c.G, b5, lean=lean),
+                         dtype=torch.uint8, device=DEV)
+        dW5 = torch.empty_like(d.W)
+        dX5 = torch.full_like(dX, 2.0)
+        H.haste_tail_prepare(d.X, d.idx, c.L, c.G, b5, ws, lean=lean)
+        H.haste_tail_step_dw(d.X, d.idx, d.W, c.L, c.G, b5, dW5, ws, lean=lean)
+        H.haste_tail_step_dx(d.X, d.idx, d.W, c.L, c.G, b5, dX5, ws, accumulate_dX=True, lean=lean)
+        torch.cuda.synchronize()
+        check_loss(f"split step loss (lean={lean})", b5.loss.item(), r.loss_tail, "bf16")
+        assert torch.equal(dW5, dW)
+        check(f"split step dX (lean={lean})", to_f64(dX5) - 2.0, r.dX_tail, r.dX_tail_abs, "bf16",
+              nterms=ng * c.G)
 
     # tail backward, recomputing dz from the positives (no loss added)
     dW3 = torch.empty_like(d.W)
@@ -101,6 +113,11 @@ def test_bf16_tail_and_head(H, case):
     assert b3.loss.item() == 0.0
     assert torch.equal(dW3, dW)
     check("tail bwd dX", to_f64(dX3), r.dX_tail, r.dX_tail_abs, "bf16", nterms=ng * c.G)
+    dX3.zero_()
+    H.haste_tail_bwd(d.X, d.idx, d.W, c.L, c.G, dW3, dX3, bce=d.bce(c.H, s), lean=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dW3, dW)
+    check("lean bwd dX", to_f64(dX3), r.dX_tail, r.dX_tail_abs, "bf16", nterms=ng * c.G)
 
     # tail backward with a given dZ (bf16), accumulating into dX
     dZ_bits = wl.bf16_bits_from_f32(r.dZt.astype(np.float32))
