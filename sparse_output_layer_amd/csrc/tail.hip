@@ -973,6 +973,276 @@ __global__ __launch_bounds__(64 * T2_NW, 1) void k_tail_t2(TailArgs a, int dz_mo
     }
 }
 
+// ------------------------------------------------------------------ T2d
+// dX from the dz tiles of the dW pass (no recompute, no X^T chunk in LDS).
+// Workgroup = (row chunk of BC2 rows) x (range of groups), 12 waves:
+//   consumers (8): dX_chunk += dz_g * W~_g on 32x32x16 MFMAs as in T2, but
+//     the operands of step k+1 (inverse-index lookups, W^T rows, dz) are
+//     loaded into registers right behind the MFMAs of step k, so no LDS
+//     latency sits between a barrier and the next MFMA;
+//   builders (4): per step, W^T and the inverse index of the GPI groups,
+//     and the dz tiles transposed from the dW pass's layout into the
+//     A-operand layout; their operands (W rows, idx, dz) are loaded from
+//     global memory six steps ahead, four iterations before use.
+// Buffers of step s: W^T and dz in ring slot s mod 2, the inverse index in
+// slot s mod 3.  Iteration k: builders clear the inverse index of step k
+// (looked up in iteration k-1) and fill step k+2; consumers run step k and
+// load step k+1; one barrier.  The barrier is __syncthreads(): with no
+// global->LDS copies in flight it waits for LDS operations only, and the
+// compiler knows that the loads of step k+1 have landed, so it puts no
+// wait for them in front of the MFMAs of step k+1.
+constexpr int T2D_NB = 4, T2D_NW = T2_NC + T2D_NB;
+
+struct T2dLds {  // byte offsets and sizes of the LDS regions (host and device agree)
+    int wts, wts_grp, inv, ndp, exch, exch_grp, total;
+};
+
+__host__ __device__ inline T2dLds t2d_layout(int F, int G, int BC2, int NTW32) {
+    T2dLds L;
+    const int GPI = t2_gpi(G, BC2);
+    L.ndp = T2_NC * NTW32 * 32;
+    int o = 0;
+    L.wts = o;
+    L.wts_grp = ((F + 1) * (G * 2 + 8) + 15) & ~15;   // W_g^T (padded rows) + zero row F
+    o += 2 * GPI * L.wts_grp;
+    L.inv = o;
+    o += (3 * GPI * L.ndp + 15) & ~15;                // u8 inverse index
+    L.exch = o;
+    L.exch_grp = BC2 * G * 2;                          // dz of one group, MFMA A layout
+    o += 2 * GPI * L.exch_grp;
+    L.total = o;
+    return L;
+}
+
+template <int G, int BC2, int NTW32>
+__global__ __launch_bounds__(64 * T2D_NW, 1) void k_tail_t2d(TailArgs a, int n_granges) {
+    constexpr int NT = 64 * T2D_NW;
+    constexpr int GPI = t2_gpi(G, BC2);
+    constexpr int JT = G / 16, RT = BC2 / 32;
+    constexpr int GPR = G / 4, LGPR = G == 16 ? 2 : G == 32 ? 3 : 4;
+    constexpr int WTS = G * 2 + 8;             // W^T row stride, bytes
+    constexpr int NDP = T2_NC * NTW32 * 32;    // features covered by the consumer waves
+    constexpr int NB_T = T2D_NB * 64;          // builder threads
+    constexpr int UPT = (GPI * GPR * 32 + NB_T - 1) / NB_T;   // W^T units per builder thread (F <= 128)
+    constexpr int NBLK = GPI * RT * JT;        // 1 KB dz tiles per step
+    constexpr int TPB = (NBLK + T2D_NB - 1) / T2D_NB;       // dz tiles per builder wave
+    const int F = a.F;
+    const int lf4 = F == 128 ? 5 : F == 64 ? 4 : 3;        // log2(F/4)
+    const int lnq = LGPR + lf4;                             // log2(W^T units per group)
+    const T2dLds LY = t2d_layout(F, G, BC2, NTW32);
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    unsigned char *wts0 = lds + LY.wts;
+    unsigned char *inv0 = lds + LY.inv;
+    unsigned char *exch0 = lds + LY.exch;
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int gr = blockIdx.x % n_granges, bch = blockIdx.x / n_granges;
+    const int64_t gA = (int64_t)gr * a.Ng / n_granges, gB = (int64_t)(gr + 1) * a.Ng / n_granges;
+    const int ng = (int)(gB - gA);
+    const int nsteps = (ng + GPI - 1) / GPI;
+    // iterations: a multiple of four, so the builders' loop body (unrolled
+    // by four) has no exits; the extra iterations only pass the barrier
+    const int niter = (nsteps + 3) & ~3;
+    const int r0 = bch * BC2;
+    auto live = [&](int k, int q) { return gA + (int64_t)k * GPI + q < gB; };
+    const unsigned fill = (unsigned)F * 0x01010101u;
+
+    // inverse maps to "no feature" (row F), zero rows of the W^T buffers
+    for (int i = tid; i < 3 * GPI * NDP / 4; i += NT) ((unsigned *)inv0)[i] = fill;
+    for (int i = tid; i < 2 * GPI * (G / 2); i += NT)
+        ((unsigned *)(wts0 + (i / (G / 2)) * LY.wts_grp + F * WTS))[i % (G / 2)] = 0u;
+    __syncthreads();
+
+    if (w < T2_NC) {
+        // ---------------------------------------------------------- consumers
+        const int dbase = w * NTW32 * 32;      // first feature of this wave
+        f32x16 acc[RT][NTW32];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int nt = 0; nt < NTW32; ++nt) acc[rt][nt] = (f32x16){};
+        struct Opd {
+            bf16x8 A[RT][JT];                  // dz: row 32rt + lane%32, labels 16jt + 8(lane/32) ..
+            bf16x8 Bv[JT][NTW32];              // W~: feature dbase + 32nt + lane%32, same labels
+        };
+        Opd R[GPI];
+        auto load = [&](int k, int q) {
+            const unsigned char *wt = wts0 + ((k & 1) * GPI + q) * LY.wts_grp + 16 * (lane >> 5);
+            const unsigned char *iv = inv0 + ((k % 3) * GPI + q) * NDP + dbase + (lane & 31);
+            const unsigned char *ex = exch0 + ((k & 1) * GPI + q) * LY.exch_grp;
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int jt = 0; jt < JT; ++jt)
+                    R[q].A[rt][jt] = *(const bf16x8 *)(ex + ((rt * JT + jt) * 64 + lane) * 16);
+#pragma unroll
+            for (int nt = 0; nt < NTW32; ++nt) {
+                const unsigned char *br = wt + iv[32 * nt] * WTS;
+#pragma unroll
+                for (int jt = 0; jt < JT; ++jt) {
+                    const u32x2 lo = *(const u32x2 *)(br + 32 * jt);
+                    const u32x2 hi = *(const u32x2 *)(br + 32 * jt + 8);
+                    R[q].Bv[jt][nt] = __builtin_bit_cast(bf16x8, (u32x4){lo[0], lo[1], hi[0], hi[1]});
+                }
+            }
+        };
+        __syncthreads();                       // builders have filled steps 0 and 1
+#pragma unroll
+        for (int q = 0; q < GPI; ++q)
+            if (live(0, q)) load(0, q);
+        __syncthreads();                       // step 0 looked up before its inverse index is cleared
+        for (int k = 0; k < niter; ++k) {
+#pragma unroll
+            for (int q = 0; q < GPI; ++q) {
+                if (live(k, q)) {
+#pragma unroll
+                    for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+                        for (int nt = 0; nt < NTW32; ++nt)
+#pragma unroll
+                            for (int rt = 0; rt < RT; ++rt)
+                                acc[rt][nt] = mfma32x32(R[q].A[rt][jt], R[q].Bv[jt][nt], acc[rt][nt]);
+                }
+                if (live(k + 1, q)) load(k + 1, q);
+            }
+            __syncthreads();
+        }
+        // flush: reg r of tile (rt, nt) = row 32rt+8(r/4)+4(lane/32)+r%4, feature dbase+32nt+lane%32
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int nt = 0; nt < NTW32; ++nt) {
+                const int d = dbase + 32 * nt + (lane & 31);
+                if (d >= a.D) continue;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = r0 + 32 * rt + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                    if (row < a.B) atomicAdd(a.dX + (int64_t)row * a.D + d, acc[rt][nt][r]);
+                }
+            }
+    } else {
+        // ------------------------------------------------------------- builders
+        // W^T: thread = 4 labels x 4 features of W_g (as in T2).  dz: wave p
+        // takes tiles p, p+4, .. of a step (group q, 32-row block rt, label
+        // tile jt); lane (qq, mm) holds rows 4qq+i and 16+4qq+i of label mm.
+        const int bw = w - T2_NC;
+        const int bth = tid - T2_NC * 64;
+        const int mm = lane & 15, qq = lane >> 4;
+        const int64_t nch32 = a.Bp / 32;
+        struct Ops {
+            u32x2 r[UPT][4];    // rows 4ja+e, features 4fc .. +3, per unit
+            int fi;             // idx[f] of the inverse-index entry of this thread
+            u32x4 dz[TPB];      // dz tiles
+        };
+        auto unit = [&](int i, int &q, int &fc, int &ja) {
+            const int u = bth + NB_T * i;
+            q = u >> lnq;
+            const int rest = u & ((1 << lnq) - 1), r2 = rest >> 2;
+            ja = r2 & (GPR - 1);
+            fc = ((r2 >> LGPR) << 2) | (rest & 3);
+        };
+        auto tile_of = [&](int t, int &q, int &rt, int &jt) {
+            const int blk = bw + T2D_NB * t;
+            q = blk / (RT * JT);
+            rt = (blk / JT) % RT;
+            jt = blk % JT;
+            return blk < NBLK;
+        };
+        // Every load is issued on every path, from a clamped address where
+        // the group, unit or tile does not exist (the value is then unused):
+        // with no load skipped, the compiler can wait for exactly the set it
+        // needs instead of for all loads in flight.
+        auto gsafe = [&](int k, int q) {
+            const int64_t g = gA + (int64_t)k * GPI + q;
+            return g < a.Ng ? g : a.Ng - 1;
+        };
+        auto fetch = [&](int k, Ops &o) {
+#pragma unroll
+            for (int i = 0; i < UPT; ++i) {
+                int q, fc, ja;
+                unit(i, q, fc, ja);
+                if (bth + NB_T * i >= (GPI << lnq)) q = fc = ja = 0;
+                const unsigned short *wr = a.W + (gsafe(k, q) * G + 4 * ja) * (int64_t)F + 4 * fc;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o.r[i][e] = *(const u32x2 *)(wr + e * F);
+            }
+            {
+                const int q = bth < GPI * F ? bth / F : 0;
+                const int f = bth < GPI * F ? bth - q * F : 0;
+                o.fi = a.idx[gsafe(k, q) * F + f];
+            }
+#pragma unroll
+            for (int t = 0; t < TPB; ++t) {
+                int q, rt, jt;
+                if (!tile_of(t, q, rt, jt)) q = rt = jt = 0;
+                o.dz[t] = *(const u32x4 *)(a.dzt + (((gsafe(k, q) * nch32 + (r0 >> 5) + rt) * JT + jt) << 9) +
+                                           lane * 8);
+            }
+        };
+        auto build = [&](int k, const Ops &o) {
+            unsigned char *wts = wts0 + (k & 1) * GPI * LY.wts_grp;
+#pragma unroll
+            for (int i = 0; i < UPT; ++i) {
+                int q, fc, ja;
+                unit(i, q, fc, ja);
+                if (bth + NB_T * i >= (GPI << lnq) || !live(k, q)) continue;
+                unsigned char *wt = wts + q * LY.wts_grp + (4 * fc) * WTS + 8 * ja;
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {   // feature 4fc+kk: element kk of each row
+                    const unsigned sel = (kk & 1) ? 0x07060302u : 0x05040100u;
+                    const int wd = kk >> 1;
+                    const u32x2 v = {__builtin_amdgcn_perm(o.r[i][1][wd], o.r[i][0][wd], sel),
+                                     __builtin_amdgcn_perm(o.r[i][3][wd], o.r[i][2][wd], sel)};
+                    *(u32x2 *)(wt + kk * WTS) = v;
+                }
+            }
+            if (bth < GPI * F) {
+                const int q = bth / F;
+                if (live(k, q)) inv0[((k % 3) * GPI + q) * NDP + o.fi] = (unsigned char)(bth - q * F);
+            }
+#pragma unroll
+            for (int t = 0; t < TPB; ++t) {
+                int q, rt, jt;
+                if (!tile_of(t, q, rt, jt) || !live(k, q)) continue;
+                // (row rho, label mm) -> lane rho + 32(mm/8), K slot mm%8 of block (rt, jt)
+                unsigned char *ex = exch0 + ((k & 1) * GPI + q) * LY.exch_grp + (rt * JT + jt) * 1024 +
+                                    (32 * (mm >> 3)) * 16 + 2 * (mm & 7);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int rho = 16 * (e >> 2) + 4 * qq + (e & 3);
+                    const unsigned wv = o.dz[t][e >> 1];
+                    *(unsigned short *)(ex + rho * 16) = (unsigned short)((e & 1) ? (wv >> 16) : (wv & 0xffffu));
+                }
+            }
+        };
+        // operand sets: step s in set s mod 4, loaded four iterations ahead
+        Ops o0, o1, o2, o3;
+        fetch(0, o0);
+        fetch(1, o1);
+        fetch(2, o2);
+        fetch(3, o3);
+        build(0, o0);
+        fetch(4, o0);
+        build(1, o1);
+        fetch(5, o1);
+        __syncthreads();
+        __syncthreads();
+        auto iter = [&](int k, Ops &o) {
+            unsigned *ivp = (unsigned *)(inv0 + (k % 3) * GPI * NDP);
+            for (int i = bth; i < GPI * NDP / 4; i += NB_T) ivp[i] = fill;
+            build(k + 2, o);
+            fetch(k + 6, o);
+            __syncthreads();
+        };
+        for (int k = 0; k < niter; k += 4) {
+            iter(k, o2);
+            iter(k + 1, o3);
+            iter(k + 2, o0);
+            iter(k + 3, o1);
+        }
+    }
+}
+
 static int64_t t2_granges(int nbch, int64_t Ng) {
     int dev = 0, ncu = 256;
     if (hipGetDevice(&dev) == hipSuccess)
@@ -1019,6 +1289,40 @@ static hipError_t t2_pick_ntw(int dz_mode, const TailArgs &a, hipStream_t st) {
     return hipErrorInvalidValue;
 }
 
+template <int G, int BC2, int NTW32>
+static hipError_t t2d_go(const TailArgs &a, hipStream_t st) {
+    const int nbch = a.Bp / BC2;
+    const int64_t ngr = t2_granges(nbch, a.Ng);
+    if (ngr < 1) return hipSuccess;
+    const T2dLds L = t2d_layout(a.F, G, BC2, NTW32);
+    if (L.total > 160 * 1024) return hipErrorInvalidValue;
+    allow_lds((const void *)k_tail_t2d<G, BC2, NTW32>, L.total);
+    hipLaunchKernelGGL((k_tail_t2d<G, BC2, NTW32>), dim3((unsigned)(ngr * nbch)), dim3(64 * T2D_NW),
+                       L.total, st, a, (int)ngr);
+    return hipGetLastError();
+}
+
+template <int G, int BC2>
+static hipError_t t2d_pick_ntw(const TailArgs &a, hipStream_t st) {
+    switch (t2_ntw(a.D, BC2)) {
+    case 1: return t2d_go<G, BC2, 1>(a, st);
+    case 2: return t2d_go<G, BC2, 2>(a, st);
+    case 3: return t2d_go<G, BC2, 3>(a, st);
+    }
+    if constexpr (BC2 == 32)
+        if (t2_ntw(a.D, BC2) == 4) return t2d_go<G, BC2, 4>(a, st);
+    return hipErrorInvalidValue;
+}
+
+// 64-row chunks when the batch is larger than 32 rows and the accumulator
+// (2 x NTW32 32x32 tiles per consumer) stays within 96 registers
+template <int G>
+static hipError_t t2d_pick(const TailArgs &a, hipStream_t st) {
+    if constexpr (G < 64)
+        if (a.B > 32 && t2_ntw(a.D, 64) <= 3) return t2d_pick_ntw<G, 64>(a, st);
+    return t2d_pick_ntw<G, 32>(a, st);
+}
+
 // 64-row chunks when they fit in LDS, the batch is larger than 32 rows and
 // the accumulator (2 x NTW32 32x32 tiles per consumer) stays within 96 registers
 static int t2_bc(int G, int F, int D, int B) {
@@ -1036,6 +1340,14 @@ static hipError_t t2_pick(int dz_mode, const TailArgs &a, hipStream_t st) {
 hipError_t launch_tail_t2(int G, int dz_mode, const TailArgs &a, hipStream_t st) {
     if (dz_mode < 0 || dz_mode > 2 || (dz_mode == 1 && !a.dZ) || (dz_mode == 2 && !a.dzt))
         return hipErrorInvalidValue;
+    if (dz_mode == 2) {
+        switch (G) {
+        case 16: return t2d_pick<16>(a, st);
+        case 32: return t2d_pick<32>(a, st);
+        case 64: return t2d_pick<64>(a, st);
+        }
+        return hipErrorInvalidValue;
+    }
     switch (G) {
     case 16: return t2_pick<16>(dz_mode, a, st);
     case 32: return t2_pick<32>(dz_mode, a, st);
