@@ -235,6 +235,7 @@ __host__ __device__ inline int t1_blk_per_wave(int D, int NW) { return (t1_nblk(
 __host__ __device__ inline size_t t1_buf_bytes(int D, int NW) {
     return (size_t)NW * t1_blk_per_wave(D, NW) * 1024;
 }
+constexpr int T1_BUF_BYTES = 80 * 1024;    // one chunk buffer, static: D <= 1024 with NW in {4, 8}
 
 // Issue this wave's share of the asynchronous copy of chunk ch into buf.
 template <int NW>
@@ -259,8 +260,12 @@ __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, int store_z,
     constexpr int BC = T1_BC, BCP = T1_BCP;
     constexpr bool DO_Z = (MODE != T1_DW_MEM);
     constexpr bool DO_DW = (MODE != T1_FWD);
-    extern __shared__ __attribute__((aligned(16))) unsigned short tiles[];
-    const size_t bstride = t1_buf_bytes(a.D, NW) / 2;   // in shorts
+    // The two chunk buffers are distinct LDS objects and the chunk loop is
+    // unrolled by two, so every access names its buffer statically: the
+    // compiler then sees that the copy into one buffer cannot alias the
+    // reads of the other and does not wait for the copy before them.
+    __shared__ __attribute__((aligned(16))) unsigned short buf0[T1_BUF_BYTES / 2];
+    __shared__ __attribute__((aligned(16))) unsigned short buf1[T1_BUF_BYTES / 2];
 
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int q = lane >> 4, m = lane & 15;
@@ -310,14 +315,8 @@ __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, int store_z,
                 for (int jt = 0; jt < JT; ++jt) dwacc[r][ft][jt] = (f32x4){0.f, 0.f, 0.f, 0.f};
         }
 
-        __syncthreads();                  // previous run's readers are done with buffer 0
-        t1_stage_async<NW>(a, tiles, 0, w, lane);
-        for (int ch = 0; ch < nch; ++ch) {
-            __builtin_amdgcn_s_waitcnt(0);   // this wave's copies of chunk ch have landed
-            __syncthreads();                 // ... and everyone's; chunk ch-1 is consumed
-            if (ch + 1 < nch)
-                t1_stage_async<NW>(a, tiles + ((ch + 1) & 1) * bstride, ch + 1, w, lane);
-            const unsigned short *tile = tiles + (ch & 1) * bstride;
+        // one chunk of BC rows, staged in `tile`
+        auto chunk = [&](const unsigned short *tile, const int ch) {
             const int r0 = ch * BC;
 
 #pragma unroll
@@ -327,14 +326,19 @@ __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, int store_z,
                 // positives of group g in rows [r0, r0+32): lane owns rows r0+16h2+4q+i, slot 16jt+m
                 uint64_t ymask = 0;
                 bool has_pos = false;             // wave-uniform
-                for (int e = 0; e < pn[r]; ++e) {
-                    const int v = e < 64 ? __builtin_amdgcn_readlane(pe[r], e) : a.grp_ent[gp0[r] + e];
+                auto add_pos = [&](const int v) {
                     const int lb = v / G - r0, j = v % G;
-                    if (lb < 0 || lb >= BC) continue;
+                    if (lb < 0 || lb >= BC) return;
                     has_pos = true;
                     if (((lb >> 2) & 3) == q && (j & 15) == m)
                         ymask |= 1ull << (((lb >> 4) * JT + (j >> 4)) * 4 + (lb & 3));
-                }
+                };
+                // entries 0..63 from registers; the rest (a label with more than 64
+                // positives in the batch) from memory, in a loop of its own so that
+                // the register path carries no wait for loads in flight
+                const int n1 = pn[r] < 64 ? pn[r] : 64;
+                for (int e = 0; e < n1; ++e) add_pos(__builtin_amdgcn_readlane(pe[r], e));
+                for (int e = 64; e < pn[r]; ++e) add_pos(a.grp_ent[gp0[r] + e]);
                 f32x4 zacc[2][JT];
 #pragma unroll
                 for (int h2 = 0; h2 < 2; ++h2)
@@ -442,6 +446,19 @@ __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, int store_z,
                     }
                 }
             }
+        };
+        // nch is even (Bp is a multiple of 64)
+        __syncthreads();                  // previous run's readers are done with buffer 0
+        t1_stage_async<NW>(a, buf0, 0, w, lane);
+        for (int ch = 0; ch < nch; ch += 2) {
+            __builtin_amdgcn_s_waitcnt(0);   // this wave's copies of chunk ch have landed
+            __syncthreads();                 // ... and everyone's; chunk ch-1 is consumed
+            t1_stage_async<NW>(a, buf1, ch + 1, w, lane);
+            chunk(buf0, ch);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (ch + 2 < nch) t1_stage_async<NW>(a, buf0, ch + 2, w, lane);
+            chunk(buf1, ch + 1);
         }
         if (DO_DW) {
 #pragma unroll
@@ -474,7 +491,8 @@ static void allow_lds(const void *fn, size_t bytes) {
 template <int G, int F, int RW, int NW>
 static hipError_t t1_launch(int mode, const TailArgs &a, bool store_z, bool do_loss,
                             hipStream_t st) {
-    const size_t lds = t1_buf_bytes(a.D, NW) * 2;
+    if (t1_buf_bytes(a.D, NW) > (size_t)T1_BUF_BYTES) return hipErrorInvalidValue;
+    const size_t lds = 0;
     const int64_t n_runs = (a.Ng + NW * RW - 1) / (NW * RW);
     int dev = 0, ncu = 256;
     if (hipGetDevice(&dev) == hipSuccess)
@@ -484,17 +502,14 @@ static hipError_t t1_launch(int mode, const TailArgs &a, bool store_z, bool do_l
     const dim3 blk(64 * NW);
     switch (mode) {
     case T1_FWD:
-        allow_lds((const void *)k_tail_t1<G, F, RW, NW, T1_FWD>, lds);
         hipLaunchKernelGGL((k_tail_t1<G, F, RW, NW, T1_FWD>), dim3((unsigned)grid), blk, lds, st,
                            a, (int)store_z, (int)do_loss);
         break;
     case T1_DW_BCE:
-        allow_lds((const void *)k_tail_t1<G, F, RW, NW, T1_DW_BCE>, lds);
         hipLaunchKernelGGL((k_tail_t1<G, F, RW, NW, T1_DW_BCE>), dim3((unsigned)grid), blk, lds,
                            st, a, 0, (int)do_loss);
         break;
     default:
-        allow_lds((const void *)k_tail_t1<G, F, RW, NW, T1_DW_MEM>, lds);
         hipLaunchKernelGGL((k_tail_t1<G, F, RW, NW, T1_DW_MEM>), dim3((unsigned)grid), blk, lds,
                            st, a, 0, 0);
         break;
@@ -825,15 +840,17 @@ __global__ __launch_bounds__(64 * T2_NW, 1) void k_tail_t2(TailArgs a, int dz_mo
                 bool has_pos = false;                // wave-uniform
 #pragma unroll
                 for (int t = 0; t < TPW; ++t) ymask[t] = 0;
-                for (int e = 0; e < zn; ++e) {
-                    const int v = e < 64 ? __builtin_amdgcn_readlane(pe, e) : a.grp_ent[zg0 + e];
+                auto add_pos = [&](const int v) {
                     const int lb = v / G - (r0 + 16 * bt0), j = v % G;
-                    if (lb < 0 || lb >= 16 * TPW || (j >> 4) != jt) continue;
+                    if (lb < 0 || lb >= 16 * TPW || (j >> 4) != jt) return;
                     has_pos = true;
 #pragma unroll
                     for (int t = 0; t < TPW; ++t)
                         if (lb == 16 * t + m && ((j >> 2) & 3) == hq) ymask[t] |= 1u << (j & 3);
-                }
+                };
+                const int n1 = zn < 64 ? zn : 64;   // registers first, then memory
+                for (int e = 0; e < n1; ++e) add_pos(__builtin_amdgcn_readlane(pe, e));
+                for (int e = 64; e < zn; ++e) add_pos(a.grp_ent[zg0 + e]);
                 // sigmoid(z) = 1 / (1 + 2^(-z log2 e)); saturates cleanly at both ends
                 if (!has_pos && r0 + 16 * (bt0 + TPW) <= a.B && (g + 1) * G <= a.L) {
 #pragma unroll
@@ -1361,7 +1378,7 @@ bool tail_bf16_supported(int G, int F, int D) {
     if (!(F == 32 || F == 64 || F == 128)) return false;
     if (D < F || D > 1024) return false;
     // T1: two chunk buffers; T2: chunk + pipeline buffers with 32-row chunks at least
-    if (t1_buf_bytes(D, 8) * 2 > 160 * 1024 || t1_buf_bytes(D, 4) * 2 > 160 * 1024) return false;
+    if (t1_buf_bytes(D, 8) > (size_t)T1_BUF_BYTES || t1_buf_bytes(D, 4) > (size_t)T1_BUF_BYTES) return false;
     if (!t2_fits(D, F, G, 32, t2_ntw(D, 32))) return false;
     return true;
 }
