@@ -530,10 +530,12 @@ haste_status head_grads(const haste_head_desc *d, const void *X, const void *Wh,
         x.lda = d->H;
         x.ldb = d->D;
         x.C32 = dX;
-        const int tiles = ((d->B + 127) / 128) * ((d->D + 127) / 128);
-        int splits = (512 + tiles - 1) / tiles;
+        // split K so that about 256 (64-row) tiles run, each split adding
+        // its partial sums with fp32 atomics
+        const int tiles = ((d->B + 63) / 64) * ((d->D + 127) / 128);
+        int splits = (256 + tiles - 1) / tiles;
         int ks = (d->H + splits - 1) / splits;
-        ks = (ks + 31) / 32 * 32;
+        ks = (ks + 63) / 64 * 64;
         if (ks < 256) ks = 256;
         x.k_split = ks;
         TRY_HIP(launch_gemm(true, false, EPI_ATOMIC32, x, st), "head dX");

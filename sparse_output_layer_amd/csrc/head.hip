@@ -181,10 +181,240 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g) {
     }
 }
 
+// ------------------------------------------------------------ pipelined GEMM
+// Same contractions and epilogues as k_gemm, for shapes whose M, N, K and
+// split length are multiples of 8 (every head of the workloads): M tile of
+// TMT = 64 or 128 rows, N tile 128, K step 64, the operand tiles of step k+2
+// loaded into registers while step k runs (two register sets, alternating,
+// so a load has two steps to land), LDS double-buffered.  Loads are issued
+// unconditionally from clamped addresses and zeroed outside the matrix at
+// the LDS store, so the compiler waits for exactly the set it stores.
+constexpr int TK2 = 64;
+constexpr int KROW2 = TK2 + 8;    // K-major LDS row (shorts): 144 B
+
+// ROWS x 64 operand tile: ROWS/32 16-byte loads per thread.  Bit `it` of the
+// returned mask says whether segment `it` lies inside the matrix.
+template <bool KMAJ, int ROWS>
+__device__ __forceinline__ unsigned load_tile2(const unsigned short *__restrict__ P, int ld, int r0,
+                                               int rows, int k0, int K, u32x4 (&v)[ROWS / 32]) {
+    constexpr int SEG = ROWS / 8;     // M-major: 16-byte segments per K row
+    unsigned mask = 0;
+#pragma unroll
+    for (int it = 0; it < ROWS / 32; ++it) {
+        const int i = threadIdx.x + it * 256;
+        int r, k;
+        if (KMAJ) {  // row r (M or N), 8 segments of 8 along K
+            r = i >> 3;
+            k = (i & 7) * 8;
+        } else {     // row k (64 rows), SEG segments of 8 along M or N
+            k = i / SEG;
+            r = (i % SEG) * 8;
+        }
+        const int gr = r0 + r, gk = k0 + k;
+        // rows and K are multiples of 8: a segment is wholly inside or outside
+        const bool ok = gr < rows && gk < K;
+        const int cr = gr < rows ? gr : rows - (KMAJ ? 1 : 8);
+        const int ck = gk < K ? gk : K - (KMAJ ? 8 : 1);
+        v[it] = KMAJ ? *(const u32x4 *)(P + (int64_t)cr * ld + ck)
+                     : *(const u32x4 *)(P + (int64_t)ck * ld + cr);
+        mask |= (ok ? 1u : 0u) << it;
+    }
+    return mask;
+}
+
+template <bool KMAJ, int ROWS>
+__device__ __forceinline__ void store_tile2(unsigned short *S, const u32x4 (&v)[ROWS / 32],
+                                            unsigned mask) {
+    constexpr int SEG = ROWS / 8, MR = ROWS + 8;
+#pragma unroll
+    for (int it = 0; it < ROWS / 32; ++it) {
+        const int i = threadIdx.x + it * 256;
+        const u32x4 x = ((mask >> it) & 1u) ? v[it] : (u32x4){0u, 0u, 0u, 0u};
+        if (KMAJ) *(u32x4 *)(S + (i >> 3) * KROW2 + (i & 7) * 8) = x;
+        else *(u32x4 *)(S + (i / SEG) * MR + (i % SEG) * 8) = x;
+    }
+}
+
+// operand of the 16 rows from r, K slots 32ks + 8q .. +7
+template <bool KMAJ, int ROWS>
+__device__ __forceinline__ bf16x8 read_operand2(const unsigned short *S, int r, int ks, int q, int m) {
+    constexpr int MR = ROWS + 8;
+    if (KMAJ) return *(const bf16x8 *)(S + (r + m) * KROW2 + 32 * ks + 8 * q);
+    const unsigned short *Sk = S + 32 * ks * MR;
+    i16x4 a0 = lds_read_tr(Sk + (8 * q + (m >> 2)) * MR + r + 4 * (m & 3));
+    i16x4 a1 = lds_read_tr(Sk + (8 * q + 4 + (m >> 2)) * MR + r + 4 * (m & 3));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+template <bool A_KMAJ, bool B_KMAJ, int EPI, int TMT>
+__global__ __launch_bounds__(256, 2) void k_gemm2(GemmArgs g) {
+    constexpr int MI = TMT / 32;      // 16-row MFMA tiles per wave (waves: 2 along M, 2 along N)
+    constexpr int NA = TMT / 32, NB = TN / 32;
+    constexpr int ASZ = A_KMAJ ? TMT * KROW2 : TK2 * (TMT + 8);
+    constexpr int BSZ = B_KMAJ ? TN * KROW2 : TK2 * (TN + 8);
+    __shared__ __attribute__((aligned(16))) unsigned short sm[2 * (ASZ + BSZ)];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int q = lane >> 4, m = lane & 15;
+    const int wm = (w >> 1) * (TMT / 2), wn = (w & 1) * 64;
+    // Workgroups go round-robin over the 8 XCDs.  Tile t = (split, n, m),
+    // m fastest, goes to workgroup slot (t mod T/8)*8 + t/(T/8), so that the
+    // M tiles sharing one B tile (and split) run on one XCD and its L2.
+    const int gx = gridDim.x, gy = gridDim.y;
+    const int T = gx * gy * gridDim.z;
+    const int L = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+    const int t = (T & 7) == 0 ? (L & 7) * (T >> 3) + (L >> 3) : L;
+    const int by = t % gy, bx = (t / gy) % gx, bz = t / (gx * gy);
+    const int m0 = by * TMT, n0 = bx * TN;
+    const int kbeg = bz * g.k_split;
+    int kend = kbeg + g.k_split;
+    if (kend > g.K) kend = g.K;
+    // steps, rounded up to even: a step past the end loads zeros (clamped,
+    // masked) and adds nothing, and the loop below then has no exit
+    const int nk = ((kend - kbeg + TK2 - 1) / TK2 + 1) & ~1;
+    // BCE: the positives of the tile (TMT rows x 4 bitmap words) go to LDS
+    // first, so the epilogue reads them there instead of once per logit
+    __shared__ uint32_t bm_tile[EPI == EPI_BCE ? TMT * 4 : 1];
+    if (EPI == EPI_BCE) {
+        for (int i = threadIdx.x; i < TMT * 4; i += 256) {
+            const int row = m0 + (i >> 2), wd = (n0 >> 5) + (i & 3);
+            bm_tile[i] = g.bitmap && row < g.M && wd < g.bm_words
+                             ? g.bitmap[(int64_t)row * g.bm_words + wd] : 0u;
+        }
+    }
+
+    f32x4 acc[MI][4];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+    u32x4 ra0[NA], rb0[NB], ra1[NA], rb1[NB];
+    unsigned mk0 = 0, mk1 = 0;   // validity bits: A segments from bit 0, B from bit 8
+    auto load = [&](int kt, u32x4 (&ra)[NA], u32x4 (&rb)[NB], unsigned &mk) {
+        const int k0 = kbeg + kt * TK2;
+        mk = load_tile2<A_KMAJ, TMT>(g.A, g.lda, m0, g.M, k0, kend, ra);
+        mk |= load_tile2<B_KMAJ, TN>(g.Bm, g.ldb, n0, g.N, k0, kend, rb) << 8;
+    };
+    auto store = [&](int buf, const u32x4 (&ra)[NA], const u32x4 (&rb)[NB], unsigned mk) {
+        unsigned short *S = sm + buf * (ASZ + BSZ);
+        store_tile2<A_KMAJ, TMT>(S, ra, mk);
+        store_tile2<B_KMAJ, TN>(S + ASZ, rb, mk >> 8);
+    };
+    auto compute = [&](int buf) {
+        const unsigned short *SA = sm + buf * (ASZ + BSZ);
+        const unsigned short *SB = SA + ASZ;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            bf16x8 av[MI], bv[4];
+#pragma unroll
+            for (int i = 0; i < MI; ++i) av[i] = read_operand2<A_KMAJ, TMT>(SA, wm + 16 * i, ks, q, m);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) bv[j] = read_operand2<B_KMAJ, TN>(SB, wn + 16 * j, ks, q, m);
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(av[i], bv[j], acc[i][j]);
+        }
+    };
+    // iteration kt: loads of step kt+2 go out, step kt runs from LDS, step
+    // kt+1 (loaded during iteration kt-1) is stored to the other buffer.
+    if (nk > 0) {
+        load(0, ra0, rb0, mk0);
+        load(1, ra1, rb1, mk1);
+        store(0, ra0, rb0, mk0);
+        __syncthreads();
+        // the scheduling barriers keep each step's loads ahead of its MFMAs
+        for (int kt = 0; kt < nk; kt += 2) {
+            load(kt + 2, ra0, rb0, mk0);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(0);
+            __builtin_amdgcn_sched_barrier(0);
+            store(1, ra1, rb1, mk1);
+            __syncthreads();
+            load(kt + 3, ra1, rb1, mk1);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(1);
+            __builtin_amdgcn_sched_barrier(0);
+            store(0, ra0, rb0, mk0);
+            __syncthreads();
+        }
+    }
+
+    // epilogue: lane owns C[m0+wm+16i+4q+e][n0+wn+16j+m].  BCE with the
+    // hardware exp / rcp / log: sigmoid(z) from e = exp(-|z|), and
+    // softplus(z) = max(z, 0) + log(1 + e), the logs taken of products of
+    // sixteen (1 + e) factors (each in [1, 2]).
+    float lsum = 0.f, lin = 0.f, prod = 1.f;
+    uint32_t bw[MI][4][2];   // bitmap words of the lane's rows: columns wn .. wn+31, wn+32 .. wn+63
+    if (EPI == EPI_BCE) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    bw[i][e][h] = bm_tile[(wm + 16 * i + 4 * q + e) * 4 + (wn >> 5) + h];
+    }
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int col = n0 + wn + 16 * j + m;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int row = m0 + wm + 16 * i + 4 * q + e;
+                if (row >= g.M || col >= g.N) continue;
+                const float v = acc[i][j][e];
+                const int64_t o = (int64_t)row * g.N + col;
+                if (EPI == EPI_BCE) {
+                    if (g.bitmap) {
+                        const float y = (float)((bw[i][e][j >> 1] >> ((16 * j + m) & 31)) & 1u);
+                        const float ex = fast_exp_neg_abs(v);
+                        float den;
+                        const float sg = fast_sigmoid(v, ex, den);
+                        prod *= den;
+                        lin += fmaxf(v, 0.f) - y * v;
+                        if (g.dZout) g.dZout[o] = f32_to_bf16(g.s * (sg - y));
+                    }
+                    if (g.Zout) g.Zout[o] = f32_to_bf16(v);
+                } else if (EPI == EPI_STORE16) {
+                    g.C16[o] = f32_to_bf16(v);
+                } else {
+                    atomicAdd(g.C32 + o, v);
+                }
+            }
+        }
+        if (EPI == EPI_BCE) {   // sixteen factors per i
+            lsum += fast_log(prod);
+            prod = 1.f;
+        }
+    }
+    if (EPI == EPI_BCE && g.loss) {
+        float v = wave_sum(g.s * (lin + lsum));
+        if (lane == 0) atomicAdd(g.loss, v);
+    }
+}
+
 hipError_t launch_gemm(bool a_kmaj, bool b_kmaj, int epi, const GemmArgs &g, hipStream_t st) {
     if (g.M <= 0 || g.N <= 0 || g.K <= 0) return hipSuccess;
     const int splits = (g.K + g.k_split - 1) / g.k_split;
     dim3 grid((g.N + TN - 1) / TN, (g.M + TM - 1) / TM, splits);
+    if (g.M % 8 == 0 && g.N % 8 == 0 && g.K % 8 == 0 && g.k_split % 8 == 0) {
+        // 64-row M tiles (4 waves of 32 x 64, LDS-bound) only when 128-row
+        // tiles (4 waves of 64 x 64) would leave CUs idle
+        const int t128 = ((g.N + TN - 1) / TN) * ((g.M + 127) / 128) * splits;
+        const bool small = t128 < 256;
+        const dim3 grid2((g.N + TN - 1) / TN, (g.M + (small ? 63 : 127)) / (small ? 64 : 128), splits);
+#define GL2(AK, BK, E)                                                                    \
+    if (small) hipLaunchKernelGGL((k_gemm2<AK, BK, E, 64>), grid2, dim3(256), 0, st, g);  \
+    else hipLaunchKernelGGL((k_gemm2<AK, BK, E, 128>), grid2, dim3(256), 0, st, g)
+        if (epi == EPI_BCE && a_kmaj && b_kmaj) { GL2(true, true, EPI_BCE); }
+        else if (epi == EPI_STORE16 && !a_kmaj && !b_kmaj) { GL2(false, false, EPI_STORE16); }
+        else if (epi == EPI_ATOMIC32 && a_kmaj && !b_kmaj) { GL2(true, false, EPI_ATOMIC32); }
+        else return hipErrorInvalidValue;
+#undef GL2
+        return hipGetLastError();
+    }
 #define GL(AK, BK, E) \
     hipLaunchKernelGGL((k_gemm<AK, BK, E>), grid, dim3(256), 0, st, g)
     if (epi == EPI_BCE && a_kmaj && b_kmaj) GL(true, true, EPI_BCE);
