@@ -280,6 +280,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, int store_z,
         unsigned zrow[RW][KS];            // tr-gather rows: lo16 = h 0, hi16 = h 1
         unsigned frow[RW][FT / 2];        // dW rows, two f-tiles per word
         int gp0[RW], pn[RW], pe[RW];      // positives per group: first, count, entry per lane
+        int pc[RW];                       // next positive of the group not yet below the chunk
         f32x4 dwacc[RW][FT][JT];
 #pragma unroll
         for (int r = 0; r < RW; ++r) {
@@ -303,7 +304,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, int store_z,
 #pragma unroll
             for (int p = 0; p < FT / 2; ++p)
                 frow[r][p] = (unsigned)ix[32 * p + m] | ((unsigned)ix[32 * p + 16 + m] << 16);
-            gp0[r] = pn[r] = pe[r] = 0;
+            gp0[r] = pn[r] = pe[r] = pc[r] = 0;
             if (need_pos && ok) {
                 gp0[r] = __builtin_amdgcn_readfirstlane(a.grp_ptr[g]);
                 pn[r] = __builtin_amdgcn_readfirstlane(a.grp_ptr[g + 1]) - gp0[r];
@@ -333,12 +334,28 @@ __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, int store_z,
                     if (((lb >> 2) & 3) == q && (j & 15) == m)
                         ymask |= 1ull << (((lb >> 4) * JT + (j >> 4)) * 4 + (lb & 3));
                 };
-                // entries 0..63 from registers; the rest (a label with more than 64
-                // positives in the batch) from memory, in a loop of its own so that
-                // the register path carries no wait for loads in flight
-                const int n1 = pn[r] < 64 ? pn[r] : 64;
-                for (int e = 0; e < n1; ++e) add_pos(__builtin_amdgcn_readlane(pe[r], e));
-                for (int e = 64; e < pn[r]; ++e) add_pos(a.grp_ent[gp0[r] + e]);
+                // The group's entries are sorted by row, and chunks come in row
+                // order: a cursor walks the list once per run, taking the
+                // entries of this chunk's rows.  Entries 0..63 come from
+                // registers; the rest (a label with more than 64 positives in the
+                // batch) from memory, in a loop of its own so that the register
+                // path carries no wait for loads in flight.
+                {
+                    int e = pc[r];
+                    const int n1 = pn[r] < 64 ? pn[r] : 64;
+                    for (; e < n1; ++e) {
+                        const int v = __builtin_amdgcn_readlane(pe[r], e);
+                        if (v / G >= r0 + BC) break;
+                        add_pos(v);
+                    }
+                    if (e >= 64)
+                        for (; e < pn[r]; ++e) {
+                            const int v = a.grp_ent[gp0[r] + e];
+                            if (v / G >= r0 + BC) break;
+                            add_pos(v);
+                        }
+                    pc[r] = e;
+                }
                 f32x4 zacc[2][JT];
 #pragma unroll
                 for (int h2 = 0; h2 < 2; ++h2)
@@ -521,11 +538,11 @@ hipError_t launch_tail_t1(int mode, int G, const TailArgs &a, bool store_z, bool
                           hipStream_t st) {
 #define T1CASE(GG, FF, RR, NN) \
     if (G == GG && a.F == FF) return t1_launch<GG, FF, RR, NN>(mode, a, store_z, do_loss, st);
-    T1CASE(16, 32, 4, 8)
-    T1CASE(16, 64, 3, 8)
-    T1CASE(16, 128, 2, 8)
-    T1CASE(32, 32, 3, 8)
-    T1CASE(32, 64, 2, 8)
+    T1CASE(16, 32, 2, 16)
+    T1CASE(16, 64, 1, 16)
+    T1CASE(16, 128, 1, 16)
+    T1CASE(32, 32, 1, 16)
+    T1CASE(32, 64, 1, 16)
     T1CASE(32, 128, 1, 8)
     T1CASE(64, 32, 2, 8)
     T1CASE(64, 64, 1, 8)
