@@ -1018,14 +1018,21 @@ __global__ __launch_bounds__(64 * T2_NW, 1) void k_tail_t2(TailArgs a, int dz_mo
 //     and the dz tiles transposed from the dW pass's layout into the
 //     A-operand layout; their operands (W rows, idx, dz) are loaded from
 //     global memory six steps ahead, four iterations before use.
-// Buffers of step s: W^T and dz in ring slot s mod 2, the inverse index in
-// slot s mod 3.  Iteration k: builders clear the inverse index of step k
-// (looked up in iteration k-1) and fill step k+2; consumers run step k and
-// load step k+1; one barrier.  The barrier is __syncthreads(): with no
+// Buffers of step s: W^T and dz in ring slot s mod 3, the inverse index in
+// slot s mod 4.  Iteration k: builders clear the inverse index of step k-1
+// and fill step k+2; consumers run step k, loading its later groups and the
+// first groups of step k+1 as they go; one barrier.  The barrier is __syncthreads(): with no
 // global->LDS copies in flight it waits for LDS operations only, and the
 // compiler knows that the loads of step k+1 have landed, so it puts no
 // wait for them in front of the MFMAs of step k+1.
 constexpr int T2D_NB = 4, T2D_NW = T2_NC + T2D_NB;
+
+// groups per step: for groups of 16 on 64-row chunks and D > 256, twice the
+// Z^T-recompute kernel's (half as many barriers; the builders' operand sets
+// still fit in registers without spilling); otherwise the same
+__host__ __device__ constexpr int t2d_gpi(int G, int BC2, int NTW32) {
+    return G == 16 && BC2 == 64 && NTW32 > 1 ? 2 * t2_gpi(G, BC2) : t2_gpi(G, BC2);
+}
 
 struct T2dLds {  // byte offsets and sizes of the LDS regions (host and device agree)
     int wts, wts_grp, inv, ndp, exch, exch_grp, total;
@@ -1033,17 +1040,17 @@ struct T2dLds {  // byte offsets and sizes of the LDS regions (host and device a
 
 __host__ __device__ inline T2dLds t2d_layout(int F, int G, int BC2, int NTW32) {
     T2dLds L;
-    const int GPI = t2_gpi(G, BC2);
+    const int GPI = t2d_gpi(G, BC2, NTW32);
     L.ndp = T2_NC * NTW32 * 32;
     int o = 0;
     L.wts = o;
     L.wts_grp = ((F + 1) * (G * 2 + 8) + 15) & ~15;   // W_g^T (padded rows) + zero row F
-    o += 2 * GPI * L.wts_grp;
+    o += 3 * GPI * L.wts_grp;
     L.inv = o;
-    o += (3 * GPI * L.ndp + 15) & ~15;                // u8 inverse index
+    o += (4 * GPI * L.ndp + 15) & ~15;                // u8 inverse index
     L.exch = o;
     L.exch_grp = BC2 * G * 2;                          // dz of one group, MFMA A layout
-    o += 2 * GPI * L.exch_grp;
+    o += 3 * GPI * L.exch_grp;
     L.total = o;
     return L;
 }
@@ -1051,7 +1058,7 @@ __host__ __device__ inline T2dLds t2d_layout(int F, int G, int BC2, int NTW32) {
 template <int G, int BC2, int NTW32>
 __global__ __launch_bounds__(64 * T2D_NW, 1) void k_tail_t2d(TailArgs a, int n_granges) {
     constexpr int NT = 64 * T2D_NW;
-    constexpr int GPI = t2_gpi(G, BC2);
+    constexpr int GPI = t2d_gpi(G, BC2, NTW32);
     constexpr int JT = G / 16, RT = BC2 / 32;
     constexpr int GPR = G / 4, LGPR = G == 16 ? 2 : G == 32 ? 3 : 4;
     constexpr int WTS = G * 2 + 8;             // W^T row stride, bytes
@@ -1060,6 +1067,7 @@ __global__ __launch_bounds__(64 * T2D_NW, 1) void k_tail_t2d(TailArgs a, int n_g
     constexpr int UPT = (GPI * GPR * 32 + NB_T - 1) / NB_T;   // W^T units per builder thread (F <= 128)
     constexpr int NBLK = GPI * RT * JT;        // 1 KB dz tiles per step
     constexpr int TPB = (NBLK + T2D_NB - 1) / T2D_NB;       // dz tiles per builder wave
+    constexpr int FPT = (GPI * 128 + NB_T - 1) / NB_T;      // inverse entries per builder thread (F <= 128)
     const int F = a.F;
     const int lf4 = F == 128 ? 5 : F == 64 ? 4 : 3;        // log2(F/4)
     const int lnq = LGPR + lf4;                             // log2(W^T units per group)
@@ -1082,8 +1090,8 @@ __global__ __launch_bounds__(64 * T2D_NW, 1) void k_tail_t2d(TailArgs a, int n_g
     const unsigned fill = (unsigned)F * 0x01010101u;
 
     // inverse maps to "no feature" (row F), zero rows of the W^T buffers
-    for (int i = tid; i < 3 * GPI * NDP / 4; i += NT) ((unsigned *)inv0)[i] = fill;
-    for (int i = tid; i < 2 * GPI * (G / 2); i += NT)
+    for (int i = tid; i < 4 * GPI * NDP / 4; i += NT) ((unsigned *)inv0)[i] = fill;
+    for (int i = tid; i < 3 * GPI * (G / 2); i += NT)
         ((unsigned *)(wts0 + (i / (G / 2)) * LY.wts_grp + F * WTS))[i % (G / 2)] = 0u;
     __syncthreads();
 
@@ -1099,16 +1107,21 @@ __global__ __launch_bounds__(64 * T2D_NW, 1) void k_tail_t2d(TailArgs a, int n_g
             bf16x8 A[RT][JT];                  // dz: row 32rt + lane%32, labels 16jt + 8(lane/32) ..
             bf16x8 Bv[JT][NTW32];              // W~: feature dbase + 32nt + lane%32, same labels
         };
-        Opd R[GPI];
+        // Operand sets: with two or more groups per step, group q in set q % 2,
+        // the set just used taking group q+2 (of this step, or one of the
+        // first two of the next, complete since the previous iteration); with
+        // one group per step, one set taking the next step's group.
+        constexpr int NS = GPI >= 2 ? 2 : 1;
+        Opd R[NS];
         auto load = [&](int k, int q) {
-            const unsigned char *wt = wts0 + ((k & 1) * GPI + q) * LY.wts_grp + 16 * (lane >> 5);
-            const unsigned char *iv = inv0 + ((k % 3) * GPI + q) * NDP + dbase + (lane & 31);
-            const unsigned char *ex = exch0 + ((k & 1) * GPI + q) * LY.exch_grp;
+            const unsigned char *wt = wts0 + ((k % 3) * GPI + q) * LY.wts_grp + 16 * (lane >> 5);
+            const unsigned char *iv = inv0 + ((k & 3) * GPI + q) * NDP + dbase + (lane & 31);
+            const unsigned char *ex = exch0 + ((k % 3) * GPI + q) * LY.exch_grp;
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
                 for (int jt = 0; jt < JT; ++jt)
-                    R[q].A[rt][jt] = *(const bf16x8 *)(ex + ((rt * JT + jt) * 64 + lane) * 16);
+                    R[q % NS].A[rt][jt] = *(const bf16x8 *)(ex + ((rt * JT + jt) * 64 + lane) * 16);
 #pragma unroll
             for (int nt = 0; nt < NTW32; ++nt) {
                 const unsigned char *br = wt + iv[32 * nt] * WTS;
@@ -1116,13 +1129,13 @@ __global__ __launch_bounds__(64 * T2D_NW, 1) void k_tail_t2d(TailArgs a, int n_g
                 for (int jt = 0; jt < JT; ++jt) {
                     const u32x2 lo = *(const u32x2 *)(br + 32 * jt);
                     const u32x2 hi = *(const u32x2 *)(br + 32 * jt + 8);
-                    R[q].Bv[jt][nt] = __builtin_bit_cast(bf16x8, (u32x4){lo[0], lo[1], hi[0], hi[1]});
+                    R[q % NS].Bv[jt][nt] = __builtin_bit_cast(bf16x8, (u32x4){lo[0], lo[1], hi[0], hi[1]});
                 }
             }
         };
         __syncthreads();                       // builders have filled steps 0 and 1
 #pragma unroll
-        for (int q = 0; q < GPI; ++q)
+        for (int q = 0; q < NS; ++q)
             if (live(0, q)) load(0, q);
         __syncthreads();                       // step 0 looked up before its inverse index is cleared
         for (int k = 0; k < niter; ++k) {
@@ -1135,9 +1148,13 @@ __global__ __launch_bounds__(64 * T2D_NW, 1) void k_tail_t2d(TailArgs a, int n_g
                         for (int nt = 0; nt < NTW32; ++nt)
 #pragma unroll
                             for (int rt = 0; rt < RT; ++rt)
-                                acc[rt][nt] = mfma32x32(R[q].A[rt][jt], R[q].Bv[jt][nt], acc[rt][nt]);
+                                acc[rt][nt] = mfma32x32(R[q % NS].A[rt][jt], R[q % NS].Bv[jt][nt], acc[rt][nt]);
                 }
-                if (live(k + 1, q)) load(k + 1, q);
+                if (q + NS < GPI) {
+                    if (live(k, q + NS)) load(k, q + NS);
+                } else if (live(k + 1, q + NS - GPI)) {
+                    load(k + 1, q + NS - GPI);
+                }
             }
             __syncthreads();
         }
@@ -1165,7 +1182,7 @@ __global__ __launch_bounds__(64 * T2D_NW, 1) void k_tail_t2d(TailArgs a, int n_g
         const int64_t nch32 = a.Bp / 32;
         struct Ops {
             u32x2 r[UPT][4];    // rows 4ja+e, features 4fc .. +3, per unit
-            int fi;             // idx[f] of the inverse-index entry of this thread
+            int fi[FPT];        // idx[f] of the inverse-index entries bth, bth + NB_T, ..
             u32x4 dz[TPB];      // dz tiles
         };
         auto unit = [&](int i, int &q, int &fc, int &ja) {
@@ -1200,10 +1217,12 @@ __global__ __launch_bounds__(64 * T2D_NW, 1) void k_tail_t2d(TailArgs a, int n_g
 #pragma unroll
                 for (int e = 0; e < 4; ++e) o.r[i][e] = *(const u32x2 *)(wr + e * F);
             }
-            {
-                const int q = bth < GPI * F ? bth / F : 0;
-                const int f = bth < GPI * F ? bth - q * F : 0;
-                o.fi = a.idx[gsafe(k, q) * F + f];
+#pragma unroll
+            for (int i = 0; i < FPT; ++i) {
+                const int e = bth + NB_T * i;
+                const int q = e < GPI * F ? e / F : 0;
+                const int f = e < GPI * F ? e - q * F : 0;
+                o.fi[i] = a.idx[gsafe(k, q) * F + f];
             }
 #pragma unroll
             for (int t = 0; t < TPB; ++t) {
@@ -1214,7 +1233,7 @@ __global__ __launch_bounds__(64 * T2D_NW, 1) void k_tail_t2d(TailArgs a, int n_g
             }
         };
         auto build = [&](int k, const Ops &o) {
-            unsigned char *wts = wts0 + (k & 1) * GPI * LY.wts_grp;
+            unsigned char *wts = wts0 + (k % 3) * GPI * LY.wts_grp;
 #pragma unroll
             for (int i = 0; i < UPT; ++i) {
                 int q, fc, ja;
@@ -1230,16 +1249,19 @@ __global__ __launch_bounds__(64 * T2D_NW, 1) void k_tail_t2d(TailArgs a, int n_g
                     *(u32x2 *)(wt + kk * WTS) = v;
                 }
             }
-            if (bth < GPI * F) {
-                const int q = bth / F;
-                if (live(k, q)) inv0[((k % 3) * GPI + q) * NDP + o.fi] = (unsigned char)(bth - q * F);
+#pragma unroll
+            for (int i = 0; i < FPT; ++i) {
+                const int e = bth + NB_T * i;
+                if (e >= GPI * F) break;
+                const int q = e / F;
+                if (live(k, q)) inv0[((k & 3) * GPI + q) * NDP + o.fi[i]] = (unsigned char)(e - q * F);
             }
 #pragma unroll
             for (int t = 0; t < TPB; ++t) {
                 int q, rt, jt;
                 if (!tile_of(t, q, rt, jt) || !live(k, q)) continue;
                 // (row rho, label mm) -> lane rho + 32(mm/8), K slot mm%8 of block (rt, jt)
-                unsigned char *ex = exch0 + ((k & 1) * GPI + q) * LY.exch_grp + (rt * JT + jt) * 1024 +
+                unsigned char *ex = exch0 + ((k % 3) * GPI + q) * LY.exch_grp + (rt * JT + jt) * 1024 +
                                     (32 * (mm >> 3)) * 16 + 2 * (mm & 7);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
@@ -1262,7 +1284,7 @@ __global__ __launch_bounds__(64 * T2D_NW, 1) void k_tail_t2d(TailArgs a, int n_g
         __syncthreads();
         __syncthreads();
         auto iter = [&](int k, Ops &o) {
-            unsigned *ivp = (unsigned *)(inv0 + (k % 3) * GPI * NDP);
+            unsigned *ivp = (unsigned *)(inv0 + ((k + 3) & 3) * GPI * NDP);   // step k-1
             for (int i = bth; i < GPI * NDP / 4; i += NB_T) ivp[i] = fill;
             build(k + 2, o);
             fetch(k + 6, o);
