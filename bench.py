@@ -83,6 +83,8 @@ def algorithmic(cfg):
         "tail_step_dw": {"flops": 4 * B * F * L, "bytes": 2 * wbytes + idxb + xb},
         # input-gradient contraction; W read, idx, X, dX written
         "tail_step_dx": {"flops": 2 * B * F * L, "bytes": wbytes + idxb + xb + dxb},
+        # head and tail top-K lists in, merged list out
+        "topk_merge": {"flops": 0, "bytes": 3 * B * max(cfg.topk, 1) * 8},
     }
 
 
@@ -176,6 +178,11 @@ def main():
     loss = torch.zeros(1, dtype=torch.float32, device=dev)
     bce_h = H.Bce(rp, lab, 0, s, loss)
     bce_t = H.Bce(rp, lab, cfg.H, s, loss)
+    K = cfg.topk
+    if K:   # per-row top-K over head and tail, merged every step
+        for b_ in (bce_h, bce_t):
+            b_.topk_val = torch.empty(B, K, dtype=torch.float32, device=dev)
+            b_.topk_idx = torch.empty(B, K, dtype=torch.int32, device=dev)
     dX = torch.empty(B, D, dtype=torch.float32, device=dev)
     dWh = torch.empty_like(Wh)
     dW = torch.empty_like(W)
@@ -183,7 +190,7 @@ def main():
                        device=dev)
     ws_h = torch.empty(max(256, H.haste_head_workspace_bytes(X, Wh, bce_h)), dtype=torch.uint8,
                        device=dev)
-    names = ["head_step", "tail_prepare", "tail_step_dw", "tail_step_dx"]
+    names = ["head_step", "tail_prepare", "tail_step_dw", "tail_step_dx"] + (["topk_merge"] if K else [])
 
     def step(ev=None):
         loss.zero_()
@@ -201,11 +208,15 @@ def main():
         H.haste_tail_step_dx(X, idx, W, L, G, bce_t, dX, ws_t, accumulate_dX=True)
         if ev is not None:
             ev[4].record()
+        if K:
+            H.haste_topk_merge(bce_h.topk_val, bce_h.topk_idx, bce_t.topk_val, bce_t.topk_idx)
+            if ev is not None:
+                ev[5].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()

@@ -118,11 +118,23 @@ typedef struct {
     int32_t reserved1;
     float *loss;              /* device fp32 scalar; this call ADDS its loss,
                                  or NULL for no loss                          */
-    int32_t topk;             /* 0, or K in [1, 8]: per-row top-K logits      */
+    int32_t topk;             /* 0, or K in [1, 8]: per-row top-K logits (see
+                                 below)                                       */
     int32_t reserved2;
     float *topk_val;          /* device B x K, descending                     */
     int32_t *topk_idx;        /* device B x K global ids; ties -> smaller id  */
 } haste_bce;
+
+/* Top-K (top-K page, section "Method": per-bucket top-K' then a merge; here
+ * K' = K, so exact in the kernels' fp32 logits).  With topk = K > 0 the calls
+ * that form logits -- haste_tail_fwd, haste_tail_step, haste_tail_step_dw,
+ * haste_head_fwd, haste_head_step -- write to topk_val / topk_idx the K
+ * largest logits of every row over this call's labels (ids = label_offset +
+ * label), value descending, ties to the smaller id, rows with fewer than K
+ * labels padded with (-inf, -1).  The head's and the tail's lists combine
+ * with haste_topk_merge.  The workspace then also holds the call's fp32
+ * logits (B x labels x 4 bytes) and the bucket lists.  haste_tail_bwd and
+ * haste_head_bwd reject topk > 0; the other calls ignore it. */
 
 int haste_abi_version(void);
 const char *haste_status_string(int status);

@@ -50,8 +50,8 @@ inline int pad_rows(int B) { return (B + 63) / 64 * 64; }
 
 // ----------------------------------------------------------- workspace maps
 struct TailWs {
-    size_t xt, cnt, ptr, ent, dz, dzt, total;
-    bool has_dzt;
+    size_t xt, cnt, ptr, ent, dz, dzt, z32, cand, total;
+    bool has_dzt, has_topk;
 };
 
 TailWs tail_ws(const haste_tail_desc *d, const haste_bce *bce) {
@@ -74,21 +74,33 @@ TailWs tail_ws(const haste_tail_desc *d, const haste_bce *bce) {
         w.cnt = o; o += al256((size_t)ng * 4 > keys ? (size_t)ng * 4 : keys);
         w.dz = o;  o += al256((size_t)d->B * d->L * 4);
     }
+    // top-K: fp32 logits B x L, and the per-bucket lists (stage 1)
+    w.has_topk = bce && bce->topk > 0;
+    if (w.has_topk) {
+        w.z32 = o;  o += al256((size_t)d->B * d->L * 4);
+        w.cand = o; o += al256((size_t)d->B * topk_segments(d->L) * bce->topk * 8);
+    }
     w.total = o;
     return w;
 }
 
 struct HeadWs {
-    size_t bm, dz, total;
+    size_t bm, dz, z32, cand, total;
     int words;
+    bool has_topk;
 };
 
-HeadWs head_ws(const haste_head_desc *d) {
+HeadWs head_ws(const haste_head_desc *d, const haste_bce *bce) {
     HeadWs w{};
     size_t o = 0;
     w.words = (d->H + 31) / 32;
     w.bm = o; o += al256((size_t)d->B * w.words * 4);
     w.dz = o; o += al256((size_t)d->B * d->H * (d->dtype == HASTE_BF16 ? 2 : 4));
+    w.has_topk = bce && bce->topk > 0;
+    if (w.has_topk) {
+        w.z32 = o;  o += al256((size_t)d->B * d->H * 4);
+        w.cand = o; o += al256((size_t)d->B * topk_segments(d->H) * bce->topk * 8);
+    }
     w.total = o;
     return w;
 }
@@ -127,14 +139,18 @@ haste_status check_head(const haste_head_desc *d) {
     return HASTE_OK;
 }
 
-haste_status check_bce(const haste_bce *b, int B, bool need_loss_ok) {
-    (void)need_loss_ok;
+haste_status check_bce(const haste_bce *b, int B, bool topk_ok) {
     if (!b) return HASTE_OK;
     if (b->nnz < 0) return fail(HASTE_ERR_INVALID, "bce.nnz < 0");
     if (!b->row_ptr) return fail(HASTE_ERR_INVALID, "bce.row_ptr is NULL");
     if (b->nnz > 0 && !b->labels) return fail(HASTE_ERR_INVALID, "bce.labels is NULL");
     if (b->label_offset < 0) return fail(HASTE_ERR_INVALID, "bce.label_offset < 0");
-    if (b->topk != 0) return fail(HASTE_ERR_UNSUPPORTED, "bce.topk is not supported by this call");
+    if (b->topk < 0 || b->topk > 8) return fail(HASTE_ERR_INVALID, "bce.topk=%d outside [0, 8]", b->topk);
+    if (b->topk != 0) {
+        if (!topk_ok) return fail(HASTE_ERR_UNSUPPORTED, "bce.topk is not supported by this call");
+        if (!b->topk_val || !aligned(b->topk_val, 4)) return fail(HASTE_ERR_INVALID, "bce.topk_val NULL or misaligned");
+        if (!b->topk_idx || !aligned(b->topk_idx, 4)) return fail(HASTE_ERR_INVALID, "bce.topk_idx NULL or misaligned");
+    }
     (void)B;
     return HASTE_OK;
 }
@@ -173,6 +189,7 @@ TailArgs tail_args(const haste_tail_desc *d, const void *X, const int32_t *idx, 
     a.grp_ptr = (const int32_t *)B8(ws, m.ptr);
     a.grp_ent = (const int32_t *)B8(ws, m.ent);
     a.dzt = m.has_dzt ? (unsigned short *)B8(ws, m.dzt) : nullptr;
+    a.Z32 = m.has_topk ? (float *)B8(ws, m.z32) : nullptr;
     a.B = d->B;
     a.D = d->D;
     a.Bp = pad_rows(d->B);
@@ -215,6 +232,18 @@ F32Args f32_tail_args(const haste_tail_desc *d, const void *X, const int32_t *id
         a.loss = bce->loss;
     }
     return a;
+}
+
+// per-row top-K of the fp32 logits z (B x n) into bce->topk_val / topk_idx
+haste_status run_topk(const haste_bce *bce, const float *z, int B, int64_t n, void *ws, size_t cand,
+                      hipStream_t st) {
+    const int K = bce->topk;
+    const int64_t nc = (int64_t)B * topk_segments(n) * K;
+    float *cv = (float *)B8(ws, cand);
+    int32_t *ci = (int32_t *)(cv + nc);
+    TRY_HIP(launch_row_topk(z, n, B, n, bce->label_offset, K, cv, ci, bce->topk_val, bce->topk_idx, st),
+            "top-K");
+    return HASTE_OK;
 }
 
 haste_status zero_dx(float *dX, int B, int D, int accumulate, hipStream_t st) {
@@ -274,7 +303,7 @@ size_t haste_tail_workspace_bytes(const haste_tail_desc *d, const haste_bce *bce
 size_t haste_head_workspace_bytes(const haste_head_desc *d, const haste_bce *bce) {
     (void)bce;
     if (check_head(d) != HASTE_OK) return 0;
-    return head_ws(d).total;
+    return head_ws(d, bce).total;
 }
 
 haste_status haste_tail_fwd(const haste_tail_desc *d, const void *X, const int32_t *idx,
@@ -297,11 +326,13 @@ haste_status haste_tail_fwd(const haste_tail_desc *d, const void *X, const int32
             a.s = bce->grad_scale;
         }
         TRY_HIP(launch_tail_t1(T1_FWD, d->G, a, Z != nullptr, bce && bce->loss, st), "tail fwd");
+        if (m.has_topk) TRY(run_topk(bce, a.Z32, d->B, d->L, ws, m.cand, st));
     } else {
         F32Args a = f32_tail_args(d, X, idx, W, bce);
-        a.Z = (float *)Z;
-        TRY_HIP(launch_f32_tail_logits(a, Z != nullptr, bce != nullptr, bce && bce->loss, st),
+        a.Z = Z ? (float *)Z : m.has_topk ? (float *)B8(ws, m.z32) : nullptr;
+        TRY_HIP(launch_f32_tail_logits(a, a.Z != nullptr, bce != nullptr, bce && bce->loss, st),
                 "tail fwd f32");
+        if (m.has_topk) TRY(run_topk(bce, a.Z, d->B, d->L, ws, m.cand, st));
     }
     return HASTE_OK;
 }
@@ -369,13 +400,16 @@ haste_status haste_tail_step(const haste_tail_desc *d, const void *X, const int3
         a.s = bce->grad_scale;
         a.loss = bce->loss;
         TRY_HIP(launch_tail_t1(T1_DW_BCE, d->G, a, false, bce->loss != nullptr, st), "tail step dW");
+        if (m.has_topk) TRY(run_topk(bce, a.Z32, d->B, d->L, ws, m.cand, st));
         TRY_HIP(launch_tail_t2(d->G, a.dzt ? 2 : 0, a, st), "tail step dX");
     } else {
         F32Args a = f32_tail_args(d, X, idx, W, bce);
         a.dW = (float *)dW;
         a.dX = dX;
         a.dZ = (float *)B8(ws, m.dz);
-        TRY_HIP(launch_f32_tail_logits(a, false, true, bce->loss != nullptr, st), "tail step f32");
+        a.Z = m.has_topk ? (float *)B8(ws, m.z32) : nullptr;
+        TRY_HIP(launch_f32_tail_logits(a, m.has_topk, true, bce->loss != nullptr, st), "tail step f32");
+        if (m.has_topk) TRY(run_topk(bce, a.Z, d->B, d->L, ws, m.cand, st));
         TRY_HIP(launch_f32_tail_dw(a, st), "tail dW f32");
         TRY_HIP(launch_f32_tail_dx(a, st), "tail dX f32");
     }
@@ -412,11 +446,14 @@ haste_status haste_tail_step_dw(const haste_tail_desc *d, const void *X, const i
         a.s = bce->grad_scale;
         a.loss = bce->loss;
         TRY_HIP(launch_tail_t1(T1_DW_BCE, d->G, a, false, bce->loss != nullptr, st), "tail step dW");
+        if (m.has_topk) TRY(run_topk(bce, a.Z32, d->B, d->L, ws, m.cand, st));
     } else {
         F32Args a = f32_tail_args(d, X, idx, W, bce);
         a.dW = (float *)dW;
         a.dZ = (float *)B8(ws, m.dz);
-        TRY_HIP(launch_f32_tail_logits(a, false, true, bce->loss != nullptr, st), "tail step f32");
+        a.Z = m.has_topk ? (float *)B8(ws, m.z32) : nullptr;
+        TRY_HIP(launch_f32_tail_logits(a, m.has_topk, true, bce->loss != nullptr, st), "tail step f32");
+        if (m.has_topk) TRY(run_topk(bce, a.Z, d->B, d->L, ws, m.cand, st));
         TRY_HIP(launch_f32_tail_dw(a, st), "tail dW f32");
     }
     return HASTE_OK;
@@ -483,8 +520,10 @@ haste_status head_logits(const haste_head_desc *d, const void *X, const void *Wh
             g.s = bce->grad_scale;
             g.loss = want_loss ? bce->loss : nullptr;
             g.dZout = (unsigned short *)dz_out;
+            if (m.has_topk) g.Z32 = (float *)B8(ws, m.z32);
         }
         TRY_HIP(launch_gemm(true, true, EPI_BCE, g, st), "head logits");
+        if (bce && m.has_topk) TRY(run_topk(bce, g.Z32, d->B, d->H, ws, m.cand, st));
     } else {
         F32Args a{};
         a.X = (const float *)X;
@@ -501,8 +540,10 @@ haste_status head_logits(const haste_head_desc *d, const void *X, const void *Wh
             a.loss = want_loss ? bce->loss : nullptr;
             a.dZ = (float *)dz_out;
         }
-        TRY_HIP(launch_f32_head_logits(a, Zh != nullptr, bce != nullptr, want_loss, st),
+        if (!a.Z && bce && m.has_topk) a.Z = (float *)B8(ws, m.z32);
+        TRY_HIP(launch_f32_head_logits(a, a.Z != nullptr, bce != nullptr, want_loss, st),
                 "head logits f32");
+        if (bce && m.has_topk) TRY(run_topk(bce, a.Z, d->B, d->H, ws, m.cand, st));
     }
     return HASTE_OK;
 }
@@ -563,7 +604,7 @@ haste_status haste_head_fwd(const haste_head_desc *d, const void *X, const void 
     TRY(head_common(d, X, Wh));
     TRY(check_bce(bce, d->B, true));
     if (!Zh && !bce) return fail(HASTE_ERR_INVALID, "nothing to compute: Zh and bce are both NULL");
-    const HeadWs m = head_ws(d);
+    const HeadWs m = head_ws(d, bce);
     TRY(check_ws(ws, ws_bytes, bce ? m.total : 0));
     return head_logits(d, X, Wh, Zh, bce, bce && bce->loss, nullptr, ws, m, S(stream));
 }
@@ -578,7 +619,7 @@ haste_status haste_head_bwd(const haste_head_desc *d, const void *X, const void 
     TRY(need_al(dWh, d->dtype == HASTE_BF16 ? 2 : 4, "dWh"));
     TRY(need_al(dX, 4, "dX"));
     if (dZh && !aligned(dZh, 16)) return fail(HASTE_ERR_INVALID, "dZh is not 16-byte aligned");
-    const HeadWs m = head_ws(d);
+    const HeadWs m = head_ws(d, bce);
     TRY(check_ws(ws, ws_bytes, dZh ? 0 : m.total));
     hipStream_t st = S(stream);
     TRY(zero_dx(dX, d->B, d->D, accumulate_dX, st));
@@ -599,7 +640,7 @@ haste_status haste_head_step(const haste_head_desc *d, const void *X, const void
     TRY(check_bce(bce, d->B, true));
     TRY(need_al(dWh, d->dtype == HASTE_BF16 ? 2 : 4, "dWh"));
     TRY(need_al(dX, 4, "dX"));
-    const HeadWs m = head_ws(d);
+    const HeadWs m = head_ws(d, bce);
     TRY(check_ws(ws, ws_bytes, m.total));
     hipStream_t st = S(stream);
     TRY(zero_dx(dX, d->B, d->D, accumulate_dX, st));
@@ -614,7 +655,7 @@ haste_status haste_tail_group_positives(const haste_tail_desc *d, const haste_bc
     g_err.clear();
     TRY(check_tail(d));
     TRY(need(bce, "bce"));
-    TRY(check_bce(bce, d->B, false));
+    TRY(check_bce(bce, d->B, true));   // top-K settings do not matter here
     TRY(need_al(grp_ptr, 4, "grp_ptr"));
     if (bce->nnz > 0) TRY(need_al(entries, 4, "entries"));
     const TailWs m = tail_ws(d, bce);

@@ -168,6 +168,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g) {
                         if (g.dZout) g.dZout[o] = f32_to_bf16(r.dz);
                     }
                     if (g.Zout) g.Zout[o] = f32_to_bf16(v);
+                    if (g.Z32) g.Z32[o] = v;
                 } else if (EPI == EPI_STORE16) {
                     g.C16[o] = f32_to_bf16(v);
                 } else {
@@ -377,6 +378,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm2(GemmArgs g) {
                         if (g.dZout) g.dZout[o] = f32_to_bf16(g.s * (sg - y));
                     }
                     if (g.Zout) g.Zout[o] = f32_to_bf16(v);
+                    if (g.Z32) g.Z32[o] = v;
                 } else if (EPI == EPI_STORE16) {
                     g.C16[o] = f32_to_bf16(v);
                 } else {

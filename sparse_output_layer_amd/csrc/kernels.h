@@ -15,6 +15,7 @@ struct TailArgs {
     const unsigned short *W;     // (Ng*G) x F bf16
     unsigned short *Z;           // B x L bf16 (forward output)
     const unsigned short *dZ;    // B x L bf16 (given gradient)
+    float *Z32;                  // fp32 logits for the top-K: B x L, row stride L; or null
     unsigned short *dzt;         // dz tiles of the dW pass for the dX pass, or null:
                                  // Ng x (Bp/32) x (G/16) tiles of 1 KB (32 rows x 16 labels)
     unsigned short *dW;          // (Ng*G) x F bf16
@@ -46,6 +47,15 @@ hipError_t launch_tail_t2(int G, int dz_mode, const TailArgs &a,
                           hipStream_t st);
 bool tail_bf16_supported(int G, int F, int D);
 
+// Exact per-row top-K (K in [1, 8]) of fp32 logits z (rows x n, row stride
+// ld, column c has id id_offset + c): stage 1 per bucket of TOPK_SEG columns
+// into cand (rows x topk_segments(n) x K), stage 2 merge into out (rows x K).
+constexpr int64_t TOPK_SEG = 32768;
+int topk_segments(int64_t n);
+hipError_t launch_row_topk(const float *z, int64_t ld, int rows, int64_t n, int64_t id_offset,
+                           int K, float *cand_v, int32_t *cand_i, float *out_v, int32_t *out_i,
+                           hipStream_t st);
+
 // Head (dense classifier) GEMMs.
 struct GemmArgs {
     const unsigned short *A;
@@ -57,6 +67,7 @@ struct GemmArgs {
     float *C32;                // fp32 output (atomic add), ldc = N
     unsigned short *Zout;      // BCE: optional logits (bf16), ld N
     unsigned short *dZout;     // BCE: optional dz (bf16), ld N
+    float *Z32;                // BCE: optional fp32 logits (for the top-K), ld N
     const uint32_t *bitmap;    // BCE: positives bitmap, row stride bm_words
     int bm_words;
     float *loss;

@@ -400,6 +400,12 @@ __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, int store_z,
                             }
                             dzp[h2][jt][0] = pack_bf16x2(dzv[0], dzv[1]);
                             dzp[h2][jt][1] = pack_bf16x2(dzv[2], dzv[3]);
+                            if (a.Z32) {   // fp32 logits for the top-K
+                                const int64_t t = g * G + 16 * jt + m;
+#pragma unroll
+                                for (int i = 0; i < 4; ++i)
+                                    a.Z32[(int64_t)(r0 + 16 * h2 + 4 * q + i) * a.L + t] = zacc[h2][jt][i];
+                            }
                         }
                     // at most 8*JT <= 32 factors in [1, 2]: the product stays below 2^32
                     if (do_loss) lsum += a.s * (lin + fast_log(prod));
@@ -430,6 +436,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, int store_z,
                                     }
                                     if (MODE == T1_FWD && store_z && live)
                                         a.Z[(int64_t)row * a.L + t] = f32_to_bf16(z);
+                                    if (a.Z32 && live) a.Z32[(int64_t)row * a.L + t] = z;
                                 }
                                 dzv[i] = dz;
                             }

@@ -1,0 +1,198 @@
+// topk.hip -- exact per-row top-K of fp32 logits on gfx950 (top-K page,
+// section "Method": stage 1 takes the top-K' of every bucket of a row,
+// stage 2 merges the buckets' lists; with K' = K the result is exact).
+//
+// Order: value descending, ties by smaller id (the same total order as the
+// merge of two lists).  A row with fewer than K entries is padded with
+// (-inf, -1).
+//
+// Stage 1 (k_topk_stage1): one workgroup per (row, bucket of TOPK_SEG
+// consecutive columns).  Every thread keeps a sorted list of K entries in
+// registers over a strided share of the bucket (coalesced reads; a value
+// enters only if it beats the thread's K-th entry), then the 256 lists are
+// merged pairwise in LDS (eight rounds).  Stage 2 (k_topk_stage2): one
+// workgroup per row over the rows' bucket lists, same merge.
+#include "common.h"
+#include "kernels.h"
+
+namespace haste {
+
+constexpr int TOPK_MAX = 8;
+constexpr int TOPK_THREADS = 256;
+
+__device__ __forceinline__ bool tk_before(float va, int32_t ia, float vb, int32_t ib) {
+    return va > vb || (va == vb && ia < ib);
+}
+
+// Insert (v, id) into the sorted list (l_v, l_i) of K entries if it belongs.
+template <int K>
+__device__ __forceinline__ void tk_insert(float (&l_v)[K], int32_t (&l_i)[K], float v, int32_t id) {
+    if (!tk_before(v, id, l_v[K - 1], l_i[K - 1])) return;
+    float cv = v;
+    int32_t ci = id;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {   // bubble the new entry into place
+        const bool sw = tk_before(cv, ci, l_v[k], l_i[k]);
+        const float tv = l_v[k];
+        const int32_t ti = l_i[k];
+        l_v[k] = sw ? cv : tv;
+        l_i[k] = sw ? ci : ti;
+        cv = sw ? tv : cv;
+        ci = sw ? ti : ci;
+    }
+}
+
+// Merge the 256 per-thread lists held in LDS (s_v/s_i, K per thread) and
+// write the first K entries of the union to out_v/out_i (thread 0).
+template <int K>
+__device__ __forceinline__ void tk_block_merge(float *s_v, int32_t *s_i, float (&l_v)[K],
+                                               int32_t (&l_i)[K], float *out_v, int32_t *out_i) {
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        s_v[t * K + k] = l_v[k];
+        s_i[t * K + k] = l_i[k];
+    }
+    __syncthreads();
+    for (int half = TOPK_THREADS / 2; half > 0; half >>= 1) {
+        if (t < half) {
+            // two sorted lists -> first K of their union
+            const float *av = s_v + t * K, *bv = s_v + (t + half) * K;
+            const int32_t *ai = s_i + t * K, *bi = s_i + (t + half) * K;
+            int x = 0, y = 0;
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const float va = av[x < K ? x : K - 1], vb = bv[y < K ? y : K - 1];
+                const int32_t ia = ai[x < K ? x : K - 1], ib = bi[y < K ? y : K - 1];
+                const bool takea = y >= K || (x < K && tk_before(va, ia, vb, ib));
+                l_v[k] = takea ? va : vb;
+                l_i[k] = takea ? ia : ib;
+                x += takea ? 1 : 0;
+                y += takea ? 0 : 1;
+            }
+        }
+        __syncthreads();
+        if (t < half) {
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                s_v[t * K + k] = l_v[k];
+                s_i[t * K + k] = l_i[k];
+            }
+        }
+        __syncthreads();
+    }
+    if (t == 0) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            out_v[k] = s_v[k];
+            out_i[k] = s_i[k];
+        }
+    }
+}
+
+// Stage 1: z is rows x n (row stride ld), ids id_offset + column.
+template <int K>
+__global__ __launch_bounds__(TOPK_THREADS) void k_topk_stage1(const float *__restrict__ z, int64_t ld,
+                                                              int64_t n, int64_t id_offset, int nseg,
+                                                              float *cand_v, int32_t *cand_i) {
+    __shared__ float s_v[TOPK_THREADS * K];
+    __shared__ int32_t s_i[TOPK_THREADS * K];
+    const int seg = blockIdx.x, row = blockIdx.y;
+    const int64_t c0 = (int64_t)seg * TOPK_SEG;
+    const int64_t c1 = c0 + TOPK_SEG < n ? c0 + TOPK_SEG : n;
+    float l_v[K];
+    int32_t l_i[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        l_v[k] = -INFINITY;
+        l_i[k] = -1;
+    }
+    const float *zr = z + (int64_t)row * ld;
+    // scalar up to a 16-byte boundary, then four 16-byte loads in flight per
+    // thread, then the scalar remainder
+    int64_t a0 = c0 + ((4 - (int64_t)(((uintptr_t)(zr + c0) >> 2) & 3)) & 3);
+    if (a0 > c1) a0 = c1;
+    const int64_t nv = (c1 - a0) >> 2;
+    const int64_t a1 = a0 + (nv << 2);
+    for (int64_t c = c0 + threadIdx.x; c < a0; c += TOPK_THREADS)
+        tk_insert<K>(l_v, l_i, zr[c], (int32_t)(id_offset + c));
+    const f32x4 *zv = (const f32x4 *)(zr + a0);
+    constexpr int U = 4;
+    for (int64_t v0 = threadIdx.x; v0 < nv; v0 += (int64_t)TOPK_THREADS * U) {
+        f32x4 x[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t v = v0 + (int64_t)u * TOPK_THREADS;
+            x[u] = zv[v < nv ? v : nv - 1];   // clamped: no load is skipped
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t v = v0 + (int64_t)u * TOPK_THREADS;
+            if (v >= nv) break;
+            const int32_t id = (int32_t)(id_offset + a0 + 4 * v);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) tk_insert<K>(l_v, l_i, x[u][e], id + e);
+        }
+    }
+    for (int64_t c = a1 + threadIdx.x; c < c1; c += TOPK_THREADS)
+        tk_insert<K>(l_v, l_i, zr[c], (int32_t)(id_offset + c));
+    const int64_t o = ((int64_t)row * nseg + seg) * K;
+    tk_block_merge<K>(s_v, s_i, l_v, l_i, cand_v + o, cand_i + o);
+}
+
+// Stage 2: per row, the nseg lists of K entries -> K entries.
+template <int K>
+__global__ __launch_bounds__(TOPK_THREADS) void k_topk_stage2(const float *cand_v, const int32_t *cand_i,
+                                                              int nseg, float *out_v, int32_t *out_i) {
+    __shared__ float s_v[TOPK_THREADS * K];
+    __shared__ int32_t s_i[TOPK_THREADS * K];
+    const int row = blockIdx.x;
+    float l_v[K];
+    int32_t l_i[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        l_v[k] = -INFINITY;
+        l_i[k] = -1;
+    }
+    const int64_t base = (int64_t)row * nseg * K;
+    for (int64_t e = threadIdx.x; e < (int64_t)nseg * K; e += TOPK_THREADS) {
+        const int32_t id = cand_i[base + e];
+        if (id >= 0) tk_insert<K>(l_v, l_i, cand_v[base + e], id);
+    }
+    tk_block_merge<K>(s_v, s_i, l_v, l_i, out_v + (int64_t)row * K, out_i + (int64_t)row * K);
+}
+
+int topk_segments(int64_t n) { return (int)((n + TOPK_SEG - 1) / TOPK_SEG); }
+
+template <int K>
+static hipError_t topk_go(const float *z, int64_t ld, int rows, int64_t n, int64_t id_offset,
+                          float *cand_v, int32_t *cand_i, float *out_v, int32_t *out_i,
+                          hipStream_t st) {
+    const int nseg = topk_segments(n);
+    hipLaunchKernelGGL(k_topk_stage1<K>, dim3((unsigned)nseg, (unsigned)rows), dim3(TOPK_THREADS), 0,
+                       st, z, ld, n, id_offset, nseg, cand_v, cand_i);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_topk_stage2<K>, dim3((unsigned)rows), dim3(TOPK_THREADS), 0, st, cand_v,
+                       cand_i, nseg, out_v, out_i);
+    return hipGetLastError();
+}
+
+hipError_t launch_row_topk(const float *z, int64_t ld, int rows, int64_t n, int64_t id_offset,
+                           int K, float *cand_v, int32_t *cand_i, float *out_v, int32_t *out_i,
+                           hipStream_t st) {
+    if (rows <= 0) return hipSuccess;
+    switch (K) {
+    case 1: return topk_go<1>(z, ld, rows, n, id_offset, cand_v, cand_i, out_v, out_i, st);
+    case 2: return topk_go<2>(z, ld, rows, n, id_offset, cand_v, cand_i, out_v, out_i, st);
+    case 3: return topk_go<3>(z, ld, rows, n, id_offset, cand_v, cand_i, out_v, out_i, st);
+    case 4: return topk_go<4>(z, ld, rows, n, id_offset, cand_v, cand_i, out_v, out_i, st);
+    case 5: return topk_go<5>(z, ld, rows, n, id_offset, cand_v, cand_i, out_v, out_i, st);
+    case 6: return topk_go<6>(z, ld, rows, n, id_offset, cand_v, cand_i, out_v, out_i, st);
+    case 7: return topk_go<7>(z, ld, rows, n, id_offset, cand_v, cand_i, out_v, out_i, st);
+    case 8: return topk_go<8>(z, ld, rows, n, id_offset, cand_v, cand_i, out_v, out_i, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace haste

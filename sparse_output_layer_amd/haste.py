@@ -144,12 +144,21 @@ class Bce:
     label_offset: int = 0
     grad_scale: float = 1.0
     loss: Optional[torch.Tensor] = None   # float32 scalar (1 element), device
+    topk_val: Optional[torch.Tensor] = None   # float32 B x K, device: per-row top-K logits
+    topk_idx: Optional[torch.Tensor] = None   # int32 B x K, device: their global label ids
 
     def struct(self) -> BceStruct:
         _need(self.row_ptr, "row_ptr", torch.int32)
         _need(self.labels, "labels", torch.int32)
         if self.loss is not None:
             _need(self.loss, "loss", torch.float32)
+        if (self.topk_val is None) != (self.topk_idx is None):
+            raise ValueError("topk_val and topk_idx go together")
+        if self.topk_val is not None:
+            _need(self.topk_val, "topk_val", torch.float32)
+            _need(self.topk_idx, "topk_idx", torch.int32)
+            if self.topk_val.shape != self.topk_idx.shape or self.topk_val.dim() != 2:
+                raise ValueError("topk_val / topk_idx must both be B x K")
         s = BceStruct()
         s.row_ptr = self.row_ptr.data_ptr()
         s.labels = self.labels.data_ptr() if self.labels.numel() else None
@@ -158,6 +167,10 @@ class Bce:
         s.grad_scale = float(self.grad_scale)
         s.loss = self.loss.data_ptr() if self.loss is not None else None
         s.topk = 0
+        if self.topk_val is not None:
+            s.topk = int(self.topk_val.shape[1])
+            s.topk_val = self.topk_val.data_ptr()
+            s.topk_idx = self.topk_idx.data_ptr()
         return s
 
 

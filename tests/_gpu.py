@@ -81,3 +81,49 @@ def check(name, got, ref, absref, dtype, nterms=None):
 def check_loss(name, got, ref, dtype):
     rel = 1e-4 if dtype == "bf16" else 1e-5
     assert abs(got - ref) <= rel * abs(ref) + 1e-6, f"{name}: got {got} ref {ref}"
+
+
+def check_topk_lists(name, got_v, got_i, ov, oi, tol, zfun, K, N, id0=0):
+    """Per-row top-K against the oracle's top-(K+1) lists ov / oi (value
+    descending, ties to the smaller id), with per-row logit tolerance tol[b]
+    and zfun(b, id) giving the oracle logit of one label.  The kernels rank
+    fp32 logits, the oracle fp64 ones, so the order is compared where the
+    oracle's neighbours are further apart than twice the tolerance;
+    everywhere the returned value must be the k-th largest within tolerance
+    and the returned id's own logit."""
+    got_v = np.asarray(got_v, dtype=np.float64)
+    got_i = np.asarray(got_i, dtype=np.int64)
+    n = min(K, N)
+    for b in range(got_v.shape[0]):
+        ids = got_i[b]
+        assert np.all(ids[:n] >= 0) and np.all(ids[n:] == -1), f"{name}: row {b} ids {ids}"
+        assert np.all(np.isneginf(got_v[b, n:])), f"{name}: row {b} padding {got_v[b]}"
+        li = ids[:n]
+        assert len(set(li.tolist())) == li.size, f"{name}: row {b} repeats an id: {li}"
+        assert np.all((li >= id0) & (li < id0 + N)), f"{name}: row {b} id out of range: {li}"
+        for k in range(n):
+            zk = zfun(b, int(ids[k]))
+            assert abs(got_v[b, k] - zk) <= tol[b], \
+                f"{name}: row {b} pos {k}: value {got_v[b, k]} vs its logit {zk} (tol {tol[b]})"
+            assert abs(got_v[b, k] - ov[b, k]) <= tol[b], \
+                f"{name}: row {b} pos {k}: value {got_v[b, k]} vs k-th largest {ov[b, k]} (tol {tol[b]})"
+            if k > 0:
+                assert got_v[b, k] <= got_v[b, k - 1], f"{name}: row {b} not descending"
+            sep_hi = k == 0 or ov[b, k - 1] - ov[b, k] > 2 * tol[b]
+            sep_lo = k + 1 >= n or k + 1 >= ov.shape[1] or ov[b, k] - ov[b, k + 1] > 2 * tol[b]
+            if sep_hi and sep_lo:
+                assert ids[k] == oi[b, k], f"{name}: row {b} pos {k}: id {ids[k]} vs oracle {oi[b, k]}"
+
+
+def topk_tol(zabs_rowmax, dtype):
+    rel, ab = TOL_BF16 if dtype == "bf16" else TOL_F32
+    return rel * np.asarray(zabs_rowmax, dtype=np.float64) + ab
+
+
+def check_topk(name, got_v, got_i, z, zabs, K, dtype, id0=0):
+    """check_topk_lists with the oracle's full logits z / zabs (rows x N,
+    column c has id id0 + c)."""
+    rows, N = z.shape
+    ov, oi = oracle.topk(z, min(K + 1, N), id_offset=id0) if N > 0 else (np.zeros((rows, 0)), None)
+    tol = topk_tol(zabs.max(axis=1) if N else np.zeros(rows), dtype)
+    check_topk_lists(name, got_v, got_i, ov, oi, tol, lambda b, i: z[b, i - id0], K, N, id0)

@@ -83,8 +83,19 @@ def test_argument_errors_fail_before_launch(L):
     assert _status(L, _desc(), bce=ctypes.byref(b)) == H.HASTE_ERR_INVALID
     b = H.BceStruct(nnz=5, row_ptr=0x1000, labels=None)
     assert _status(L, _desc(), bce=ctypes.byref(b)) == H.HASTE_ERR_INVALID
+    # top-K: K in [0, 8], output buffers required; the backward rejects it
+    b = H.BceStruct(nnz=5, row_ptr=0x1000, labels=0x1000, topk=9, topk_val=0x1000, topk_idx=0x1000)
+    assert _status(L, _desc(), bce=ctypes.byref(b)) == H.HASTE_ERR_INVALID
     b = H.BceStruct(nnz=5, row_ptr=0x1000, labels=0x1000, topk=5)
-    assert _status(L, _desc(), bce=ctypes.byref(b)) == H.HASTE_ERR_UNSUPPORTED
+    assert _status(L, _desc(), bce=ctypes.byref(b)) == H.HASTE_ERR_INVALID
+    b = H.BceStruct(nnz=5, row_ptr=0x1000, labels=0x1000, topk=5, topk_val=0x1000, topk_idx=0x1000)
+    assert _status(L, _desc(), bce=ctypes.byref(b)) == H.HASTE_ERR_WORKSPACE
+    assert L.haste_tail_bwd(ctypes.byref(_desc()), 0x1000, 0x1000, 0x1000, None, ctypes.byref(b),
+                            0x1000, 0x1000, 0, 0x1000, 1 << 30, None) == H.HASTE_ERR_UNSUPPORTED
+    # the top-K adds the fp32 logits (B x L x 4 bytes) to the workspace
+    n0 = L.haste_tail_workspace_bytes(ctypes.byref(_desc()), ctypes.byref(H.BceStruct(nnz=5)))
+    n1 = L.haste_tail_workspace_bytes(ctypes.byref(_desc()), ctypes.byref(b))
+    assert n1 - n0 >= 8 * 1024 * 4
     # fp32 accepts any G / F
     d = _desc(dtype=H.HASTE_F32, G=3, F=7)
     assert _status(L, d) == H.HASTE_ERR_WORKSPACE

@@ -9,16 +9,18 @@ checks are on outputs it computes one by one:
   - dX of sampled rows (all head and tail labels);
   - the total loss, streamed over chunks of groups.
 
-The top-K of the 8.6M-label workload is not built; that workload is checked
-without it.  The 3M-label workload runs the lean form (dz recomputed in the
-dX pass, nothing of size B x L stored); the others keep the dz tiles."""
+The 8.6M-label workload also asks for the per-row top-5 over all labels
+(head and tail lists merged); its oracle is streamed over the same chunks
+of groups as the loss.  The 3M-label workload runs the lean form (dz
+recomputed in the dX pass, nothing of size B x L stored); the others keep
+the dz tiles."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
 import workloads as wl
-from _gpu import DEV, Dev, check, check_loss, to_f64
+from _gpu import DEV, Dev, check, check_loss, check_topk_lists, to_f64, topk_tol
 
 pytestmark = pytest.mark.gpu
 
@@ -38,7 +40,8 @@ def _sample(n, fixed, extra, rng):
 @pytest.mark.parametrize("name", ["c2", "c3", "c4", "c5"])
 def test_full_size_step(H, name):
     print("full-size step", name, flush=True)
-    cfg = wl.CONFIGS[name].replace(topk=0)
+    cfg = wl.CONFIGS[name]
+    K = cfg.topk
     inp = wl.make_inputs(cfg)
     c = inp.cfg
     B, D, L, G, Hn = c.B, c.D, c.L, c.G, c.H
@@ -51,6 +54,11 @@ def test_full_size_step(H, name):
     loss = torch.zeros(1, dtype=torch.float32, device=DEV)
     bh = H.Bce(d.row_ptr, d.labels, 0, s, loss)
     bt = H.Bce(d.row_ptr, d.labels, Hn, s, loss)
+    if K:
+        bh.topk_val = torch.empty(B, K, dtype=torch.float32, device=DEV)
+        bh.topk_idx = torch.empty(B, K, dtype=torch.int32, device=DEV)
+        bt.topk_val = torch.empty_like(bh.topk_val)
+        bt.topk_idx = torch.empty_like(bh.topk_idx)
     dX = torch.empty(B, D, dtype=torch.float32, device=DEV)
     dWh = torch.empty_like(d.Wh)
     dW = torch.empty_like(d.W)
@@ -62,6 +70,8 @@ def test_full_size_step(H, name):
     H.haste_tail_prepare(d.X, d.idx, L, G, bt, ws_t, lean=lean)
     H.haste_tail_step_dw(d.X, d.idx, d.W, L, G, bt, dW, ws_t, lean=lean)
     H.haste_tail_step_dx(d.X, d.idx, d.W, L, G, bt, dX, ws_t, accumulate_dX=True, lean=lean)
+    if K:
+        mv, mi = H.haste_topk_merge(bh.topk_val, bh.topk_idx, bt.topk_val, bt.topk_idx)
     torch.cuda.synchronize()
     print("  GPU step done", flush=True)
 
@@ -106,13 +116,48 @@ def test_full_size_step(H, name):
     check("dX sampled rows", got, rXt + rXh, rXta + rXha, "bf16", nterms=ng * G + Hn)
     print("  sampled outputs match", flush=True)
 
-    # total loss: head from the full head logits, tail streamed over groups
+    # total loss: head from the full head logits, tail streamed over groups;
+    # with a top-K, the running top-(K+1) of every row rides along
     ref_loss = float(lth.sum())
+    if K:
+        Zh_full, Zha_full = oracle.head_logits(X, Wh, want_abs=True)
+        tv_, ti_ = oracle.topk(Zh_full, K + 1, id_offset=0)
+        amax = Zha_full.max(axis=1)
     chunk = max(1, (1 << 24) // (B * G))
     for g0 in range(0, ng, chunk):
         g1 = min(ng, g0 + chunk)
-        Z, _ = oracle.tail_logits(X, inp.idx, Wt, L, G, g0=g0, g1=g1, want_abs=False)
+        Z, Za = oracle.tail_logits(X, inp.idx, Wt, L, G, g0=g0, g1=g1, want_abs=bool(K))
         Y = oracle.positive_mask(inp.row_ptr, inp.labels, Hn + g0 * G, Z.shape[1])
         _, lt = oracle.bce(Z, Y, s)
         ref_loss += float(lt.sum())
+        if K:
+            cv, ci = oracle.topk(Z, min(K + 1, Z.shape[1]), id_offset=Hn + g0 * G)
+            tv_, ti_ = _merge_lists(tv_, ti_, cv, ci, K + 1)
+            amax = np.maximum(amax, Za.max(axis=1))
     check_loss("step loss", loss.item(), ref_loss, "bf16")
+    if K:
+        def zfun(b, gid):
+            if gid < Hn:
+                return float(oracle.head_logits(X, Wh, rows=np.array([b], np.int32), h0=gid, h1=gid + 1,
+                                                want_abs=False)[0][0, 0])
+            t = gid - Hn
+            g = t // G
+            Zg, _ = oracle.tail_logits(X, inp.idx, Wt, L, G, rows=np.array([b], np.int32),
+                                       g0=g, g1=g + 1, want_abs=False)
+            return float(Zg[0, t - g * G])
+        check_topk_lists("merged top-K", mv.cpu().numpy(), mi.cpu().numpy(), tv_, ti_,
+                         topk_tol(amax, "bf16"), zfun, K, Hn + L)
+        print("  top-K matches", flush=True)
+
+
+def _merge_lists(av, ai, bv, bi, n):
+    """First n of the union of two per-row lists (value desc, ties to the
+    smaller id), by the oracle's own selection over the concatenation."""
+    v = np.concatenate([av, bv], axis=1)
+    i = np.concatenate([ai, bi], axis=1)
+    out_v = np.empty((v.shape[0], n))
+    out_i = np.empty((v.shape[0], n), np.int64)
+    for r in range(v.shape[0]):
+        ov, oi = oracle.topk(v[r:r + 1], n, ids=i[r])
+        out_v[r], out_i[r] = ov[0], oi[0]
+    return out_v, out_i
