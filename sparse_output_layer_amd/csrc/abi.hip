@@ -50,7 +50,7 @@ inline int pad_rows(int B) { return (B + 63) / 64 * 64; }
 
 // ----------------------------------------------------------- workspace maps
 struct TailWs {
-    size_t xt, cnt, ptr, ent, dz, dzt, z32, cand, total;
+    size_t xt, cnt, ptr, ent, idxp, perm, dz, dzt, z32, cand, total;
     bool has_dzt, has_topk;
 };
 
@@ -64,6 +64,9 @@ TailWs tail_ws(const haste_tail_desc *d, const haste_bce *bce) {
         w.cnt = o; o += al256((size_t)(nnz > 0 ? nnz : 1) * 20 + 8);  // keys, sorted, ranks, count
         w.ptr = o; o += al256((size_t)(ng + 4) * 4);   // +3: 16-byte reads of a pair
         w.ent = o; o += al256((size_t)(nnz > 0 ? nnz : 1) * 4);
+        // the dW/logits pass's feature order: idx reordered, and the order
+        w.idxp = o; o += al256((size_t)ng * d->F * 2);
+        w.perm = o; o += al256((size_t)ng * d->F);
         // dz of the dW pass, kept for the dX pass unless the caller asks for
         // the lean form (which recomputes it): Bp x (Ng*G) bf16 in 1 KB tiles
         w.has_dzt = bce && !(d->flags & HASTE_TAIL_LEAN);
@@ -188,6 +191,8 @@ TailArgs tail_args(const haste_tail_desc *d, const void *X, const int32_t *idx, 
     a.W = (const unsigned short *)W;
     a.grp_ptr = (const int32_t *)B8(ws, m.ptr);
     a.grp_ent = (const int32_t *)B8(ws, m.ent);
+    a.idxp = (const unsigned short *)B8(ws, m.idxp);
+    a.perm = (const unsigned char *)B8(ws, m.perm);
     a.dzt = m.has_dzt ? (unsigned short *)B8(ws, m.dzt) : nullptr;
     a.Z32 = m.has_topk ? (float *)B8(ws, m.z32) : nullptr;
     a.B = d->B;
@@ -209,6 +214,16 @@ haste_status bf16_prep(const haste_tail_desc *d, const void *X, const haste_bce 
                                        (int32_t *)B8(ws, m.ptr), (int32_t *)B8(ws, m.ent), st),
                 "group positives");
     }
+    return HASTE_OK;
+}
+
+// The order in which the dW/logits pass reads each group's features; it
+// depends on idx alone and is formed before every such pass.
+haste_status feature_order(const haste_tail_desc *d, const int32_t *idx, void *ws, const TailWs &m,
+                           hipStream_t st) {
+    TRY_HIP(launch_feature_order(idx, n_groups(d), d->F, (unsigned short *)B8(ws, m.idxp),
+                                 (unsigned char *)B8(ws, m.perm), st),
+            "feature order");
     return HASTE_OK;
 }
 
@@ -325,6 +340,7 @@ haste_status haste_tail_fwd(const haste_tail_desc *d, const void *X, const int32
             a.loss = bce->loss;
             a.s = bce->grad_scale;
         }
+        TRY(feature_order(d, idx, ws, m, st));
         TRY_HIP(launch_tail_t1(T1_FWD, d->G, a, Z != nullptr, bce && bce->loss, st), "tail fwd");
         if (m.has_topk) TRY(run_topk(bce, a.Z32, d->B, d->L, ws, m.cand, st));
     } else {
@@ -360,6 +376,7 @@ haste_status haste_tail_bwd(const haste_tail_desc *d, const void *X, const int32
         a.dX = dX;
         a.dZ = (const unsigned short *)dZ;
         if (b) a.s = b->grad_scale;
+        TRY(feature_order(d, idx, ws, m, st));
         TRY_HIP(launch_tail_t1(dZ ? T1_DW_MEM : T1_DW_BCE, d->G, a, false, false, st), "tail dW");
         TRY_HIP(launch_tail_t2(d->G, dZ ? 1 : a.dzt ? 2 : 0, a, st), "tail dX");
     } else {
@@ -399,6 +416,7 @@ haste_status haste_tail_step(const haste_tail_desc *d, const void *X, const int3
         a.dX = dX;
         a.s = bce->grad_scale;
         a.loss = bce->loss;
+        TRY(feature_order(d, idx, ws, m, st));
         TRY_HIP(launch_tail_t1(T1_DW_BCE, d->G, a, false, bce->loss != nullptr, st), "tail step dW");
         if (m.has_topk) TRY(run_topk(bce, a.Z32, d->B, d->L, ws, m.cand, st));
         TRY_HIP(launch_tail_t2(d->G, a.dzt ? 2 : 0, a, st), "tail step dX");
@@ -445,6 +463,7 @@ haste_status haste_tail_step_dw(const haste_tail_desc *d, const void *X, const i
         a.dW = (unsigned short *)dW;
         a.s = bce->grad_scale;
         a.loss = bce->loss;
+        TRY(feature_order(d, idx, ws, m, st));
         TRY_HIP(launch_tail_t1(T1_DW_BCE, d->G, a, false, bce->loss != nullptr, st), "tail step dW");
         if (m.has_topk) TRY(run_topk(bce, a.Z32, d->B, d->L, ws, m.cand, st));
     } else {

@@ -16,6 +16,8 @@ struct TailArgs {
     unsigned short *Z;           // B x L bf16 (forward output)
     const unsigned short *dZ;    // B x L bf16 (given gradient)
     float *Z32;                  // fp32 logits for the top-K: B x L, row stride L; or null
+    const unsigned short *idxp;  // Ng x F: idx in T1's bank-aware order (idxp[g][k] = idx[g][perm[g][k]])
+    const unsigned char *perm;   // Ng x F: that order's feature per position
     unsigned short *dzt;         // dz tiles of the dW pass for the dX pass, or null:
                                  // Ng x (Bp/32) x (G/16) tiles of 1 KB (32 rows x 16 labels)
     unsigned short *dW;          // (Ng*G) x F bf16
@@ -34,6 +36,8 @@ enum T1Mode { T1_FWD = 0, T1_DW_BCE = 1, T1_DW_MEM = 2 };
 hipError_t launch_transpose_x(const unsigned short *X, unsigned short *XT,
                               int B, int D, int Bp, hipStream_t st);
 hipError_t launch_fill_u32(void *p, uint32_t v, size_t n, hipStream_t st);
+hipError_t launch_feature_order(const int32_t *idx, int64_t Ng, int F, unsigned short *idxp,
+                                unsigned char *perm, hipStream_t st);
 hipError_t launch_group_positives(const int32_t *row_ptr, const int32_t *labels,
                                   int nnz, int B, int64_t label_offset,
                                   int64_t L, int G, int64_t Ng, long long *keys,

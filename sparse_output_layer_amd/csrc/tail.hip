@@ -57,6 +57,148 @@ hipError_t launch_transpose_x(const unsigned short *X, unsigned short *XT, int B
     return hipGetLastError();
 }
 
+// ------------------------------------------------------- feature order
+// Order of each group's F features in which T1 reads the gathered rows, so
+// that its LDS reads hit distinct banks.  A chunk row (feature d) is 80 bytes
+// long, so its bank position depends on d mod 16 (its class).  T1 reads, per
+// instruction, the 16 features of 16 consecutive positions (dW operands: each
+// 16 bytes of a row, conflict-free when the 16 classes differ) and, per half
+// wave, the 8 features of positions {0-3, 8-11} or {4-7, 12-15} of a block of
+// 16 (transposing reads: 32 bytes of a row, conflict-free when the classes
+// are distinct and of one parity).  So position k of a block takes class
+// c(k mod 16): even classes at slots 0-3 and 8-11, odd ones at 4-7, 12-15.
+// Per group (one wave, features f = lane and lane + 64): the r-th feature of
+// class c (in f order) takes block r at its class's slot while r < F/16; the
+// features left over (classes with more than F/16 members) fill the empty
+// positions, those of their own parity first, in order.  perm[g][k] is the
+// position's feature f, idxp[g][k] = idx[g][perm[g][k]].  Any order is a
+// correct contraction; this one only removes bank conflicts.
+__device__ __forceinline__ int fo_slot_of(int c) {
+    const int j = c >> 1;
+    return (c & 1) ? (j < 4 ? 4 + j : 8 + j) : (j < 4 ? j : 4 + j);
+}
+__device__ __forceinline__ int fo_class_of_slot(int s) {
+    return 2 * ((s & 3) + 4 * (s >> 3)) + ((s >> 2) & 1);
+}
+
+constexpr int FO_WAVES = 4;   // waves per block
+constexpr int FO_GPW = 4;     // groups per wave, their loads issued together
+
+__global__ __launch_bounds__(64 * FO_WAVES) void k_feature_order(const int32_t *idx, int64_t Ng,
+                                                                 int F, unsigned short *idxp,
+                                                                 unsigned char *perm) {
+    __shared__ unsigned char s_pos[FO_WAVES][128], s_ovf[FO_WAVES][2][128];
+    __shared__ unsigned short s_ix[FO_WAVES][128];
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int nb = F >> 4;
+    const unsigned long long lt = (1ull << lane) - 1;
+    const int64_t g0 = (blockIdx.x * (int64_t)FO_WAVES + w) * FO_GPW;
+    int ixr[FO_GPW][2];
+#pragma unroll
+    for (int u = 0; u < FO_GPW; ++u)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int f = lane + 64 * h;
+            ixr[u][h] = g0 + u < Ng && f < F ? idx[(g0 + u) * F + f] : -1;
+        }
+    const int ssl = fo_class_of_slot(lane & 15);   // class of this lane's positions
+#pragma unroll
+    for (int u = 0; u < FO_GPW; ++u) {
+        const int64_t g = g0 + u;
+        const bool ok = g < Ng;
+        int cls[2], rank[2] = {0, 0};
+#pragma unroll
+        for (int h = 0; h < 2; ++h) cls[h] = ixr[u][h] >= 0 ? (ixr[u][h] & 15) : -1;
+        // bit-sliced ballots: the features of class c in half h are the valid
+        // ones whose four class bits match c
+        unsigned long long vm[2], bm[2][4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            vm[h] = __ballot(cls[h] >= 0);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) bm[h][k] = __ballot(cls[h] >= 0 && ((cls[h] >> k) & 1));
+        }
+        auto members = [&](int c, int h) {
+            unsigned long long mk = vm[h];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) mk &= ((c >> k) & 1) ? bm[h][k] : ~bm[h][k];
+            return mk;
+        };
+        // rank of each feature within its class; the count of this lane's
+        // position class
+        if (cls[0] >= 0) rank[0] = __popcll(members(cls[0], 0) & lt);
+        if (cls[1] >= 0) rank[1] = __popcll(members(cls[1], 0)) + __popcll(members(cls[1], 1) & lt);
+        const int scnt = __popcll(members(ssl, 0)) + __popcll(members(ssl, 1));
+        // overflow features: index among those of their parity
+        bool ov[2];
+        int oi[2] = {0, 0}, on[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) ov[h] = cls[h] >= 0 && rank[h] >= nb;
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq) {
+            const bool s0 = ov[0] && (cls[0] & 1) == qq, s1 = ov[1] && (cls[1] & 1) == qq;
+            const unsigned long long m0 = __ballot(s0), m1 = __ballot(s1);
+            const int n0 = __popcll(m0);
+            on[qq] = n0 + __popcll(m1);
+            if (s0) oi[0] = __popcll(m0 & lt);
+            if (s1) oi[1] = n0 + __popcll(m1 & lt);
+        }
+        // empty positions: index among those of their parity
+        bool em[2];
+        int ei[2] = {0, 0}, en[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int k = lane + 64 * h;
+            em[h] = ok && k < F && scnt <= (k >> 4);
+        }
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const bool s0 = em[0] && (ssl & 1) == p, s1 = em[1] && (ssl & 1) == p;
+            const unsigned long long m0 = __ballot(s0), m1 = __ballot(s1);
+            const int n0 = __popcll(m0);
+            en[p] = n0 + __popcll(m1);
+            if (s0) ei[0] = __popcll(m0 & lt);
+            if (s1) ei[1] = n0 + __popcll(m1 & lt);
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int f = lane + 64 * h;
+            if (cls[h] < 0) continue;
+            s_ix[w][f] = (unsigned short)ixr[u][h];
+            if (ov[h]) s_ovf[w][cls[h] & 1][oi[h]] = (unsigned char)f;
+            else s_pos[w][16 * rank[h] + fo_slot_of(cls[h])] = (unsigned char)f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int k = lane + 64 * h;
+            if (!ok || k >= F) continue;
+            int f;
+            if (!em[h]) {
+                f = s_pos[w][k];
+            } else {
+                // own parity while its overflow lasts, then the other parity's
+                // surplus (the part its own empty positions leave over)
+                const int p = ssl & 1;
+                f = ei[h] < on[p] ? s_ovf[w][p][ei[h]] : s_ovf[w][p ^ 1][en[p ^ 1] + ei[h] - on[p]];
+            }
+            perm[g * F + k] = (unsigned char)f;
+            idxp[g * F + k] = s_ix[w][f];
+        }
+        __syncthreads();   // the next group reuses the wave's LDS
+    }
+}
+
+hipError_t launch_feature_order(const int32_t *idx, int64_t Ng, int F, unsigned short *idxp,
+                                unsigned char *perm, hipStream_t st) {
+    if (Ng <= 0) return hipSuccess;
+    if (F % 16 != 0 || F > 128) return hipErrorInvalidValue;
+    const int64_t per_block = FO_WAVES * FO_GPW;
+    hipLaunchKernelGGL(k_feature_order, dim3((unsigned)((Ng + per_block - 1) / per_block)),
+                       dim3(64 * FO_WAVES), 0, st, idx, Ng, F, idxp, perm);
+    return hipGetLastError();
+}
+
 __global__ void k_fill_u32(uint32_t *p, uint32_t v, size_t n) {
     size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
     size_t stride = (size_t)gridDim.x * blockDim.x;
@@ -229,28 +371,36 @@ __device__ __forceinline__ uint64_t pos_mask_slots4(const int32_t *grp_ptr, cons
 constexpr int T1_BC = 32;
 constexpr int T1_BCP = T1_BC + 8;          // padded row: 80 B = 5 slots of 16 B
 
-// bytes of one chunk buffer: 5 slots per feature row, whole 1 KB wave blocks
-__host__ __device__ inline int t1_nblk(int D) { return (5 * D + 63) / 64; }   // 1 KB blocks
-__host__ __device__ inline int t1_blk_per_wave(int D, int NW) { return (t1_nblk(D) + NW - 1) / NW; }
+// bytes of one chunk buffer: 5 slots of 16 bytes per feature row
 __host__ __device__ inline size_t t1_buf_bytes(int D, int NW) {
-    return (size_t)NW * t1_blk_per_wave(D, NW) * 1024;
+    (void)NW;
+    return (size_t)D * T1_BCP * 2;
 }
-constexpr int T1_BUF_BYTES = 80 * 1024;    // one chunk buffer, static: D <= 1024 with NW in {4, 8}
+constexpr int T1_BUF_BYTES = 80 * 1024;    // one chunk buffer, static: D <= 1024
+constexpr int T1_ROWS_PER_COPY = 12;       // feature rows per copy instruction (60 lanes)
 
-// Issue this wave's share of the asynchronous copy of chunk ch into buf.
+// Source offset (bytes) of this lane's 16-byte slot within a block of 12
+// feature rows: row lane/5, segment lane%5 (the pad slot repeats segment 3).
+// It does not depend on the block or the chunk, so the copies need no
+// per-lane arithmetic.
+__device__ __forceinline__ unsigned t1_copy_voff(int lane, int Bp) {
+    const int row = lane / 5, seg = lane % 5;
+    return (unsigned)(row * Bp + 8 * (seg == 4 ? 3 : seg)) * 2u;
+}
+
+// Issue this wave's share of the asynchronous copy of chunk ch into buf: one
+// direct global->LDS copy per block of 12 rows (lanes 60..63 idle); the last
+// block is moved back to end at row D (its overlap rewrites equal data).
 template <int NW>
 __device__ __forceinline__ void t1_stage_async(const TailArgs &a, unsigned short *buf, int ch,
-                                               int w, int lane) {
-    const int nbw = t1_blk_per_wave(a.D, NW);
-    for (int i = 0; i < nbw; ++i) {
-        const int blk = w * nbw + i;
-        const int s = blk * 64 + lane;            // 16-byte slot of the padded tile
-        int row = s / 5, seg = s % 5;
-        if (seg == 4) seg = 3;                    // pad slot: harmless duplicate
-        if (row >= a.D) { row = 0; seg = 0; }     // beyond the tile: dummy source
-        const unsigned short *src = a.XT + (int64_t)row * a.Bp + ch * T1_BC + seg * 8;
-        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)(
-                                                  (char *)buf + (size_t)blk * 1024), 16, 0, 0);
+                                               int w, int lane, unsigned voff) {
+    const int nblk = (a.D + T1_ROWS_PER_COPY - 1) / T1_ROWS_PER_COPY;
+    for (int b = w; b < nblk; b += NW) {
+        const int r0 = min(T1_ROWS_PER_COPY * b, a.D - T1_ROWS_PER_COPY);
+        const char *src = (const char *)(a.XT + (int64_t)r0 * a.Bp + ch * T1_BC);
+        if (lane < 5 * T1_ROWS_PER_COPY)
+            __builtin_amdgcn_global_load_lds(src + voff, (__attribute__((address_space(3))) void *)(
+                                                             buf + r0 * T1_BCP), 16, 0, 0);
     }
 }
 
@@ -258,6 +408,12 @@ template <int G, int F, int RW, int NW, int MODE>
 __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, int store_z, int do_loss) {
     constexpr int JT = G / 16, KS = F / 32, FT = F / 16;
     constexpr int BC = T1_BC, BCP = T1_BCP;
+    // a group's W / dW slab (G x F) passes through LDS, one row per WSP
+    // elements (16 bytes of padding: rows 4 banks apart), to turn the feature
+    // order into full-width global accesses; WPL 16-byte pieces per lane
+    constexpr int WSP = F + 8, WPL = G * F / 8 / 64;
+    static_assert(G * F % 512 == 0, "slab pieces must fill whole waves");
+    static_assert(NW * G * WSP * 2 <= T1_BUF_BYTES, "slab staging exceeds a chunk buffer");
     constexpr bool DO_Z = (MODE != T1_DW_MEM);
     constexpr bool DO_DW = (MODE != T1_FWD);
     // The two chunk buffers are distinct LDS objects and the chunk loop is
@@ -268,6 +424,8 @@ __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, int store_z,
     __shared__ __attribute__((aligned(16))) unsigned short buf1[T1_BUF_BYTES / 2];
 
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int wu = __builtin_amdgcn_readfirstlane(w);   // wave index in a scalar register
+    const unsigned voff = t1_copy_voff(lane, a.Bp);
     const int q = lane >> 4, m = lane & 15;
     const int nch = a.Bp / BC;
     const int64_t n_runs = (a.Ng + NW * RW - 1) / (NW * RW);
@@ -277,6 +435,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, int store_z,
     for (int64_t run = blockIdx.x; run < n_runs; run += gridDim.x) {
         const int64_t gw = run * (NW * RW) + (int64_t)w * RW;
         bf16x8 wreg[RW][KS][JT];
+        u32x2 pwz[DO_Z ? RW : 1][KS];     // perm bytes of positions 32s + 8q .. + 7
         unsigned zrow[RW][KS];            // tr-gather rows: lo16 = h 0, hi16 = h 1
         unsigned frow[RW][FT / 2];        // dW rows, two f-tiles per word
         int gp0[RW], pn[RW], pe[RW];      // positives per group: first, count, entry per lane
@@ -286,20 +445,16 @@ __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, int store_z,
         for (int r = 0; r < RW; ++r) {
             const int64_t g = gw + r;
             const bool ok = g < a.Ng;
-            const int32_t *ix = a.idx + (ok ? g : 0) * (int64_t)F;
+            // features in the bank-aware order: position k reads feature
+            // perm[g][k] (row idxp[g][k] of the chunk, column perm[g][k] of W)
+            const int64_t gs = ok ? g : 0;
+            const unsigned short *ix = a.idxp + gs * (int64_t)F;
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
                 const unsigned lo = (unsigned)ix[32 * s + 8 * q + (m >> 2)];
                 const unsigned hi = (unsigned)ix[32 * s + 8 * q + 4 + (m >> 2)];
                 zrow[r][s] = lo | (hi << 16);
-                if (DO_Z) {
-#pragma unroll
-                    for (int jt = 0; jt < JT; ++jt) {
-                        const unsigned short *wp =
-                            a.W + (((ok ? g : 0) * G + 16 * jt + m) * (int64_t)F + 32 * s + 8 * q);
-                        wreg[r][s][jt] = *(const bf16x8 *)wp;
-                    }
-                }
+                if (DO_Z) pwz[r][s] = *(const u32x2 *)(a.perm + gs * F + 32 * s + 8 * q);
             }
 #pragma unroll
             for (int p = 0; p < FT / 2; ++p)
@@ -472,32 +627,74 @@ __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, int store_z,
             }
         };
         // nch is even (Bp is a multiple of 64)
-        __syncthreads();                  // previous run's readers are done with buffer 0
-        t1_stage_async<NW>(a, buf0, 0, w, lane);
+        __syncthreads();                  // previous run's readers are done with both buffers
+        t1_stage_async<NW>(a, buf0, 0, wu, lane, voff);
+        if (DO_Z) {
+            // W operands in the feature order, through this wave's slab in
+            // buffer 1 (free until the loop's first barrier; groups in turn)
+            unsigned short *ws = buf1 + w * (G * WSP);
+#pragma unroll
+            for (int r = 0; r < RW; ++r) {
+                const int64_t gs = gw + r < a.Ng ? gw + r : 0;
+                u32x4 wraw[WPL];
+#pragma unroll
+                for (int i = 0; i < WPL; ++i)
+                    wraw[i] = *(const u32x4 *)(a.W + gs * G * (int64_t)F + 8 * (64 * i + lane));
+#pragma unroll
+                for (int i = 0; i < WPL; ++i) {
+                    const int pc16 = 64 * i + lane;
+                    *(u32x4 *)(ws + (pc16 / (F / 8)) * WSP + 8 * (pc16 % (F / 8))) = wraw[i];
+                }
+#pragma unroll
+                for (int s = 0; s < KS; ++s)
+#pragma unroll
+                    for (int jt = 0; jt < JT; ++jt) {
+                        const unsigned short *wr = ws + (16 * jt + m) * WSP;
+                        unsigned short e8[8];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            e8[e] = wr[(pwz[r][s][e >> 2] >> (8 * (e & 3))) & 255u];
+                        wreg[r][s][jt] = __builtin_bit_cast(bf16x8, e8);
+                    }
+            }
+        }
         for (int ch = 0; ch < nch; ch += 2) {
             __builtin_amdgcn_s_waitcnt(0);   // this wave's copies of chunk ch have landed
             __syncthreads();                 // ... and everyone's; chunk ch-1 is consumed
-            t1_stage_async<NW>(a, buf1, ch + 1, w, lane);
+            t1_stage_async<NW>(a, buf1, ch + 1, wu, lane, voff);
             chunk(buf0, ch);
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
-            if (ch + 2 < nch) t1_stage_async<NW>(a, buf0, ch + 2, w, lane);
+            if (ch + 2 < nch) t1_stage_async<NW>(a, buf0, ch + 2, wu, lane, voff);
             chunk(buf1, ch + 1);
         }
         if (DO_DW) {
+            // dW back to the natural feature order through this wave's slab in
+            // buffer 0 (no copy into it is pending and every wave has read
+            // its last chunk), then full-width stores; groups in turn
+            unsigned short *ws = buf0 + w * (G * WSP);
 #pragma unroll
             for (int r = 0; r < RW; ++r) {
                 const int64_t g = gw + r;
-                if (g >= a.Ng) continue;
+                if (g >= a.Ng) continue;   // wave-uniform
+                unsigned pw[FT];           // perm bytes of positions 16ft + 4q .. + 3
+#pragma unroll
+                for (int ft = 0; ft < FT; ++ft) pw[ft] = *(const unsigned *)(a.perm + g * F + 16 * ft + 4 * q);
 #pragma unroll
                 for (int ft = 0; ft < FT; ++ft)
 #pragma unroll
                     for (int jt = 0; jt < JT; ++jt) {
-                        const f32x4 v = dwacc[r][ft][jt];
-                        const int64_t t = g * G + 16 * jt + m;  // padded rows get dz = 0
-                        u32x2 o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-                        *(u32x2 *)(a.dW + t * F + 16 * ft + 4 * q) = o;
+                        const f32x4 v = dwacc[r][ft][jt];   // padded rows get dz = 0
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            ws[(16 * jt + m) * WSP + ((pw[ft] >> (8 * i)) & 255u)] = f32_to_bf16(v[i]);
                     }
+#pragma unroll
+                for (int i = 0; i < WPL; ++i) {
+                    const int pc16 = 64 * i + lane;
+                    const u32x4 v = *(const u32x4 *)(ws + (pc16 / (F / 8)) * WSP + 8 * (pc16 % (F / 8)));
+                    *(u32x4 *)(a.dW + g * G * (int64_t)F + 8 * pc16) = v;
+                }
             }
         }
     }
