@@ -49,8 +49,12 @@ __device__ __forceinline__ unsigned short f32_to_bf16(float x) {
     return __builtin_bit_cast(unsigned short, h);
 }
 
+// Two floats to a bf16 pair (lo in bits 0-15), one packed conversion.
 __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
-    return (unsigned)f32_to_bf16(lo) | ((unsigned)f32_to_bf16(hi) << 16);
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2_t));
 }
 
 // Sigmoid-BCE on one logit, fp32, scaled by s.  e = exp(-|z|) is shared by

@@ -537,8 +537,10 @@ __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, int store_z,
                 unsigned dzp[2][JT][2];
                 const bool tile_live = (r0 + BC <= a.B) && ((g + 1) * G <= a.L);
                 if (MODE != T1_DW_MEM && tile_live && !has_pos && !(MODE == T1_FWD && store_z)) {
-                    // fast path: every element live, no positive, no logits to store
-                    float lin = 0.f, prod = 1.f;
+                    // fast path: every element live, no positive, no logits to store;
+                    // lin2 = sum of z + |z| = twice the sum of max(z, 0), exactly
+                    float lin2 = 0.f, prod = 1.f;
+                    const float hs = 0.5f * a.s;
 #pragma unroll
                     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
@@ -546,12 +548,14 @@ __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, int store_z,
                             float dzv[4];
 #pragma unroll
                             for (int i = 0; i < 4; ++i) {
+                                // r = 1/(1 + exp(-|z|)) is sigmoid(|z|); s*sigmoid(z)
+                                // = s/2 + sign(z) * (s*r - s/2)
                                 const float z = zacc[h2][jt][i];
-                                const float e = fast_exp_neg_abs(z);
-                                float den;
-                                dzv[i] = a.s * fast_sigmoid(z, e, den);
+                                const float den = 1.0f + fast_exp_neg_abs(z);
+                                const float r = __builtin_amdgcn_rcpf(den);
+                                dzv[i] = hs + __builtin_copysignf(__builtin_fmaf(a.s, r, -hs), z);
                                 prod *= den;
-                                lin += fmaxf(z, 0.f);
+                                lin2 += z + fabsf(z);
                             }
                             dzp[h2][jt][0] = pack_bf16x2(dzv[0], dzv[1]);
                             dzp[h2][jt][1] = pack_bf16x2(dzv[2], dzv[3]);
@@ -563,7 +567,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, int store_z,
                             }
                         }
                     // at most 8*JT <= 32 factors in [1, 2]: the product stays below 2^32
-                    if (do_loss) lsum += a.s * (lin + fast_log(prod));
+                    if (do_loss) lsum += a.s * (0.5f * lin2 + fast_log(prod));
                 } else {
 #pragma unroll
                     for (int h2 = 0; h2 < 2; ++h2)
@@ -614,9 +618,13 @@ __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, int store_z,
                     for (int ft = 0; ft < FT; ++ft) {
                         const unsigned row =
                             (ft & 1) ? (frow[r][ft >> 1] >> 16) : (frow[r][ft >> 1] & 0xffffu);
-                        const unsigned short *p = tile + row * BCP + 4 * q;
-                        u32x2 lo = *(const u32x2 *)p;
-                        u32x2 hi = *(const u32x2 *)(p + 16);
+                        // two separate 8-byte reads: fused into one paired read
+                        // (ds_read2_b64) they take about twice the LDS cycles
+                        const unsigned o_lo = row * BCP + 4 * q;
+                        unsigned o_hi = o_lo + 16;
+                        asm volatile("" : "+v"(o_hi));
+                        u32x2 lo = *(const u32x2 *)(tile + o_lo);
+                        u32x2 hi = *(const u32x2 *)(tile + o_hi);
                         u32x4 v = {lo.x, lo.y, hi.x, hi.y};
                         bf16x8 A = __builtin_bit_cast(bf16x8, v);
 #pragma unroll
