@@ -1256,7 +1256,7 @@ __host__ __device__ inline T2dLds t2d_layout(int F, int G, int BC2, int NTW32) {
     L.ndp = T2_NC * NTW32 * 32;
     int o = 0;
     L.wts = o;
-    L.wts_grp = ((F + 1) * (G * 2 + 8) + 15) & ~15;   // W_g^T (padded rows) + zero row F
+    L.wts_grp = (F + 1) * (G * 2 + 16);                // W_g^T (padded rows) + zero row F
     o += 3 * GPI * L.wts_grp;
     L.inv = o;
     o += (4 * GPI * L.ndp + 15) & ~15;                // u8 inverse index
@@ -1273,7 +1273,9 @@ __global__ __launch_bounds__(64 * T2D_NW, 1) void k_tail_t2d(TailArgs a, int n_g
     constexpr int GPI = t2d_gpi(G, BC2, NTW32);
     constexpr int JT = G / 16, RT = BC2 / 32;
     constexpr int GPR = G / 4, LGPR = G == 16 ? 2 : G == 32 ? 3 : 4;
-    constexpr int WTS = G * 2 + 8;             // W^T row stride, bytes
+    // W^T row stride, bytes: 16 bytes of padding keep every operand read one
+    // aligned 16-byte read (a pair of 8-byte reads costs about twice as much)
+    constexpr int WTS = G * 2 + 16;
     constexpr int NDP = T2_NC * NTW32 * 32;    // features covered by the consumer waves
     constexpr int NB_T = T2D_NB * 64;          // builder threads
     constexpr int UPT = (GPI * GPR * 32 + NB_T - 1) / NB_T;   // W^T units per builder thread (F <= 128)
@@ -1338,11 +1340,7 @@ __global__ __launch_bounds__(64 * T2D_NW, 1) void k_tail_t2d(TailArgs a, int n_g
             for (int nt = 0; nt < NTW32; ++nt) {
                 const unsigned char *br = wt + iv[32 * nt] * WTS;
 #pragma unroll
-                for (int jt = 0; jt < JT; ++jt) {
-                    const u32x2 lo = *(const u32x2 *)(br + 32 * jt);
-                    const u32x2 hi = *(const u32x2 *)(br + 32 * jt + 8);
-                    R[q % NS].Bv[jt][nt] = __builtin_bit_cast(bf16x8, (u32x4){lo[0], lo[1], hi[0], hi[1]});
-                }
+                for (int jt = 0; jt < JT; ++jt) R[q % NS].Bv[jt][nt] = *(const bf16x8 *)(br + 32 * jt);
             }
         };
         __syncthreads();                       // builders have filled steps 0 and 1
