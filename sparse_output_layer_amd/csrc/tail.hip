@@ -813,7 +813,7 @@ __host__ __device__ inline T2Lds t2_layout(int D, int F, int G, int BC2, int NTW
     L.ndp = T2_NC * NTW32 * 32;
     int o = (D * BC2 * 2 + 15) & ~15;            // X^T chunk, rows of BC2 bf16
     L.wts = o;
-    L.wts_grp = ((F + 1) * (G * 2 + 8) + 15) & ~15;   // W_g^T (padded rows) + zero row F
+    L.wts_grp = (F + 1) * (G * 2 + 16);          // W_g^T (padded rows) + zero row F
     o += 3 * GPI * L.wts_grp;                    // three steps
     L.inv = o;
     o += (4 * GPI * L.ndp + 15) & ~15;           // u8 inverse index, four steps
@@ -831,7 +831,9 @@ __global__ __launch_bounds__(64 * T2_NW, 1) void k_tail_t2(TailArgs a, int dz_mo
     constexpr int JT = G / 16, BT = BC2 / 16, RT = BC2 / 32;
     constexpr int NU = BC2 / 8;                // 16-byte units per chunk row
     constexpr int GPR = G / 4, LGPR = G == 16 ? 2 : G == 32 ? 3 : 4;
-    constexpr int WTS = G * 2 + 8;             // W^T row stride, bytes
+    // W^T row stride, bytes: 16 bytes of padding keep every operand read one
+    // aligned 16-byte read (a pair of 8-byte reads costs about twice as much)
+    constexpr int WTS = G * 2 + 16;
     constexpr int NDP = T2_NC * NTW32 * 32;    // features covered by the consumer waves
     constexpr int LROW = BC2 == 64 ? 7 : 6;    // log2 of a chunk row in bytes
     constexpr int NTILE = GPI * JT * BT;       // 16x16 Z^T tiles per step
@@ -916,9 +918,7 @@ __global__ __launch_bounds__(64 * T2_NW, 1) void k_tail_t2(TailArgs a, int dz_mo
                         Am[rt] = *(const bf16x8 *)(exch + q * LY.exch_grp + ((rt * JT + jt) * 64 + lane) * 16);
 #pragma unroll
                     for (int nt = 0; nt < NTW32; ++nt) {   // labels 16jt + 8(lane/32) .. +7 of row f
-                        const u32x2 lo = *(const u32x2 *)(brow[nt] + 32 * jt);
-                        const u32x2 hi = *(const u32x2 *)(brow[nt] + 32 * jt + 8);
-                        const bf16x8 Bv = __builtin_bit_cast(bf16x8, (u32x4){lo[0], lo[1], hi[0], hi[1]});
+                        const bf16x8 Bv = *(const bf16x8 *)(brow[nt] + 32 * jt);
 #pragma unroll
                         for (int rt = 0; rt < RT; ++rt) acc[rt][nt] = mfma32x32(Am[rt], Bv, acc[rt][nt]);
                     }
