@@ -1326,11 +1326,22 @@ __global__ __launch_bounds__(64 * T2D_NW, 1) void k_tail_t2d(TailArgs a, int n_g
         // first two of the next, complete since the previous iteration); with
         // one group per step, one set taking the next step's group.
         constexpr int NS = GPI >= 2 ? 2 : 1;
+        // With at least NS + 2 groups per step, the inverse-index bytes of a
+        // load's group are read one load earlier (that group is then at most
+        // in step k+1, whose index is complete), so the W~ row reads do not
+        // wait for them.  Steps with fewer groups look them up in the load.
+        constexpr bool IVPF = GPI >= NS + 2;
         Opd R[NS];
+        unsigned ivn[NTW32];
+        auto load_iv = [&](int k, int q) {
+            const unsigned char *iv = inv0 + ((k & 3) * GPI + q) * NDP + dbase + (lane & 31);
+#pragma unroll
+            for (int nt = 0; nt < NTW32; ++nt) ivn[nt] = iv[32 * nt];
+        };
         auto load = [&](int k, int q) {
             const unsigned char *wt = wts0 + ((k % 3) * GPI + q) * LY.wts_grp + 16 * (lane >> 5);
-            const unsigned char *iv = inv0 + ((k & 3) * GPI + q) * NDP + dbase + (lane & 31);
             const unsigned char *ex = exch0 + ((k % 3) * GPI + q) * LY.exch_grp;
+            if (!IVPF) load_iv(k, q);
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -1338,15 +1349,18 @@ __global__ __launch_bounds__(64 * T2D_NW, 1) void k_tail_t2d(TailArgs a, int n_g
                     R[q % NS].A[rt][jt] = *(const bf16x8 *)(ex + ((rt * JT + jt) * 64 + lane) * 16);
 #pragma unroll
             for (int nt = 0; nt < NTW32; ++nt) {
-                const unsigned char *br = wt + iv[32 * nt] * WTS;
+                const unsigned char *br = wt + ivn[nt] * WTS;
 #pragma unroll
                 for (int jt = 0; jt < JT; ++jt) R[q % NS].Bv[jt][nt] = *(const bf16x8 *)(br + 32 * jt);
             }
         };
         __syncthreads();                       // builders have filled steps 0 and 1
 #pragma unroll
-        for (int q = 0; q < NS; ++q)
+        for (int q = 0; q < NS; ++q) {
+            if (IVPF) load_iv(0, q);
             if (live(0, q)) load(0, q);
+        }
+        if (IVPF) load_iv(0, NS);
         __syncthreads();                       // step 0 looked up before its inverse index is cleared
         for (int k = 0; k < niter; ++k) {
 #pragma unroll
@@ -1360,10 +1374,16 @@ __global__ __launch_bounds__(64 * T2D_NW, 1) void k_tail_t2d(TailArgs a, int n_g
                             for (int rt = 0; rt < RT; ++rt)
                                 acc[rt][nt] = mfma32x32(R[q % NS].A[rt][jt], R[q % NS].Bv[jt][nt], acc[rt][nt]);
                 }
+                // operands of group q + NS (this step or the next), then the
+                // inverse-index bytes of the group after it
                 if (q + NS < GPI) {
                     if (live(k, q + NS)) load(k, q + NS);
                 } else if (live(k + 1, q + NS - GPI)) {
                     load(k + 1, q + NS - GPI);
+                }
+                if (IVPF) {
+                    if (q + NS + 1 < GPI) load_iv(k, q + NS + 1);
+                    else load_iv(k + 1, q + NS + 1 - GPI);
                 }
             }
             __syncthreads();

@@ -22,6 +22,11 @@ CASES = [
     dict(B=33, D=1024, H=96, L=700, G=64, F=64, idx_dist="skew10"),
     dict(B=65, D=768, H=128, L=1000, G=64, F=128, pos_per_row=7),
     dict(B=130, D=768, H=136, L=1500, G=32, F=128),
+    # groups of 16 on wide inputs: 32-row dX chunks at D = 1024, 64-row
+    # chunks at D = 544, and a batch of at most 32 rows
+    dict(B=40, D=1024, H=64, L=600, G=16, F=64),
+    dict(B=96, D=544, H=64, L=800, G=16, F=32),
+    dict(B=20, D=448, H=48, L=400, G=16, F=128),
 ]
 
 
