@@ -41,6 +41,12 @@ def parse():
     p.add_argument("--calib-mib", type=int, default=0,
                    help="after timing, one device-to-device copy of this many MiB: the "
                         "known-size reference for the FETCH_SIZE / WRITE_SIZE counters")
+    p.add_argument("--mode", choices=["train", "infer"], default="train",
+                   help="train: the training step (default); infer: head + tail forward "
+                        "with a per-row top-K, exact and approximate")
+    p.add_argument("--topk", type=int, default=5, help="K of the inference mode")
+    p.add_argument("--recall", type=float, default=0.95,
+                   help="recall target of the approximate top-K in the inference mode")
     return p.parse_args()
 
 
@@ -143,6 +149,99 @@ def cpu_baseline(inp, seconds):
                       f"scaled by group/label count to the full step ({full:.1f} s per step)"}
 
 
+def run_infer(args, cfg, inp, t_gen):
+    """Inference: head + tail forward, per-row top-K over each branch (the
+    top-K page's two stages), merged over the whole output space; first with
+    K' = K on buckets of 32768 labels (exact), then with the (K', buckets)
+    that haste_topk_plan picks for the recall target."""
+    import numpy as np
+    import torch
+
+    from sparse_output_layer_amd import haste as H
+    dev = "cuda:0"
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    X, Wh, W = bf(inp.X), bf(inp.Wh), bf(inp.W)
+    idx = torch.from_numpy(inp.idx).to(dev)
+    rp = torch.from_numpy(inp.row_ptr).to(dev)
+    lab = torch.from_numpy(inp.labels).to(dev)
+    B, L, G, K = cfg.B, cfg.L, cfg.G, args.topk
+    # stage-1 parallelism: at least about four workgroups per CU over all rows
+    min_b = max(1, -(-4 * 256 // B))
+    kp, nb = H.haste_topk_plan(L, K, args.recall, min_b)
+    exp_recall = H.haste_topk_expected_recall(L, K, kp, nb)
+    out = {}
+    lists = {}
+    for name, (kprime, nbk) in (("exact", (0, 0)), ("approx", (kp, nb))):
+        bh = H.Bce(rp, lab, 0, 1.0 / B)
+        bt = H.Bce(rp, lab, cfg.H, 1.0 / B, topk_kprime=kprime, topk_buckets=nbk)
+        for b_ in (bh, bt):
+            b_.topk_val = torch.empty(B, K, dtype=torch.float32, device=dev)
+            b_.topk_idx = torch.empty(B, K, dtype=torch.int32, device=dev)
+        ws_t = torch.empty(H.haste_tail_workspace_bytes(X, idx, L, G, bt), dtype=torch.uint8, device=dev)
+        ws_h = torch.empty(max(256, H.haste_head_workspace_bytes(X, Wh, bh)), dtype=torch.uint8, device=dev)
+        names = ["head_fwd", "tail_fwd", "topk_merge"]
+
+        def step(ev=None):
+            if ev is not None:
+                ev[0].record()
+            H.haste_head_fwd(X, Wh, bce=bh, workspace=ws_h)
+            if ev is not None:
+                ev[1].record()
+            H.haste_tail_fwd(X, idx, W, L, G, bce=bt, workspace=ws_t)
+            if ev is not None:
+                ev[2].record()
+            r = H.haste_topk_merge(bh.topk_val, bh.topk_idx, bt.topk_val, bt.topk_idx)
+            if ev is not None:
+                ev[3].record()
+            return r
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for k in range(args.steps):
+            step(evs[k])
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / args.steps
+        per = {n: round(float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) * 1e3, 2)
+               for i, n in enumerate(names)}
+        mv, mi = step()
+        torch.cuda.synchronize()
+        lists[name] = (bt.topk_idx.cpu().numpy(), mi.cpu().numpy())
+        out[name] = {"value": round(B / (ms * 1e-3), 1), "ms_per_step": round(ms, 4), "kernels_us": per}
+    # recall of the approximate lists against the exact ones (tail, and merged)
+    tail_rec = float(np.mean([len(set(a) & set(e)) / K for a, e in zip(lists["approx"][0], lists["exact"][0])]))
+    all_rec = float(np.mean([len(set(a) & set(e)) / K for a, e in zip(lists["approx"][1], lists["exact"][1])]))
+    res = {
+        "metric": "inference samples/sec (head+tail fwd + per-row top-%d) at %s" % (K, cfg.name),
+        "value": out["exact"]["value"],
+        "unit": "samples/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": out["exact"]["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {cfg.note}; B={B} D={cfg.D} H={cfg.H} L={L} G={G} "
+                               f"F={cfg.F}, top-{K}", "global_batch": B, "parallelism": "single GPU"},
+        "exact": out["exact"],
+        "approx": dict(out["approx"], kprime=kp, buckets=nb, recall_target=args.recall,
+                       expected_recall_tail=round(exp_recall, 5), measured_recall_tail=round(tail_rec, 5),
+                       measured_recall_merged=round(all_rec, 5)),
+        "gen_s": round(t_gen, 2),
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -165,6 +264,8 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     assert cfg.dtype == "bf16"
+    if args.mode == "infer":
+        return run_infer(args, cfg, inp, t_gen)
 
     def bf(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)

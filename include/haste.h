@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define HASTE_ABI_VERSION 2
+#define HASTE_ABI_VERSION 3
 
 typedef enum {
     HASTE_OK = 0,
@@ -115,26 +115,56 @@ typedef struct {
     int32_t reserved0;
     int64_t label_offset;     /* global id of this branch's label 0           */
     float grad_scale;         /* s: dz = s*(sigmoid(z) - y); usually 1/B      */
-    int32_t reserved1;
+    int32_t topk_buckets;     /* buckets per row, in [1, 65535]; 0: the
+                                 library's choice (only with K' = K)          */
     float *loss;              /* device fp32 scalar; this call ADDS its loss,
                                  or NULL for no loss                          */
     int32_t topk;             /* 0, or K in [1, 8]: per-row top-K logits (see
                                  below)                                       */
-    int32_t reserved2;
+    int32_t topk_kprime;      /* 0: K' = K (exact); else K' in [1, topk]      */
     float *topk_val;          /* device B x K, descending                     */
     int32_t *topk_idx;        /* device B x K global ids; ties -> smaller id  */
 } haste_bce;
 
-/* Top-K (top-K page, section "Method": per-bucket top-K' then a merge; here
- * K' = K, so exact in the kernels' fp32 logits).  With topk = K > 0 the calls
- * that form logits -- haste_tail_fwd, haste_tail_step, haste_tail_step_dw,
- * haste_head_fwd, haste_head_step -- write to topk_val / topk_idx the K
- * largest logits of every row over this call's labels (ids = label_offset +
- * label), value descending, ties to the smaller id, rows with fewer than K
- * labels padded with (-inf, -1).  The head's and the tail's lists combine
- * with haste_topk_merge.  The workspace then also holds the call's fp32
- * logits (B x labels x 4 bytes) and the bucket lists.  haste_tail_bwd and
- * haste_head_bwd reject topk > 0; the other calls ignore it. */
+/* Top-K (top-K page, section "Method": the top-K' of every bucket, then a
+ * merge of the buckets' lists).  With topk = K > 0 the calls that form
+ * logits -- haste_tail_fwd, haste_tail_step, haste_tail_step_dw,
+ * haste_head_fwd, haste_head_step -- write to topk_val / topk_idx K logits of
+ * every row over this call's labels (ids = label_offset + label), value
+ * descending, ties to the smaller id, rows with fewer than K candidates
+ * padded with (-inf, -1).  A bucket is a run of consecutive labels:
+ * topk_buckets runs of ceil(labels / topk_buckets) (fewer if that leaves the
+ * last ones empty).  With topk_kprime = 0 (K' = K) the result is the exact
+ * top-K of the kernels' fp32 logits for any bucket count, and
+ * topk_buckets = 0 lets the library pick one (about 1024 / B, at least one:
+ * enough stage-1 workgroups over all rows).  With K' < K it is the page's
+ * approximate two-stage top-K (a logit of the true top-K is missed when more
+ * than K' of them share its bucket) and topk_buckets must be given;
+ * haste_topk_plan picks K' and the bucket count for a recall target.  The head's and the tail's lists combine with
+ * haste_topk_merge.  The workspace then also holds the call's fp32 logits
+ * (B x labels x 4 bytes) and the bucket lists (B x buckets x K' x 8 bytes).
+ * haste_tail_bwd and haste_head_bwd reject topk > 0; the other calls ignore
+ * it. */
+
+/* Expected recall of the two-stage top-K (top-K page, "Theoretical
+ * analysis": the K largest of n items fall into the buckets as a uniformly
+ * random placement, so the number in a bucket of m items is hypergeometric,
+ * and a bucket contributes min(that number, K')).  Buckets as the calls form
+ * them for `buckets` buckets.  Host only; returns the expected fraction of
+ * the true top-K that the result holds, or -1 for invalid arguments (n < 1,
+ * K outside [1, 8], K' outside [1, K], buckets < 1). */
+double haste_topk_expected_recall(int64_t n, int K, int kprime, int64_t buckets);
+
+/* Automatic parameter choice (top-K page, "automatic parameter selection"):
+ * among K' in [1, K] and bucket counts in [min_buckets, min(n, 65535)], the
+ * pair whose expected recall is at least `target` with the fewest stage-2
+ * candidates buckets * K' (ties: the smaller K').  min_buckets is the least
+ * number of buckets the caller wants for stage 1's parallelism (with 1 the
+ * answer is always the exact K' = K over one bucket: K candidates).  Host
+ * only.  out = {K', buckets}.  Returns HASTE_ERR_INVALID for bad arguments
+ * (target outside (0, 1], min_buckets outside [1, min(n, 65535)]) and
+ * HASTE_ERR_UNSUPPORTED when no pair reaches the target. */
+haste_status haste_topk_plan(int64_t n, int K, double target, int64_t min_buckets, int32_t *out);
 
 int haste_abi_version(void);
 const char *haste_status_string(int status);

@@ -215,6 +215,87 @@ def topk(z, K, ids=None, id_offset=0):
     return val, out
 
 
+# ----------------------------------------------------------------- top-K
+# Two-stage top-K of the top-K page (gist.science summary of "A Faster
+# Generalized Two-Stage Approximate Top-K", sections "Method" and
+# "Theoretical analysis").  Buckets are runs of consecutive labels:
+# seg_len = ceil(n / buckets) (the last bucket shorter).
+
+def topk_seg_len(n, buckets):
+    assert buckets >= 1
+    return -(-n // min(buckets, n))
+
+
+def topk_two_stage(z, K, kprime, seg_len, id_offset=0):
+    """Stage 1: the top-K' of every bucket (value descending, ties to the
+    smaller id); stage 2: the top-K of all the buckets' picks.  Rows with
+    fewer than K picks are padded with (-inf, -1).  Returns (val, idx) with
+    K + 1 columns (the extra one for separation checks)."""
+    z = _c(z, np.float64)
+    rows, n = z.shape
+    SENT = 1 << 62                      # id of a missing pick: sorts last
+    cv, ci = [], []
+    for c0 in range(0, n, seg_len):
+        c1 = min(c0 + seg_len, n)
+        v, i = topk(z[:, c0:c1], kprime, id_offset=id_offset + c0)
+        i = np.where(i < 0, SENT, i)    # a bucket shorter than K' pads
+        cv.append(v)
+        ci.append(i)
+    V = np.concatenate(cv, axis=1)
+    I = np.concatenate(ci, axis=1)
+    val = np.empty((rows, K + 1))
+    idx = np.empty((rows, K + 1), np.int64)
+    for r in range(rows):               # merge over the row's picks (ids given)
+        v, i = topk(V[r:r + 1], K + 1, ids=I[r])
+        val[r], idx[r] = v[0], i[0]
+    missing = idx >= SENT
+    val[missing] = -np.inf
+    idx[missing] = -1
+    return val, idx
+
+
+def topk_expected_recall(n, K, kprime, seg_len):
+    """Expected recall as an exact fraction: the K largest of n items fall on
+    a uniformly random K-subset of the positions, the number X that lands in a
+    bucket of m items is hypergeometric, P(X = x) = C(K, x) C(n-K, m-x) / C(n, m),
+    and a bucket returns min(X, K') of them; recall = sum over buckets of
+    E[min(X, K')] / min(K, n)."""
+    from fractions import Fraction
+    from math import comb
+    Kt = min(K, n)
+    nseg = -(-n // seg_len)
+    sizes = [seg_len] * (nseg - 1) + [n - (nseg - 1) * seg_len]
+    total = Fraction(0)
+    cache = {}
+    for m in sizes:
+        if m not in cache:
+            e = Fraction(0)
+            for x in range(0, min(Kt, m) + 1):
+                if m - x > n - Kt:
+                    continue
+                e += Fraction(comb(Kt, x) * comb(n - Kt, m - x), comb(n, m)) * min(x, kprime)
+            cache[m] = e
+        total += cache[m]
+    return total / Kt
+
+
+def topk_plan(n, K, target, min_buckets=1):
+    """Plain search: for every K' in 1..K the smallest bucket count in
+    min_buckets..min(n, 65535) whose expected recall reaches the target; the
+    pair with the fewest stage-2 candidates (buckets x K'), ties to the
+    smaller K'."""
+    from fractions import Fraction
+    target = Fraction(target)
+    best = None
+    for kp in range(1, K + 1):
+        for b in range(min_buckets, min(n, 65535) + 1):
+            if topk_expected_recall(n, K, kp, topk_seg_len(n, b)) >= target:
+                if best is None or b * kp < best[0]:
+                    best = (b * kp, kp, b)
+                break
+    return None if best is None else (best[1], best[2])
+
+
 def group_positives(row_ptr, labels, label_offset, L, G):
     row_ptr, labels = _c(row_ptr, np.int32), _c(labels, np.int32)
     B = row_ptr.size - 1

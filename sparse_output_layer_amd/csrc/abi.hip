@@ -44,6 +44,14 @@ haste_status hip_ok(hipError_t e, const char *what) {
     } while (0)
 
 inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// bytes of the top-K bucket lists (value + id per entry) for B rows of n logits
+size_t topk_cand_bytes(int B, int64_t n, const haste_bce *bce) {
+    const int K = bce->topk;
+    const int KP = bce->topk_kprime > 0 && bce->topk_kprime <= K ? bce->topk_kprime : K;
+    const int64_t nb = bce->topk_buckets > 0 ? bce->topk_buckets : 0;
+    return (size_t)B * (size_t)topk_buckets(n, nb, B).nseg * (size_t)KP * 8;
+}
 inline bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 inline int64_t n_groups(const haste_tail_desc *d) { return (d->L + d->G - 1) / d->G; }
 inline int pad_rows(int B) { return (B + 63) / 64 * 64; }
@@ -81,7 +89,7 @@ TailWs tail_ws(const haste_tail_desc *d, const haste_bce *bce) {
     w.has_topk = bce && bce->topk > 0;
     if (w.has_topk) {
         w.z32 = o;  o += al256((size_t)d->B * d->L * 4);
-        w.cand = o; o += al256((size_t)d->B * topk_segments(d->L) * bce->topk * 8);
+        w.cand = o; o += al256(topk_cand_bytes(d->B, d->L, bce));
     }
     w.total = o;
     return w;
@@ -102,7 +110,7 @@ HeadWs head_ws(const haste_head_desc *d, const haste_bce *bce) {
     w.has_topk = bce && bce->topk > 0;
     if (w.has_topk) {
         w.z32 = o;  o += al256((size_t)d->B * d->H * 4);
-        w.cand = o; o += al256((size_t)d->B * topk_segments(d->H) * bce->topk * 8);
+        w.cand = o; o += al256(topk_cand_bytes(d->B, d->H, bce));
     }
     w.total = o;
     return w;
@@ -151,6 +159,12 @@ haste_status check_bce(const haste_bce *b, int B, bool topk_ok) {
     if (b->topk < 0 || b->topk > 8) return fail(HASTE_ERR_INVALID, "bce.topk=%d outside [0, 8]", b->topk);
     if (b->topk != 0) {
         if (!topk_ok) return fail(HASTE_ERR_UNSUPPORTED, "bce.topk is not supported by this call");
+        if (b->topk_kprime < 0 || b->topk_kprime > b->topk)
+            return fail(HASTE_ERR_INVALID, "bce.topk_kprime=%d outside [0, topk=%d]", b->topk_kprime, b->topk);
+        if (b->topk_buckets < 0 || b->topk_buckets > 65535)
+            return fail(HASTE_ERR_INVALID, "bce.topk_buckets=%d outside [0, 65535]", b->topk_buckets);
+        if (b->topk_kprime > 0 && b->topk_kprime < b->topk && b->topk_buckets == 0)
+            return fail(HASTE_ERR_INVALID, "an approximate top-K (K' < K) needs bce.topk_buckets > 0");
         if (!b->topk_val || !aligned(b->topk_val, 4)) return fail(HASTE_ERR_INVALID, "bce.topk_val NULL or misaligned");
         if (!b->topk_idx || !aligned(b->topk_idx, 4)) return fail(HASTE_ERR_INVALID, "bce.topk_idx NULL or misaligned");
     }
@@ -252,11 +266,12 @@ F32Args f32_tail_args(const haste_tail_desc *d, const void *X, const int32_t *id
 // per-row top-K of the fp32 logits z (B x n) into bce->topk_val / topk_idx
 haste_status run_topk(const haste_bce *bce, const float *z, int B, int64_t n, void *ws, size_t cand,
                       hipStream_t st) {
-    const int K = bce->topk;
-    const int64_t nc = (int64_t)B * topk_segments(n) * K;
+    const int K = bce->topk, KP = bce->topk_kprime ? bce->topk_kprime : K;
+    const int64_t nc = (int64_t)B * topk_buckets(n, bce->topk_buckets, B).nseg * KP;
     float *cv = (float *)B8(ws, cand);
     int32_t *ci = (int32_t *)(cv + nc);
-    TRY_HIP(launch_row_topk(z, n, B, n, bce->label_offset, K, cv, ci, bce->topk_val, bce->topk_idx, st),
+    TRY_HIP(launch_row_topk(z, n, B, n, bce->label_offset, K, KP, bce->topk_buckets, cv, ci,
+                            bce->topk_val, bce->topk_idx, st),
             "top-K");
     return HASTE_OK;
 }
@@ -694,6 +709,72 @@ haste_status haste_tail_validate(const haste_tail_desc *d, const int32_t *idx,
     TRY(need_al(idx, 4, "idx"));
     TRY(need_al(first_bad_group, 4, "first_bad_group"));
     TRY_HIP(launch_validate(idx, n_groups(d), d->F, d->D, first_bad_group, S(stream)), "validate");
+    return HASTE_OK;
+}
+
+// ------------------------------------------------------ top-K parameters
+// Expected min(X, K') for X the number of the K largest of n items that land
+// in a bucket of m items under a uniformly random placement: X is
+// hypergeometric, P(X = x) = C(m, x) C(n - m, K - x) / C(n, K); with K <= 8
+// every product below has at most eight factors.
+static double topk_bucket_expect(int64_t n, int K, int kp, int64_t m) {
+    double e = 0.0;
+    for (int x = 1; x <= K && x <= m; ++x) {
+        if (K - x > n - m) continue;
+        double p = 1.0;
+        for (int i = 0; i < x; ++i) p *= (double)(m - i) / (double)(x - i);        // C(m, x)
+        for (int i = 0; i < K - x; ++i) p *= (double)(n - m - i) / (double)(K - x - i);  // C(n-m, K-x)
+        for (int i = 0; i < K; ++i) p *= (double)(K - i) / (double)(n - i);        // / C(n, K)
+        e += p * (double)(x < kp ? x : kp);
+    }
+    return e;
+}
+
+// Expected recall for buckets of seg consecutive items (the last one shorter)
+static double topk_recall_seg(int64_t n, int K, int kp, int64_t seg) {
+    const int64_t nseg = (n + seg - 1) / seg, last = n - (nseg - 1) * seg;
+    if (K >= n)   // all n items are the top; a bucket keeps min(its size, K') of them
+        return ((double)(nseg - 1) * (double)(seg < kp ? seg : kp) + (double)(last < kp ? last : kp)) /
+               (double)n;
+    const double s = (double)(nseg - 1) * topk_bucket_expect(n, K, kp, seg) +
+                     topk_bucket_expect(n, K, kp, last);
+    return s / (double)K;
+}
+
+double haste_topk_expected_recall(int64_t n, int K, int kprime, int64_t buckets) {
+    if (n < 1 || K < 1 || K > 8 || kprime < 1 || kprime > K || buckets < 1) return -1.0;
+    const int64_t seg = topk_buckets(n, buckets, 1).seg_len;
+    return topk_recall_seg(n, K, kprime, seg);
+}
+
+haste_status haste_topk_plan(int64_t n, int K, double target, int64_t min_buckets, int32_t *out) {
+    g_err.clear();
+    if (!out) return fail(HASTE_ERR_INVALID, "out is NULL");
+    if (n < 1 || K < 1 || K > 8) return fail(HASTE_ERR_INVALID, "n=%lld K=%d", (long long)n, K);
+    if (!(target > 0.0 && target <= 1.0)) return fail(HASTE_ERR_INVALID, "target %g outside (0, 1]", target);
+    const int64_t bmax = n < 65535 ? n : 65535;
+    if (min_buckets < 1 || min_buckets > bmax)
+        return fail(HASTE_ERR_INVALID, "min_buckets=%lld outside [1, %lld]", (long long)min_buckets, (long long)bmax);
+    int64_t best_cost = -1;
+    for (int kp = 1; kp <= K; ++kp) {
+        // smallest bucket count reaching the target; counts with the same
+        // bucket length give the same buckets, so each length is tried once
+        int64_t prev_seg = -1;
+        for (int64_t b = min_buckets; b <= bmax; ++b) {
+            if (best_cost >= 0 && b * kp >= best_cost) break;   // cannot beat the best
+            const int64_t seg = (n + b - 1) / b;
+            if (seg == prev_seg) continue;
+            prev_seg = seg;
+            if (topk_recall_seg(n, K, kp, seg) >= target) {
+                best_cost = b * kp;
+                out[0] = kp;
+                out[1] = (int32_t)b;
+                break;
+            }
+        }
+    }
+    if (best_cost < 0) return fail(HASTE_ERR_UNSUPPORTED, "no K' <= %d and at most %lld buckets reach recall %g",
+                                   K, (long long)bmax, target);
     return HASTE_OK;
 }
 

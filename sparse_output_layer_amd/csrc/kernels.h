@@ -51,14 +51,19 @@ hipError_t launch_tail_t2(int G, int dz_mode, const TailArgs &a,
                           hipStream_t st);
 bool tail_bf16_supported(int G, int F, int D);
 
-// Exact per-row top-K (K in [1, 8]) of fp32 logits z (rows x n, row stride
-// ld, column c has id id_offset + c): stage 1 per bucket of TOPK_SEG columns
-// into cand (rows x topk_segments(n) x K), stage 2 merge into out (rows x K).
-constexpr int64_t TOPK_SEG = 32768;
-int topk_segments(int64_t n);
+// Per-row top-K (K in [1, 8]) of fp32 logits z (rows x n, row stride ld,
+// column c has id id_offset + c): stage 1 keeps the top-KP (1 <= KP <= K;
+// 0 means K) of every bucket into cand (rows x nseg x KP), stage 2 merges
+// them into out (rows x K).  Buckets: nbuckets runs of ceil(n / nbuckets)
+// consecutive columns; nbuckets == 0 -> about TOPK_WG / rows of them.
+constexpr int64_t TOPK_WG = 1024;
+struct TopkBuckets {
+    int64_t seg_len, nseg;
+};
+TopkBuckets topk_buckets(int64_t n, int64_t nbuckets, int64_t rows);
 hipError_t launch_row_topk(const float *z, int64_t ld, int rows, int64_t n, int64_t id_offset,
-                           int K, float *cand_v, int32_t *cand_i, float *out_v, int32_t *out_i,
-                           hipStream_t st);
+                           int K, int KP, int64_t nbuckets, float *cand_v, int32_t *cand_i,
+                           float *out_v, int32_t *out_i, hipStream_t st);
 
 // Head (dense classifier) GEMMs.
 struct GemmArgs {

@@ -1,6 +1,7 @@
-// topk.hip -- exact per-row top-K of fp32 logits on gfx950 (top-K page,
-// section "Method": stage 1 takes the top-K' of every bucket of a row,
-// stage 2 merges the buckets' lists; with K' = K the result is exact).
+// topk.hip -- per-row top-K of fp32 logits on gfx950 (top-K page, section
+// "Method": stage 1 takes the top-K' of every bucket of a row, stage 2
+// merges the buckets' lists; with K' = K the result is exact, with K' < K it
+// is the page's approximate two-stage top-K).
 //
 // Order: value descending, ties by smaller id (the same total order as the
 // merge of two lists).  A row with fewer than K entries is padded with
@@ -90,20 +91,23 @@ __device__ __forceinline__ void tk_block_merge(float *s_v, int32_t *s_i, float (
     }
 }
 
-// Stage 1: z is rows x n (row stride ld), ids id_offset + column.
-template <int K>
+// Stage 1: z is rows x n (row stride ld), ids id_offset + column; bucket
+// `seg` covers columns [seg*seg_len, min((seg+1)*seg_len, n)).  Each thread
+// keeps its top-KP (a bucket's top-KP lies in the union of those lists).
+template <int KP>
 __global__ __launch_bounds__(TOPK_THREADS) void k_topk_stage1(const float *__restrict__ z, int64_t ld,
                                                               int64_t n, int64_t id_offset, int nseg,
-                                                              float *cand_v, int32_t *cand_i) {
-    __shared__ float s_v[TOPK_THREADS * K];
-    __shared__ int32_t s_i[TOPK_THREADS * K];
+                                                              int64_t seg_len, float *cand_v,
+                                                              int32_t *cand_i) {
+    __shared__ float s_v[TOPK_THREADS * KP];
+    __shared__ int32_t s_i[TOPK_THREADS * KP];
     const int seg = blockIdx.x, row = blockIdx.y;
-    const int64_t c0 = (int64_t)seg * TOPK_SEG;
-    const int64_t c1 = c0 + TOPK_SEG < n ? c0 + TOPK_SEG : n;
-    float l_v[K];
-    int32_t l_i[K];
+    const int64_t c0 = (int64_t)seg * seg_len;
+    const int64_t c1 = c0 + seg_len < n ? c0 + seg_len : n;
+    float l_v[KP];
+    int32_t l_i[KP];
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
+    for (int k = 0; k < KP; ++k) {
         l_v[k] = -INFINITY;
         l_i[k] = -1;
     }
@@ -115,7 +119,7 @@ __global__ __launch_bounds__(TOPK_THREADS) void k_topk_stage1(const float *__res
     const int64_t nv = (c1 - a0) >> 2;
     const int64_t a1 = a0 + (nv << 2);
     for (int64_t c = c0 + threadIdx.x; c < a0; c += TOPK_THREADS)
-        tk_insert<K>(l_v, l_i, zr[c], (int32_t)(id_offset + c));
+        tk_insert<KP>(l_v, l_i, zr[c], (int32_t)(id_offset + c));
     const f32x4 *zv = (const f32x4 *)(zr + a0);
     constexpr int U = 4;
     for (int64_t v0 = threadIdx.x; v0 < nv; v0 += (int64_t)TOPK_THREADS * U) {
@@ -131,19 +135,19 @@ __global__ __launch_bounds__(TOPK_THREADS) void k_topk_stage1(const float *__res
             if (v >= nv) break;
             const int32_t id = (int32_t)(id_offset + a0 + 4 * v);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) tk_insert<K>(l_v, l_i, x[u][e], id + e);
+            for (int e = 0; e < 4; ++e) tk_insert<KP>(l_v, l_i, x[u][e], id + e);
         }
     }
     for (int64_t c = a1 + threadIdx.x; c < c1; c += TOPK_THREADS)
-        tk_insert<K>(l_v, l_i, zr[c], (int32_t)(id_offset + c));
-    const int64_t o = ((int64_t)row * nseg + seg) * K;
-    tk_block_merge<K>(s_v, s_i, l_v, l_i, cand_v + o, cand_i + o);
+        tk_insert<KP>(l_v, l_i, zr[c], (int32_t)(id_offset + c));
+    const int64_t o = ((int64_t)row * nseg + seg) * KP;
+    tk_block_merge<KP>(s_v, s_i, l_v, l_i, cand_v + o, cand_i + o);
 }
 
-// Stage 2: per row, the nseg lists of K entries -> K entries.
+// Stage 2: per row, ncand candidates (the buckets' lists) -> K entries.
 template <int K>
 __global__ __launch_bounds__(TOPK_THREADS) void k_topk_stage2(const float *cand_v, const int32_t *cand_i,
-                                                              int nseg, float *out_v, int32_t *out_i) {
+                                                              int64_t ncand, float *out_v, int32_t *out_i) {
     __shared__ float s_v[TOPK_THREADS * K];
     __shared__ int32_t s_i[TOPK_THREADS * K];
     const int row = blockIdx.x;
@@ -154,43 +158,77 @@ __global__ __launch_bounds__(TOPK_THREADS) void k_topk_stage2(const float *cand_
         l_v[k] = -INFINITY;
         l_i[k] = -1;
     }
-    const int64_t base = (int64_t)row * nseg * K;
-    for (int64_t e = threadIdx.x; e < (int64_t)nseg * K; e += TOPK_THREADS) {
+    const int64_t base = (int64_t)row * ncand;
+    for (int64_t e = threadIdx.x; e < ncand; e += TOPK_THREADS) {
         const int32_t id = cand_i[base + e];
         if (id >= 0) tk_insert<K>(l_v, l_i, cand_v[base + e], id);
     }
     tk_block_merge<K>(s_v, s_i, l_v, l_i, out_v + (int64_t)row * K, out_i + (int64_t)row * K);
 }
 
-int topk_segments(int64_t n) { return (int)((n + TOPK_SEG - 1) / TOPK_SEG); }
+// Buckets of a row of n logits: nbuckets buckets of ceil(n / nbuckets)
+// consecutive labels (fewer when that length leaves the last ones empty);
+// nbuckets == 0 -> about TOPK_WG / rows buckets (at least one), so that
+// stage 1 has about TOPK_WG workgroups over all rows.
+TopkBuckets topk_buckets(int64_t n, int64_t nbuckets, int64_t rows) {
+    TopkBuckets b{};
+    if (n <= 0) return b;
+    if (nbuckets <= 0) {
+        nbuckets = rows > 0 ? (TOPK_WG + rows - 1) / rows : 1;
+        if (nbuckets > 65535) nbuckets = 65535;
+    }
+    if (nbuckets > n) nbuckets = n;
+    b.seg_len = (n + nbuckets - 1) / nbuckets;
+    b.nseg = (n + b.seg_len - 1) / b.seg_len;
+    return b;
+}
+
+template <int KP>
+static hipError_t topk_stage1_go(const float *z, int64_t ld, int rows, int64_t n, int64_t id_offset,
+                                 const TopkBuckets &b, float *cand_v, int32_t *cand_i, hipStream_t st) {
+    hipLaunchKernelGGL(k_topk_stage1<KP>, dim3((unsigned)b.nseg, (unsigned)rows), dim3(TOPK_THREADS), 0,
+                       st, z, ld, n, id_offset, (int)b.nseg, b.seg_len, cand_v, cand_i);
+    return hipGetLastError();
+}
 
 template <int K>
-static hipError_t topk_go(const float *z, int64_t ld, int rows, int64_t n, int64_t id_offset,
-                          float *cand_v, int32_t *cand_i, float *out_v, int32_t *out_i,
-                          hipStream_t st) {
-    const int nseg = topk_segments(n);
-    hipLaunchKernelGGL(k_topk_stage1<K>, dim3((unsigned)nseg, (unsigned)rows), dim3(TOPK_THREADS), 0,
-                       st, z, ld, n, id_offset, nseg, cand_v, cand_i);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+static hipError_t topk_stage2_go(int rows, int64_t ncand, const float *cand_v, const int32_t *cand_i,
+                                 float *out_v, int32_t *out_i, hipStream_t st) {
     hipLaunchKernelGGL(k_topk_stage2<K>, dim3((unsigned)rows), dim3(TOPK_THREADS), 0, st, cand_v,
-                       cand_i, nseg, out_v, out_i);
+                       cand_i, ncand, out_v, out_i);
     return hipGetLastError();
 }
 
 hipError_t launch_row_topk(const float *z, int64_t ld, int rows, int64_t n, int64_t id_offset,
-                           int K, float *cand_v, int32_t *cand_i, float *out_v, int32_t *out_i,
-                           hipStream_t st) {
+                           int K, int KP, int64_t nbuckets, float *cand_v, int32_t *cand_i,
+                           float *out_v, int32_t *out_i, hipStream_t st) {
     if (rows <= 0) return hipSuccess;
+    if (KP == 0) KP = K;
+    if (K < 1 || K > TOPK_MAX || KP < 1 || KP > K || nbuckets < 0) return hipErrorInvalidValue;
+    const TopkBuckets b = topk_buckets(n, nbuckets, rows);
+    if (b.nseg < 1 || b.nseg > 65535) return hipErrorInvalidValue;
+    hipError_t e = hipErrorInvalidValue;
+    switch (KP) {
+    case 1: e = topk_stage1_go<1>(z, ld, rows, n, id_offset, b, cand_v, cand_i, st); break;
+    case 2: e = topk_stage1_go<2>(z, ld, rows, n, id_offset, b, cand_v, cand_i, st); break;
+    case 3: e = topk_stage1_go<3>(z, ld, rows, n, id_offset, b, cand_v, cand_i, st); break;
+    case 4: e = topk_stage1_go<4>(z, ld, rows, n, id_offset, b, cand_v, cand_i, st); break;
+    case 5: e = topk_stage1_go<5>(z, ld, rows, n, id_offset, b, cand_v, cand_i, st); break;
+    case 6: e = topk_stage1_go<6>(z, ld, rows, n, id_offset, b, cand_v, cand_i, st); break;
+    case 7: e = topk_stage1_go<7>(z, ld, rows, n, id_offset, b, cand_v, cand_i, st); break;
+    case 8: e = topk_stage1_go<8>(z, ld, rows, n, id_offset, b, cand_v, cand_i, st); break;
+    }
+    if (e != hipSuccess) return e;
+    const int64_t ncand = b.nseg * KP;
     switch (K) {
-    case 1: return topk_go<1>(z, ld, rows, n, id_offset, cand_v, cand_i, out_v, out_i, st);
-    case 2: return topk_go<2>(z, ld, rows, n, id_offset, cand_v, cand_i, out_v, out_i, st);
-    case 3: return topk_go<3>(z, ld, rows, n, id_offset, cand_v, cand_i, out_v, out_i, st);
-    case 4: return topk_go<4>(z, ld, rows, n, id_offset, cand_v, cand_i, out_v, out_i, st);
-    case 5: return topk_go<5>(z, ld, rows, n, id_offset, cand_v, cand_i, out_v, out_i, st);
-    case 6: return topk_go<6>(z, ld, rows, n, id_offset, cand_v, cand_i, out_v, out_i, st);
-    case 7: return topk_go<7>(z, ld, rows, n, id_offset, cand_v, cand_i, out_v, out_i, st);
-    case 8: return topk_go<8>(z, ld, rows, n, id_offset, cand_v, cand_i, out_v, out_i, st);
+    case 1: return topk_stage2_go<1>(rows, ncand, cand_v, cand_i, out_v, out_i, st);
+    case 2: return topk_stage2_go<2>(rows, ncand, cand_v, cand_i, out_v, out_i, st);
+    case 3: return topk_stage2_go<3>(rows, ncand, cand_v, cand_i, out_v, out_i, st);
+    case 4: return topk_stage2_go<4>(rows, ncand, cand_v, cand_i, out_v, out_i, st);
+    case 5: return topk_stage2_go<5>(rows, ncand, cand_v, cand_i, out_v, out_i, st);
+    case 6: return topk_stage2_go<6>(rows, ncand, cand_v, cand_i, out_v, out_i, st);
+    case 7: return topk_stage2_go<7>(rows, ncand, cand_v, cand_i, out_v, out_i, st);
+    case 8: return topk_stage2_go<8>(rows, ncand, cand_v, cand_i, out_v, out_i, st);
     }
     return hipErrorInvalidValue;
 }

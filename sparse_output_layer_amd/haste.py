@@ -46,8 +46,8 @@ class BceStruct(ctypes.Structure):
     _fields_ = [("row_ptr", ctypes.c_void_p), ("labels", ctypes.c_void_p),
                 ("nnz", ctypes.c_int32), ("reserved0", ctypes.c_int32),
                 ("label_offset", ctypes.c_int64), ("grad_scale", ctypes.c_float),
-                ("reserved1", ctypes.c_int32), ("loss", ctypes.c_void_p),
-                ("topk", ctypes.c_int32), ("reserved2", ctypes.c_int32),
+                ("topk_buckets", ctypes.c_int32), ("loss", ctypes.c_void_p),
+                ("topk", ctypes.c_int32), ("topk_kprime", ctypes.c_int32),
                 ("topk_val", ctypes.c_void_p), ("topk_idx", ctypes.c_void_p)]
 
 
@@ -81,6 +81,8 @@ _SIGS = {
     "haste_tail_group_positives": (ctypes.c_int, [_PD, _PB, _vp, _vp, _vp, _sz, _vp]),
     "haste_tail_validate": (ctypes.c_int, [_PD, _vp, _vp, _vp]),
     "haste_topk_merge": (ctypes.c_int, [_i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "haste_topk_expected_recall": (ctypes.c_double, [_i64, ctypes.c_int, ctypes.c_int, _i64]),
+    "haste_topk_plan": (ctypes.c_int, [_i64, ctypes.c_int, ctypes.c_double, _i64, ctypes.POINTER(_i32)]),
 }
 
 
@@ -146,6 +148,8 @@ class Bce:
     loss: Optional[torch.Tensor] = None   # float32 scalar (1 element), device
     topk_val: Optional[torch.Tensor] = None   # float32 B x K, device: per-row top-K logits
     topk_idx: Optional[torch.Tensor] = None   # int32 B x K, device: their global label ids
+    topk_kprime: int = 0             # 0: exact (K' = K); else K' per bucket, 1 <= K' <= K
+    topk_buckets: int = 0            # 0: buckets of 32768 labels; else buckets per row
 
     def struct(self) -> BceStruct:
         _need(self.row_ptr, "row_ptr", torch.int32)
@@ -171,6 +175,8 @@ class Bce:
             s.topk = int(self.topk_val.shape[1])
             s.topk_val = self.topk_val.data_ptr()
             s.topk_idx = self.topk_idx.data_ptr()
+            s.topk_kprime = int(self.topk_kprime)
+            s.topk_buckets = int(self.topk_buckets)
         return s
 
 
@@ -355,6 +361,22 @@ def haste_tail_validate(idx, D, L, G) -> torch.Tensor:
     out = torch.empty(1, dtype=torch.int32, device=idx.device)
     _check(lib().haste_tail_validate(ctypes.byref(d), _ptr(idx), _ptr(out), _stream()))
     return out
+
+
+def haste_topk_expected_recall(n: int, K: int, kprime: int, buckets: int = 0) -> float:
+    """Expected recall of the two-stage top-K for rows of n logits (host)."""
+    r = lib().haste_topk_expected_recall(int(n), int(K), int(kprime), int(buckets))
+    if r < 0:
+        raise ValueError(f"invalid top-K parameters n={n} K={K} K'={kprime} buckets={buckets}")
+    return r
+
+
+def haste_topk_plan(n: int, K: int, target: float, min_buckets: int = 1):
+    """(K', buckets >= min_buckets) with expected recall >= target and the
+    fewest stage-2 candidates."""
+    out = (_i32 * 2)()
+    _check(lib().haste_topk_plan(int(n), int(K), float(target), int(min_buckets), out))
+    return int(out[0]), int(out[1])
 
 
 def haste_topk_merge(a_val, a_idx, b_val, b_idx):

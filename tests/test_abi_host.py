@@ -20,7 +20,7 @@ def test_exports_every_declared_symbol(L):
     assert "haste_tail_fwd" in names and "haste_tail_step" in names
     missing = [n for n in names if not hasattr(L, n)]
     assert missing == []
-    assert L.haste_abi_version() == 2
+    assert L.haste_abi_version() == 3
     for s in range(5):
         assert L.haste_status_string(s)
 
@@ -112,4 +112,34 @@ def test_head_and_step_argument_errors(L):
     assert L.haste_tail_step(ctypes.byref(d), 0x1000, 0x1000, 0x1000, None, 0x1000, 0x1000, 0,
                              None, 0, None) == H.HASTE_ERR_INVALID       # bce required
     assert L.haste_topk_merge(4, 0, 1, 1, 1, 1, 1, 1, None) == H.HASTE_ERR_INVALID
+    # approximate top-K: K' in [0, K], buckets in [0, 65535]
+    for kp, nbk in ((6, 0), (-1, 0), (2, -1), (2, 70000), (2, 0)):
+        b = H.BceStruct(nnz=5, row_ptr=0x1000, labels=0x1000, topk=5, topk_val=0x1000,
+                        topk_idx=0x1000, topk_kprime=kp, topk_buckets=nbk)
+        assert _status(L, _desc(), bce=ctypes.byref(b)) == H.HASTE_ERR_INVALID, (kp, nbk)
+    b = H.BceStruct(nnz=5, row_ptr=0x1000, labels=0x1000, topk=5, topk_val=0x1000,
+                    topk_idx=0x1000, topk_kprime=2, topk_buckets=64)
+    assert _status(L, _desc(), bce=ctypes.byref(b)) == H.HASTE_ERR_WORKSPACE
     assert L.haste_tail_validate(None, 0x1000, 0x1000, None) == H.HASTE_ERR_INVALID
+
+
+def test_topk_recall_and_plan_match_the_oracle(L):
+    """The library's expected recall and parameter choice (host code) against
+    the oracle's exact-fraction formula and plain search."""
+    import oracle
+    from sparse_output_layer_amd import haste as Hp
+    for n, K, kp, nb in ((1000, 5, 1, 50), (3000, 8, 3, 7), (70000, 5, 2, 1), (40, 6, 2, 13),
+                         (5, 8, 2, 2), (123457, 4, 1, 999)):
+        got = Hp.haste_topk_expected_recall(n, K, kp, nb)
+        want = float(oracle.topk_expected_recall(n, K, kp, oracle.topk_seg_len(n, nb)))
+        assert abs(got - want) <= 1e-12 * max(1.0, want), (n, K, kp, nb, got, want)
+    for n, K, target, bmin in ((500, 5, 0.9, 10), (800, 4, 0.97, 30), (300, 8, 0.8, 1), (2000, 5, 0.99, 64)):
+        assert Hp.haste_topk_plan(n, K, target, bmin) == oracle.topk_plan(n, K, target, bmin), \
+            (n, K, target, bmin)
+    assert L.haste_topk_expected_recall(10, 9, 1, 0) < 0
+    assert L.haste_topk_expected_recall(10, 5, 6, 1) < 0
+    assert L.haste_topk_expected_recall(10, 5, 2, 0) < 0
+    out = (ctypes.c_int32 * 2)()
+    assert L.haste_topk_plan(100, 5, 1.5, 1, out) == H.HASTE_ERR_INVALID
+    assert L.haste_topk_plan(100, 5, 0.9, 0, out) == H.HASTE_ERR_INVALID
+    assert L.haste_topk_plan(100, 5, 0.9, 101, out) == H.HASTE_ERR_INVALID

@@ -7,7 +7,7 @@ import torch
 
 import oracle
 import workloads as wl
-from _gpu import DEV, Dev, check_topk
+from _gpu import DEV, Dev, check_topk, topk_tol
 
 pytestmark = pytest.mark.gpu
 
@@ -91,3 +91,95 @@ def test_topk(H, case):
     torch.cuda.synchronize()
     check_topk("merged", mv.cpu().numpy(), mi.cpu().numpy(), np.concatenate([Zh, Zt], axis=1),
                np.concatenate([Zha, Zta], axis=1), K, dt, id0=0)
+
+
+APPROX = [
+    # tail: (K, K', buckets); head last
+    dict(B=24, D=128, H=64, L=70000, G=64, F=64, K=5, KP=2, NB=7),
+    dict(B=20, D=96, H=48, L=1000, G=16, F=32, K=8, KP=1, NB=50),
+    dict(B=16, D=96, H=48, L=600, G=32, F=64, K=5, KP=5, NB=3),      # exact on custom buckets
+    dict(B=12, D=64, H=64, L=300, G=16, F=32, K=4, KP=2, NB=4, head=True),
+]
+
+
+def _check_two_stage(name, got_v, got_i, z, zabs, K, kp, seg, dtype, id0, nterms):
+    """Against the oracle's two-stage top-K (top-K page, "Method") on the same
+    buckets.  Ranks are decided with the fp32 summation bound of the kernels'
+    logits (the same bf16 inputs, fp32 accumulation of nterms products):
+    t = 2 * nterms * 2^-24 * sum|x w| per logit.  Where a bucket's K'-th and
+    (K'+1)-th oracle logits lie within their two bounds, the kernels may pick
+    either: such rows are checked for validity only.  Returns the number of
+    rows compared by id."""
+    rows, N = z.shape
+    u = 2.0 ** -24
+    ov, oi = oracle.topk_two_stage(z, K, kp, seg, id_offset=id0)
+    vtol = topk_tol(zabs.max(axis=1), dtype)
+
+    def rt(b, ids):            # rank tolerance of the logits of these ids in row b
+        return 2 * nterms * u * zabs[b, np.asarray(ids) - id0]
+
+    amb = np.zeros(rows, bool)
+    surv = 0
+    for c0 in range(0, N, seg):
+        c1 = min(c0 + seg, N)
+        surv += min(kp, c1 - c0)
+        if c1 - c0 > kp:
+            bv, bi = oracle.topk(z[:, c0:c1], kp + 1, id_offset=id0 + c0)
+            for b in range(rows):
+                t2 = rt(b, bi[b, kp - 1:kp + 1])
+                amb[b] |= bv[b, kp - 1] - bv[b, kp] <= t2.sum()
+    n = min(K, surv)
+    got_v = np.asarray(got_v, np.float64)
+    got_i = np.asarray(got_i, np.int64)
+    for b in range(rows):
+        ids = got_i[b]
+        assert np.all(ids[:n] >= id0) and np.all(ids[:n] < id0 + N), f"{name}: row {b}: {ids}"
+        assert np.all(ids[n:] == -1) and np.all(np.isneginf(got_v[b, n:])), f"{name}: row {b} padding"
+        assert len(set(ids[:n].tolist())) == n, f"{name}: row {b} repeats an id"
+        for k in range(n):
+            assert abs(got_v[b, k] - z[b, ids[k] - id0]) <= vtol[b], f"{name}: row {b} pos {k} value"
+            if k:
+                assert got_v[b, k] <= got_v[b, k - 1], f"{name}: row {b} not descending"
+        if amb[b]:
+            continue
+        m = min(n + 1, ov.shape[1])
+        valid = oi[b, :m] >= 0
+        tk = np.zeros(m)
+        tk[valid] = rt(b, oi[b, :m][valid])
+        for k in range(n):
+            assert abs(got_v[b, k] - ov[b, k]) <= vtol[b], f"{name}: row {b} pos {k}: {got_v[b, k]} vs {ov[b, k]}"
+            sep_hi = k == 0 or ov[b, k - 1] - ov[b, k] > tk[k - 1] + tk[k]
+            sep_lo = k + 1 >= m or not valid[k + 1] or ov[b, k] - ov[b, k + 1] > tk[k] + tk[k + 1]
+            if sep_hi and sep_lo:
+                assert ids[k] == oi[b, k], f"{name}: row {b} pos {k}: id {ids[k]} vs oracle {oi[b, k]}"
+    return int((~amb).sum())
+
+
+@pytest.mark.parametrize("case", APPROX, ids=[
+    "B{B}-L{L}-K{K}-Kp{KP}-nb{NB}".format(**c) + ("-head" if c.get("head") else "") for c in APPROX])
+def test_topk_two_stage(H, case):
+    print("case", case, flush=True)
+    case = dict(case)
+    K, KP, NB, head = case.pop("K"), case.pop("KP"), case.pop("NB"), case.pop("head", False)
+    inp = wl.make_inputs(wl.tiny("tk2", **case))
+    c = inp.cfg
+    d = Dev(inp)
+    X, Wt, Wh = inp.X_f64(), inp.W_f64(), inp.Wh_f64()
+    tv = torch.full((c.B, K), 7.0, dtype=torch.float32, device=DEV)
+    ti = torch.full((c.B, K), 7, dtype=torch.int32, device=DEV)
+    b = d.bce(0 if head else c.H, 1.0 / c.B)
+    b.topk_val, b.topk_idx, b.topk_kprime, b.topk_buckets = tv, ti, KP, NB
+    if head:
+        z, za = oracle.head_logits(X, Wh, want_abs=True)
+        H.haste_head_fwd(d.X, d.Wh, bce=b)
+        n, id0, nterms = c.H, 0, c.D
+    else:
+        z, za = oracle.tail_logits(X, inp.idx, Wt, c.L, c.G, want_abs=True)
+        H.haste_tail_fwd(d.X, d.idx, d.W, c.L, c.G, bce=b)
+        n, id0, nterms = c.L, c.H, c.F
+    torch.cuda.synchronize()
+    seg = oracle.topk_seg_len(n, NB)
+    done = _check_two_stage("two-stage", tv.cpu().numpy(), ti.cpu().numpy(), z, za, K, KP, seg,
+                            c.dtype, id0, nterms)
+    print(f"rows compared by id: {done} of {c.B}", flush=True)
+    assert done >= c.B // 2

@@ -279,6 +279,70 @@ def test_p6_topk_brute_force_and_two_stage_merge():
             assert np.array_equal(i2[0], ids[r])
 
 
+def test_p6_two_stage_approximate_topk_brute_force():
+    """The approximate two-stage top-K (top-K page, section "Method": top-K'
+    per bucket of consecutive ids, K' < K, then the top-K of the survivors)
+    equals the top-K, found by a full lexicographic sort, of the set of items
+    whose rank inside their own bucket is below K'.  A hand case: the top
+    five all in the first of two buckets with K' = 2 keeps two of them, the
+    other bucket gives its two, and the fifth place stays empty."""
+    rng = np.random.default_rng(5)
+    z = np.round(rng.standard_normal((6, 300)) * 3) / 3      # ties
+    for K, kp, seg in ((5, 2, 37), (8, 1, 16), (4, 4, 300), (6, 3, 1000), (3, 1, 1)):
+        val, ids = oracle.topk_two_stage(z, K, kp, seg, id_offset=7)
+        for r in range(z.shape[0]):
+            keep = []
+            for c0 in range(0, 300, seg):
+                cols = np.arange(c0, min(c0 + seg, 300))
+                order = cols[np.lexsort((cols, -z[r, cols]))]
+                keep.extend(order[:kp].tolist())
+            keep = np.array(keep)
+            best = keep[np.lexsort((keep, -z[r, keep]))][:K]
+            n = best.size
+            assert np.array_equal(ids[r, :n], best + 7), (K, kp, seg, r)
+            assert np.array_equal(val[r, :n], z[r, best])
+            assert np.all(ids[r, n:K] == -1) and np.all(np.isneginf(val[r, n:K]))
+    z = np.array([[9.0, 8.0, 7.0, 6.0, 5.0, 1.0, 0.5, 0.4, 0.3, 0.2]])
+    val, ids = oracle.topk_two_stage(z, 5, 2, 5)
+    assert ids[0, :5].tolist() == [0, 1, 5, 6, -1]
+    assert val[0, :4].tolist() == [9.0, 8.0, 1.0, 0.5] and np.isneginf(val[0, 4])
+
+
+def test_p6_expected_recall_exhaustive_and_closed_forms():
+    """Expected recall of the two-stage top-K (top-K page, section
+    "Theoretical analysis": hypergeometric placement of the top-K in the
+    buckets) equals, exactly, the average over every placement of the K
+    largest items on n positions, found by enumeration; K' = K and buckets
+    of one item give 1, one bucket gives K'/K; a Monte Carlo estimate at a
+    larger n agrees within four standard errors."""
+    from fractions import Fraction
+    from itertools import combinations
+    for n, K, kp, seg in ((9, 3, 1, 3), (9, 3, 2, 4), (10, 4, 1, 3), (8, 5, 2, 3), (7, 2, 1, 7), (6, 8, 2, 4)):
+        Kt = min(K, n)
+        tot, cnt = Fraction(0), 0
+        for pos in combinations(range(n), Kt):
+            per = {}
+            for p_ in pos:
+                per[p_ // seg] = per.get(p_ // seg, 0) + 1
+            tot += Fraction(sum(min(c, kp) for c in per.values()), Kt)
+            cnt += 1
+        assert oracle.topk_expected_recall(n, K, kp, seg) == tot / cnt, (n, K, kp, seg)
+    for n, K in ((1000, 5), (77, 8), (33, 1)):
+        assert oracle.topk_expected_recall(n, K, K, 50) == 1
+        assert oracle.topk_expected_recall(n, K, 1, 1) == 1
+        assert oracle.topk_expected_recall(n, K, 1, n) == Fraction(1, K)
+        assert oracle.topk_expected_recall(n, K, min(2, K), n) == Fraction(min(2, K), K)
+    rng = np.random.default_rng(9)
+    n, K, kp, seg, trials = 2000, 6, 2, 128, 20000
+    rec = np.empty(trials)
+    for i in range(trials):
+        pos = rng.choice(n, K, replace=False)
+        cnt = np.bincount(pos // seg)
+        rec[i] = np.minimum(cnt, kp).sum() / K
+    exact = float(oracle.topk_expected_recall(n, K, kp, seg))
+    assert abs(rec.mean() - exact) < 4 * rec.std() / np.sqrt(trials) + 1e-12, (rec.mean(), exact)
+
+
 # --------------------------------------------------------------------- P7
 def test_p7_group_positives_brute_force():
     inp = wl.make_inputs("c1", L=203, G=16, pos_per_row=9)
