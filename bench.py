@@ -41,9 +41,11 @@ def parse():
     p.add_argument("--calib-mib", type=int, default=0,
                    help="after timing, one device-to-device copy of this many MiB: the "
                         "known-size reference for the FETCH_SIZE / WRITE_SIZE counters")
-    p.add_argument("--mode", choices=["train", "infer"], default="train",
+    p.add_argument("--mode", choices=["train", "infer", "dense", "sgd"], default="train",
                    help="train: the training step (default); infer: head + tail forward "
-                        "with a per-row top-K, exact and approximate")
+                        "with a per-row top-K, exact and approximate; dense: the tail next "
+                        "to a FLOPs-matched dense bottleneck layer; sgd: the tail step with "
+                        "its SGD update fused into the dW pass, next to step + update")
     p.add_argument("--topk", type=int, default=5, help="K of the inference mode")
     p.add_argument("--recall", type=float, default=0.95,
                    help="recall target of the approximate top-K in the inference mode")
@@ -242,6 +244,138 @@ def run_infer(args, cfg, inp, t_gen):
     print(json.dumps(res), flush=True)
 
 
+def run_dense(args, cfg, inp, t_gen):
+    """The tail (group-shared fixed fan-in, F indices per group) next to a
+    FLOPs-matched dense bottleneck: a dense layer from F inputs to the same L
+    labels, (B x F) . (F x L), with the same sigmoid-BCE over the same
+    positives, forward and training step (logits, dW, dX), on the dense
+    kernels of this library (the head's GEMMs with D = F, H = L).  Inputs of
+    the bottleneck: x ~ N(0, 1), W ~ N(0, 0.02), bf16."""
+    import numpy as np
+    import torch
+
+    from sparse_output_layer_amd import haste as H
+    dev = "cuda:0"
+    g = torch.Generator(device="cpu").manual_seed(1)
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    X, W = bf(inp.X), bf(inp.W)
+    idx = torch.from_numpy(inp.idx).to(dev)
+    rp = torch.from_numpy(inp.row_ptr).to(dev)
+    lab = torch.from_numpy(inp.labels).to(dev)
+    B, D, L, G, F = cfg.B, cfg.D, cfg.L, cfg.G, cfg.F
+    s = 1.0 / B
+    Xb = torch.randn(B, F, generator=g).to(torch.bfloat16).to(dev)
+    Wb = (torch.randn(L, F, generator=g) * 0.02).to(torch.bfloat16).to(dev)
+    loss = torch.zeros(1, dtype=torch.float32, device=dev)
+    bt = H.Bce(rp, lab, cfg.H, s, loss)
+    ws_t = torch.empty(H.haste_tail_workspace_bytes(X, idx, L, G, bt), dtype=torch.uint8, device=dev)
+    ws_d = torch.empty(H.haste_head_workspace_bytes(Xb, Wb, bt), dtype=torch.uint8, device=dev)
+    dW, dX = torch.empty_like(W), torch.empty(B, D, dtype=torch.float32, device=dev)
+    dWb, dXb = torch.empty_like(Wb), torch.empty(B, F, dtype=torch.float32, device=dev)
+    calls = {
+        "sparse_fwd": lambda: H.haste_tail_fwd(X, idx, W, L, G, bce=bt, workspace=ws_t),
+        "dense_fwd": lambda: H.haste_head_fwd(Xb, Wb, bce=bt, workspace=ws_d),
+        "sparse_step": lambda: (H.haste_tail_prepare(X, idx, L, G, bt, ws_t),
+                                H.haste_tail_step_dw(X, idx, W, L, G, bt, dW, ws_t),
+                                H.haste_tail_step_dx(X, idx, W, L, G, bt, dX, ws_t)),
+        "dense_step": lambda: H.haste_head_step(Xb, Wb, bt, dWb, dXb, workspace=ws_d),
+    }
+    res = {}
+    for name, fn in calls.items():
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(args.steps):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        res[name] = t0.elapsed_time(t1) / args.steps * 1e3     # microseconds
+    fl_fwd, fl_step = 2 * B * F * L, 6 * B * F * L
+    out = {
+        "metric": "tail (G=%d shared fan-in) vs FLOPs-matched dense bottleneck (B x F)(F x L), "
+                  "fwd and training step at %s" % (G, cfg.name),
+        "unit": "us",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "higher_is_better": False, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: B={B} D={D} L={L} G={G} F={F}; dense bottleneck "
+                               f"x: B x F, W: L x F", "global_batch": B, "parallelism": "single GPU"},
+        "us": {k: round(v, 2) for k, v in res.items()},
+        "tflops": {k: round((fl_fwd if "fwd" in k else fl_step) / (v * 1e-6) / 1e12, 1)
+                   for k, v in res.items()},
+        "sparse_over_dense_time": {"fwd": round(res["sparse_fwd"] / res["dense_fwd"], 3),
+                                   "step": round(res["sparse_step"] / res["dense_step"], 3)},
+        "gen_s": round(t_gen, 2),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def run_sgd(args, cfg, inp, t_gen):
+    """Tail training step plus an SGD update of W: unfused (the step writes
+    dW, then W' = W - lr dW in a second pass) and fused (the dW pass writes
+    W' directly into a second buffer; the buffers swap every step)."""
+    import numpy as np
+    import torch
+
+    from sparse_output_layer_amd import haste as H
+    dev = "cuda:0"
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    X, W = bf(inp.X), bf(inp.W)
+    idx = torch.from_numpy(inp.idx).to(dev)
+    rp = torch.from_numpy(inp.row_ptr).to(dev)
+    lab = torch.from_numpy(inp.labels).to(dev)
+    B, D, L, G = cfg.B, cfg.D, cfg.L, cfg.G
+    lr = 1e-3
+    loss = torch.zeros(1, dtype=torch.float32, device=dev)
+    bt = H.Bce(rp, lab, cfg.H, 1.0 / B, loss)
+    ws = torch.empty(H.haste_tail_workspace_bytes(X, idx, L, G, bt), dtype=torch.uint8, device=dev)
+    dX = torch.empty(B, D, dtype=torch.float32, device=dev)
+    dW = torch.empty_like(W)
+    bufs = [W.clone(), W.clone()]
+    state = {"k": 0}
+
+    def unfused():
+        H.haste_tail_step(X, idx, bufs[0], L, G, bt, dW, dX, workspace=ws)
+        H.haste_sgd_update(bufs[0], dW, lr)             # in place
+
+    def fused():
+        k = state["k"]
+        H.haste_tail_step_sgd(X, idx, bufs[k], L, G, bt, lr, bufs[1 - k], dX, workspace=ws)
+        state["k"] = 1 - k
+
+    res = {}
+    for name, fn in (("step_then_update", unfused), ("fused_step", fused)):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(args.steps):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        res[name] = t0.elapsed_time(t1) / args.steps * 1e3
+    out = {
+        "metric": "tail step + SGD update of W at %s, unfused vs fused into the dW pass" % cfg.name,
+        "unit": "us", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "higher_is_better": False, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: B={B} D={D} L={L} G={G} F={cfg.F}, lr={lr}",
+                   "global_batch": B, "parallelism": "single GPU"},
+        "us": {k: round(v, 2) for k, v in res.items()},
+        "samples_per_s": {k: round(B / (v * 1e-6), 1) for k, v in res.items()},
+        "fused_speedup": round(res["step_then_update"] / res["fused_step"], 3),
+        "gen_s": round(t_gen, 2),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -266,6 +400,10 @@ def main():
     assert cfg.dtype == "bf16"
     if args.mode == "infer":
         return run_infer(args, cfg, inp, t_gen)
+    if args.mode == "dense":
+        return run_dense(args, cfg, inp, t_gen)
+    if args.mode == "sgd":
+        return run_sgd(args, cfg, inp, t_gen)
 
     def bf(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)

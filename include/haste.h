@@ -212,6 +212,29 @@ haste_status haste_tail_step(const haste_tail_desc *d, const void *X,
                              int accumulate_dX, void *ws, size_t ws_bytes,
                              void *stream);
 
+/* Fused tail training step with the optimizer update in the dW pass's
+ * epilogue (plain SGD, no momentum; the pages name no optimizer): as
+ * haste_tail_step, but instead of dW it writes W_out = W - lr * dW, where
+ * dW is rounded to bf16 as haste_tail_step would store it and the update is
+ * one fp32 fma rounded to bf16 -- bit for bit what haste_sgd_update gives
+ * after haste_tail_step, without the dW write and the second pass.  dX is
+ * computed with the old W, so W_out must not overlap W (swap the two
+ * buffers between steps); HASTE_ERR_INVALID if it does.  bf16 only (fp32:
+ * HASTE_ERR_UNSUPPORTED).  Caller-owned W_out, 16-byte aligned, same shape
+ * as W; padded rows get W's values. */
+haste_status haste_tail_step_sgd(const haste_tail_desc *d, const void *X,
+                                 const int32_t *idx, const void *W,
+                                 const haste_bce *bce, float lr, void *W_out,
+                                 float *dX, int accumulate_dX, void *ws,
+                                 size_t ws_bytes, void *stream);
+
+/* SGD update after a step (the unfused form): W_out[i] = W[i] - lr * dW[i]
+ * for n elements of dtype (bf16: fp32 fma of the bf16 values, rounded to
+ * bf16).  W_out may equal W (in place).  Asynchronous on `stream`. */
+haste_status haste_sgd_update(int64_t n, int32_t dtype, const void *W,
+                              const void *dW, float lr, void *W_out,
+                              void *stream);
+
 /* Split form of haste_tail_step, for callers that time or overlap its
  * parts.  haste_tail_prepare writes into ws the transposed X and the
  * group-major positives.  haste_tail_step_dw (one kernel) then adds the

@@ -370,3 +370,10 @@ def step(X, Wh, idx, Wt, row_ptr, labels, L, G, s=None) -> StepResult:
                       dX_tail=dXt, dX_tail_abs=dXta, dX_head=dXh,
                       dX_head_abs=dXha, loss_head=float(lh.sum()),
                       loss_tail=float(lt.sum()))
+
+
+def sgd(W, dW, lr):
+    """Plain gradient-descent update after a step, W - lr * dW (fp64).  The
+    pages name no optimizer; this is the textbook step the fused update
+    implements."""
+    return _c(W, np.float64) - lr * _c(dW, np.float64)

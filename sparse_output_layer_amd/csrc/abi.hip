@@ -449,6 +449,56 @@ haste_status haste_tail_step(const haste_tail_desc *d, const void *X, const int3
     return HASTE_OK;
 }
 
+haste_status haste_tail_step_sgd(const haste_tail_desc *d, const void *X, const int32_t *idx,
+                                 const void *W, const haste_bce *bce, float lr, void *W_out,
+                                 float *dX, int accumulate_dX, void *ws, size_t ws_bytes,
+                                 void *stream) {
+    g_err.clear();
+    TRY(tail_common(d, X, idx, W));
+    TRY(need(bce, "bce"));
+    TRY(check_bce(bce, d->B, true));
+    TRY(need_al(W_out, 16, "W_out"));
+    TRY(need_al(dX, 4, "dX"));
+    if (d->dtype != HASTE_BF16)
+        return fail(HASTE_ERR_UNSUPPORTED, "the fused SGD step is a bf16 path; fp32 takes "
+                                           "haste_tail_step + haste_sgd_update");
+    if (!(lr == lr)) return fail(HASTE_ERR_INVALID, "lr is NaN");
+    const size_t wbytes = (size_t)n_groups(d) * d->G * d->F * 2;
+    const char *w0 = (const char *)W, *o0 = (const char *)W_out;
+    if (o0 < w0 + wbytes && w0 < o0 + wbytes)
+        return fail(HASTE_ERR_INVALID, "W_out overlaps W (the dX pass reads W after the update is written)");
+    const TailWs m = tail_ws(d, bce);
+    TRY(check_ws(ws, ws_bytes, m.total));
+    hipStream_t st = S(stream);
+    TRY(zero_dx(dX, d->B, d->D, accumulate_dX, st));
+    TRY(bf16_prep(d, X, bce, ws, m, st));
+    TailArgs a = tail_args(d, X, idx, W, ws, m);
+    a.Wout = (unsigned short *)W_out;
+    a.lr = lr;
+    a.dX = dX;
+    a.s = bce->grad_scale;
+    a.loss = bce->loss;
+    TRY(feature_order(d, idx, ws, m, st));
+    TRY_HIP(launch_tail_t1(T1_DW_BCE, d->G, a, false, bce->loss != nullptr, st), "tail SGD step dW");
+    if (m.has_topk) TRY(run_topk(bce, a.Z32, d->B, d->L, ws, m.cand, st));
+    TRY_HIP(launch_tail_t2(d->G, a.dzt ? 2 : 0, a, st), "tail SGD step dX");
+    return HASTE_OK;
+}
+
+haste_status haste_sgd_update(int64_t n, int32_t dtype, const void *W, const void *dW, float lr,
+                              void *W_out, void *stream) {
+    g_err.clear();
+    if (n < 0) return fail(HASTE_ERR_INVALID, "n < 0");
+    if (dtype != HASTE_BF16 && dtype != HASTE_F32) return fail(HASTE_ERR_INVALID, "dtype %d", dtype);
+    if (n == 0) return HASTE_OK;
+    const size_t es = dtype == HASTE_BF16 ? 2 : 4;
+    TRY(need_al(W, es, "W"));
+    TRY(need_al(dW, es, "dW"));
+    TRY(need_al(W_out, es, "W_out"));
+    TRY_HIP(launch_sgd(W, dW, lr, W_out, n, dtype == HASTE_BF16, S(stream)), "SGD update");
+    return HASTE_OK;
+}
+
 haste_status haste_tail_prepare(const haste_tail_desc *d, const void *X, const haste_bce *bce,
                                 void *ws, size_t ws_bytes, void *stream) {
     g_err.clear();

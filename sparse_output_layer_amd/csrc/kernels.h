@@ -20,7 +20,9 @@ struct TailArgs {
     const unsigned char *perm;   // Ng x F: that order's feature per position
     unsigned short *dzt;         // dz tiles of the dW pass for the dX pass, or null:
                                  // Ng x (Bp/32) x (G/16) tiles of 1 KB (32 rows x 16 labels)
-    unsigned short *dW;          // (Ng*G) x F bf16
+    unsigned short *dW;          // (Ng*G) x F bf16, or null when Wout is set
+    unsigned short *Wout;        // (Ng*G) x F bf16: W - lr * dW (fused SGD), or null
+    float lr;                    // SGD step of Wout
     float *dX;                   // B x D fp32 (atomically accumulated)
     const int32_t *grp_ptr;      // Ng + 1 group-major positives
     const int32_t *grp_ent;      // entries b*G + j
@@ -36,6 +38,9 @@ enum T1Mode { T1_FWD = 0, T1_DW_BCE = 1, T1_DW_MEM = 2 };
 hipError_t launch_transpose_x(const unsigned short *X, unsigned short *XT,
                               int B, int D, int Bp, hipStream_t st);
 hipError_t launch_fill_u32(void *p, uint32_t v, size_t n, hipStream_t st);
+// out = W - lr * dW elementwise (bf16 or fp32 by `bf16`), n elements
+hipError_t launch_sgd(const void *W, const void *dW, float lr, void *out, int64_t n, bool bf16,
+                      hipStream_t st);
 hipError_t launch_feature_order(const int32_t *idx, int64_t Ng, int F, unsigned short *idxp,
                                 unsigned char *perm, hipStream_t st);
 hipError_t launch_group_positives(const int32_t *row_ptr, const int32_t *labels,

@@ -205,6 +205,30 @@ __global__ void k_fill_u32(uint32_t *p, uint32_t v, size_t n) {
     for (; i < n; i += stride) p[i] = v;
 }
 
+// SGD update after a step: out = fma(-lr, dW, W) (bf16: both read as bf16,
+// one fp32 fma, one rounding to bf16)
+__global__ void k_sgd(const void *W, const void *dW, float lr, void *out, int64_t n, int bf16) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += stride) {
+        if (bf16) {
+            const float w = __uint_as_float((unsigned)((const unsigned short *)W)[i] << 16);
+            const float g = __uint_as_float((unsigned)((const unsigned short *)dW)[i] << 16);
+            ((unsigned short *)out)[i] = f32_to_bf16(__builtin_fmaf(-lr, g, w));
+        } else {
+            ((float *)out)[i] = __builtin_fmaf(-lr, ((const float *)dW)[i], ((const float *)W)[i]);
+        }
+    }
+}
+
+hipError_t launch_sgd(const void *W, const void *dW, float lr, void *out, int64_t n, bool bf16,
+                      hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    hipLaunchKernelGGL(k_sgd, dim3((unsigned)blocks), dim3(256), 0, st, W, dW, lr, out, n, (int)bf16);
+    return hipGetLastError();
+}
+
 hipError_t launch_fill_u32(void *p, uint32_t v, size_t n, hipStream_t st) {
     if (n == 0) return hipSuccess;
     size_t blocks = (n + 255) / 256;
@@ -701,7 +725,22 @@ __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, int store_z,
                 for (int i = 0; i < WPL; ++i) {
                     const int pc16 = 64 * i + lane;
                     const u32x4 v = *(const u32x4 *)(ws + (pc16 / (F / 8)) * WSP + 8 * (pc16 % (F / 8)));
-                    *(u32x4 *)(a.dW + g * G * (int64_t)F + 8 * pc16) = v;
+                    const int64_t o = g * G * (int64_t)F + 8 * pc16;
+                    if (!a.Wout) {
+                        *(u32x4 *)(a.dW + o) = v;
+                    } else {
+                        // fused SGD: Wout = fma(-lr, dW, W) with dW as it would be
+                        // stored (bf16): the same arithmetic as k_sgd after a step
+                        const u32x4 w = *(const u32x4 *)(a.W + o);
+                        u32x4 r;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float w0 = __uint_as_float(w[e] << 16), w1 = __uint_as_float(w[e] & 0xffff0000u);
+                            const float g0 = __uint_as_float(v[e] << 16), g1 = __uint_as_float(v[e] & 0xffff0000u);
+                            r[e] = pack_bf16x2(__builtin_fmaf(-a.lr, g0, w0), __builtin_fmaf(-a.lr, g1, w1));
+                        }
+                        *(u32x4 *)(a.Wout + o) = r;
+                    }
                 }
             }
         }

@@ -69,6 +69,9 @@ _SIGS = {
                                       _vp, _sz, _vp]),
     "haste_tail_step": (ctypes.c_int, [_PD, _vp, _vp, _vp, _PB, _vp, _vp, ctypes.c_int, _vp,
                                        _sz, _vp]),
+    "haste_tail_step_sgd": (ctypes.c_int, [_PD, _vp, _vp, _vp, _PB, ctypes.c_float, _vp, _vp,
+                                           ctypes.c_int, _vp, _sz, _vp]),
+    "haste_sgd_update": (ctypes.c_int, [_i64, _i32, _vp, _vp, ctypes.c_float, _vp, _vp]),
     "haste_tail_prepare": (ctypes.c_int, [_PD, _vp, _PB, _vp, _sz, _vp]),
     "haste_tail_step_dw": (ctypes.c_int, [_PD, _vp, _vp, _vp, _PB, _vp, _vp, _sz, _vp]),
     "haste_tail_step_dx": (ctypes.c_int, [_PD, _vp, _vp, _vp, _PB, _vp, ctypes.c_int, _vp,
@@ -268,6 +271,34 @@ def haste_tail_step(X, idx, W, L, G, bce: Bce, dW, dX, accumulate_dX=False, work
     ws, nb = _workspace(lib().haste_tail_workspace_bytes(ctypes.byref(d), b), X.device, workspace)
     _check(lib().haste_tail_step(ctypes.byref(d), _ptr(X), _ptr(idx), _ptr(W), b, _ptr(dW),
                                  _ptr(dX), int(bool(accumulate_dX)), _ptr(ws), nb, _stream()))
+
+
+def haste_tail_step_sgd(X, idx, W, L, G, bce: Bce, lr, W_out, dX, accumulate_dX=False,
+                        workspace=None, lean=False):
+    """Training step with the SGD update fused into the dW pass: writes
+    W_out = W - lr * dW (W_out must not overlap W) instead of dW."""
+    _tail_in(X, idx, W)
+    _need(W_out, "W_out", X.dtype)
+    if W_out.shape != W.shape:
+        raise ValueError("W_out must have W's shape")
+    _need(dX, "dX", torch.float32)
+    d = tail_desc(X, idx, L, G, lean)
+    b = _bref(bce)
+    ws, nb = _workspace(lib().haste_tail_workspace_bytes(ctypes.byref(d), b), X.device, workspace)
+    _check(lib().haste_tail_step_sgd(ctypes.byref(d), _ptr(X), _ptr(idx), _ptr(W), b, float(lr),
+                                     _ptr(W_out), _ptr(dX), int(bool(accumulate_dX)), _ptr(ws), nb,
+                                     _stream()))
+
+
+def haste_sgd_update(W, dW, lr, W_out=None):
+    """W_out = W - lr * dW elementwise (W_out defaults to W: in place)."""
+    W_out = W if W_out is None else W_out
+    for t_, n in ((W, "W"), (dW, "dW"), (W_out, "W_out")):
+        _need(t_, n, W.dtype)
+    if dW.shape != W.shape or W_out.shape != W.shape:
+        raise ValueError("W, dW and W_out must have one shape")
+    dt = HASTE_BF16 if W.dtype == torch.bfloat16 else HASTE_F32
+    _check(lib().haste_sgd_update(W.numel(), dt, _ptr(W), _ptr(dW), float(lr), _ptr(W_out), _stream()))
 
 
 def haste_tail_prepare(X, idx, L, G, bce: Bce, workspace: torch.Tensor, lean=False):

@@ -143,3 +143,28 @@ def test_topk_recall_and_plan_match_the_oracle(L):
     assert L.haste_topk_plan(100, 5, 1.5, 1, out) == H.HASTE_ERR_INVALID
     assert L.haste_topk_plan(100, 5, 0.9, 0, out) == H.HASTE_ERR_INVALID
     assert L.haste_topk_plan(100, 5, 0.9, 101, out) == H.HASTE_ERR_INVALID
+
+
+def test_sgd_entry_points_reject_bad_arguments(L):
+    """Argument checks of the fused SGD step and the SGD update (all return
+    before any GPU work)."""
+    d = _desc()
+    b = H.BceStruct(nnz=5, row_ptr=0x1000, labels=0x1000)
+    f, vp = ctypes.c_float, ctypes.c_void_p
+    # W_out missing, overlapping W, or the fp32 dtype
+    assert L.haste_tail_step_sgd(ctypes.byref(d), vp(0x1000), vp(0x1000), vp(0x2000), ctypes.byref(b),
+                                 f(0.1), None, vp(0x1000), 0, vp(0x1000), 1 << 30, None) == H.HASTE_ERR_INVALID
+    assert L.haste_tail_step_sgd(ctypes.byref(d), vp(0x1000), vp(0x1000), vp(0x2000), ctypes.byref(b),
+                                 f(0.1), vp(0x2010), vp(0x1000), 0, vp(0x1000), 1 << 30, None) == H.HASTE_ERR_INVALID
+    d32 = _desc(dtype=H.HASTE_F32)
+    assert L.haste_tail_step_sgd(ctypes.byref(d32), vp(0x1000), vp(0x1000), vp(0x2000), ctypes.byref(b),
+                                 f(0.1), vp(1 << 40), vp(0x1000), 0, vp(0x1000), 1 << 30, None) == \
+        H.HASTE_ERR_UNSUPPORTED
+    assert L.haste_tail_step_sgd(ctypes.byref(d), vp(0x1000), vp(0x1000), vp(0x2000), None,
+                                 f(0.1), vp(1 << 40), vp(0x1000), 0, vp(0x1000), 1 << 30, None) == H.HASTE_ERR_INVALID
+    assert L.haste_sgd_update(-1, H.HASTE_BF16, vp(0x1000), vp(0x1000), f(0.1), vp(0x1000), None) == \
+        H.HASTE_ERR_INVALID
+    assert L.haste_sgd_update(8, 7, vp(0x1000), vp(0x1000), f(0.1), vp(0x1000), None) == H.HASTE_ERR_INVALID
+    assert L.haste_sgd_update(8, H.HASTE_F32, vp(0x1001), vp(0x1000), f(0.1), vp(0x1000), None) == \
+        H.HASTE_ERR_INVALID
+    assert L.haste_sgd_update(0, H.HASTE_BF16, None, None, f(0.1), None, None) == H.HASTE_OK

@@ -10,7 +10,7 @@ import torch
 
 import oracle
 import workloads as wl
-from _gpu import DEV, Dev, check, check_loss, dev_array, to_f64
+from _gpu import DEV, TOL_BF16, Dev, check, check_loss, dev_array, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -108,6 +108,30 @@ def test_bf16_tail_and_head(H, case):
         assert torch.equal(dW5, dW)
         check(f"split step dX (lean={lean})", to_f64(dX5) - 2.0, r.dX_tail, r.dX_tail_abs, "bf16",
               nterms=ng * c.G)
+
+    # fused SGD step: W_out = W - lr * dW, bit for bit the update after the
+    # step; against the oracle's W - lr * dW within one bf16 rounding plus
+    # lr times the dW tolerance; dX and the loss as the plain step
+    lr = 0.5
+    Wo = torch.full_like(d.W, 9.0)
+    dX7 = torch.empty_like(dX)
+    b7 = d.bce(c.H, s)
+    H.haste_tail_step_sgd(d.X, d.idx, d.W, c.L, c.G, b7, lr, Wo, dX7)
+    Wu = torch.empty_like(d.W)
+    H.haste_sgd_update(d.W, dW, lr, Wu)
+    torch.cuda.synchronize()
+    assert torch.equal(Wo, Wu), "fused and unfused SGD updates differ"
+    check_loss("SGD step loss", b7.loss.item(), r.loss_tail, "bf16")
+    check("SGD step dX", to_f64(dX7), r.dX_tail, r.dX_tail_abs, "bf16", nterms=ng * c.G)
+    Wt64 = inp.W_f64()
+    ref = oracle.sgd(Wt64[:c.L], r.dWt, lr)
+    got = to_f64(Wo[:c.L])
+    # W_out's bf16 rounding, plus lr times (dW's tolerance + dW's bf16 rounding)
+    bound = 2.0 ** -8 * np.abs(ref) + lr * (TOL_BF16[0] * r.dWt_abs + TOL_BF16[1] +
+                                           2.0 ** -8 * np.abs(r.dWt)) + 1e-30
+    bad = np.abs(got - ref) > bound
+    assert not bad.any(), f"SGD W_out: {bad.sum()} elements off, worst {np.abs(got - ref)[bad].max()}"
+    assert torch.equal(Wo[c.L:], d.W[c.L:]), "padded rows keep W"
 
     # tail backward, recomputing dz from the positives (no loss added)
     dW3 = torch.empty_like(d.W)

@@ -343,6 +343,30 @@ def test_p6_expected_recall_exhaustive_and_closed_forms():
     assert abs(rec.mean() - exact) < 4 * rec.std() / np.sqrt(trials) + 1e-12, (rec.mean(), exact)
 
 
+def test_sgd_step_descends_at_first_order_rate():
+    """The update W - lr * dW with the oracle's tail gradient lowers the
+    oracle's loss, and (L(W - lr g) - L(W)) / lr tends to -|g|^2 as lr -> 0
+    (first-order Taylor): pins the update's sign and scale together with the
+    gradient it uses."""
+    inp = wl.make_inputs(wl.tiny("sgd", B=6, D=40, H=8, L=60, G=4, F=8, dtype="f32"))
+    c = inp.cfg
+    X, Wh, Wt = _f64(inp)
+    r0 = oracle.step(X, Wh, inp.idx, Wt, inp.row_ptr, inp.labels, c.L, c.G)
+    g2 = float((r0.dWt ** 2).sum())
+    assert g2 > 0
+    prev = None
+    for lr in (1e-1, 1e-2, 1e-3):
+        W1 = oracle.sgd(Wt, r0.dWt, lr)
+        r1 = oracle.step(X, Wh, inp.idx, W1, inp.row_ptr, inp.labels, c.L, c.G)
+        slope = (r1.loss - r0.loss) / lr
+        assert r1.loss < r0.loss
+        err = abs(slope + g2)
+        if prev is not None:
+            assert err < 0.2 * prev + 1e-12, (lr, slope, -g2)   # error shrinks with lr
+        prev = err
+    assert prev < 1e-2 * g2
+
+
 # --------------------------------------------------------------------- P7
 def test_p7_group_positives_brute_force():
     inp = wl.make_inputs("c1", L=203, G=16, pos_per_row=9)
