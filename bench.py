@@ -245,12 +245,14 @@ def run_infer(args, cfg, inp, t_gen):
 
 
 def run_dense(args, cfg, inp, t_gen):
-    """The tail (group-shared fixed fan-in, F indices per group) next to a
-    FLOPs-matched dense bottleneck: a dense layer from F inputs to the same L
-    labels, (B x F) . (F x L), with the same sigmoid-BCE over the same
-    positives, forward and training step (logits, dW, dX), on the dense
-    kernels of this library (the head's GEMMs with D = F, H = L).  Inputs of
-    the bottleneck: x ~ N(0, 1), W ~ N(0, 0.02), bf16."""
+    """The tail (group-shared fixed fan-in, F indices per group) next to its
+    two comparison points: the same layer with G = 1 (F indices per label;
+    forward: logits and loss) and a FLOPs-matched dense bottleneck, a dense
+    layer from F inputs to the same L labels, (B x F) . (F x L), with the same
+    sigmoid-BCE over the same positives, forward and training step (logits,
+    dW, dX), on the dense kernels of this library (the head's GEMMs with
+    D = F, H = L).  Inputs of the bottleneck: x ~ N(0, 1), W ~ N(0, 0.02),
+    bf16."""
     import numpy as np
     import torch
 
@@ -275,7 +277,18 @@ def run_dense(args, cfg, inp, t_gen):
     ws_d = torch.empty(H.haste_head_workspace_bytes(Xb, Wb, bt), dtype=torch.uint8, device=dev)
     dW, dX = torch.empty_like(W), torch.empty(B, D, dtype=torch.float32, device=dev)
     dWb, dXb = torch.empty_like(Wb), torch.empty(B, F, dtype=torch.float32, device=dev)
+    # the same layer with G = 1: every label its own F indices (uniform without
+    # replacement, sorted), drawn on the device
+    idx1 = torch.empty(L, F, dtype=torch.int32, device=dev)
+    gd = torch.Generator(device=dev).manual_seed(2)
+    for c0 in range(0, L, 65536):
+        n = min(65536, L - c0)
+        keys = torch.rand(n, D, generator=gd, device=dev)
+        idx1[c0:c0 + n] = keys.argsort(dim=1)[:, :F].sort(dim=1).values.to(torch.int32)
+        del keys
+    ws_1 = torch.empty(H.haste_tail_workspace_bytes(X, idx1, L, 1, bt), dtype=torch.uint8, device=dev)
     calls = {
+        "fanin1_fwd": lambda: H.haste_tail_fwd(X, idx1, W, L, 1, bce=bt, workspace=ws_1),
         "sparse_fwd": lambda: H.haste_tail_fwd(X, idx, W, L, G, bce=bt, workspace=ws_t),
         "dense_fwd": lambda: H.haste_head_fwd(Xb, Wb, bce=bt, workspace=ws_d),
         "sparse_step": lambda: (H.haste_tail_prepare(X, idx, L, G, bt, ws_t),
@@ -297,8 +310,8 @@ def run_dense(args, cfg, inp, t_gen):
         res[name] = t0.elapsed_time(t1) / args.steps * 1e3     # microseconds
     fl_fwd, fl_step = 2 * B * F * L, 6 * B * F * L
     out = {
-        "metric": "tail (G=%d shared fan-in) vs FLOPs-matched dense bottleneck (B x F)(F x L), "
-                  "fwd and training step at %s" % (G, cfg.name),
+        "metric": "tail (G=%d shared fan-in) vs G=1 fixed fan-in (fwd) and a FLOPs-matched "
+                  "dense bottleneck (B x F)(F x L), fwd and training step at %s" % (G, cfg.name),
         "unit": "us",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "higher_is_better": False, "dtype": "bf16", "data": "synthetic",
@@ -309,6 +322,7 @@ def run_dense(args, cfg, inp, t_gen):
                    for k, v in res.items()},
         "sparse_over_dense_time": {"fwd": round(res["sparse_fwd"] / res["dense_fwd"], 3),
                                    "step": round(res["sparse_step"] / res["dense_step"], 3)},
+        "fanin1_over_sparse_fwd_time": round(res["fanin1_fwd"] / res["sparse_fwd"], 3),
         "gen_s": round(t_gen, 2),
     }
     print(json.dumps(out), flush=True)

@@ -75,7 +75,11 @@ typedef enum { HASTE_F32 = 0, HASTE_BF16 = 1 } haste_dtype;
 /* Tail shape.  Supported: B >= 1, D >= F, F >= 1, L >= 1, G >= 1.
  * bf16 kernels additionally need G in {16, 32, 64}, F a multiple of 32 with
  * F <= 128 (F in {32, 64, 128}), D <= 1024; other shapes
- * return HASTE_ERR_UNSUPPORTED.  fp32 accepts any G and F. */
+ * return HASTE_ERR_UNSUPPORTED.  G = 1 (every label its own F indices: the
+ * per-label fixed fan-in layout the HASTE page compares against) is taken
+ * in bf16 by haste_tail_fwd only (logits and loss, no top-K, D >= 16); the
+ * other bf16 tail calls return HASTE_ERR_UNSUPPORTED for it.  fp32 accepts
+ * any G and F. */
 typedef struct {
     int32_t B;      /* rows in the batch                    */
     int32_t D;      /* input feature width                  */

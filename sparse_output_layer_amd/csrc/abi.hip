@@ -73,11 +73,14 @@ TailWs tail_ws(const haste_tail_desc *d, const haste_bce *bce) {
         w.ptr = o; o += al256((size_t)(ng + 4) * 4);   // +3: 16-byte reads of a pair
         w.ent = o; o += al256((size_t)(nnz > 0 ? nnz : 1) * 4);
         // the dW/logits pass's feature order: idx reordered, and the order
-        w.idxp = o; o += al256((size_t)ng * d->F * 2);
-        w.perm = o; o += al256((size_t)ng * d->F);
+        // (groups of 16 and more; G = 1 gathers per label)
+        if (d->G > 1) {
+            w.idxp = o; o += al256((size_t)ng * d->F * 2);
+            w.perm = o; o += al256((size_t)ng * d->F);
+        }
         // dz of the dW pass, kept for the dX pass unless the caller asks for
         // the lean form (which recomputes it): Bp x (Ng*G) bf16 in 1 KB tiles
-        w.has_dzt = bce && !(d->flags & HASTE_TAIL_LEAN);
+        w.has_dzt = bce && !(d->flags & HASTE_TAIL_LEAN) && d->G > 1;
         if (w.has_dzt) { w.dzt = o; o += al256((size_t)ng * d->G * pad_rows(d->B) * 2); }
     } else {
         // per-group counts; also the key space of haste_tail_group_positives
@@ -282,6 +285,13 @@ haste_status zero_dx(float *dX, int B, int D, int accumulate, hipStream_t st) {
 }
 
 // common argument checks of tail compute calls
+// bf16 with G = 1 (per-label fan-in) has the forward only
+haste_status not_g1(const haste_tail_desc *d) {
+    if (d->dtype == HASTE_BF16 && d->G == 1)
+        return fail(HASTE_ERR_UNSUPPORTED, "bf16 with G = 1 supports haste_tail_fwd only");
+    return HASTE_OK;
+}
+
 haste_status tail_common(const haste_tail_desc *d, const void *X, const int32_t *idx,
                          const void *W) {
     TRY(check_tail(d));
@@ -347,7 +357,17 @@ haste_status haste_tail_fwd(const haste_tail_desc *d, const void *X, const int32
     const TailWs m = tail_ws(d, bce);
     TRY(check_ws(ws, ws_bytes, m.total));
     hipStream_t st = S(stream);
-    if (d->dtype == HASTE_BF16) {
+    if (d->dtype == HASTE_BF16 && d->G == 1) {
+        if (m.has_topk) return fail(HASTE_ERR_UNSUPPORTED, "no top-K with G = 1");
+        TRY(bf16_prep(d, X, bce, ws, m, st));
+        TailArgs a = tail_args(d, X, idx, W, ws, m);
+        a.Z = (unsigned short *)Z;
+        if (bce) {
+            a.loss = bce->loss;
+            a.s = bce->grad_scale;
+        }
+        TRY_HIP(launch_fanin1_fwd(a, Z != nullptr, bce && bce->loss, st), "tail fwd (G = 1)");
+    } else if (d->dtype == HASTE_BF16) {
         TRY(bf16_prep(d, X, bce, ws, m, st));
         TailArgs a = tail_args(d, X, idx, W, ws, m);
         a.Z = (unsigned short *)Z;
@@ -374,6 +394,7 @@ haste_status haste_tail_bwd(const haste_tail_desc *d, const void *X, const int32
                             void *stream) {
     g_err.clear();
     TRY(tail_common(d, X, idx, W));
+    TRY(not_g1(d));
     if (!dZ && !bce) return fail(HASTE_ERR_INVALID, "need dZ or bce to form the gradient");
     if (!dZ) TRY(check_bce(bce, d->B, false));
     TRY(need_al(dW, d->dtype == HASTE_BF16 ? 8 : 4, "dW"));
@@ -416,6 +437,7 @@ haste_status haste_tail_step(const haste_tail_desc *d, const void *X, const int3
                              int accumulate_dX, void *ws, size_t ws_bytes, void *stream) {
     g_err.clear();
     TRY(tail_common(d, X, idx, W));
+    TRY(not_g1(d));
     TRY(need(bce, "bce"));
     TRY(check_bce(bce, d->B, true));
     TRY(need_al(dW, d->dtype == HASTE_BF16 ? 8 : 4, "dW"));
@@ -455,6 +477,7 @@ haste_status haste_tail_step_sgd(const haste_tail_desc *d, const void *X, const 
                                  void *stream) {
     g_err.clear();
     TRY(tail_common(d, X, idx, W));
+    TRY(not_g1(d));
     TRY(need(bce, "bce"));
     TRY(check_bce(bce, d->B, true));
     TRY(need_al(W_out, 16, "W_out"));
@@ -503,6 +526,7 @@ haste_status haste_tail_prepare(const haste_tail_desc *d, const void *X, const h
                                 void *ws, size_t ws_bytes, void *stream) {
     g_err.clear();
     TRY(check_tail(d));
+    TRY(not_g1(d));
     TRY(need_al(X, d->dtype == HASTE_BF16 ? 16 : 4, "X"));
     TRY(need(bce, "bce"));
     TRY(check_bce(bce, d->B, true));
@@ -517,6 +541,7 @@ haste_status haste_tail_step_dw(const haste_tail_desc *d, const void *X, const i
                                 size_t ws_bytes, void *stream) {
     g_err.clear();
     TRY(tail_common(d, X, idx, W));
+    TRY(not_g1(d));
     TRY(need(bce, "bce"));
     TRY(check_bce(bce, d->B, true));
     TRY(need_al(dW, d->dtype == HASTE_BF16 ? 8 : 4, "dW"));
@@ -548,6 +573,7 @@ haste_status haste_tail_step_dx(const haste_tail_desc *d, const void *X, const i
                                 int accumulate_dX, void *ws, size_t ws_bytes, void *stream) {
     g_err.clear();
     TRY(tail_common(d, X, idx, W));
+    TRY(not_g1(d));
     TRY(need(bce, "bce"));
     TRY(check_bce(bce, d->B, true));
     TRY(need_al(dX, 4, "dX"));

@@ -55,6 +55,8 @@ hipError_t launch_tail_t1(int mode, int G, const TailArgs &a, bool store_z,
 hipError_t launch_tail_t2(int G, int dz_mode, const TailArgs &a,
                           hipStream_t st);
 bool tail_bf16_supported(int G, int F, int D);
+// G = 1 (per-label fan-in): logits and loss only
+hipError_t launch_fanin1_fwd(const TailArgs &a, bool store_z, bool do_loss, hipStream_t st);
 
 // Per-row top-K (K in [1, 8]) of fp32 logits z (rows x n, row stride ld,
 // column c has id id_offset + c): stage 1 keeps the top-KP (1 <= KP <= K;

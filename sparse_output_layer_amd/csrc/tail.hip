@@ -785,6 +785,141 @@ static hipError_t t1_launch(int mode, const TailArgs &a, bool store_z, bool do_l
     return hipGetLastError();
 }
 
+// ------------------------------------------------------- fixed fan-in, G = 1
+// Every label keeps its own F indices (the per-label layout that the HASTE
+// page compares against, section "Results"): the forward has to gather F
+// rows of X for every label instead of every group.  Logits and the
+// sigmoid-BCE loss only.  Workgroup = FF_R labels over the whole batch: their
+// tables of (row offset, weight) pairs are built once in LDS; 32-row chunks
+// of X^T (rows of 64 bytes) stream through LDS, double-buffered with direct
+// global->LDS copies; each wave owns eight labels, four at a time (one per
+// quarter-wave; a lane per two adjacent rows, read as one 4-byte word), and
+// reads the table four entries at a time.
+constexpr int FF_NW = 8;                   // waves per workgroup
+constexpr int FF_R = 64;                   // labels per workgroup (eight per wave)
+constexpr int FF_BUF_BYTES = 64 * 1024;    // one chunk buffer: D <= 1024 rows of 64 bytes
+
+// This wave's share of the copy of chunk ch: one copy instruction per 16 rows
+// (lane: row lane/4, 16-byte segment lane%4); the last block moved back to
+// end at row D (its overlap rewrites equal data).
+__device__ __forceinline__ void ff_stage_async(const TailArgs &a, unsigned short *buf, int ch, int w,
+                                               unsigned voff) {
+    const int nblk = (a.D + 15) / 16;
+    for (int b = w; b < nblk; b += FF_NW) {
+        const int r0 = min(16 * b, a.D - 16);
+        const char *src = (const char *)(a.XT + (int64_t)r0 * a.Bp + ch * 32);
+        __builtin_amdgcn_global_load_lds(src + voff, (__attribute__((address_space(3))) void *)(
+                                                         buf + r0 * 32), 16, 0, 0);
+    }
+}
+
+template <int F>
+__global__ __launch_bounds__(64 * FF_NW, 1) void k_fanin1_fwd(TailArgs a, int store_z, int do_loss) {
+    __shared__ __attribute__((aligned(16))) unsigned short fbuf0[FF_BUF_BYTES / 2];
+    __shared__ __attribute__((aligned(16))) unsigned short fbuf1[FF_BUF_BYTES / 2];
+    __shared__ __attribute__((aligned(16))) unsigned tab[FF_R][F];  // row offset | bf16 weight << 16
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    const int qd = lane >> 4, rp = lane & 15;      // label of the quad, row pair
+    const unsigned voff = (unsigned)((lane >> 2) * a.Bp + 8 * (lane & 3)) * 2u;
+    const int nch = a.Bp / 32;
+    const int64_t t_begin = (int64_t)blockIdx.x * FF_R;
+    float lsum = 0.f;
+
+    ff_stage_async(a, fbuf0, 0, wu, voff);
+    // the workgroup's tables (labels past L: offset 0, weight 0)
+    for (int e = threadIdx.x; e < FF_R * F; e += 64 * FF_NW) {
+        const int64_t t = t_begin + e / F;
+        unsigned v = 0;
+        if (t < a.L) v = (unsigned)a.idx[t * F + e % F] * 64u | (unsigned)a.W[t * F + e % F] << 16;
+        tab[e / F][e % F] = v;
+    }
+    // this lane's two labels (quads 8w..8w+3 and 8w+4..8w+7) and their positives
+    int p0[2], p1[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int64_t t = t_begin + 8 * wu + 4 * k + qd;
+        p0[k] = p1[k] = 0;
+        if (t < a.L) {
+            p0[k] = a.grp_ptr[t];
+            p1[k] = a.grp_ptr[t + 1];
+        }
+    }
+
+    auto chunk = [&](const unsigned short *tile, const int ch) {
+        const int row0 = ch * 32 + 2 * rp;
+        const unsigned char *tb = (const unsigned char *)tile + 4 * rp;
+        // both quads of the wave in one loop: two independent chains of LDS
+        // round trips (table entries, then the rows they point at)
+        float z[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+        const int lt0 = 8 * wu + qd;
+#pragma unroll 2
+        for (int f4 = 0; f4 < F; f4 += 4) {
+            u32x4 v4[2];
+#pragma unroll
+            for (int k = 0; k < 2; ++k) v4[k] = *(const u32x4 *)&tab[lt0 + 4 * k][f4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    const unsigned x2 = *(const unsigned *)(tb + (v4[k][j] & 0xffffu));
+                    const float wf = __uint_as_float(v4[k][j] & 0xffff0000u);
+                    z[k][0] = __builtin_fmaf(__uint_as_float(x2 << 16), wf, z[k][0]);
+                    z[k][1] = __builtin_fmaf(__uint_as_float(x2 & 0xffff0000u), wf, z[k][1]);
+                }
+        }
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int64_t t = t_begin + lt0 + 4 * k;
+            if (t >= a.L) continue;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int row = row0 + i;
+                if (row >= a.B) continue;
+                if (store_z) a.Z[(int64_t)row * a.L + t] = f32_to_bf16(z[k][i]);
+                if (do_loss) {
+                    float y = 0.f;
+                    for (int e = p0[k]; e < p1[k]; ++e) y = a.grp_ent[e] == row ? 1.f : y;
+                    const float den = 1.0f + fast_exp_neg_abs(z[k][i]);
+                    lsum += a.s * ((fmaxf(z[k][i], 0.f) - y * z[k][i]) + fast_log(den));
+                }
+            }
+        }
+    };
+    // nch is even (Bp is a multiple of 64); the first barrier also publishes the tables
+    for (int ch = 0; ch < nch; ch += 2) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        ff_stage_async(a, fbuf1, ch + 1, wu, voff);
+        chunk(fbuf0, ch);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (ch + 2 < nch) ff_stage_async(a, fbuf0, ch + 2, wu, voff);
+        chunk(fbuf1, ch + 1);
+    }
+    if (do_loss && a.loss) {
+        const float v = wave_sum(lsum);
+        if (lane == 0) atomicAdd(a.loss, v);
+    }
+}
+
+hipError_t launch_fanin1_fwd(const TailArgs &a, bool store_z, bool do_loss, hipStream_t st) {
+    if (a.D > FF_BUF_BYTES / 64 || a.D < 16) return hipErrorInvalidValue;
+    const int64_t grid = (a.L + FF_R - 1) / FF_R;
+    if (grid <= 0) return hipSuccess;
+#define FFCASE(FF)                                                                                 \
+    if (a.F == FF) {                                                                               \
+        hipLaunchKernelGGL((k_fanin1_fwd<FF>), dim3((unsigned)grid), dim3(64 * FF_NW), 0, st, a,   \
+                           (int)store_z, (int)do_loss);                                            \
+        return hipGetLastError();                                                                  \
+    }
+    FFCASE(32)
+    FFCASE(64)
+    FFCASE(128)
+#undef FFCASE
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_tail_t1(int mode, int G, const TailArgs &a, bool store_z, bool do_loss,
                           hipStream_t st) {
 #define T1CASE(GG, FF, RR, NN) \
@@ -1682,6 +1817,7 @@ hipError_t launch_tail_t2(int G, int dz_mode, const TailArgs &a, hipStream_t st)
 }
 
 bool tail_bf16_supported(int G, int F, int D) {
+    if (G == 1) return (F == 32 || F == 64 || F == 128) && D >= F && D >= 16 && D <= 1024;
     if (!(G == 16 || G == 32 || G == 64)) return false;
     if (!(F == 32 || F == 64 || F == 128)) return false;
     if (D < F || D > 1024) return false;

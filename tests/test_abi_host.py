@@ -111,6 +111,14 @@ def test_head_and_step_argument_errors(L):
     d = _desc()
     assert L.haste_tail_step(ctypes.byref(d), 0x1000, 0x1000, 0x1000, None, 0x1000, 0x1000, 0,
                              None, 0, None) == H.HASTE_ERR_INVALID       # bce required
+    # bf16 with G = 1 (per-label fan-in): the forward only
+    g1 = _desc(G=1)
+    b = H.BceStruct(nnz=5, row_ptr=0x1000, labels=0x1000)
+    assert _status(L, g1) == H.HASTE_ERR_WORKSPACE                       # forward: accepted
+    assert L.haste_tail_step(ctypes.byref(g1), 0x1000, 0x1000, 0x1000, ctypes.byref(b), 0x1000,
+                             0x1000, 0, 0x1000, 1 << 30, None) == H.HASTE_ERR_UNSUPPORTED
+    assert L.haste_tail_prepare(ctypes.byref(g1), 0x1000, ctypes.byref(b), 0x1000, 1 << 30,
+                                None) == H.HASTE_ERR_UNSUPPORTED
     assert L.haste_topk_merge(4, 0, 1, 1, 1, 1, 1, 1, None) == H.HASTE_ERR_INVALID
     # approximate top-K: K' in [0, K], buckets in [0, 65535]
     for kp, nbk in ((6, 0), (-1, 0), (2, -1), (2, 70000), (2, 0)):

@@ -310,3 +310,36 @@ def test_group_positives_edges(H, B, L, G, per_row, dup, dtype):
     torch.cuda.synchronize()
     assert np.array_equal(gp.cpu().numpy(), rp)
     assert np.array_equal(ent.cpu().numpy()[:re_.size], re_)
+
+
+FANIN1 = [
+    dict(B=40, D=96, H=48, L=300, G=1, F=32),
+    dict(B=70, D=768, H=64, L=1500, G=1, F=128),
+    dict(B=33, D=1024, H=64, L=700, G=1, F=64, idx_dist="skew10"),
+]
+
+
+@pytest.mark.parametrize("case", FANIN1, ids=[_ids(c) for c in FANIN1])
+def test_bf16_fixed_fan_in_forward(H, case):
+    """G = 1 (every label its own F indices; the per-label fixed fan-in the
+    HASTE page compares against): logits and loss of haste_tail_fwd against
+    the oracle, which at G = 1 is the fixed fan-in loop (pin P1)."""
+    print("case", case, flush=True)
+    inp = wl.make_inputs(wl.tiny("g1", **case))
+    c = inp.cfg
+    s = 1.0 / c.B
+    X, Wt = inp.X_f64(), inp.W_f64()
+    Zr, Zra = oracle.tail_logits(X, inp.idx, Wt, c.L, c.G, want_abs=True)
+    Y = oracle.positive_mask(inp.row_ptr, inp.labels, c.H, c.L)
+    _, lt = oracle.bce(Zr, Y, s)
+    d = Dev(inp)
+    Z = torch.empty(c.B, c.L, dtype=torch.bfloat16, device=DEV)
+    b = d.bce(c.H, s)
+    H.haste_tail_fwd(d.X, d.idx, d.W, c.L, c.G, Z=Z, bce=b)
+    torch.cuda.synchronize()
+    check("G=1 Z", to_f64(Z), Zr, Zra, "bf16", nterms=c.F)
+    check_loss("G=1 loss", b.loss.item(), float(lt.sum()), "bf16")
+    b2 = d.bce(c.H, s)
+    H.haste_tail_fwd(d.X, d.idx, d.W, c.L, c.G, bce=b2)     # loss only, no Z
+    torch.cuda.synchronize()
+    check_loss("G=1 loss (no Z)", b2.loss.item(), float(lt.sum()), "bf16")
