@@ -174,9 +174,13 @@ def run_infer(args, cfg, inp, t_gen):
     min_b = max(1, -(-4 * 256 // B))
     kp, nb = H.haste_topk_plan(L, K, args.recall, min_b)
     exp_recall = H.haste_topk_expected_recall(L, K, kp, nb)
+    ng = (L + G - 1) // G
+    exp_fused = H.haste_topk_expected_recall(L, K, 1, ng)
     out = {}
     lists = {}
-    for name, (kprime, nbk) in (("exact", (0, 0)), ("approx", (kp, nb))):
+    # exact; the planned (K', buckets); one bucket per label group with K' = 1,
+    # whose stage 1 runs inside the logits pass
+    for name, (kprime, nbk) in (("exact", (0, 0)), ("approx", (kp, nb)), ("fused", (1, ng))):
         bh = H.Bce(rp, lab, 0, 1.0 / B)
         bt = H.Bce(rp, lab, cfg.H, 1.0 / B, topk_kprime=kprime, topk_buckets=nbk)
         for b_ in (bh, bt):
@@ -218,8 +222,8 @@ def run_infer(args, cfg, inp, t_gen):
         lists[name] = (bt.topk_idx.cpu().numpy(), mi.cpu().numpy())
         out[name] = {"value": round(B / (ms * 1e-3), 1), "ms_per_step": round(ms, 4), "kernels_us": per}
     # recall of the approximate lists against the exact ones (tail, and merged)
-    tail_rec = float(np.mean([len(set(a) & set(e)) / K for a, e in zip(lists["approx"][0], lists["exact"][0])]))
-    all_rec = float(np.mean([len(set(a) & set(e)) / K for a, e in zip(lists["approx"][1], lists["exact"][1])]))
+    def recall(name, i):
+        return float(np.mean([len(set(a) & set(e)) / K for a, e in zip(lists[name][i], lists["exact"][i])]))
     res = {
         "metric": "inference samples/sec (head+tail fwd + per-row top-%d) at %s" % (K, cfg.name),
         "value": out["exact"]["value"],
@@ -237,8 +241,11 @@ def run_infer(args, cfg, inp, t_gen):
                                f"F={cfg.F}, top-{K}", "global_batch": B, "parallelism": "single GPU"},
         "exact": out["exact"],
         "approx": dict(out["approx"], kprime=kp, buckets=nb, recall_target=args.recall,
-                       expected_recall_tail=round(exp_recall, 5), measured_recall_tail=round(tail_rec, 5),
-                       measured_recall_merged=round(all_rec, 5)),
+                       expected_recall_tail=round(exp_recall, 5), measured_recall_tail=round(recall("approx", 0), 5),
+                       measured_recall_merged=round(recall("approx", 1), 5)),
+        "fused": dict(out["fused"], kprime=1, buckets=ng, expected_recall_tail=round(exp_fused, 6),
+                      measured_recall_tail=round(recall("fused", 0), 6),
+                      measured_recall_merged=round(recall("fused", 1), 6)),
         "gen_s": round(t_gen, 2),
     }
     print(json.dumps(res), flush=True)

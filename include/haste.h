@@ -119,7 +119,7 @@ typedef struct {
     int32_t reserved0;
     int64_t label_offset;     /* global id of this branch's label 0           */
     float grad_scale;         /* s: dz = s*(sigmoid(z) - y); usually 1/B      */
-    int32_t topk_buckets;     /* buckets per row, in [1, 65535]; 0: the
+    int32_t topk_buckets;     /* buckets per row, in [1, 2^24]; 0: the
                                  library's choice (only with K' = K)          */
     float *loss;              /* device fp32 scalar; this call ADDS its loss,
                                  or NULL for no loss                          */
@@ -144,7 +144,11 @@ typedef struct {
  * enough stage-1 workgroups over all rows).  With K' < K it is the page's
  * approximate two-stage top-K (a logit of the true top-K is missed when more
  * than K' of them share its bucket) and topk_buckets must be given;
- * haste_topk_plan picks K' and the bucket count for a recall target.  The head's and the tail's lists combine with
+ * haste_topk_plan picks K' and the bucket count for a recall target.  When
+ * the buckets are exactly the tail's label groups (ceil(L / topk_buckets)
+ * = G, bf16) and K' = 1, stage 1 runs inside the logits pass (the top-K
+ * page's matmul-fused stage 1): the same result without the fp32 logits in
+ * the workspace.  The head's and the tail's lists combine with
  * haste_topk_merge.  The workspace then also holds the call's fp32 logits
  * (B x labels x 4 bytes) and the bucket lists (B x buckets x K' x 8 bytes).
  * haste_tail_bwd and haste_head_bwd reject topk > 0; the other calls ignore

@@ -59,8 +59,17 @@ inline int pad_rows(int B) { return (B + 63) / 64 * 64; }
 // ----------------------------------------------------------- workspace maps
 struct TailWs {
     size_t xt, cnt, ptr, ent, idxp, perm, dz, dzt, z32, cand, total;
-    bool has_dzt, has_topk;
+    bool has_dzt, has_topk, tk_fused;
 };
+
+// The top-K's stage 1 runs inside the logits pass when its buckets are the
+// label groups and K' = 1 (bf16, groups of 16 and more): same buckets, same
+// K', same result as the separate stage 1, without the fp32 logits.
+bool topk_fused(const haste_tail_desc *d, const haste_bce *bce) {
+    if (!bce || bce->topk <= 0 || d->dtype != HASTE_BF16 || d->G < 16) return false;
+    if (bce->topk_kprime != 1 || bce->topk_buckets <= 0) return false;
+    return topk_buckets(d->L, bce->topk_buckets, d->B).seg_len == d->G;
+}
 
 TailWs tail_ws(const haste_tail_desc *d, const haste_bce *bce) {
     TailWs w{};
@@ -88,11 +97,17 @@ TailWs tail_ws(const haste_tail_desc *d, const haste_bce *bce) {
         w.cnt = o; o += al256((size_t)ng * 4 > keys ? (size_t)ng * 4 : keys);
         w.dz = o;  o += al256((size_t)d->B * d->L * 4);
     }
-    // top-K: fp32 logits B x L, and the per-bucket lists (stage 1)
+    // top-K: fp32 logits B x L and the per-bucket lists; when stage 1 is fused,
+    // the group-major lists (N_g x B_pad) and the merge's segment lists instead
     w.has_topk = bce && bce->topk > 0;
-    if (w.has_topk) {
+    w.tk_fused = topk_fused(d, bce);
+    if (w.has_topk && !w.tk_fused) {
         w.z32 = o;  o += al256((size_t)d->B * d->L * 4);
         w.cand = o; o += al256(topk_cand_bytes(d->B, d->L, bce));
+    } else if (w.has_topk) {
+        w.cand = o;
+        o += al256((size_t)ng * pad_rows(d->B) * 8 +
+                   (size_t)d->B * topk_gm_segments(ng) * bce->topk * 8);
     }
     w.total = o;
     return w;
@@ -164,8 +179,8 @@ haste_status check_bce(const haste_bce *b, int B, bool topk_ok) {
         if (!topk_ok) return fail(HASTE_ERR_UNSUPPORTED, "bce.topk is not supported by this call");
         if (b->topk_kprime < 0 || b->topk_kprime > b->topk)
             return fail(HASTE_ERR_INVALID, "bce.topk_kprime=%d outside [0, topk=%d]", b->topk_kprime, b->topk);
-        if (b->topk_buckets < 0 || b->topk_buckets > 65535)
-            return fail(HASTE_ERR_INVALID, "bce.topk_buckets=%d outside [0, 65535]", b->topk_buckets);
+        if (b->topk_buckets < 0 || b->topk_buckets > (1 << 24))
+            return fail(HASTE_ERR_INVALID, "bce.topk_buckets=%d outside [0, 2^24]", b->topk_buckets);
         if (b->topk_kprime > 0 && b->topk_kprime < b->topk && b->topk_buckets == 0)
             return fail(HASTE_ERR_INVALID, "an approximate top-K (K' < K) needs bce.topk_buckets > 0");
         if (!b->topk_val || !aligned(b->topk_val, 4)) return fail(HASTE_ERR_INVALID, "bce.topk_val NULL or misaligned");
@@ -211,7 +226,11 @@ TailArgs tail_args(const haste_tail_desc *d, const void *X, const int32_t *idx, 
     a.idxp = (const unsigned short *)B8(ws, m.idxp);
     a.perm = (const unsigned char *)B8(ws, m.perm);
     a.dzt = m.has_dzt ? (unsigned short *)B8(ws, m.dzt) : nullptr;
-    a.Z32 = m.has_topk ? (float *)B8(ws, m.z32) : nullptr;
+    a.Z32 = m.has_topk && !m.tk_fused ? (float *)B8(ws, m.z32) : nullptr;
+    if (m.tk_fused) {   // the group-major bucket lists, written by the logits pass (K' = 1)
+        a.tk_v = (float *)B8(ws, m.cand);
+        a.tk_i = (int32_t *)(a.tk_v + n_groups(d) * pad_rows(d->B));
+    }
     a.B = d->B;
     a.D = d->D;
     a.Bp = pad_rows(d->B);
@@ -276,6 +295,20 @@ haste_status run_topk(const haste_bce *bce, const float *z, int B, int64_t n, vo
     TRY_HIP(launch_row_topk(z, n, B, n, bce->label_offset, K, KP, bce->topk_buckets, cv, ci,
                             bce->topk_val, bce->topk_idx, st),
             "top-K");
+    return HASTE_OK;
+}
+
+// the tail's top-K after its logits pass: stage 2 alone when stage 1 was fused
+haste_status tail_topk(const haste_tail_desc *d, const haste_bce *bce, const TailWs &m,
+                       const TailArgs &a, void *ws, hipStream_t st) {
+    if (!m.has_topk) return HASTE_OK;
+    if (!m.tk_fused) return run_topk(bce, a.Z32, d->B, d->L, ws, m.cand, st);
+    const int64_t ng = n_groups(d);
+    float *mid_v = (float *)(a.tk_i + ng * pad_rows(d->B));
+    int32_t *mid_i = (int32_t *)(mid_v + (int64_t)d->B * topk_gm_segments(ng) * bce->topk);
+    TRY_HIP(launch_topk_group_major(a.tk_v, a.tk_i, pad_rows(d->B), d->B, ng, bce->topk, mid_v, mid_i,
+                                    bce->topk_val, bce->topk_idx, st),
+            "top-K merge");
     return HASTE_OK;
 }
 
@@ -361,6 +394,7 @@ haste_status haste_tail_fwd(const haste_tail_desc *d, const void *X, const int32
         if (m.has_topk) return fail(HASTE_ERR_UNSUPPORTED, "no top-K with G = 1");
         TRY(bf16_prep(d, X, bce, ws, m, st));
         TailArgs a = tail_args(d, X, idx, W, ws, m);
+        a.tk_off = bce ? bce->label_offset : 0;
         a.Z = (unsigned short *)Z;
         if (bce) {
             a.loss = bce->loss;
@@ -370,6 +404,7 @@ haste_status haste_tail_fwd(const haste_tail_desc *d, const void *X, const int32
     } else if (d->dtype == HASTE_BF16) {
         TRY(bf16_prep(d, X, bce, ws, m, st));
         TailArgs a = tail_args(d, X, idx, W, ws, m);
+        a.tk_off = bce ? bce->label_offset : 0;
         a.Z = (unsigned short *)Z;
         if (bce) {
             a.loss = bce->loss;
@@ -377,7 +412,7 @@ haste_status haste_tail_fwd(const haste_tail_desc *d, const void *X, const int32
         }
         TRY(feature_order(d, idx, ws, m, st));
         TRY_HIP(launch_tail_t1(T1_FWD, d->G, a, Z != nullptr, bce && bce->loss, st), "tail fwd");
-        if (m.has_topk) TRY(run_topk(bce, a.Z32, d->B, d->L, ws, m.cand, st));
+        TRY(tail_topk(d, bce, m, a, ws, st));
     } else {
         F32Args a = f32_tail_args(d, X, idx, W, bce);
         a.Z = Z ? (float *)Z : m.has_topk ? (float *)B8(ws, m.z32) : nullptr;
@@ -449,13 +484,14 @@ haste_status haste_tail_step(const haste_tail_desc *d, const void *X, const int3
     if (d->dtype == HASTE_BF16) {
         TRY(bf16_prep(d, X, bce, ws, m, st));
         TailArgs a = tail_args(d, X, idx, W, ws, m);
+        a.tk_off = bce ? bce->label_offset : 0;
         a.dW = (unsigned short *)dW;
         a.dX = dX;
         a.s = bce->grad_scale;
         a.loss = bce->loss;
         TRY(feature_order(d, idx, ws, m, st));
         TRY_HIP(launch_tail_t1(T1_DW_BCE, d->G, a, false, bce->loss != nullptr, st), "tail step dW");
-        if (m.has_topk) TRY(run_topk(bce, a.Z32, d->B, d->L, ws, m.cand, st));
+        TRY(tail_topk(d, bce, m, a, ws, st));
         TRY_HIP(launch_tail_t2(d->G, a.dzt ? 2 : 0, a, st), "tail step dX");
     } else {
         F32Args a = f32_tail_args(d, X, idx, W, bce);
@@ -496,6 +532,7 @@ haste_status haste_tail_step_sgd(const haste_tail_desc *d, const void *X, const 
     TRY(zero_dx(dX, d->B, d->D, accumulate_dX, st));
     TRY(bf16_prep(d, X, bce, ws, m, st));
     TailArgs a = tail_args(d, X, idx, W, ws, m);
+    a.tk_off = bce->label_offset;
     a.Wout = (unsigned short *)W_out;
     a.lr = lr;
     a.dX = dX;
@@ -503,7 +540,7 @@ haste_status haste_tail_step_sgd(const haste_tail_desc *d, const void *X, const 
     a.loss = bce->loss;
     TRY(feature_order(d, idx, ws, m, st));
     TRY_HIP(launch_tail_t1(T1_DW_BCE, d->G, a, false, bce->loss != nullptr, st), "tail SGD step dW");
-    if (m.has_topk) TRY(run_topk(bce, a.Z32, d->B, d->L, ws, m.cand, st));
+    TRY(tail_topk(d, bce, m, a, ws, st));
     TRY_HIP(launch_tail_t2(d->G, a.dzt ? 2 : 0, a, st), "tail SGD step dX");
     return HASTE_OK;
 }
@@ -550,12 +587,13 @@ haste_status haste_tail_step_dw(const haste_tail_desc *d, const void *X, const i
     hipStream_t st = S(stream);
     if (d->dtype == HASTE_BF16) {
         TailArgs a = tail_args(d, X, idx, W, ws, m);
+        a.tk_off = bce ? bce->label_offset : 0;
         a.dW = (unsigned short *)dW;
         a.s = bce->grad_scale;
         a.loss = bce->loss;
         TRY(feature_order(d, idx, ws, m, st));
         TRY_HIP(launch_tail_t1(T1_DW_BCE, d->G, a, false, bce->loss != nullptr, st), "tail step dW");
-        if (m.has_topk) TRY(run_topk(bce, a.Z32, d->B, d->L, ws, m.cand, st));
+        TRY(tail_topk(d, bce, m, a, ws, st));
     } else {
         F32Args a = f32_tail_args(d, X, idx, W, bce);
         a.dW = (float *)dW;

@@ -112,6 +112,34 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// DPP lane exchange inside a row of 16 lanes (all lanes active).
+// Controls: quad_perm [1,0,3,2] = 0xB1, quad_perm [2,3,0,1] = 0x4E,
+// row_half_mirror = 0x141, row_mirror = 0x140.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+template <int CTRL>
+__device__ __forceinline__ unsigned dpp_u32(unsigned v) {
+    return (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
+}
+// max over the 16 lanes of the row, and the smallest key among the lanes
+// holding it (every lane receives both)
+__device__ __forceinline__ void row16_argmax(float &v, unsigned &key) {
+    float m = v;
+    m = fmaxf(m, dpp_f32<0xB1>(m));
+    m = fmaxf(m, dpp_f32<0x4E>(m));
+    m = fmaxf(m, dpp_f32<0x141>(m));
+    m = fmaxf(m, dpp_f32<0x140>(m));
+    unsigned k = v == m ? key : 0xffffffffu;
+    k = min(k, dpp_u32<0xB1>(k));
+    k = min(k, dpp_u32<0x4E>(k));
+    k = min(k, dpp_u32<0x141>(k));
+    k = min(k, dpp_u32<0x140>(k));
+    v = m;
+    key = k;
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
     for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
     return v;

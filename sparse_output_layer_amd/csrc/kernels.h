@@ -16,6 +16,9 @@ struct TailArgs {
     unsigned short *Z;           // B x L bf16 (forward output)
     const unsigned short *dZ;    // B x L bf16 (given gradient)
     float *Z32;                  // fp32 logits for the top-K: B x L, row stride L; or null
+    float *tk_v;                 // fused top-K stage 1 (one bucket per group, K' = 1): Ng x Bp
+    int32_t *tk_i;               //   largest logit of each (group, row) and its id (-1: none); or null
+    int64_t tk_off;              //   id of tail label 0
     const unsigned short *idxp;  // Ng x F: idx in T1's bank-aware order (idxp[g][k] = idx[g][perm[g][k]])
     const unsigned char *perm;   // Ng x F: that order's feature per position
     unsigned short *dzt;         // dz tiles of the dW pass for the dX pass, or null:
@@ -71,6 +74,18 @@ TopkBuckets topk_buckets(int64_t n, int64_t nbuckets, int64_t rows);
 hipError_t launch_row_topk(const float *z, int64_t ld, int rows, int64_t n, int64_t id_offset,
                            int K, int KP, int64_t nbuckets, float *cand_v, int32_t *cand_i,
                            float *out_v, int32_t *out_i, hipStream_t st);
+// stage 2 alone over rows x ncand candidates
+hipError_t launch_topk_merge_cands(const float *cand_v, const int32_t *cand_i, int rows,
+                                   int64_t ncand, int K, float *out_v, int32_t *out_i,
+                                   hipStream_t st);
+// Merge of group-major candidates (ngroups x ld, row-contiguous; stage 1 fused
+// into the logits pass): segments of TOPK_GSEG groups per (32-row block) into
+// mid (rows x nseg x K), then per row into out (rows x K)
+constexpr int64_t TOPK_GSEG = 1024;
+int64_t topk_gm_segments(int64_t ngroups);
+hipError_t launch_topk_group_major(const float *gv, const int32_t *gi, int64_t ld, int rows,
+                                   int64_t ngroups, int K, float *mid_v, int32_t *mid_i,
+                                   float *out_v, int32_t *out_i, hipStream_t st);
 
 // Head (dense classifier) GEMMs.
 struct GemmArgs {

@@ -428,7 +428,8 @@ __device__ __forceinline__ void t1_stage_async(const TailArgs &a, unsigned short
     }
 }
 
-template <int G, int F, int RW, int NW, int MODE>
+// TK: the fused top-K stage 1 (one bucket per group, K' = 1) is compiled in
+template <int G, int F, int RW, int NW, int MODE, bool TK = false>
 __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, int store_z, int do_loss) {
     constexpr int JT = G / 16, KS = F / 32, FT = F / 16;
     constexpr int BC = T1_BC, BCP = T1_BCP;
@@ -627,6 +628,39 @@ __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, int store_z,
                             dzp[h2][jt][1] = pack_bf16x2(dzv[2], dzv[3]);
                         }
                 }
+                if (TK) {
+                    // top-K stage 1 fused here, one bucket per group and K' = 1:
+                    // per row, the group's largest logit (ties: smaller id), into
+                    // group-major lists (Ng x Bp): lane m = 0 of each q stores
+                    // rows 4q..4q+3 and 16+4q.. of the chunk, 16 bytes each
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2) {
+                        f32x4 cv;
+                        u32x4 ci;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            float bv = -INFINITY;
+                            unsigned bj = 0xffffffffu;
+#pragma unroll
+                            for (int jt = 0; jt < JT; ++jt) {   // ascending slots: ties keep the first
+                                const unsigned j = 16 * jt + m;
+                                const float z = zacc[h2][jt][i];
+                                if (g * G + j < a.L && (bj == 0xffffffffu || z > bv)) {
+                                    bv = z;
+                                    bj = j;
+                                }
+                            }
+                            row16_argmax(bv, bj);
+                            cv[i] = bj == 0xffffffffu ? -INFINITY : bv;
+                            ci[i] = bj == 0xffffffffu ? 0xffffffffu : (unsigned)(a.tk_off + g * G + bj);
+                        }
+                        if (m == 0) {
+                            const int64_t o = g * (int64_t)a.Bp + r0 + 16 * h2 + 4 * q;
+                            *(f32x4 *)(a.tk_v + o) = cv;
+                            *(u32x4 *)(a.tk_i + o) = ci;
+                        }
+                    }
+                }
                 if (DO_DW) {
                     bf16x8 Bj[JT];
 #pragma unroll
@@ -768,16 +802,26 @@ static hipError_t t1_launch(int mode, const TailArgs &a, bool store_z, bool do_l
     const int64_t grid = n_runs < ncu ? n_runs : ncu;
     if (grid <= 0) return hipSuccess;
     const dim3 blk(64 * NW);
+    const bool tk = a.tk_v != nullptr;
     switch (mode) {
     case T1_FWD:
-        hipLaunchKernelGGL((k_tail_t1<G, F, RW, NW, T1_FWD>), dim3((unsigned)grid), blk, lds, st,
-                           a, (int)store_z, (int)do_loss);
+        if (tk)
+            hipLaunchKernelGGL((k_tail_t1<G, F, RW, NW, T1_FWD, true>), dim3((unsigned)grid), blk, lds,
+                               st, a, (int)store_z, (int)do_loss);
+        else
+            hipLaunchKernelGGL((k_tail_t1<G, F, RW, NW, T1_FWD>), dim3((unsigned)grid), blk, lds, st,
+                               a, (int)store_z, (int)do_loss);
         break;
     case T1_DW_BCE:
-        hipLaunchKernelGGL((k_tail_t1<G, F, RW, NW, T1_DW_BCE>), dim3((unsigned)grid), blk, lds,
-                           st, a, 0, (int)do_loss);
+        if (tk)
+            hipLaunchKernelGGL((k_tail_t1<G, F, RW, NW, T1_DW_BCE, true>), dim3((unsigned)grid), blk,
+                               lds, st, a, 0, (int)do_loss);
+        else
+            hipLaunchKernelGGL((k_tail_t1<G, F, RW, NW, T1_DW_BCE>), dim3((unsigned)grid), blk, lds,
+                               st, a, 0, (int)do_loss);
         break;
     default:
+        if (tk) return hipErrorInvalidValue;
         hipLaunchKernelGGL((k_tail_t1<G, F, RW, NW, T1_DW_MEM>), dim3((unsigned)grid), blk, lds,
                            st, a, 0, 0);
         break;

@@ -199,6 +199,104 @@ static hipError_t topk_stage2_go(int rows, int64_t ncand, const float *cand_v, c
     return hipGetLastError();
 }
 
+// Group-major candidates (ngroups x ld: entry (g, row) at g*ld + row): a
+// workgroup takes 32 rows x one segment of TOPK_GSEG groups; thread (row r,
+// part p) reads groups seg0 + p, + 8, .. (32 consecutive rows per group:
+// coalesced) into a K-list; the row's eight lists merge in LDS.
+template <int K>
+__global__ __launch_bounds__(256) void k_topk_group_major(const float *gv, const int32_t *gi, int64_t ld,
+                                                          int rows, int64_t ngroups, int nseg,
+                                                          float *mid_v, int32_t *mid_i) {
+    __shared__ float s_v[256 * K];
+    __shared__ int32_t s_i[256 * K];
+    const int r = threadIdx.x & 31, p = threadIdx.x >> 5;
+    const int row = blockIdx.x * 32 + r, seg = blockIdx.y;
+    const int64_t g0 = (int64_t)seg * TOPK_GSEG;
+    const int64_t g1 = g0 + TOPK_GSEG < ngroups ? g0 + TOPK_GSEG : ngroups;
+    float l_v[K];
+    int32_t l_i[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        l_v[k] = -INFINITY;
+        l_i[k] = -1;
+    }
+    if (row < rows)
+        for (int64_t g = g0 + p; g < g1; g += 8) {
+            const int32_t id = gi[g * ld + row];
+            if (id >= 0) tk_insert<K>(l_v, l_i, gv[g * ld + row], id);
+        }
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        s_v[threadIdx.x * K + k] = l_v[k];
+        s_i[threadIdx.x * K + k] = l_i[k];
+    }
+    __syncthreads();
+    if (p == 0 && row < rows) {
+        for (int pp = 1; pp < 8; ++pp)
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const int e = (pp * 32 + r) * K + k;
+                if (s_i[e] >= 0) tk_insert<K>(l_v, l_i, s_v[e], s_i[e]);
+            }
+        const int64_t o = ((int64_t)row * nseg + seg) * K;
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            mid_v[o + k] = l_v[k];
+            mid_i[o + k] = l_i[k];
+        }
+    }
+}
+
+int64_t topk_gm_segments(int64_t ngroups) { return (ngroups + TOPK_GSEG - 1) / TOPK_GSEG; }
+
+template <int K>
+static hipError_t topk_gm_go(const float *gv, const int32_t *gi, int64_t ld, int rows, int64_t ngroups,
+                             float *mid_v, int32_t *mid_i, float *out_v, int32_t *out_i,
+                             hipStream_t st) {
+    const int64_t nseg = topk_gm_segments(ngroups);
+    hipLaunchKernelGGL(k_topk_group_major<K>, dim3((unsigned)((rows + 31) / 32), (unsigned)nseg),
+                       dim3(256), 0, st, gv, gi, ld, rows, ngroups, (int)nseg, mid_v, mid_i);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return topk_stage2_go<K>(rows, nseg * K, mid_v, mid_i, out_v, out_i, st);
+}
+
+hipError_t launch_topk_group_major(const float *gv, const int32_t *gi, int64_t ld, int rows,
+                                   int64_t ngroups, int K, float *mid_v, int32_t *mid_i,
+                                   float *out_v, int32_t *out_i, hipStream_t st) {
+    if (rows <= 0 || ngroups <= 0) return hipSuccess;
+    if (topk_gm_segments(ngroups) > 65535) return hipErrorInvalidValue;
+    switch (K) {
+    case 1: return topk_gm_go<1>(gv, gi, ld, rows, ngroups, mid_v, mid_i, out_v, out_i, st);
+    case 2: return topk_gm_go<2>(gv, gi, ld, rows, ngroups, mid_v, mid_i, out_v, out_i, st);
+    case 3: return topk_gm_go<3>(gv, gi, ld, rows, ngroups, mid_v, mid_i, out_v, out_i, st);
+    case 4: return topk_gm_go<4>(gv, gi, ld, rows, ngroups, mid_v, mid_i, out_v, out_i, st);
+    case 5: return topk_gm_go<5>(gv, gi, ld, rows, ngroups, mid_v, mid_i, out_v, out_i, st);
+    case 6: return topk_gm_go<6>(gv, gi, ld, rows, ngroups, mid_v, mid_i, out_v, out_i, st);
+    case 7: return topk_gm_go<7>(gv, gi, ld, rows, ngroups, mid_v, mid_i, out_v, out_i, st);
+    case 8: return topk_gm_go<8>(gv, gi, ld, rows, ngroups, mid_v, mid_i, out_v, out_i, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+// Stage 2 alone, over candidate lists written elsewhere (rows x ncand)
+hipError_t launch_topk_merge_cands(const float *cand_v, const int32_t *cand_i, int rows,
+                                   int64_t ncand, int K, float *out_v, int32_t *out_i,
+                                   hipStream_t st) {
+    if (rows <= 0) return hipSuccess;
+    switch (K) {
+    case 1: return topk_stage2_go<1>(rows, ncand, cand_v, cand_i, out_v, out_i, st);
+    case 2: return topk_stage2_go<2>(rows, ncand, cand_v, cand_i, out_v, out_i, st);
+    case 3: return topk_stage2_go<3>(rows, ncand, cand_v, cand_i, out_v, out_i, st);
+    case 4: return topk_stage2_go<4>(rows, ncand, cand_v, cand_i, out_v, out_i, st);
+    case 5: return topk_stage2_go<5>(rows, ncand, cand_v, cand_i, out_v, out_i, st);
+    case 6: return topk_stage2_go<6>(rows, ncand, cand_v, cand_i, out_v, out_i, st);
+    case 7: return topk_stage2_go<7>(rows, ncand, cand_v, cand_i, out_v, out_i, st);
+    case 8: return topk_stage2_go<8>(rows, ncand, cand_v, cand_i, out_v, out_i, st);
+    }
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_row_topk(const float *z, int64_t ld, int rows, int64_t n, int64_t id_offset,
                            int K, int KP, int64_t nbuckets, float *cand_v, int32_t *cand_i,
                            float *out_v, int32_t *out_i, hipStream_t st) {
@@ -206,7 +304,7 @@ hipError_t launch_row_topk(const float *z, int64_t ld, int rows, int64_t n, int6
     if (KP == 0) KP = K;
     if (K < 1 || K > TOPK_MAX || KP < 1 || KP > K || nbuckets < 0) return hipErrorInvalidValue;
     const TopkBuckets b = topk_buckets(n, nbuckets, rows);
-    if (b.nseg < 1 || b.nseg > 65535) return hipErrorInvalidValue;
+    if (b.nseg < 1 || b.nseg > (1 << 24)) return hipErrorInvalidValue;
     hipError_t e = hipErrorInvalidValue;
     switch (KP) {
     case 1: e = topk_stage1_go<1>(z, ld, rows, n, id_offset, b, cand_v, cand_i, st); break;

@@ -120,8 +120,8 @@ def test_head_and_step_argument_errors(L):
     assert L.haste_tail_prepare(ctypes.byref(g1), 0x1000, ctypes.byref(b), 0x1000, 1 << 30,
                                 None) == H.HASTE_ERR_UNSUPPORTED
     assert L.haste_topk_merge(4, 0, 1, 1, 1, 1, 1, 1, None) == H.HASTE_ERR_INVALID
-    # approximate top-K: K' in [0, K], buckets in [0, 65535]
-    for kp, nbk in ((6, 0), (-1, 0), (2, -1), (2, 70000), (2, 0)):
+    # approximate top-K: K' in [0, K], buckets in [0, 2^24]
+    for kp, nbk in ((6, 0), (-1, 0), (2, -1), (2, (1 << 24) + 1), (2, 0)):
         b = H.BceStruct(nnz=5, row_ptr=0x1000, labels=0x1000, topk=5, topk_val=0x1000,
                         topk_idx=0x1000, topk_kprime=kp, topk_buckets=nbk)
         assert _status(L, _desc(), bce=ctypes.byref(b)) == H.HASTE_ERR_INVALID, (kp, nbk)

@@ -99,6 +99,10 @@ APPROX = [
     dict(B=20, D=96, H=48, L=1000, G=16, F=32, K=8, KP=1, NB=50),
     dict(B=16, D=96, H=48, L=600, G=32, F=64, K=5, KP=5, NB=3),      # exact on custom buckets
     dict(B=12, D=64, H=64, L=300, G=16, F=32, K=4, KP=2, NB=4, head=True),
+    # one bucket per label group with K' = 1: stage 1 runs inside the logits pass
+    dict(B=40, D=128, H=48, L=4000, G=16, F=64, K=5, KP=1, NB=250),
+    dict(B=70, D=200, H=48, L=3000, G=64, F=32, K=8, KP=1, NB=47),
+    dict(B=33, D=768, H=48, L=2000, G=32, F=128, K=3, KP=1, NB=63, step=True),
 ]
 
 
@@ -156,11 +160,13 @@ def _check_two_stage(name, got_v, got_i, z, zabs, K, kp, seg, dtype, id0, nterms
 
 
 @pytest.mark.parametrize("case", APPROX, ids=[
-    "B{B}-L{L}-K{K}-Kp{KP}-nb{NB}".format(**c) + ("-head" if c.get("head") else "") for c in APPROX])
+    "B{B}-L{L}-K{K}-Kp{KP}-nb{NB}".format(**c) + ("-head" if c.get("head") else "") +
+    ("-step" if c.get("step") else "") for c in APPROX])
 def test_topk_two_stage(H, case):
     print("case", case, flush=True)
     case = dict(case)
     K, KP, NB, head = case.pop("K"), case.pop("KP"), case.pop("NB"), case.pop("head", False)
+    step = case.pop("step", False)
     inp = wl.make_inputs(wl.tiny("tk2", **case))
     c = inp.cfg
     d = Dev(inp)
@@ -175,7 +181,11 @@ def test_topk_two_stage(H, case):
         n, id0, nterms = c.H, 0, c.D
     else:
         z, za = oracle.tail_logits(X, inp.idx, Wt, c.L, c.G, want_abs=True)
-        H.haste_tail_fwd(d.X, d.idx, d.W, c.L, c.G, bce=b)
+        if step:
+            H.haste_tail_step(d.X, d.idx, d.W, c.L, c.G, b, torch.empty_like(d.W),
+                              torch.empty(c.B, c.D, dtype=torch.float32, device=DEV))
+        else:
+            H.haste_tail_fwd(d.X, d.idx, d.W, c.L, c.G, bce=b)
         n, id0, nterms = c.L, c.H, c.F
     torch.cuda.synchronize()
     seg = oracle.topk_seg_len(n, NB)
