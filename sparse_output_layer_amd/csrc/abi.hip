@@ -107,7 +107,7 @@ TailWs tail_ws(const haste_tail_desc *d, const haste_bce *bce) {
     } else if (w.has_topk) {
         w.cand = o;
         o += al256((size_t)ng * pad_rows(d->B) * 8 +
-                   (size_t)d->B * topk_gm_segments(ng) * bce->topk * 8);
+                   (size_t)d->B * topk_gm_segments(ng, d->B).nseg * bce->topk * 8);
     }
     w.total = o;
     return w;
@@ -305,7 +305,7 @@ haste_status tail_topk(const haste_tail_desc *d, const haste_bce *bce, const Tai
     if (!m.tk_fused) return run_topk(bce, a.Z32, d->B, d->L, ws, m.cand, st);
     const int64_t ng = n_groups(d);
     float *mid_v = (float *)(a.tk_i + ng * pad_rows(d->B));
-    int32_t *mid_i = (int32_t *)(mid_v + (int64_t)d->B * topk_gm_segments(ng) * bce->topk);
+    int32_t *mid_i = (int32_t *)(mid_v + (int64_t)d->B * topk_gm_segments(ng, d->B).nseg * bce->topk);
     TRY_HIP(launch_topk_group_major(a.tk_v, a.tk_i, pad_rows(d->B), d->B, ng, bce->topk, mid_v, mid_i,
                                     bce->topk_val, bce->topk_idx, st),
             "top-K merge");

@@ -123,20 +123,34 @@ template <int CTRL>
 __device__ __forceinline__ unsigned dpp_u32(unsigned v) {
     return (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
 }
-// max over the 16 lanes of the row, and the smallest key among the lanes
-// holding it (every lane receives both)
+// Order-preserving map of a float to an unsigned key: a larger float has a
+// larger key, -0 is taken as +0 (so that key order is the float order), and
+// key 0 lies below every mapped number (-inf maps to 0x007fffff).  Integer
+// max folds into one DPP instruction; a float max over a DPP operand does
+// not (its operands are first quieted).
+__device__ __forceinline__ unsigned f32_order_key(float v) {
+    const unsigned b = __float_as_uint(v + 0.0f);
+    return b ^ ((unsigned)((int)b >> 31) | 0x80000000u);
+}
+__device__ __forceinline__ float f32_from_order_key(unsigned u) {
+    return __uint_as_float(u ^ (~(unsigned)((int)u >> 31) | 0x80000000u));
+}
+
+// Over the 16 lanes of the row: the largest value, and the smallest key among
+// the lanes holding it (every lane receives both); the max runs on order keys
 __device__ __forceinline__ void row16_argmax(float &v, unsigned &key) {
-    float m = v;
-    m = fmaxf(m, dpp_f32<0xB1>(m));
-    m = fmaxf(m, dpp_f32<0x4E>(m));
-    m = fmaxf(m, dpp_f32<0x141>(m));
-    m = fmaxf(m, dpp_f32<0x140>(m));
-    unsigned k = v == m ? key : 0xffffffffu;
+    const unsigned u0 = f32_order_key(v);
+    unsigned u = u0;
+    u = max(u, dpp_u32<0xB1>(u));
+    u = max(u, dpp_u32<0x4E>(u));
+    u = max(u, dpp_u32<0x141>(u));
+    u = max(u, dpp_u32<0x140>(u));
+    unsigned k = u0 == u ? key : 0xffffffffu;
     k = min(k, dpp_u32<0xB1>(k));
     k = min(k, dpp_u32<0x4E>(k));
     k = min(k, dpp_u32<0x141>(k));
     k = min(k, dpp_u32<0x140>(k));
-    v = m;
+    v = f32_from_order_key(u);
     key = k;
 }
 

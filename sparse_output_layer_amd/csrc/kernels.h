@@ -79,10 +79,13 @@ hipError_t launch_topk_merge_cands(const float *cand_v, const int32_t *cand_i, i
                                    int64_t ncand, int K, float *out_v, int32_t *out_i,
                                    hipStream_t st);
 // Merge of group-major candidates (ngroups x ld, row-contiguous; stage 1 fused
-// into the logits pass): segments of TOPK_GSEG groups per (32-row block) into
-// mid (rows x nseg x K), then per row into out (rows x K)
-constexpr int64_t TOPK_GSEG = 1024;
-int64_t topk_gm_segments(int64_t ngroups);
+// into the logits pass): segments of groups per block of rows into mid
+// (rows x nseg x K), then per row into out (rows x K)
+constexpr int64_t TOPK_GM_BLOCKS = 512;
+struct TopkGmSegs {
+    int64_t seg_groups, nseg;
+};
+TopkGmSegs topk_gm_segments(int64_t ngroups, int64_t rows);
 hipError_t launch_topk_group_major(const float *gv, const int32_t *gi, int64_t ld, int rows,
                                    int64_t ngroups, int K, float *mid_v, int32_t *mid_i,
                                    float *out_v, int32_t *out_i, hipStream_t st);

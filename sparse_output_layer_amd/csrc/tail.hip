@@ -631,33 +631,82 @@ __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, int store_z,
                 if (TK) {
                     // top-K stage 1 fused here, one bucket per group and K' = 1:
                     // per row, the group's largest logit (ties: smaller id), into
-                    // group-major lists (Ng x Bp): lane m = 0 of each q stores
-                    // rows 4q..4q+3 and 16+4q.. of the chunk, 16 bytes each
+                    // group-major lists (Ng x Bp); lane m = 0 of each q stores rows
+                    // 4q..4q+3 and 16+4q.. of the chunk, 16 bytes each.  The max
+                    // runs on order keys (key 0: label past L).  Groups of 16: the
+                    // lane's 8 rows (h2, i) reduce over the 16 lanes side by side;
+                    // larger groups: the lane's own slots first, then row by row
+                    // (the faster form for each, measured).
+                    if constexpr (JT == 1) {
+                        unsigned ku[8], k0[8], kj[8];
 #pragma unroll
-                    for (int h2 = 0; h2 < 2; ++h2) {
-                        f32x4 cv;
-                        u32x4 ci;
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            float bv = -INFINITY;
-                            unsigned bj = 0xffffffffu;
-#pragma unroll
-                            for (int jt = 0; jt < JT; ++jt) {   // ascending slots: ties keep the first
-                                const unsigned j = 16 * jt + m;
-                                const float z = zacc[h2][jt][i];
-                                if (g * G + j < a.L && (bj == 0xffffffffu || z > bv)) {
-                                    bv = z;
-                                    bj = j;
-                                }
-                            }
-                            row16_argmax(bv, bj);
-                            cv[i] = bj == 0xffffffffu ? -INFINITY : bv;
-                            ci[i] = bj == 0xffffffffu ? 0xffffffffu : (unsigned)(a.tk_off + g * G + bj);
+                        for (int r8 = 0; r8 < 8; ++r8) {
+                            ku[r8] = k0[r8] =
+                                g * G + m < a.L ? f32_order_key(zacc[r8 >> 2][0][r8 & 3]) : 0u;
+                            kj[r8] = (unsigned)m;
                         }
+#pragma unroll
+                        for (int r8 = 0; r8 < 8; ++r8) ku[r8] = max(ku[r8], dpp_u32<0xB1>(ku[r8]));
+#pragma unroll
+                        for (int r8 = 0; r8 < 8; ++r8) ku[r8] = max(ku[r8], dpp_u32<0x4E>(ku[r8]));
+#pragma unroll
+                        for (int r8 = 0; r8 < 8; ++r8) ku[r8] = max(ku[r8], dpp_u32<0x141>(ku[r8]));
+#pragma unroll
+                        for (int r8 = 0; r8 < 8; ++r8) ku[r8] = max(ku[r8], dpp_u32<0x140>(ku[r8]));
+#pragma unroll
+                        for (int r8 = 0; r8 < 8; ++r8) kj[r8] = k0[r8] == ku[r8] ? kj[r8] : 0xffffffffu;
+#pragma unroll
+                        for (int r8 = 0; r8 < 8; ++r8) kj[r8] = min(kj[r8], dpp_u32<0xB1>(kj[r8]));
+#pragma unroll
+                        for (int r8 = 0; r8 < 8; ++r8) kj[r8] = min(kj[r8], dpp_u32<0x4E>(kj[r8]));
+#pragma unroll
+                        for (int r8 = 0; r8 < 8; ++r8) kj[r8] = min(kj[r8], dpp_u32<0x141>(kj[r8]));
+#pragma unroll
+                        for (int r8 = 0; r8 < 8; ++r8) kj[r8] = min(kj[r8], dpp_u32<0x140>(kj[r8]));
                         if (m == 0) {
-                            const int64_t o = g * (int64_t)a.Bp + r0 + 16 * h2 + 4 * q;
-                            *(f32x4 *)(a.tk_v + o) = cv;
-                            *(u32x4 *)(a.tk_i + o) = ci;
+#pragma unroll
+                            for (int h2 = 0; h2 < 2; ++h2) {
+                                f32x4 cv;
+                                u32x4 ci;
+#pragma unroll
+                                for (int i = 0; i < 4; ++i) {
+                                    const unsigned u = ku[4 * h2 + i];
+                                    cv[i] = u == 0u ? -INFINITY : f32_from_order_key(u);
+                                    ci[i] = u == 0u ? 0xffffffffu
+                                                    : (unsigned)(a.tk_off + g * G + kj[4 * h2 + i]);
+                                }
+                                const int64_t o = g * (int64_t)a.Bp + r0 + 16 * h2 + 4 * q;
+                                *(f32x4 *)(a.tk_v + o) = cv;
+                                *(u32x4 *)(a.tk_i + o) = ci;
+                            }
+                        }
+                    } else {
+#pragma unroll
+                        for (int h2 = 0; h2 < 2; ++h2) {
+                            f32x4 cv;
+                            u32x4 ci;
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                float bv = -INFINITY;
+                                unsigned bj = 0xffffffffu;
+#pragma unroll
+                                for (int jt = 0; jt < JT; ++jt) {   // ascending slots: ties keep the first
+                                    const unsigned j = 16 * jt + m;
+                                    const float z = zacc[h2][jt][i];
+                                    if (g * G + j < a.L && (bj == 0xffffffffu || z > bv)) {
+                                        bv = z;
+                                        bj = j;
+                                    }
+                                }
+                                row16_argmax(bv, bj);
+                                cv[i] = bj == 0xffffffffu ? -INFINITY : bv;
+                                ci[i] = bj == 0xffffffffu ? 0xffffffffu : (unsigned)(a.tk_off + g * G + bj);
+                            }
+                            if (m == 0) {
+                                const int64_t o = g * (int64_t)a.Bp + r0 + 16 * h2 + 4 * q;
+                                *(f32x4 *)(a.tk_v + o) = cv;
+                                *(u32x4 *)(a.tk_i + o) = ci;
+                            }
                         }
                     }
                 }

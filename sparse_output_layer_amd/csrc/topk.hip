@@ -199,73 +199,140 @@ static hipError_t topk_stage2_go(int rows, int64_t ncand, const float *cand_v, c
     return hipGetLastError();
 }
 
-// Group-major candidates (ngroups x ld: entry (g, row) at g*ld + row): a
-// workgroup takes 32 rows x one segment of TOPK_GSEG groups; thread (row r,
-// part p) reads groups seg0 + p, + 8, .. (32 consecutive rows per group:
-// coalesced) into a K-list; the row's eight lists merge in LDS.
+// Group-major candidates (ngroups x ld, entry (g, row) at g*ld + row, ld a
+// multiple of 4, both arrays 16-byte aligned): a workgroup takes 4*LPG rows x
+// one segment of groups.  Lane l of wave w keeps a K-list for each of rows
+// 4(l % LPG) .. +3 of the block over groups seg0 + GPW*w + l / LPG, + 4*GPW,
+// .. (GPW = 64 / LPG groups per wave and load: a block of fewer than 256 rows
+// still fills the wave).  Every load is 16 bytes, LPG lanes read consecutive
+// rows of one group, and TOPK_GM_UNROLL loads are in flight per lane.  The
+// 4*GPW lists of a row then merge in LDS, one thread per row.
+constexpr int TOPK_GM_UNROLL = 8;
+
 template <int K>
 __global__ __launch_bounds__(256) void k_topk_group_major(const float *gv, const int32_t *gi, int64_t ld,
-                                                          int rows, int64_t ngroups, int nseg,
-                                                          float *mid_v, int32_t *mid_i) {
-    __shared__ float s_v[256 * K];
-    __shared__ int32_t s_i[256 * K];
-    const int r = threadIdx.x & 31, p = threadIdx.x >> 5;
-    const int row = blockIdx.x * 32 + r, seg = blockIdx.y;
-    const int64_t g0 = (int64_t)seg * TOPK_GSEG;
-    const int64_t g1 = g0 + TOPK_GSEG < ngroups ? g0 + TOPK_GSEG : ngroups;
-    float l_v[K];
-    int32_t l_i[K];
+                                                          int rows, int lpg, int64_t ngroups,
+                                                          int64_t seg_groups, int nseg, float *mid_v,
+                                                          int32_t *mid_i) {
+    __shared__ float s_v[1024 * K];
+    __shared__ int32_t s_i[1024 * K];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int gpw = 64 / lpg, sub = lane / lpg, lr = lane % lpg;
+    const int64_t rb = (int64_t)blockIdx.x * (4 * lpg);
+    const int64_t r4 = rb + 4 * lr;   // this lane's first row; r4 + 4 <= ld when r4 < rows
+    const int seg = blockIdx.y;
+    const int64_t g0 = (int64_t)seg * seg_groups;
+    const int64_t g1 = g0 + seg_groups < ngroups ? g0 + seg_groups : ngroups;
+    float l_v[4][K];
+    int32_t l_i[4][K];
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-        l_v[k] = -INFINITY;
-        l_i[k] = -1;
-    }
-    if (row < rows)
-        for (int64_t g = g0 + p; g < g1; g += 8) {
-            const int32_t id = gi[g * ld + row];
-            if (id >= 0) tk_insert<K>(l_v, l_i, gv[g * ld + row], id);
-        }
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-        s_v[threadIdx.x * K + k] = l_v[k];
-        s_i[threadIdx.x * K + k] = l_i[k];
-    }
-    __syncthreads();
-    if (p == 0 && row < rows) {
-        for (int pp = 1; pp < 8; ++pp)
-#pragma unroll
-            for (int k = 0; k < K; ++k) {
-                const int e = (pp * 32 + r) * K + k;
-                if (s_i[e] >= 0) tk_insert<K>(l_v, l_i, s_v[e], s_i[e]);
-            }
-        const int64_t o = ((int64_t)row * nseg + seg) * K;
+    for (int e = 0; e < 4; ++e)
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-            mid_v[o + k] = l_v[k];
-            mid_i[o + k] = l_i[k];
+            l_v[e][k] = -INFINITY;
+            l_i[e][k] = -1;
+        }
+    if (r4 < rows) {
+        constexpr int U = TOPK_GM_UNROLL;
+        const int64_t step = 4 * gpw;
+        for (int64_t gb = g0 + gpw * w + sub; gb < g1; gb += step * U) {
+            f32x4 xv[U];
+            u32x4 xi[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t g = gb + step * u < g1 ? gb + step * u : gb;   // clamped: no load is skipped
+                xv[u] = *(const f32x4 *)(gv + g * ld + r4);
+                xi[u] = *(const u32x4 *)(gi + g * ld + r4);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (gb + step * u >= g1) break;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int32_t id = (int32_t)xi[u][e];
+                    if (id >= 0 && r4 + e < rows) tk_insert<K>(l_v[e], l_i[e], xv[u][e], id);
+                }
+            }
+        }
+    }
+    // list (w, sub) of block row 4*lr + e at slot ((w*64 + lane)*4 + e)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            s_v[((w * 64 + lane) * 4 + e) * K + k] = l_v[e][k];
+            s_i[((w * 64 + lane) * 4 + e) * K + k] = l_i[e][k];
+        }
+    __syncthreads();
+    const int t = threadIdx.x;
+    const int64_t row = rb + t;
+    if (t < 4 * lpg && row < rows) {
+        float m_v[K];
+        int32_t m_i[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            m_v[k] = -INFINITY;
+            m_i[k] = -1;
+        }
+        for (int ww = 0; ww < 4; ++ww)
+            for (int sb = 0; sb < gpw; ++sb) {
+                const int base = ((ww * 64 + sb * lpg + (t >> 2)) * 4 + (t & 3)) * K;
+#pragma unroll
+                for (int k = 0; k < K; ++k)
+                    if (s_i[base + k] >= 0) tk_insert<K>(m_v, m_i, s_v[base + k], s_i[base + k]);
+            }
+        const int64_t o = (row * nseg + seg) * K;
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            mid_v[o + k] = m_v[k];
+            mid_i[o + k] = m_i[k];
         }
     }
 }
 
-int64_t topk_gm_segments(int64_t ngroups) { return (ngroups + TOPK_GSEG - 1) / TOPK_GSEG; }
+// Lanes per group of the group-major merge: 64 (256 rows a block), or the
+// fewest power of two whose 4 rows a lane cover all rows (at least 8)
+static int topk_gm_lpg(int64_t rows) {
+    int lpg = 8;
+    while (lpg < 64 && 4 * lpg < rows) lpg *= 2;
+    return lpg;
+}
+
+// Segments of the group-major merge: about TOPK_GM_BLOCKS workgroups over
+// all row blocks, at least 16 groups per wave and row
+TopkGmSegs topk_gm_segments(int64_t ngroups, int64_t rows) {
+    TopkGmSegs s{};
+    if (ngroups <= 0 || rows <= 0) return s;
+    const int lpg = topk_gm_lpg(rows);
+    const int64_t rblocks = (rows + 4 * lpg - 1) / (4 * lpg);
+    const int64_t want = (TOPK_GM_BLOCKS + rblocks - 1) / rblocks;
+    const int64_t minseg = 16 * 4 * (64 / lpg);
+    s.seg_groups = (ngroups + want - 1) / want;
+    if (s.seg_groups < minseg) s.seg_groups = minseg;
+    s.nseg = (ngroups + s.seg_groups - 1) / s.seg_groups;
+    return s;
+}
 
 template <int K>
 static hipError_t topk_gm_go(const float *gv, const int32_t *gi, int64_t ld, int rows, int64_t ngroups,
                              float *mid_v, int32_t *mid_i, float *out_v, int32_t *out_i,
                              hipStream_t st) {
-    const int64_t nseg = topk_gm_segments(ngroups);
-    hipLaunchKernelGGL(k_topk_group_major<K>, dim3((unsigned)((rows + 31) / 32), (unsigned)nseg),
-                       dim3(256), 0, st, gv, gi, ld, rows, ngroups, (int)nseg, mid_v, mid_i);
+    const TopkGmSegs s = topk_gm_segments(ngroups, rows);
+    const int lpg = topk_gm_lpg(rows);
+    hipLaunchKernelGGL(k_topk_group_major<K>,
+                       dim3((unsigned)((rows + 4 * lpg - 1) / (4 * lpg)), (unsigned)s.nseg), dim3(256), 0,
+                       st, gv, gi, ld, rows, lpg, ngroups, s.seg_groups, (int)s.nseg, mid_v, mid_i);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return topk_stage2_go<K>(rows, nseg * K, mid_v, mid_i, out_v, out_i, st);
+    return topk_stage2_go<K>(rows, s.nseg * K, mid_v, mid_i, out_v, out_i, st);
 }
 
 hipError_t launch_topk_group_major(const float *gv, const int32_t *gi, int64_t ld, int rows,
                                    int64_t ngroups, int K, float *mid_v, int32_t *mid_i,
                                    float *out_v, int32_t *out_i, hipStream_t st) {
     if (rows <= 0 || ngroups <= 0) return hipSuccess;
-    if (topk_gm_segments(ngroups) > 65535) return hipErrorInvalidValue;
+    if ((ld & 3) || ld < rows || (((uintptr_t)gv | (uintptr_t)gi) & 15)) return hipErrorInvalidValue;
+    if (topk_gm_segments(ngroups, rows).nseg > 65535) return hipErrorInvalidValue;
     switch (K) {
     case 1: return topk_gm_go<1>(gv, gi, ld, rows, ngroups, mid_v, mid_i, out_v, out_i, st);
     case 2: return topk_gm_go<2>(gv, gi, ld, rows, ngroups, mid_v, mid_i, out_v, out_i, st);

@@ -11,7 +11,8 @@ checks are on outputs it computes one by one:
 
 The 8.6M-label workload also asks for the per-row top-5 over all labels
 (head and tail lists merged); its oracle is streamed over the same chunks
-of groups as the loss.  The 3M-label workload runs the lean form (dz
+of groups as the loss, and so is the two-stage oracle of the inference form
+(stage 1 inside the logits pass, one bucket per label group, K' = 1).  The 3M-label workload runs the lean form (dz
 recomputed in the dX pass, nothing of size B x L stored); the others keep
 the dz tiles."""
 import numpy as np
@@ -72,6 +73,13 @@ def test_full_size_step(H, name):
     H.haste_tail_step_dx(d.X, d.idx, d.W, L, G, bt, dX, ws_t, accumulate_dX=True, lean=lean)
     if K:
         mv, mi = H.haste_topk_merge(bh.topk_val, bh.topk_idx, bt.topk_val, bt.topk_idx)
+        # the inference form: top-K stage 1 inside the logits pass (one bucket
+        # per label group, K' = 1), merged with the head's exact lists
+        bf = H.Bce(d.row_ptr, d.labels, Hn, s, topk_kprime=1, topk_buckets=ng)
+        bf.topk_val = torch.empty_like(bh.topk_val)
+        bf.topk_idx = torch.empty_like(bh.topk_idx)
+        H.haste_tail_fwd(d.X, d.idx, d.W, L, G, bce=bf)
+        fv, fi = H.haste_topk_merge(bh.topk_val, bh.topk_idx, bf.topk_val, bf.topk_idx)
     torch.cuda.synchronize()
     print("  GPU step done", flush=True)
 
@@ -122,6 +130,7 @@ def test_full_size_step(H, name):
     if K:
         Zh_full, Zha_full = oracle.head_logits(X, Wh, want_abs=True)
         tv_, ti_ = oracle.topk(Zh_full, K + 1, id_offset=0)
+        tf_, tfi_ = tv_.copy(), ti_.copy()
         amax = Zha_full.max(axis=1)
     chunk = max(1, (1 << 24) // (B * G))
     for g0 in range(0, ng, chunk):
@@ -133,6 +142,9 @@ def test_full_size_step(H, name):
         if K:
             cv, ci = oracle.topk(Z, min(K + 1, Z.shape[1]), id_offset=Hn + g0 * G)
             tv_, ti_ = _merge_lists(tv_, ti_, cv, ci, K + 1)
+            # two-stage lists of the chunk's whole groups (buckets of G labels)
+            sv, si = oracle.topk_two_stage(Z, K, 1, G, id_offset=Hn + g0 * G)
+            tf_, tfi_ = _merge_lists(tf_, tfi_, sv, si, K + 1)
             amax = np.maximum(amax, Za.max(axis=1))
     check_loss("step loss", loss.item(), ref_loss, "bf16")
     if K:
@@ -147,7 +159,9 @@ def test_full_size_step(H, name):
             return float(Zg[0, t - g * G])
         check_topk_lists("merged top-K", mv.cpu().numpy(), mi.cpu().numpy(), tv_, ti_,
                          topk_tol(amax, "bf16"), zfun, K, Hn + L)
-        print("  top-K matches", flush=True)
+        check_topk_lists("merged top-K, stage 1 fused", fv.cpu().numpy(), fi.cpu().numpy(), tf_, tfi_,
+                         topk_tol(amax, "bf16"), zfun, K, Hn + L)
+        print("  top-K matches (exact and fused stage 1)", flush=True)
 
 
 def _merge_lists(av, ai, bv, bi, n):

@@ -103,6 +103,10 @@ APPROX = [
     dict(B=40, D=128, H=48, L=4000, G=16, F=64, K=5, KP=1, NB=250),
     dict(B=70, D=200, H=48, L=3000, G=64, F=32, K=8, KP=1, NB=47),
     dict(B=33, D=768, H=48, L=2000, G=32, F=128, K=3, KP=1, NB=63, step=True),
+    # the merge's lane layouts (8 and 64 lanes per group), several group
+    # segments with a ragged last one, two row blocks with a ragged last one
+    dict(B=20, D=64, H=48, L=30000, G=32, F=32, K=4, KP=1, NB=938),
+    dict(B=300, D=64, H=48, L=40000, G=16, F=32, K=5, KP=1, NB=2500),
 ]
 
 
