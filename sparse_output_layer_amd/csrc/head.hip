@@ -185,75 +185,89 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g) {
 // ------------------------------------------------------------ pipelined GEMM
 // Same contractions and epilogues as k_gemm, for shapes whose M, N, K and
 // split length are multiples of 8 (every head of the workloads): M tile of
-// TMT = 64 or 128 rows, N tile 128, K step 64, the operand tiles of step k+2
-// loaded into registers while step k runs (two register sets, alternating,
-// so a load has two steps to land), LDS double-buffered.  Loads are issued
-// unconditionally from clamped addresses and zeroed outside the matrix at
-// the LDS store, so the compiler waits for exactly the set it stores.
+// TMT = 64 or 128 rows, N tile 128, K step 64.  Operand tiles go from global
+// memory straight into LDS (16 bytes a lane, 1 KB a wave instruction) through
+// a ring of GEMM_NS stages, so the copies of the next GEMM_NS - 1 steps are in
+// flight while one step is computed.  Each stage is an LDS array of its own
+// and the K loop is unrolled by GEMM_NS, so every access names its stage and
+// the compiler sees that a read of one stage does not need the copies into
+// the others.  Addresses are clamped into the matrix (nothing is skipped);
+// K slots past the split's end are zeroed in the operand registers.
 constexpr int TK2 = 64;
-constexpr int KROW2 = TK2 + 8;    // K-major LDS row (shorts): 144 B
+constexpr int GEMM_NS = 3;
 
-// ROWS x 64 operand tile: ROWS/32 16-byte loads per thread.  Bit `it` of the
-// returned mask says whether segment `it` lies inside the matrix.
-template <bool KMAJ, int ROWS>
-__device__ __forceinline__ unsigned load_tile2(const unsigned short *__restrict__ P, int ld, int r0,
-                                               int rows, int k0, int K, u32x4 (&v)[ROWS / 32]) {
-    constexpr int SEG = ROWS / 8;     // M-major: 16-byte segments per K row
-    unsigned mask = 0;
-#pragma unroll
-    for (int it = 0; it < ROWS / 32; ++it) {
-        const int i = threadIdx.x + it * 256;
-        int r, k;
-        if (KMAJ) {  // row r (M or N), 8 segments of 8 along K
-            r = i >> 3;
-            k = (i & 7) * 8;
-        } else {     // row k (64 rows), SEG segments of 8 along M or N
-            k = i / SEG;
-            r = (i % SEG) * 8;
-        }
-        const int gr = r0 + r, gk = k0 + k;
-        // rows and K are multiples of 8: a segment is wholly inside or outside
-        const bool ok = gr < rows && gk < K;
-        const int cr = gr < rows ? gr : rows - (KMAJ ? 1 : 8);
-        const int ck = gk < K ? gk : K - (KMAJ ? 8 : 1);
-        v[it] = KMAJ ? *(const u32x4 *)(P + (int64_t)cr * ld + ck)
-                     : *(const u32x4 *)(P + (int64_t)ck * ld + cr);
-        mask |= (ok ? 1u : 0u) << it;
-    }
-    return mask;
+// LDS layouts (no padding: the copies write 1 KB contiguous).
+// K-major tile, ROWS rows x 64 K (128 B a row): the 16-byte segment s of row r
+// sits at s ^ ((r >> 1) & 7), so the 16 consecutive rows of an operand read
+// fall on 16 different 16-byte bank groups.
+__device__ __forceinline__ int kmaj_seg(int r, int s) { return s ^ ((r >> 1) & 7); }
+// M-major tile, 64 K rows x ROWS (2 ROWS bytes a row): the 32-byte chunk of a
+// K row is permuted by bits of the row, so that the 16 K rows a transposing
+// read covers (8q + j, q and j in 0..3) spread over all chunks, two apiece.
+template <int ROWS>
+__device__ __forceinline__ int mmaj_seg(int k, int s) {
+    if (ROWS == 128) return s ^ (2 * ((k & 3) | (((k >> 3) & 1) << 2)));
+    return s ^ (2 * (((k >> 1) & 1) | (((k >> 3) & 1) << 1)));
 }
 
+// Copies of one ROWS x 64 operand tile of step k0 into S: ROWS/32 one-KB
+// blocks per wave.
 template <bool KMAJ, int ROWS>
-__device__ __forceinline__ void store_tile2(unsigned short *S, const u32x4 (&v)[ROWS / 32],
-                                            unsigned mask) {
-    constexpr int SEG = ROWS / 8, MR = ROWS + 8;
+__device__ __forceinline__ void copy_tile3(const unsigned short *P, int ld, int r0, int rows, int k0,
+                                           int K, unsigned short *S, int w, int lane) {
+    constexpr int NC = ROWS / 32;
 #pragma unroll
-    for (int it = 0; it < ROWS / 32; ++it) {
-        const int i = threadIdx.x + it * 256;
-        const u32x4 x = ((mask >> it) & 1u) ? v[it] : (u32x4){0u, 0u, 0u, 0u};
-        if (KMAJ) *(u32x4 *)(S + (i >> 3) * KROW2 + (i & 7) * 8) = x;
-        else *(u32x4 *)(S + (i / SEG) * MR + (i % SEG) * 8) = x;
+    for (int c = 0; c < NC; ++c) {
+        const int blk = w * NC + c;
+        const unsigned short *src;
+        if (KMAJ) {   // 8 rows of 128 B per block
+            const int row = 8 * blk + (lane >> 3);
+            const int sg = kmaj_seg(row, lane & 7);
+            const int gr = r0 + row < rows ? r0 + row : rows - 1;
+            const int gk = k0 + 8 * sg <= K - 8 ? k0 + 8 * sg : K - 8;
+            src = P + (int64_t)gr * ld + gk;
+        } else {      // ROWS/8 lanes per K row
+            constexpr int LPR = ROWS / 8;
+            const int kr = blk * (64 / LPR) + lane / LPR;
+            const int sg = mmaj_seg<ROWS>(kr, lane % LPR);
+            const int gk = k0 + kr < K ? k0 + kr : K - 1;
+            const int gc = r0 + 8 * sg <= rows - 8 ? r0 + 8 * sg : rows - 8;
+            src = P + (int64_t)gk * ld + gc;
+        }
+        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)(S + blk * 512), 16,
+                                         0, 0);
     }
 }
 
 // operand of the 16 rows from r, K slots 32ks + 8q .. +7
 template <bool KMAJ, int ROWS>
-__device__ __forceinline__ bf16x8 read_operand2(const unsigned short *S, int r, int ks, int q, int m) {
-    constexpr int MR = ROWS + 8;
-    if (KMAJ) return *(const bf16x8 *)(S + (r + m) * KROW2 + 32 * ks + 8 * q);
-    const unsigned short *Sk = S + 32 * ks * MR;
-    i16x4 a0 = lds_read_tr(Sk + (8 * q + (m >> 2)) * MR + r + 4 * (m & 3));
-    i16x4 a1 = lds_read_tr(Sk + (8 * q + 4 + (m >> 2)) * MR + r + 4 * (m & 3));
+__device__ __forceinline__ bf16x8 read_operand3(const unsigned short *S, int r, int ks, int q, int m) {
+    if (KMAJ) {
+        const int row = r + m;
+        return *(const bf16x8 *)(S + row * TK2 + 8 * kmaj_seg(row, 4 * ks + q));
+    }
+    const int col = r + 4 * (m & 3), sg = col >> 3, within = col & 7;
+    const int k0 = 32 * ks + 8 * q + (m >> 2);
+    i16x4 a0 = lds_read_tr(S + k0 * ROWS + 8 * mmaj_seg<ROWS>(k0, sg) + within);
+    i16x4 a1 = lds_read_tr(S + (k0 + 4) * ROWS + 8 * mmaj_seg<ROWS>(k0 + 4, sg) + within);
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// s_waitcnt with only the vector-memory count constrained
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 template <bool A_KMAJ, bool B_KMAJ, int EPI, int TMT>
 __global__ __launch_bounds__(256, 2) void k_gemm2(GemmArgs g) {
     constexpr int MI = TMT / 32;      // 16-row MFMA tiles per wave (waves: 2 along M, 2 along N)
-    constexpr int NA = TMT / 32, NB = TN / 32;
-    constexpr int ASZ = A_KMAJ ? TMT * KROW2 : TK2 * (TMT + 8);
-    constexpr int BSZ = B_KMAJ ? TN * KROW2 : TK2 * (TN + 8);
-    __shared__ __attribute__((aligned(16))) unsigned short sm[2 * (ASZ + BSZ)];
+    constexpr int ASZ = TMT * TK2, BSZ = TN * TK2;   // shorts
+    constexpr int LPS = TMT / 32 + TN / 32;          // copies per wave and step
+    __shared__ __attribute__((aligned(1024))) unsigned short st0[ASZ + BSZ];
+    __shared__ __attribute__((aligned(1024))) unsigned short st1[ASZ + BSZ];
+    __shared__ __attribute__((aligned(1024))) unsigned short st2[ASZ + BSZ];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int q = lane >> 4, m = lane & 15;
     const int wm = (w >> 1) * (TMT / 2), wn = (w & 1) * 64;
@@ -269,9 +283,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm2(GemmArgs g) {
     const int kbeg = bz * g.k_split;
     int kend = kbeg + g.k_split;
     if (kend > g.K) kend = g.K;
-    // steps, rounded up to even: a step past the end loads zeros (clamped,
-    // masked) and adds nothing, and the loop below then has no exit
-    const int nk = ((kend - kbeg + TK2 - 1) / TK2 + 1) & ~1;
+    const int nk = (kend - kbeg + TK2 - 1) / TK2;
     // BCE: the positives of the tile (TMT rows x 4 bitmap words) go to LDS
     // first, so the epilogue reads them there instead of once per logit
     __shared__ uint32_t bm_tile[EPI == EPI_BCE ? TMT * 4 : 1];
@@ -289,62 +301,70 @@ __global__ __launch_bounds__(256, 2) void k_gemm2(GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-    u32x4 ra0[NA], rb0[NB], ra1[NA], rb1[NB];
-    unsigned mk0 = 0, mk1 = 0;   // validity bits: A segments from bit 0, B from bit 8
-    auto load = [&](int kt, u32x4 (&ra)[NA], u32x4 (&rb)[NB], unsigned &mk) {
+    auto issue = [&](int kt, unsigned short *S) {
         const int k0 = kbeg + kt * TK2;
-        mk = load_tile2<A_KMAJ, TMT>(g.A, g.lda, m0, g.M, k0, kend, ra);
-        mk |= load_tile2<B_KMAJ, TN>(g.Bm, g.ldb, n0, g.N, k0, kend, rb) << 8;
+        copy_tile3<A_KMAJ, TMT>(g.A, g.lda, m0, g.M, k0, g.K, S, w, lane);
+        copy_tile3<B_KMAJ, TN>(g.Bm, g.ldb, n0, g.N, k0, g.K, S + ASZ, w, lane);
     };
-    auto store = [&](int buf, const u32x4 (&ra)[NA], const u32x4 (&rb)[NB], unsigned mk) {
-        unsigned short *S = sm + buf * (ASZ + BSZ);
-        store_tile2<A_KMAJ, TMT>(S, ra, mk);
-        store_tile2<B_KMAJ, TN>(S + ASZ, rb, mk >> 8);
-    };
-    auto compute = [&](int buf) {
-        const unsigned short *SA = sm + buf * (ASZ + BSZ);
-        const unsigned short *SB = SA + ASZ;
+    auto compute = [&](int kt, const unsigned short *S) {
+        const int k0 = kbeg + kt * TK2;
+        const bool tail = k0 + TK2 > kend;   // wave-uniform
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             bf16x8 av[MI], bv[4];
 #pragma unroll
-            for (int i = 0; i < MI; ++i) av[i] = read_operand2<A_KMAJ, TMT>(SA, wm + 16 * i, ks, q, m);
+            for (int i = 0; i < MI; ++i) av[i] = read_operand3<A_KMAJ, TMT>(S, wm + 16 * i, ks, q, m);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) bv[j] = read_operand2<B_KMAJ, TN>(SB, wn + 16 * j, ks, q, m);
+            for (int j = 0; j < 4; ++j) bv[j] = read_operand3<B_KMAJ, TN>(S + ASZ, wn + 16 * j, ks, q, m);
+            if (tail && k0 + 32 * ks + 8 * q >= kend) {
+                // K slots past the split: zero on both sides
+#pragma unroll
+                for (int i = 0; i < MI; ++i) av[i] = (bf16x8){};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) bv[j] = (bf16x8){};
+            }
 #pragma unroll
             for (int i = 0; i < MI; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(av[i], bv[j], acc[i][j]);
         }
     };
-    // iteration kt: loads of step kt+2 go out, step kt runs from LDS, step
-    // kt+1 (loaded during iteration kt-1) is stored to the other buffer.
-    if (nk > 0) {
-        load(0, ra0, rb0, mk0);
-        load(1, ra1, rb1, mk1);
-        store(0, ra0, rb0, mk0);
-        __syncthreads();
-        // the scheduling barriers keep each step's loads ahead of its MFMAs
-        for (int kt = 0; kt < nk; kt += 2) {
-            load(kt + 2, ra0, rb0, mk0);
-            __builtin_amdgcn_sched_barrier(0);
-            compute(0);
-            __builtin_amdgcn_sched_barrier(0);
-            store(1, ra1, rb1, mk1);
-            __syncthreads();
-            load(kt + 3, ra1, rb1, mk1);
-            __builtin_amdgcn_sched_barrier(0);
-            compute(1);
-            __builtin_amdgcn_sched_barrier(0);
-            store(0, ra0, rb0, mk0);
-            __syncthreads();
-        }
+    // Step kt: wait for this wave's copies of step kt (those of step kt+1 stay
+    // in flight), then a barrier: everyone's copies have landed, and every
+    // wave is done with step kt-1, whose stage the copies of step kt+2 then
+    // overwrite.  A bare s_barrier: the fence of __syncthreads would wait for
+    // every copy in flight (the LDS reads of step kt-1 have returned: their
+    // MFMAs are issued).  The loop has no exit but its end (the steps run up
+    // to a multiple of GEMM_NS; those past the split's end see zeroed operands
+    // and add nothing) and copies are issued unconditionally (clamped
+    // addresses), so the compiler's own count of copies in flight is the same
+    // on every path and it does not wait for the other stages; an exit in the
+    // middle costs a full wait there and twice the registers.  All copies are
+    // drained after the loop.
+    auto sync = [&]() {
+        wait_vm<LPS>();
+        asm volatile("s_barrier" ::: "memory");
+    };
+    issue(0, st0);
+    issue(1, st1);
+    for (int kt = 0; kt < nk; kt += GEMM_NS) {
+        sync();
+        issue(kt + 2, st2);
+        compute(kt, st0);
+        sync();
+        issue(kt + 3, st0);
+        compute(kt + 1, st1);
+        sync();
+        issue(kt + 4, st1);
+        compute(kt + 2, st2);
     }
+    wait_vm<0>();
 
     // epilogue: lane owns C[m0+wm+16i+4q+e][n0+wn+16j+m].  BCE with the
     // hardware exp / rcp / log: sigmoid(z) from e = exp(-|z|), and
     // softplus(z) = max(z, 0) + log(1 + e), the logs taken of products of
-    // sixteen (1 + e) factors (each in [1, 2]).
+    // sixteen (1 + e) factors (each in [1, 2]).  Whole tiles take a path with
+    // no per-element branches.
     float lsum = 0.f, lin = 0.f, prod = 1.f;
     uint32_t bw[MI][4][2];   // bitmap words of the lane's rows: columns wn .. wn+31, wn+32 .. wn+63
     if (EPI == EPI_BCE) {
@@ -356,39 +376,77 @@ __global__ __launch_bounds__(256, 2) void k_gemm2(GemmArgs g) {
                 for (int h = 0; h < 2; ++h)
                     bw[i][e][h] = bm_tile[(wm + 16 * i + 4 * q + e) * 4 + (wn >> 5) + h];
     }
+    const bool whole = m0 + TMT <= g.M && n0 + TN <= g.N;
+    if (EPI == EPI_BCE && whole && g.bitmap && g.dZout && !g.Zout && !g.Z32) {
 #pragma unroll
-    for (int i = 0; i < MI; ++i) {
+        for (int i = 0; i < MI; ++i) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int col = n0 + wn + 16 * j + m;
+            for (int j = 0; j < 4; ++j) {
+                const int col = n0 + wn + 16 * j + m;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int row = m0 + wm + 16 * i + 4 * q + e;
-                if (row >= g.M || col >= g.N) continue;
-                const float v = acc[i][j][e];
-                const int64_t o = (int64_t)row * g.N + col;
-                if (EPI == EPI_BCE) {
-                    if (g.bitmap) {
-                        const float y = (float)((bw[i][e][j >> 1] >> ((16 * j + m) & 31)) & 1u);
-                        const float ex = fast_exp_neg_abs(v);
-                        float den;
-                        const float sg = fast_sigmoid(v, ex, den);
-                        prod *= den;
-                        lin += fmaxf(v, 0.f) - y * v;
-                        if (g.dZout) g.dZout[o] = f32_to_bf16(g.s * (sg - y));
-                    }
-                    if (g.Zout) g.Zout[o] = f32_to_bf16(v);
-                    if (g.Z32) g.Z32[o] = v;
-                } else if (EPI == EPI_STORE16) {
-                    g.C16[o] = f32_to_bf16(v);
-                } else {
-                    atomicAdd(g.C32 + o, v);
+                for (int e = 0; e < 4; ++e) {
+                    const int row = m0 + wm + 16 * i + 4 * q + e;
+                    const float v = acc[i][j][e];
+                    const float y = (float)((bw[i][e][j >> 1] >> ((16 * j + m) & 31)) & 1u);
+                    const float ex = fast_exp_neg_abs(v);
+                    float den;
+                    const float sg = fast_sigmoid(v, ex, den);
+                    prod *= den;
+                    lin += fmaxf(v, 0.f) - y * v;
+                    g.dZout[(int64_t)row * g.N + col] = f32_to_bf16(g.s * (sg - y));
                 }
             }
-        }
-        if (EPI == EPI_BCE) {   // sixteen factors per i
             lsum += fast_log(prod);
             prod = 1.f;
+        }
+    } else if (EPI != EPI_BCE && whole) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int col = n0 + wn + 16 * j + m;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int64_t o = (int64_t)(m0 + wm + 16 * i + 4 * q + e) * g.N + col;
+                    if (EPI == EPI_STORE16) g.C16[o] = f32_to_bf16(acc[i][j][e]);
+                    else atomicAdd(g.C32 + o, acc[i][j][e]);
+                }
+            }
+    } else {
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int col = n0 + wn + 16 * j + m;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int row = m0 + wm + 16 * i + 4 * q + e;
+                    if (row >= g.M || col >= g.N) continue;
+                    const float v = acc[i][j][e];
+                    const int64_t o = (int64_t)row * g.N + col;
+                    if (EPI == EPI_BCE) {
+                        if (g.bitmap) {
+                            const float y = (float)((bw[i][e][j >> 1] >> ((16 * j + m) & 31)) & 1u);
+                            const float ex = fast_exp_neg_abs(v);
+                            float den;
+                            const float sg = fast_sigmoid(v, ex, den);
+                            prod *= den;
+                            lin += fmaxf(v, 0.f) - y * v;
+                            if (g.dZout) g.dZout[o] = f32_to_bf16(g.s * (sg - y));
+                        }
+                        if (g.Zout) g.Zout[o] = f32_to_bf16(v);
+                        if (g.Z32) g.Z32[o] = v;
+                    } else if (EPI == EPI_STORE16) {
+                        g.C16[o] = f32_to_bf16(v);
+                    } else {
+                        atomicAdd(g.C32 + o, v);
+                    }
+                }
+            }
+            if (EPI == EPI_BCE) {   // sixteen factors per i
+                lsum += fast_log(prod);
+                prod = 1.f;
+            }
         }
     }
     if (EPI == EPI_BCE && g.loss) {
