@@ -8,11 +8,15 @@ D=768 bf16 features, H=8,192 head labels, L=662,000 tail labels in groups of
 G=16 sharing F=128 fan-in indices, W ~ N(0, 0.02), 5 Zipf(1.1) positives per
 row; synthetic, seeded, resident in HBM before timing starts.
 
-One step = haste_head_step + haste_tail_prepare + haste_tail_step_dw +
-haste_tail_step_dx (the split form of haste_tail_step), all on one stream.
-W warm-up steps, then K timed steps between device synchronisations; HIP
-events around every call give each kernel's average duration inside the
-timed region.  Prints one JSON line.
+One step = haste_tail_prepare + haste_tail_step_dw + haste_tail_step_dx (the
+split form of haste_tail_step) on the main stream and haste_head_step on a
+side stream beside the dW/logits pass, both adding into one dX.  W warm-up
+steps, then K timed steps between device synchronisations; HIP events on the
+main stream around the dominant tail pass give its average duration inside
+the timed region (the roofline figure).  A serial pass of K steps before
+them, one call after another with an event between each, gives the
+per-kernel breakdown ("kernels_serial") and picks the dominant pass.  Prints
+one JSON line.
 """
 from __future__ import annotations
 
@@ -451,53 +455,100 @@ def main():
     ws_h = torch.empty(max(256, H.haste_head_workspace_bytes(X, Wh, bce_h)), dtype=torch.uint8,
                        device=dev)
     names = ["head_step", "tail_prepare", "tail_step_dw", "tail_step_dx"] + (["topk_merge"] if K else [])
+    side = torch.cuda.Stream()   # default priority, like every stream here
 
-    def step(ev=None):
+    def step(ev, dom_dx=False):
+        """One training step.  The head's step runs on a side stream once the
+        tail's prep is done, beside the tail's dW/logits pass: its workgroups
+        take the CUs that pass leaves idle (the pass hands out its runs
+        dynamically).  Both branches add into dX and the loss atomically, so
+        both are zeroed first.  ev: two events on the main stream around the
+        dW pass (around the dX pass when dom_dx); ev[0] also releases the
+        side stream."""
+        main = torch.cuda.current_stream()
         loss.zero_()
-        if ev is not None:
-            ev[0].record()
-        H.haste_head_step(X, Wh, bce_h, dWh, dX, workspace=ws_h)
-        if ev is not None:
-            ev[1].record()
+        dX.zero_()
         H.haste_tail_prepare(X, idx, L, G, bce_t, ws_t)
-        if ev is not None:
-            ev[2].record()
-        H.haste_tail_step_dw(X, idx, W, L, G, bce_t, dW, ws_t)
-        if ev is not None:
-            ev[3].record()
-        H.haste_tail_step_dx(X, idx, W, L, G, bce_t, dX, ws_t, accumulate_dX=True)
-        if ev is not None:
-            ev[4].record()
+        ev[0].record(main)
+        if dom_dx:
+            H.haste_tail_step_dw(X, idx, W, L, G, bce_t, dW, ws_t)
+            ev[0].record(main)
+        side.wait_event(ev[0])
+        with torch.cuda.stream(side):
+            H.haste_head_step(X, Wh, bce_h, dWh, dX, accumulate_dX=True, workspace=ws_h)
+        if not dom_dx:
+            H.haste_tail_step_dw(X, idx, W, L, G, bce_t, dW, ws_t)
+        else:
+            H.haste_tail_step_dx(X, idx, W, L, G, bce_t, dX, ws_t, accumulate_dX=True)
+        ev[1].record(main)
+        if not dom_dx:
+            H.haste_tail_step_dx(X, idx, W, L, G, bce_t, dX, ws_t, accumulate_dX=True)
+        main.wait_stream(side)
         if K:
             H.haste_topk_merge(bce_h.topk_val, bce_h.topk_idx, bce_t.topk_val, bce_t.topk_idx)
-            if ev is not None:
-                ev[5].record()
 
+    def serial_step(ev):
+        """The same calls one after another on one stream, an event between
+        each: the per-kernel breakdown (not the timed figure)."""
+        loss.zero_()
+        ev[0].record()
+        H.haste_head_step(X, Wh, bce_h, dWh, dX, workspace=ws_h)
+        ev[1].record()
+        H.haste_tail_prepare(X, idx, L, G, bce_t, ws_t)
+        ev[2].record()
+        H.haste_tail_step_dw(X, idx, W, L, G, bce_t, dW, ws_t)
+        ev[3].record()
+        H.haste_tail_step_dx(X, idx, W, L, G, bce_t, dX, ws_t, accumulate_dX=True)
+        ev[4].record()
+        if K:
+            H.haste_topk_merge(bce_h.topk_val, bce_h.topk_idx, bce_t.topk_val, bce_t.topk_idx)
+            ev[5].record()
+
+    def mkev(n):
+        return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+    # warm-up, then the serial breakdown (it picks the dominant tail pass,
+    # the one the timed steps carry events around)
     for _ in range(args.warmup):
-        step()
+        serial_step(mkev(len(names) + 1))
+    sevs = [mkev(len(names) + 1) for _ in range(args.steps)]
+    for k in range(args.steps):
+        serial_step(sevs[k])
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+    per = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in sevs])) * 1e3
+           for i, n in enumerate(names)}          # microseconds
+    dom = max(["tail_step_dw", "tail_step_dx"], key=lambda n: per[n])
+    dom_dx = dom == "tail_step_dx"
+    for _ in range(args.warmup):
+        step(mkev(2), dom_dx)
+    torch.cuda.synchronize()
+    evs = [mkev(2) for _ in range(args.steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t0.record()
     for k in range(args.steps):
-        step(evs[k])
+        step(evs[k], dom_dx)
     t1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms = t0.elapsed_time(t1) / args.steps
-    per = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) * 1e3
+    live_dom = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e3
+    step_loss = loss.item()
+    # per-kernel breakdown: the same number of serial steps, after the timed ones
+    sevs = [mkev(len(names) + 1) for _ in range(args.steps)]
+    for k in range(args.steps):
+        serial_step(sevs[k])
+    torch.cuda.synchronize()
+    per = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in sevs])) * 1e3
            for i, n in enumerate(names)}          # microseconds
     step_loss = loss.item()
 
     alg = algorithmic(cfg)
     tot_flops = sum(v["flops"] for v in alg.values())
     tot_bytes = sum(v["bytes"] for v in alg.values())
-    tail_kernels = ["tail_step_dw", "tail_step_dx"]
-    dom = max(tail_kernels, key=lambda n: per[n])
-    a_tf = alg[dom]["flops"] / (per[dom] * 1e-6) / 1e12
+    a_tf = alg[dom]["flops"] / (live_dom * 1e-6) / 1e12
     kernels = {n: {"avg_us": round(per[n], 2),
                    "tflops": round(alg[n]["flops"] / (per[n] * 1e-6) / 1e12, 1),
                    "gbs": round(alg[n]["bytes"] / (per[n] * 1e-6) / 1e9, 1)} for n in names}
@@ -525,14 +576,14 @@ def main():
                      "frac": round(a_tf / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(dom, cfg.name),
                      "algorithmic_flops_per_launch": alg[dom]["flops"],
-                     "avg_launch_us": round(per[dom], 2)},
+                     "avg_launch_us": round(live_dom, 2)},
         "step_roofline": {"algorithmic_tflop": round(tot_flops / 1e12, 4),
                           "algorithmic_gb": round(tot_bytes / 1e9, 4),
                           "achieved_tflops": round(step_tf, 1),
                           "frac_mfma": round(step_tf / PEAK_BF16_TFLOPS, 4),
                           "tail_tflops": round(tail_tf, 1),
                           "tail_frac_mfma": round(tail_tf / PEAK_BF16_TFLOPS, 4)},
-        "kernels": kernels,
+        "kernels_serial": kernels,
         "loss": step_loss,
         "wall_s": round(wall, 3),
         "gen_s": round(t_gen, 2),

@@ -58,7 +58,7 @@ inline int pad_rows(int B) { return (B + 63) / 64 * 64; }
 
 // ----------------------------------------------------------- workspace maps
 struct TailWs {
-    size_t xt, cnt, ptr, ent, idxp, perm, dz, dzt, z32, cand, total;
+    size_t xt, cnt, ptr, ent, idxp, perm, sched, dz, dzt, z32, cand, total;
     bool has_dzt, has_topk, tk_fused;
 };
 
@@ -81,6 +81,7 @@ TailWs tail_ws(const haste_tail_desc *d, const haste_bce *bce) {
         w.cnt = o; o += al256((size_t)(nnz > 0 ? nnz : 1) * 20 + 8);  // keys, sorted, ranks, count
         w.ptr = o; o += al256((size_t)(ng + 4) * 4);   // +3: 16-byte reads of a pair
         w.ent = o; o += al256((size_t)(nnz > 0 ? nnz : 1) * 4);
+        w.sched = o; o += 256;   // the dW/logits pass's run counters
         // the dW/logits pass's feature order: idx reordered, and the order
         // (groups of 16 and more; G = 1 gathers per label)
         if (d->G > 1) {
@@ -226,6 +227,7 @@ TailArgs tail_args(const haste_tail_desc *d, const void *X, const int32_t *idx, 
     a.idxp = (const unsigned short *)B8(ws, m.idxp);
     a.perm = (const unsigned char *)B8(ws, m.perm);
     a.dzt = m.has_dzt ? (unsigned short *)B8(ws, m.dzt) : nullptr;
+    a.sched = (unsigned *)B8(ws, m.sched);
     a.Z32 = m.has_topk && !m.tk_fused ? (float *)B8(ws, m.z32) : nullptr;
     if (m.tk_fused) {   // the group-major bucket lists, written by the logits pass (K' = 1)
         a.tk_v = (float *)B8(ws, m.cand);
@@ -243,7 +245,8 @@ TailArgs tail_args(const haste_tail_desc *d, const void *X, const int32_t *idx, 
 haste_status bf16_prep(const haste_tail_desc *d, const void *X, const haste_bce *bce, void *ws,
                        const TailWs &m, hipStream_t st) {
     TRY_HIP(launch_transpose_x((const unsigned short *)X, (unsigned short *)B8(ws, m.xt), d->B,
-                               d->D, pad_rows(d->B), st), "transpose X");
+                               d->D, pad_rows(d->B), (unsigned *)B8(ws, m.sched), st),
+            "transpose X");
     if (bce) {
         TRY_HIP(launch_group_positives(bce->row_ptr, bce->labels, bce->nnz, d->B, bce->label_offset,
                                        d->L, d->G, n_groups(d), (long long *)B8(ws, m.cnt),

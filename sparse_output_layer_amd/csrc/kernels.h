@@ -31,6 +31,9 @@ struct TailArgs {
     const int32_t *grp_ent;      // entries b*G + j
     float *loss;                 // fp32 scalar (+=)
     float s;                     // gradient scale
+    unsigned *sched;             // 2 counters of the dW/logits pass's dynamic run order (zero
+                                 //   between launches: the prep zeroes them, the pass's last
+                                 //   workgroup resets them)
     int B, D, Bp, F;
     int64_t L, Ng;
 };
@@ -38,8 +41,8 @@ struct TailArgs {
 enum T1Mode { T1_FWD = 0, T1_DW_BCE = 1, T1_DW_MEM = 2 };
 
 // Launch helpers return hipSuccess or the launch error.
-hipError_t launch_transpose_x(const unsigned short *X, unsigned short *XT,
-                              int B, int D, int Bp, hipStream_t st);
+hipError_t launch_transpose_x(const unsigned short *X, unsigned short *XT, int B, int D, int Bp,
+                              unsigned *sched, hipStream_t st);
 hipError_t launch_fill_u32(void *p, uint32_t v, size_t n, hipStream_t st);
 // out = W - lr * dW elementwise (bf16 or fp32 by `bf16`), n elements
 hipError_t launch_sgd(const void *W, const void *dW, float lr, void *out, int64_t n, bool bf16,

@@ -32,11 +32,13 @@ namespace haste {
 
 // ------------------------------------------------------------------ prep
 // XT[d][b] = X[b][d] for b < B, 0 for B <= b < Bp.  64x64 tiles via LDS.
+// Also zeroes the dW/logits pass's run counters (sched, 2 words) when given.
 __global__ __launch_bounds__(256) void k_transpose_x(const unsigned short *__restrict__ X,
                                                      unsigned short *__restrict__ XT,
-                                                     int B, int D, int Bp) {
+                                                     int B, int D, int Bp, unsigned *sched) {
     __shared__ unsigned short t[64][66];
     const int b0 = blockIdx.x * 64, d0 = blockIdx.y * 64;
+    if (sched && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 2) sched[threadIdx.x] = 0u;
     for (int i = threadIdx.x; i < 64 * 64; i += 256) {
         int bb = i / 64, dd = i % 64;
         int b = b0 + bb, d = d0 + dd;
@@ -50,10 +52,10 @@ __global__ __launch_bounds__(256) void k_transpose_x(const unsigned short *__res
     }
 }
 
-hipError_t launch_transpose_x(const unsigned short *X, unsigned short *XT, int B,
-                              int D, int Bp, hipStream_t st) {
+hipError_t launch_transpose_x(const unsigned short *X, unsigned short *XT, int B, int D, int Bp,
+                              unsigned *sched, hipStream_t st) {
     dim3 grid((Bp + 63) / 64, (D + 63) / 64);
-    hipLaunchKernelGGL(k_transpose_x, grid, dim3(256), 0, st, X, XT, B, D, Bp);
+    hipLaunchKernelGGL(k_transpose_x, grid, dim3(256), 0, st, X, XT, B, D, Bp, sched);
     return hipGetLastError();
 }
 
@@ -457,7 +459,15 @@ __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, int store_z,
     const bool need_pos = MODE != T1_DW_MEM && (do_loss || DO_DW);
     float lsum = 0.f;
 
-    for (int64_t run = blockIdx.x; run < n_runs; run += gridDim.x) {
+    // Runs in a dynamic order: a workgroup's first run is its index, the next
+    // ones come from a ticket counter (so that workgroups which start late,
+    // behind other work on their CU, take fewer runs); the last workgroup to
+    // finish resets the counters for the next launch.  The ticket reaches the
+    // waves through the padding of row 0 of buffer 1 (never read; at the end
+    // of a run no copy into buffer 1 is pending and the next run's W staging
+    // comes after its first barrier).
+    int *const s_ticket = (int *)(buf1 + 32);
+    for (int64_t run = blockIdx.x; run < n_runs;) {
         const int64_t gw = run * (NW * RW) + (int64_t)w * RW;
         bf16x8 wreg[RW][KS][JT];
         u32x2 pwz[DO_Z ? RW : 1][KS];     // perm bytes of positions 32s + 8q .. + 7
@@ -826,6 +836,22 @@ __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, int store_z,
                     }
                 }
             }
+        }
+        if (a.sched) {
+            if (threadIdx.x == 0) *s_ticket = (int)gridDim.x + (int)atomicAdd(a.sched, 1u);
+            __syncthreads();
+            run = *s_ticket;
+        } else {
+            run += gridDim.x;
+        }
+    }
+    if (a.sched && threadIdx.x == 0) {
+        // a workgroup counts itself out after its last ticket: the last one
+        // out knows that every ticket is taken
+        __threadfence();
+        if (atomicAdd(a.sched + 1, 1u) == gridDim.x - 1) {
+            atomicExch(a.sched, 0u);
+            atomicExch(a.sched + 1, 0u);
         }
     }
     if (do_loss && a.loss) {
