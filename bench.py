@@ -45,11 +45,12 @@ def parse():
     p.add_argument("--calib-mib", type=int, default=0,
                    help="after timing, one device-to-device copy of this many MiB: the "
                         "known-size reference for the FETCH_SIZE / WRITE_SIZE counters")
-    p.add_argument("--mode", choices=["train", "infer", "dense", "sgd"], default="train",
+    p.add_argument("--mode", choices=["train", "infer", "dense", "sgd", "calls"], default="train",
                    help="train: the training step (default); infer: head + tail forward "
                         "with a per-row top-K, exact and approximate; dense: the tail next "
                         "to a FLOPs-matched dense bottleneck layer; sgd: the tail step with "
-                        "its SGD update fused into the dW pass, next to step + update")
+                        "its SGD update fused into the dW pass, next to step + update; "
+                        "calls: every forward, backward and step entry point on its own")
     p.add_argument("--topk", type=int, default=5, help="K of the inference mode")
     p.add_argument("--recall", type=float, default=0.95,
                    help="recall target of the approximate top-K in the inference mode")
@@ -98,6 +99,36 @@ def algorithmic(cfg):
         # head and tail top-K lists in, merged list out
         "topk_merge": {"flops": 0, "bytes": 3 * B * max(cfg.topk, 1) * 8},
     }
+
+
+def measured_peaks(H, torch):
+    """Peaks attained on this GPU, beside the datasheet's: the library's MFMA
+    probe (bf16 16x16x32 on register operands, no memory traffic; 2048
+    workgroups of 4 waves x 100 rounds of 16 MFMAs) and a 1 GiB device-to-
+    device copy (bytes read + written per second), each timed with HIP events
+    after a warm-up run."""
+    sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+    H.haste_probe_mfma(256, 10, sink)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    flops = H.haste_probe_mfma(2048, 100, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    tf = flops / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(5):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 2 * n * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, b
+    return {"mfma_bf16_tflops": round(tf, 1), "hbm_copy_gbs": round(gbs, 1)}
 
 
 def cpu_baseline(inp, seconds):
@@ -149,7 +180,14 @@ def cpu_baseline(inp, seconds):
     h = int(min(cfg.H, max(h0, h0 * (0.2 * seconds) / max(th0, 1e-6))))
     th = head_time(h)
     full = tt * ng / n + th * cfg.H / h
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), cpu)
+    except OSError:
+        pass
     return {"value": B / full, "unit": "samples/s", "cores": nth, "kind": "oracle",
+            "cpu_model": cpu, "host_cpus": os.cpu_count(),
             "sample": f"fp64 oracle training step on the first {n} of {ng} tail groups "
                       f"({tt:.1f} s) and the first {h} of {cfg.H} head labels ({th:.1f} s), "
                       f"scaled by group/label count to the full step ({full:.1f} s per step)"}
@@ -339,6 +377,76 @@ def run_dense(args, cfg, inp, t_gen):
     print(json.dumps(out), flush=True)
 
 
+def run_calls(args, cfg, inp, t_gen):
+    """Each public forward, backward and step call on its own (head and tail),
+    with its algorithmic flops and bytes: the forward with the loss (no logits
+    stored), the backward from a given bf16 dZ and, for the tail, also with dZ
+    recomputed from the positives, and the one-call step."""
+    import numpy as np
+    import torch
+
+    from sparse_output_layer_amd import haste as H
+    dev = "cuda:0"
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    X, Wh, W = bf(inp.X), bf(inp.Wh), bf(inp.W)
+    idx = torch.from_numpy(inp.idx).to(dev)
+    rp = torch.from_numpy(inp.row_ptr).to(dev)
+    lab = torch.from_numpy(inp.labels).to(dev)
+    B, D, Hn, L, G, F = cfg.B, cfg.D, cfg.H, cfg.L, cfg.G, cfg.F
+    s = 1.0 / B
+    loss = torch.zeros(1, dtype=torch.float32, device=dev)
+    bh = H.Bce(rp, lab, 0, s, loss)
+    bt = H.Bce(rp, lab, Hn, s, loss)
+    dX = torch.zeros(B, D, dtype=torch.float32, device=dev)
+    dWh, dW = torch.empty_like(Wh), torch.empty_like(W)
+    # a given dZ: small values of both signs (only its size and layout matter here)
+    g = torch.Generator(device=dev).manual_seed(1)
+    dZh = (torch.randn(B, Hn, device=dev, generator=g) * s).to(torch.bfloat16)
+    dZt = (torch.randn(B, L, device=dev, generator=g) * s).to(torch.bfloat16)
+    ws_h = torch.empty(max(256, H.haste_head_workspace_bytes(X, Wh, bh)), dtype=torch.uint8, device=dev)
+    ws_t = torch.empty(H.haste_tail_workspace_bytes(X, idx, L, G, bt), dtype=torch.uint8, device=dev)
+    ng = (L + G - 1) // G
+    xb, dxb = B * D * 2, B * D * 4
+    whb, wb, ib = Hn * D * 2, ng * G * F * 2, ng * F * 4
+    calls = {
+        "head_fwd": (lambda: H.haste_head_fwd(X, Wh, bce=bh, workspace=ws_h),
+                     2 * B * D * Hn, whb + xb),
+        "head_bwd_dZ": (lambda: H.haste_head_bwd(X, Wh, dWh, dX, dZh=dZh, workspace=ws_h),
+                        4 * B * D * Hn, 2 * whb + xb + dxb + B * Hn * 2),
+        "head_step": (lambda: H.haste_head_step(X, Wh, bh, dWh, dX, workspace=ws_h),
+                      6 * B * D * Hn, 2 * whb + xb + dxb),
+        "tail_fwd": (lambda: H.haste_tail_fwd(X, idx, W, L, G, bce=bt, workspace=ws_t),
+                     2 * B * F * L, wb + ib + xb),
+        "tail_bwd_dZ": (lambda: H.haste_tail_bwd(X, idx, W, L, G, dW, dX, dZ=dZt, workspace=ws_t),
+                        4 * B * F * L, 2 * wb + ib + xb + dxb + B * L * 2),
+        "tail_bwd_recompute": (lambda: H.haste_tail_bwd(X, idx, W, L, G, dW, dX, bce=bt, workspace=ws_t),
+                               6 * B * F * L, 2 * wb + ib + xb + dxb),
+        "tail_step": (lambda: H.haste_tail_step(X, idx, W, L, G, bt, dW, dX, workspace=ws_t),
+                      6 * B * F * L, 2 * wb + ib + xb + dxb),
+    }
+    out = {}
+    for name, (fn, flops, nbytes) in calls.items():
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / args.steps * 1e3
+        out[name] = {"avg_us": round(us, 2), "tflops": round(flops / (us * 1e-6) / 1e12, 1),
+                     "gbs": round(nbytes / (us * 1e-6) / 1e9, 1)}
+    print(json.dumps({"metric": f"per-call times at {cfg.name}", "unit": "us",
+                      "config": {"workload": f"{cfg.name}: {cfg.note}; B={B} D={D} H={Hn} L={L} G={G} F={F}"},
+                      "dtype": "bf16", "data": "synthetic", "steps": args.steps, "warmup": args.warmup,
+                      "calls": out, "gen_s": round(t_gen, 2)}), flush=True)
+
+
 def run_sgd(args, cfg, inp, t_gen):
     """Tail training step plus an SGD update of W: unfused (the step writes
     dW, then W' = W - lr dW in a second pass) and fused (the dW pass writes
@@ -429,6 +537,8 @@ def main():
         return run_dense(args, cfg, inp, t_gen)
     if args.mode == "sgd":
         return run_sgd(args, cfg, inp, t_gen)
+    if args.mode == "calls":
+        return run_calls(args, cfg, inp, t_gen)
 
     def bf(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -545,6 +655,7 @@ def main():
            for i, n in enumerate(names)}          # microseconds
     step_loss = loss.item()
 
+    peaks = measured_peaks(H, torch)
     alg = algorithmic(cfg)
     tot_flops = sum(v["flops"] for v in alg.values())
     tot_bytes = sum(v["bytes"] for v in alg.values())
@@ -576,7 +687,10 @@ def main():
                      "frac": round(a_tf / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(dom, cfg.name),
                      "algorithmic_flops_per_launch": alg[dom]["flops"],
-                     "avg_launch_us": round(live_dom, 2)},
+                     "avg_launch_us": round(live_dom, 2),
+                     "peak_measured": peaks["mfma_bf16_tflops"],
+                     "frac_measured": round(a_tf / peaks["mfma_bf16_tflops"], 4)},
+        "measured_peaks": peaks,
         "step_roofline": {"algorithmic_tflop": round(tot_flops / 1e12, 4),
                           "algorithmic_gb": round(tot_bytes / 1e9, 4),
                           "achieved_tflops": round(step_tf, 1),

@@ -308,6 +308,17 @@ haste_status haste_topk_merge(int32_t B, int32_t K, const float *a_val,
                               const int32_t *b_idx, float *out_val,
                               int32_t *out_idx, void *stream);
 
+/* Measurement utility, not a step of the layer: `blocks` workgroups of four
+ * waves each run `iters` rounds of 16 independent 16x16x32 bf16 MFMA
+ * accumulations on register operands (16*16*32*2 flops each; 4 * 16 * iters
+ * per workgroup), with no memory traffic.  Timed by the caller, the rate is
+ * the matrix cores' attainable bf16 peak.  sink: one device float, 4-byte
+ * aligned, caller-owned, written only if the sum of the accumulators happens
+ * to equal 12345 (that test keeps the loop).  Errors:
+ * HASTE_ERR_INVALID for blocks < 1, iters < 1 or a NULL / misaligned sink;
+ * HASTE_ERR_HIP for a failed launch.  Asynchronous on `stream`. */
+haste_status haste_probe_mfma(int blocks, int iters, float *sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libhaste.so")
-SOURCES = ["abi.hip", "tail.hip", "head.hip", "f32path.hip", "topk.hip"]
+SOURCES = ["abi.hip", "tail.hip", "head.hip", "f32path.hip", "topk.hip", "probe.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -818,6 +818,14 @@ haste_status haste_tail_group_positives(const haste_tail_desc *d, const haste_bc
     return HASTE_OK;
 }
 
+haste_status haste_probe_mfma(int blocks, int iters, float *sink, void *stream) {
+    g_err.clear();
+    if (blocks < 1 || iters < 1) return fail(HASTE_ERR_INVALID, "blocks and iters must be >= 1");
+    TRY(need_al(sink, 4, "sink"));
+    TRY_HIP(launch_probe_mfma(blocks, iters, sink, S(stream)), "MFMA probe");
+    return HASTE_OK;
+}
+
 haste_status haste_tail_validate(const haste_tail_desc *d, const int32_t *idx,
                                  int32_t *first_bad_group, void *stream) {
     g_err.clear();

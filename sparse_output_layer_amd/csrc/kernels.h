@@ -93,6 +93,10 @@ hipError_t launch_topk_group_major(const float *gv, const int32_t *gi, int64_t l
                                    int64_t ngroups, int K, float *mid_v, int32_t *mid_i,
                                    float *out_v, int32_t *out_i, hipStream_t st);
 
+// Measurement utility: blocks x 4 waves, iters rounds of 16 independent
+// 16x16x32 bf16 MFMAs each (no memory traffic)
+hipError_t launch_probe_mfma(int blocks, int iters, float *sink, hipStream_t st);
+
 // Head (dense classifier) GEMMs.
 struct GemmArgs {
     const unsigned short *A;

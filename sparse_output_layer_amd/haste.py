@@ -86,6 +86,7 @@ _SIGS = {
     "haste_topk_merge": (ctypes.c_int, [_i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "haste_topk_expected_recall": (ctypes.c_double, [_i64, ctypes.c_int, ctypes.c_int, _i64]),
     "haste_topk_plan": (ctypes.c_int, [_i64, ctypes.c_int, ctypes.c_double, _i64, ctypes.POINTER(_i32)]),
+    "haste_probe_mfma": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _vp, _vp]),
 }
 
 
@@ -384,6 +385,15 @@ def haste_tail_group_positives(B, D, L, G, F, bce: Bce, dtype=torch.bfloat16, wo
     _check(lib().haste_tail_group_positives(ctypes.byref(d), b, _ptr(grp_ptr), _ptr(ent),
                                             _ptr(ws), nb, _stream()))
     return grp_ptr, ent
+
+
+def haste_probe_mfma(blocks: int, iters: int, sink=None):
+    """Measurement utility: blocks x 4 waves x iters x 16 bf16 MFMAs (16x16x32)
+    with no memory traffic, on the current stream; returns the flop count."""
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+    _check(lib().haste_probe_mfma(int(blocks), int(iters), _ptr(sink), _stream()))
+    return blocks * 4 * iters * 16 * (16 * 16 * 32 * 2)
 
 
 def haste_tail_validate(idx, D, L, G) -> torch.Tensor:

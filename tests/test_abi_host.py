@@ -176,3 +176,14 @@ def test_sgd_entry_points_reject_bad_arguments(L):
     assert L.haste_sgd_update(8, H.HASTE_F32, vp(0x1001), vp(0x1000), f(0.1), vp(0x1000), None) == \
         H.HASTE_ERR_INVALID
     assert L.haste_sgd_update(0, H.HASTE_BF16, None, None, f(0.1), None, None) == H.HASTE_OK
+
+
+def test_probe_argument_checks(L):
+    """The MFMA-rate probe rejects empty launches and a missing sink before any launch."""
+    L.haste_probe_mfma.restype = ctypes.c_int
+    L.haste_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    assert L.haste_probe_mfma(0, 10, 0x1000, None) == H.HASTE_ERR_INVALID
+    assert L.haste_probe_mfma(4, 0, 0x1000, None) == H.HASTE_ERR_INVALID
+    assert L.haste_probe_mfma(4, 10, None, None) == H.HASTE_ERR_INVALID
+    assert L.haste_probe_mfma(4, 10, 0x1002, None) == H.HASTE_ERR_INVALID
+

@@ -343,3 +343,14 @@ def test_bf16_fixed_fan_in_forward(H, case):
     H.haste_tail_fwd(d.X, d.idx, d.W, c.L, c.G, bce=b2)     # loss only, no Z
     torch.cuda.synchronize()
     check_loss("G=1 loss (no Z)", b2.loss.item(), float(lt.sum()), "bf16")
+
+
+def test_mfma_probe_runs(H):
+    """The measurement probe (not a step of the layer) launches and completes;
+    its flop count is blocks x 4 waves x iters x 16 MFMAs of 16x16x32x2."""
+    print("case mfma probe", flush=True)
+    sink = torch.zeros(1, dtype=torch.float32, device=DEV)
+    flops = H.haste_probe_mfma(8, 4, sink)
+    torch.cuda.synchronize()
+    assert flops == 8 * 4 * 4 * 16 * (16 * 16 * 32 * 2)
+    assert sink.item() == 0.0
