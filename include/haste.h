@@ -93,10 +93,13 @@ typedef struct {
 /* Tail flag.  By default the bf16 training calls that form dz from the
  * positives (haste_tail_step, its split form, haste_tail_bwd with dZ NULL)
  * keep dz of the dW pass in the workspace as bf16 tiles, B_pad x (N_g*G)
- * x 2 bytes (B_pad = B rounded up to 64), and the dX pass reads them back.
- * HASTE_TAIL_LEAN drops that buffer: the dX pass recomputes Z and dz from X,
- * W and the positives, and nothing of size B x L is stored.  Both forms give
- * the same results up to the summation order of Z. */
+ * x 2 bytes (B_pad = B rounded up to 64), and the dX pass reads them back;
+ * haste_tail_bwd with a given dZ first copies dZ into the same tiles, which
+ * both of its passes then read.  The workspace size includes the tiles
+ * whether or not bce is given.  HASTE_TAIL_LEAN drops that buffer: the dX
+ * pass recomputes Z and dz from X, W and the positives (or reads the given
+ * dZ in place), and nothing of size B x L is stored.  Both forms give the
+ * same results up to the summation order of Z. */
 #define HASTE_TAIL_LEAN 1
 
 /* Head shape (dense classifier).  bf16 needs D a multiple of 32. */

@@ -90,7 +90,8 @@ TailWs tail_ws(const haste_tail_desc *d, const haste_bce *bce) {
         }
         // dz of the dW pass, kept for the dX pass unless the caller asks for
         // the lean form (which recomputes it): Bp x (Ng*G) bf16 in 1 KB tiles
-        w.has_dzt = bce && !(d->flags & HASTE_TAIL_LEAN) && d->G > 1;
+        // (also without bce: the backward from a given dZ forms the same tiles)
+        w.has_dzt = !(d->flags & HASTE_TAIL_LEAN) && d->G > 1;
         if (w.has_dzt) { w.dzt = o; o += al256((size_t)ng * d->G * pad_rows(d->B) * 2); }
     } else {
         // per-group counts; also the key space of haste_tail_group_positives
@@ -451,8 +452,11 @@ haste_status haste_tail_bwd(const haste_tail_desc *d, const void *X, const int32
         a.dZ = (const unsigned short *)dZ;
         if (b) a.s = b->grad_scale;
         TRY(feature_order(d, idx, ws, m, st));
+        if (dZ && a.dzt)   // the given dZ in the tile layout: both passes then read it coalesced
+            TRY_HIP(launch_dz_tiles((const unsigned short *)dZ, d->B, d->L, d->G, a.Bp, a.Ng, a.dzt, st),
+                    "dZ tiles");
         TRY_HIP(launch_tail_t1(dZ ? T1_DW_MEM : T1_DW_BCE, d->G, a, false, false, st), "tail dW");
-        TRY_HIP(launch_tail_t2(d->G, dZ ? 1 : a.dzt ? 2 : 0, a, st), "tail dX");
+        TRY_HIP(launch_tail_t2(d->G, a.dzt ? 2 : dZ ? 1 : 0, a, st), "tail dX");
     } else {
         F32Args a = f32_tail_args(d, X, idx, W, b);
         a.loss = nullptr;

@@ -93,6 +93,10 @@ hipError_t launch_topk_group_major(const float *gv, const int32_t *gi, int64_t l
                                    int64_t ngroups, int K, float *mid_v, int32_t *mid_i,
                                    float *out_v, int32_t *out_i, hipStream_t st);
 
+// A caller's dZ (B x L bf16, row-major) into the dW pass's dz tiles
+hipError_t launch_dz_tiles(const unsigned short *dZ, int B, int64_t L, int G, int Bp, int64_t Ng,
+                           unsigned short *dzt, hipStream_t st);
+
 // Measurement utility: blocks x 4 waves, iters rounds of 16 independent
 // 16x16x32 bf16 MFMAs each (no memory traffic)
 hipError_t launch_probe_mfma(int blocks, int iters, float *sink, hipStream_t st);

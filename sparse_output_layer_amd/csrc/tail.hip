@@ -59,6 +59,53 @@ hipError_t launch_transpose_x(const unsigned short *X, unsigned short *XT, int B
     return hipGetLastError();
 }
 
+// ------------------------------------------------- given dZ -> dz tiles
+// The backward from a caller's dZ (B x L bf16, row-major) reuses the step's
+// dz tiles: tile ((g * nch + ch) * JT + jt) holds 1 KB, lane (q, m) the rows
+// 32ch + 16h2 + 4q + i (i = 0..3, h2 = 0..1) of label gG + 16jt + m, zero past
+// B and past L.  A workgroup reads 32 rows x 256 labels (512-byte row
+// pieces) into LDS and writes 16 tiles, each by one wave in 16-byte stores.
+constexpr int DZT_LAB = 256;
+__global__ __launch_bounds__(256) void k_dz_tiles(const unsigned short *__restrict__ dZ, int B, int64_t L,
+                                                  int G, int nch, int64_t ntiles16,
+                                                  unsigned short *__restrict__ dzt) {
+    __shared__ unsigned short s[32][DZT_LAB + 2];
+    const int t = threadIdx.x, ch = blockIdx.y;
+    const int64_t l0 = (int64_t)blockIdx.x * DZT_LAB;
+    for (int r = 0; r < 32; ++r) {
+        const int row = 32 * ch + r;
+        const int64_t lab = l0 + t;
+        s[r][t] = row < B && lab < L ? dZ[(int64_t)row * L + lab] : (unsigned short)0;
+    }
+    __syncthreads();
+    const int lane = t & 63, w = t >> 6, q = lane >> 4, m = lane & 15;
+    const int JT = G / 16;
+    for (int k = w; k < DZT_LAB / 16; k += 4) {
+        const int64_t lt = l0 / 16 + k;            // 16-label tile: group lt / JT, slot block lt % JT
+        if (lt >= ntiles16) break;
+        const int64_t g = lt / JT, jt = lt % JT;
+        unsigned v[4];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {             // pairs (h2, i), (h2, i + 1)
+            const int h2 = h >> 1, i = 2 * (h & 1);
+            const int r = 16 * h2 + 4 * q + i;
+            v[h] = (unsigned)s[r][16 * k + m] | ((unsigned)s[r + 1][16 * k + m] << 16);
+        }
+        *(u32x4 *)(dzt + (((g * nch + ch) * JT + jt) << 9) + lane * 8) = (u32x4){v[0], v[1], v[2], v[3]};
+    }
+}
+
+hipError_t launch_dz_tiles(const unsigned short *dZ, int B, int64_t L, int G, int Bp, int64_t Ng,
+                           unsigned short *dzt, hipStream_t st) {
+    if (B <= 0 || L <= 0) return hipSuccess;
+    if (G % 16 != 0 || Bp % 32 != 0) return hipErrorInvalidValue;
+    const int nch = Bp / 32;
+    const int64_t nlab = Ng * G;                   // padded label count: whole tiles
+    const dim3 grid((unsigned)((nlab + DZT_LAB - 1) / DZT_LAB), (unsigned)nch);
+    hipLaunchKernelGGL(k_dz_tiles, grid, dim3(256), 0, st, dZ, B, L, G, nch, Ng * (G / 16), dzt);
+    return hipGetLastError();
+}
+
 // ------------------------------------------------------- feature order
 // Order of each group's F features in which T1 reads the gathered rows, so
 // that its LDS reads hit distinct banks.  A chunk row (feature d) is 80 bytes
@@ -571,7 +618,18 @@ __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, int store_z,
                 // ---- epilogue: lane owns (row r0+16h2+4q+i, slot 16jt+m)
                 unsigned dzp[2][JT][2];
                 const bool tile_live = (r0 + BC <= a.B) && ((g + 1) * G <= a.L);
-                if (MODE != T1_DW_MEM && tile_live && !has_pos && !(MODE == T1_FWD && store_z)) {
+                if (MODE == T1_DW_MEM && a.dzt) {
+                    // the caller's dZ, already in the tile layout (zero past B and L)
+#pragma unroll
+                    for (int jt = 0; jt < JT; ++jt) {
+                        const u32x4 v =
+                            *(const u32x4 *)(a.dzt + ((((int64_t)g * nch + ch) * JT + jt) << 9) + lane * 8);
+                        dzp[0][jt][0] = v[0];
+                        dzp[0][jt][1] = v[1];
+                        dzp[1][jt][0] = v[2];
+                        dzp[1][jt][1] = v[3];
+                    }
+                } else if (MODE != T1_DW_MEM && tile_live && !has_pos && !(MODE == T1_FWD && store_z)) {
                     // fast path: every element live, no positive, no logits to store;
                     // lin2 = sum of z + |z| = twice the sum of max(z, 0), exactly
                     float lin2 = 0.f, prod = 1.f;

@@ -160,6 +160,13 @@ def test_bf16_tail_and_head(H, case):
     rX, rXa = oracle.tail_dX(inp.idx, inp.W_f64(), dZ64, c.D, c.L, c.G)
     check("tail bwd(dZ) dW", to_f64(dW4[:c.L]), rW, rWa, "bf16", nterms=c.B)
     check("tail bwd(dZ) dX", to_f64(dX4) - 1.0, rX, rXa, "bf16", nterms=ng * c.G)
+    # the lean form reads the given dZ in place instead of copying it into tiles
+    dW4l = torch.empty_like(d.W)
+    dX4l = torch.empty_like(dX)
+    H.haste_tail_bwd(d.X, d.idx, d.W, c.L, c.G, dW4l, dX4l, dZ=dZt, lean=True)
+    torch.cuda.synchronize()
+    check("lean tail bwd(dZ) dW", to_f64(dW4l[:c.L]), rW, rWa, "bf16", nterms=c.B)
+    check("lean tail bwd(dZ) dX", to_f64(dX4l), rX, rXa, "bf16", nterms=ng * c.G)
 
     # head: forward logits + loss, fused step accumulating into the tail's dX
     Zh = torch.empty(c.B, c.H, dtype=bf, device=DEV)
