@@ -332,18 +332,21 @@ __global__ __launch_bounds__(256, 2) void k_gemm2(GemmArgs g) {
     // Step kt: wait for this wave's copies of step kt (those of step kt+1 stay
     // in flight), then a barrier: everyone's copies have landed, and every
     // wave is done with step kt-1, whose stage the copies of step kt+2 then
-    // overwrite.  A bare s_barrier: the fence of __syncthreads would wait for
-    // every copy in flight (the LDS reads of step kt-1 have returned: their
-    // MFMAs are issued).  The loop has no exit but its end (the steps run up
-    // to a multiple of GEMM_NS; those past the split's end see zeroed operands
-    // and add nothing) and copies are issued unconditionally (clamped
+    // overwrite.  No __syncthreads: its fence would wait for every copy in
+    // flight.  The barrier waits for this wave's LDS reads instead: the
+    // compiler may move the MFMAs that consume the reads of step kt-1 below
+    // the barrier, and its own wait for those reads with them, and a read
+    // still in flight there would race with the copies that overwrite its
+    // stage right after the barrier.  The loop has no exit but its end (the
+    // steps run up to a multiple of GEMM_NS; those past the split's end see
+    // zeroed operands and add nothing) and copies are issued unconditionally (clamped
     // addresses), so the compiler's own count of copies in flight is the same
     // on every path and it does not wait for the other stages; an exit in the
     // middle costs a full wait there and twice the registers.  All copies are
     // drained after the loop.
     auto sync = [&]() {
         wait_vm<LPS>();
-        asm volatile("s_barrier" ::: "memory");
+        lds_barrier();
     };
     issue(0, st0);
     issue(1, st1);

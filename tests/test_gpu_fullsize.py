@@ -1,8 +1,11 @@
-"""Parity at the workloads' full sizes, in the launch configuration that
-bench.py times (haste_head_step, then haste_tail_prepare, haste_tail_step_dw
-and haste_tail_step_dx on one stream, head and tail accumulating into one
-dX).  The oracle cannot evaluate these steps whole in test time, so the
-checks are on outputs it computes one by one:
+"""Parity at the workloads' full sizes, in the calls that bench.py times
+(haste_head_step, haste_tail_prepare, haste_tail_step_dw and
+haste_tail_step_dx, head and tail accumulating into one dX), made one after
+another on one stream; test_overlapped_steps then checks that the
+arrangement bench.py times, the head on a second stream beside the tail,
+gives the same outputs on every call.  The oracle cannot evaluate these
+steps whole in test time, so the checks are on outputs it computes one by
+one:
 
   - dW of sampled tail groups (all rows), including the ragged last group;
   - dWh of sampled head labels (all rows);
@@ -175,3 +178,87 @@ def _merge_lists(av, ai, bv, bi, n):
         ov, oi = oracle.topk(v[r:r + 1], n, ids=i[r])
         out_v[r], out_i[r] = ov[0], oi[0]
     return out_v, out_i
+
+
+def test_overlapped_steps(H):
+    """The head's step on a second stream beside the tail's calls, repeated:
+    every call's dW and dWh equal those of the calls made in order on one
+    stream, bit for bit, and dX (fp32 atomics from both sides, in an order
+    that varies) agrees to a small multiple of fp32 rounding.  Two
+    arrangements: the head launched once the tail's prep is done (as
+    bench.py times it) and at the very start of the step, beside the prep
+    kernels, whose LDS traffic slows the head GEMM's LDS reads; a GEMM
+    barrier that did not wait for those reads gave a wrong dX tile in about
+    one call in thirty there."""
+    print("overlapped steps c2", flush=True)
+    inp = wl.make_inputs(wl.CONFIGS["c2"])
+    c = inp.cfg
+    B, D, L, G, Hn = c.B, c.D, c.L, c.G, c.H
+    s = 1.0 / B
+    d = Dev(inp)
+    loss = torch.zeros(1, dtype=torch.float32, device=DEV)
+    bh = H.Bce(d.row_ptr, d.labels, 0, s, loss)
+    bt = H.Bce(d.row_ptr, d.labels, Hn, s, loss)
+    dX = torch.empty(B, D, dtype=torch.float32, device=DEV)
+    dWh = torch.empty_like(d.Wh)
+    dW = torch.empty_like(d.W)
+    ws_t = torch.empty(H.haste_tail_workspace_bytes(d.X, d.idx, L, G, bt), dtype=torch.uint8,
+                       device=DEV)
+    ws_h = torch.empty(max(256, H.haste_head_workspace_bytes(d.X, d.Wh, bh)), dtype=torch.uint8,
+                       device=DEV)
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+
+    def tail_prep():
+        H.haste_tail_prepare(d.X, d.idx, L, G, bt, ws_t)
+
+    def tail_rest():
+        H.haste_tail_step_dw(d.X, d.idx, d.W, L, G, bt, dW, ws_t)
+        H.haste_tail_step_dx(d.X, d.idx, d.W, L, G, bt, dX, ws_t, accumulate_dX=True)
+
+    def head_on_side():
+        with torch.cuda.stream(side):
+            H.haste_head_step(d.X, d.Wh, bh, dWh, dX, accumulate_dX=True, workspace=ws_h)
+
+    def in_order():
+        loss.zero_()
+        H.haste_head_step(d.X, d.Wh, bh, dWh, dX, workspace=ws_h)
+        tail_prep()
+        tail_rest()
+
+    def after_prep():
+        loss.zero_()
+        dX.zero_()
+        tail_prep()
+        ev = torch.cuda.Event()
+        ev.record(main)
+        side.wait_event(ev)
+        head_on_side()
+        tail_rest()
+        main.wait_stream(side)
+
+    def at_start():
+        loss.zero_()
+        dX.zero_()
+        side.wait_stream(main)
+        head_on_side()
+        tail_prep()
+        tail_rest()
+        main.wait_stream(side)
+
+    in_order()
+    torch.cuda.synchronize()
+    ref_dx, ref_dw, ref_dwh = dX.clone(), dW.view(torch.int16).clone(), dWh.view(torch.int16).clone()
+    tol = 1e-5 * float(ref_dx.abs().max())
+    for name, f in (("after prep", after_prep), ("at start", at_start)):
+        bad = []
+        for it in range(120):
+            f()
+            torch.cuda.synchronize()
+            err = float((dX - ref_dx).abs().max())
+            same_w = torch.equal(dW.view(torch.int16), ref_dw)
+            same_wh = torch.equal(dWh.view(torch.int16), ref_dwh)
+            if err > tol or not same_w or not same_wh:
+                bad.append((it, err, same_w, same_wh))
+        print(f"  head {name}: 120 calls, {len(bad)} differ (dX tol {tol:.2e})", flush=True)
+        assert not bad, f"head {name}: (call, dX max diff, dW equal, dWh equal) {bad[:5]}"
