@@ -10,7 +10,7 @@ row; synthetic, seeded, resident in HBM before timing starts.
 
 One step = haste_tail_prepare + haste_tail_step_dw + haste_tail_step_dx (the
 split form of haste_tail_step) on the main stream and haste_head_step on a
-side stream beside the dW/logits pass, both adding into one dX.  W warm-up
+side stream from the step's start, both adding into one dX.  W warm-up
 steps, then K timed steps between device synchronisations; HIP events on the
 main stream around the dominant tail pass give its average duration inside
 the timed region (the roofline figure).  A serial pass of K steps before
@@ -568,24 +568,23 @@ def main():
     side = torch.cuda.Stream()   # default priority, like every stream here
 
     def step(ev, dom_dx=False):
-        """One training step.  The head's step runs on a side stream once the
-        tail's prep is done, beside the tail's dW/logits pass: its workgroups
-        take the CUs that pass leaves idle (the pass hands out its runs
-        dynamically).  Both branches add into dX and the loss atomically, so
-        both are zeroed first.  ev: two events on the main stream around the
-        dW pass (around the dX pass when dom_dx); ev[0] also releases the
-        side stream."""
+        """One training step.  The head's step runs on a side stream from the
+        start of the step, beside the tail's prep and the first part of its
+        dW/logits pass: its workgroups take the CUs that the prep's small
+        kernels leave idle, and later those that the dW pass leaves idle (it
+        hands out its runs dynamically).  Both branches add into dX and the
+        loss atomically, so both are zeroed first.  ev: two events on the
+        main stream around the dW pass (around the dX pass when dom_dx)."""
         main = torch.cuda.current_stream()
         loss.zero_()
         dX.zero_()
-        H.haste_tail_prepare(X, idx, L, G, bce_t, ws_t)
-        ev[0].record(main)
-        if dom_dx:
-            H.haste_tail_step_dw(X, idx, W, L, G, bce_t, dW, ws_t)
-            ev[0].record(main)
-        side.wait_event(ev[0])
+        side.wait_stream(main)
         with torch.cuda.stream(side):
             H.haste_head_step(X, Wh, bce_h, dWh, dX, accumulate_dX=True, workspace=ws_h)
+        H.haste_tail_prepare(X, idx, L, G, bce_t, ws_t)
+        if dom_dx:
+            H.haste_tail_step_dw(X, idx, W, L, G, bce_t, dW, ws_t)
+        ev[0].record(main)
         if not dom_dx:
             H.haste_tail_step_dw(X, idx, W, L, G, bce_t, dW, ws_t)
         else:

@@ -185,11 +185,11 @@ def test_overlapped_steps(H):
     every call's dW and dWh equal those of the calls made in order on one
     stream, bit for bit, and dX (fp32 atomics from both sides, in an order
     that varies) agrees to a small multiple of fp32 rounding.  Two
-    arrangements: the head launched once the tail's prep is done (as
-    bench.py times it) and at the very start of the step, beside the prep
-    kernels, whose LDS traffic slows the head GEMM's LDS reads; a GEMM
-    barrier that did not wait for those reads gave a wrong dX tile in about
-    one call in thirty there."""
+    arrangements: the head launched once the tail's prep is done, and at the
+    very start of the step (as bench.py times it), beside the prep kernels,
+    whose LDS traffic slows the head GEMM's LDS reads; a GEMM barrier that
+    did not wait for those reads gave a wrong dX tile in about one call in
+    thirty there."""
     print("overlapped steps c2", flush=True)
     inp = wl.make_inputs(wl.CONFIGS["c2"])
     c = inp.cfg
