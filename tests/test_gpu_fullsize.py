@@ -180,7 +180,8 @@ def _merge_lists(av, ai, bv, bi, n):
     return out_v, out_i
 
 
-def test_overlapped_steps(H):
+@pytest.mark.parametrize("name", ["c2", "c5"])
+def test_overlapped_steps(H, name):
     """The head's step on a second stream beside the tail's calls, repeated:
     every call's dW and dWh equal those of the calls made in order on one
     stream, bit for bit, and dX (fp32 atomics from both sides, in an order
@@ -189,9 +190,10 @@ def test_overlapped_steps(H):
     very start of the step (as bench.py times it), beside the prep kernels,
     whose LDS traffic slows the head GEMM's LDS reads; a GEMM barrier that
     did not wait for those reads gave a wrong dX tile in about one call in
-    thirty there."""
-    print("overlapped steps c2", flush=True)
-    inp = wl.make_inputs(wl.CONFIGS["c2"])
+    thirty there.  The 8.6M-label workload adds its per-row top-5 lists
+    (head and tail merged after both streams meet), compared bit for bit."""
+    print("overlapped steps", name, flush=True)
+    inp = wl.make_inputs(wl.CONFIGS[name])
     c = inp.cfg
     B, D, L, G, Hn = c.B, c.D, c.L, c.G, c.H
     s = 1.0 / B
@@ -199,6 +201,11 @@ def test_overlapped_steps(H):
     loss = torch.zeros(1, dtype=torch.float32, device=DEV)
     bh = H.Bce(d.row_ptr, d.labels, 0, s, loss)
     bt = H.Bce(d.row_ptr, d.labels, Hn, s, loss)
+    K = c.topk
+    if K:
+        for b_ in (bh, bt):
+            b_.topk_val = torch.empty(B, K, dtype=torch.float32, device=DEV)
+            b_.topk_idx = torch.empty(B, K, dtype=torch.int32, device=DEV)
     dX = torch.empty(B, D, dtype=torch.float32, device=DEV)
     dWh = torch.empty_like(d.Wh)
     dW = torch.empty_like(d.W)
@@ -220,11 +227,15 @@ def test_overlapped_steps(H):
         with torch.cuda.stream(side):
             H.haste_head_step(d.X, d.Wh, bh, dWh, dX, accumulate_dX=True, workspace=ws_h)
 
+    def merged():
+        return H.haste_topk_merge(bh.topk_val, bh.topk_idx, bt.topk_val, bt.topk_idx) if K else None
+
     def in_order():
         loss.zero_()
         H.haste_head_step(d.X, d.Wh, bh, dWh, dX, workspace=ws_h)
         tail_prep()
         tail_rest()
+        return merged()
 
     def after_prep():
         loss.zero_()
@@ -236,6 +247,7 @@ def test_overlapped_steps(H):
         head_on_side()
         tail_rest()
         main.wait_stream(side)
+        return merged()
 
     def at_start():
         loss.zero_()
@@ -245,20 +257,22 @@ def test_overlapped_steps(H):
         tail_prep()
         tail_rest()
         main.wait_stream(side)
+        return merged()
 
-    in_order()
+    ref_tk = in_order()
     torch.cuda.synchronize()
     ref_dx, ref_dw, ref_dwh = dX.clone(), dW.view(torch.int16).clone(), dWh.view(torch.int16).clone()
     tol = 1e-5 * float(ref_dx.abs().max())
     for name, f in (("after prep", after_prep), ("at start", at_start)):
         bad = []
         for it in range(120):
-            f()
+            tk = f()
             torch.cuda.synchronize()
             err = float((dX - ref_dx).abs().max())
             same_w = torch.equal(dW.view(torch.int16), ref_dw)
             same_wh = torch.equal(dWh.view(torch.int16), ref_dwh)
-            if err > tol or not same_w or not same_wh:
-                bad.append((it, err, same_w, same_wh))
+            same_tk = not K or (torch.equal(tk[0], ref_tk[0]) and torch.equal(tk[1], ref_tk[1]))
+            if err > tol or not same_w or not same_wh or not same_tk:
+                bad.append((it, err, same_w, same_wh, same_tk))
         print(f"  head {name}: 120 calls, {len(bad)} differ (dX tol {tol:.2e})", flush=True)
-        assert not bad, f"head {name}: (call, dX max diff, dW equal, dWh equal) {bad[:5]}"
+        assert not bad, f"head {name}: (call, dX max diff, dW, dWh, top-K equal) {bad[:5]}"
