@@ -197,7 +197,10 @@ def run_infer(args, cfg, inp, t_gen):
     """Inference: head + tail forward, per-row top-K over each branch (the
     top-K page's two stages), merged over the whole output space; first with
     K' = K on buckets of 32768 labels (exact), then with the (K', buckets)
-    that haste_topk_plan picks for the recall target."""
+    that haste_topk_plan picks for the recall target, then with stage 1 fused
+    into the logits pass.  A serial pass with events between the calls gives
+    the per-call breakdown; the timed steps run the head's forward on a side
+    stream beside the tail's, and their lists must equal the serial ones."""
     import numpy as np
     import torch
 
@@ -220,6 +223,7 @@ def run_infer(args, cfg, inp, t_gen):
     exp_fused = H.haste_topk_expected_recall(L, K, 1, ng)
     out = {}
     lists = {}
+    side = torch.cuda.Stream()   # default priority
     # exact; the planned (K', buckets); one bucket per label group with K' = 1,
     # whose stage 1 runs inside the logits pass
     for name, (kprime, nbk) in (("exact", (0, 0)), ("approx", (kp, nb)), ("fused", (1, ng))):
@@ -246,21 +250,41 @@ def run_infer(args, cfg, inp, t_gen):
                 ev[3].record()
             return r
 
+        def step_overlapped():
+            """The timed form: the head's forward on the side stream beside the
+            tail's, the merge once both are done."""
+            main = torch.cuda.current_stream()
+            side.wait_stream(main)
+            with torch.cuda.stream(side):
+                H.haste_head_fwd(X, Wh, bce=bh, workspace=ws_h)
+            H.haste_tail_fwd(X, idx, W, L, G, bce=bt, workspace=ws_t)
+            main.wait_stream(side)
+            return H.haste_topk_merge(bh.topk_val, bh.topk_idx, bt.topk_val, bt.topk_idx)
+
+        # serial pass with events between the calls: the per-kernel breakdown
         for _ in range(args.warmup):
             step()
-        torch.cuda.synchronize()
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+        for k in range(args.steps):
+            step(evs[k])
+        torch.cuda.synchronize()
+        per = {n: round(float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) * 1e3, 2)
+               for i, n in enumerate(names)}
+        for _ in range(args.warmup):
+            step_overlapped()
+        torch.cuda.synchronize()
         t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0.record()
         for k in range(args.steps):
-            step(evs[k])
+            step_overlapped()
         t1.record()
         torch.cuda.synchronize()
         ms = t0.elapsed_time(t1) / args.steps
-        per = {n: round(float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) * 1e3, 2)
-               for i, n in enumerate(names)}
         mv, mi = step()
+        ov, oi = step_overlapped()
         torch.cuda.synchronize()
+        if not (torch.equal(mv, ov) and torch.equal(mi, oi)):
+            raise RuntimeError(f"{name}: overlapped step's top-{K} lists differ from the serial step's")
         lists[name] = (bt.topk_idx.cpu().numpy(), mi.cpu().numpy())
         out[name] = {"value": round(B / (ms * 1e-3), 1), "ms_per_step": round(ms, 4), "kernels_us": per}
     # recall of the approximate lists against the exact ones (tail, and merged)
