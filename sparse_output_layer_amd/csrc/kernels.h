@@ -61,6 +61,10 @@ hipError_t launch_tail_t1(int mode, int G, const TailArgs &a, bool store_z,
 hipError_t launch_tail_t2(int G, int dz_mode, const TailArgs &a,
                           hipStream_t st);
 bool tail_bf16_supported(int G, int F, int D);
+// dX from the stored dz tiles at the layer's own flops (Y_g = dz_g W_g, then a
+// scatter into an LDS-resident dX^T tile of 32 rows): shapes it takes, launch
+bool tail_dxs_supported(int G, int F, int D);
+hipError_t launch_tail_dxs(int G, const TailArgs &a, hipStream_t st);
 // G = 1 (per-label fan-in): logits and loss only
 hipError_t launch_fanin1_fwd(const TailArgs &a, bool store_z, bool do_loss, hipStream_t st);
 

@@ -1978,6 +1978,9 @@ hipError_t launch_tail_t2(int G, int dz_mode, const TailArgs &a, hipStream_t st)
     if (dz_mode < 0 || dz_mode > 2 || (dz_mode == 1 && !a.dZ) || (dz_mode == 2 && !a.dzt))
         return hipErrorInvalidValue;
     if (dz_mode == 2) {
+        // groups of 32 and more: the scatter form (its LDS traffic per flop
+        // falls as G grows); groups of 16: the dense form
+        if (G >= 32 && tail_dxs_supported(G, a.F, a.D)) return launch_tail_dxs(G, a, st);
         switch (G) {
         case 16: return t2d_pick<16>(a, st);
         case 32: return t2d_pick<32>(a, st);
