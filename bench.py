@@ -10,7 +10,10 @@ row; synthetic, seeded, resident in HBM before timing starts.
 
 One step = haste_tail_prepare + haste_tail_step_dw + haste_tail_step_dx (the
 split form of haste_tail_step) on the main stream and haste_head_step on a
-side stream from the step's start, both adding into one dX.  W warm-up
+side stream from the step's start, both adding into one dX.  idx is fixed
+over training, so the feature order the logits pass reads is formed once
+before the steps (haste_tail_prepare_layout) and the dW/logits call is the
+dW/logits kernel alone.  W warm-up
 steps, then K timed steps between device synchronisations; HIP events on the
 main stream around the dominant tail pass give its average duration inside
 the timed region (the roofline figure).  A serial pass of K steps before
@@ -82,6 +85,17 @@ def measured_traffic(kernel, launch_key):
     return rec["fetch_bytes"] + rec["write_bytes"]
 
 
+def step_algorithmic(cfg):
+    """Algorithmic work of one training step as the method needs it (three
+    contractions each for tail and head; W, idx, Wh, X read once; dW, dWh, dX
+    written once), per config."""
+    B, D, H, L, G, F = cfg.B, cfg.D, cfg.H, cfg.L, cfg.G, cfg.F
+    ng = (L + G - 1) // G
+    flops = 6 * B * F * L + 6 * B * D * H
+    nbytes = 2 * (ng * G * F * 2) + ng * F * 4 + 2 * (H * D * 2) + B * D * 2 + B * D * 4
+    return flops, nbytes
+
+
 def algorithmic(cfg):
     """Algorithmic flops and HBM bytes the method itself needs, per call."""
     B, D, H, L, G, F = cfg.B, cfg.D, cfg.H, cfg.L, cfg.G, cfg.F
@@ -134,29 +148,28 @@ def measured_peaks(H, torch):
 def cpu_baseline(inp, seconds):
     """The fp64 oracle, as it stands, on the host's cores: a full training
     step over the first n tail groups and the first h head labels, timed and
-    scaled to the whole step."""
+    scaled to the whole step.  The sample is sized so that one run takes
+    about a tenth of `seconds`; the figure is the median of five runs on all
+    OpenMP threads, beside one run on a single thread."""
     import numpy as np
 
     import oracle
+    import workloads as wl
     cfg = inp.cfg
     G, B = cfg.G, cfg.B
     nth = oracle.threads()
     X = inp.X_f64()
     s = 1.0 / B
+    ng = cfg.n_groups
 
     def tail_time(n):
-        W = oracle_w(n)
+        W = wl.f64_from_bf16_bits(inp.W[:n * G]) if cfg.dtype == "bf16" \
+            else inp.W[:n * G].astype(np.float64)
         t0 = time.perf_counter()
         oracle.tail_step(X, inp.idx[:n], W, inp.row_ptr, inp.labels, cfg.H, n * G, G, s)
         return time.perf_counter() - t0
 
-    def oracle_w(n):
-        import workloads as wl
-        return wl.f64_from_bf16_bits(inp.W[:n * G]) if cfg.dtype == "bf16" \
-            else inp.W[:n * G].astype(np.float64)
-
     def head_time(h):
-        import workloads as wl
         Wh = wl.f64_from_bf16_bits(inp.Wh[:h]) if cfg.dtype == "bf16" \
             else inp.Wh[:h].astype(np.float64)
         t0 = time.perf_counter()
@@ -167,19 +180,33 @@ def cpu_baseline(inp, seconds):
         oracle.head_dX(Wh, dz, want_abs=False)
         return time.perf_counter() - t0
 
-    ng = cfg.n_groups
-    n0 = min(ng, 8)
-    t0 = tail_time(n0)
-    n = int(min(ng, max(n0, n0 * (0.8 * seconds) / max(t0, 1e-6))))
-    tt = tail_time(n)
-    if tt < 0.4 * seconds and n < ng:   # first estimate was overhead-bound
-        n = int(min(ng, n * (0.8 * seconds) / max(tt, 1e-6)))
-        tt = tail_time(n)
-    h0 = min(cfg.H, 64)
-    th0 = head_time(h0)
-    h = int(min(cfg.H, max(h0, h0 * (0.2 * seconds) / max(th0, 1e-6))))
-    th = head_time(h)
-    full = tt * ng / n + th * cfg.H / h
+    def size(fn, total, n0, budget):
+        """Sample size whose run takes about `budget` seconds."""
+        n = min(total, n0)
+        t = fn(n)
+        for _ in range(3):
+            if t >= 0.5 * budget or n >= total:
+                break
+            n = int(min(total, max(n + 1, n * budget / max(t, 1e-6))))
+            t = fn(n)
+        return n
+
+    def step_estimate(n, h):
+        tt, th = tail_time(n), head_time(h)
+        return tt * ng / n + th * cfg.H / h, tt, th
+
+    run_s = seconds / 10
+    n = size(tail_time, ng, 8, 0.8 * run_s)
+    h = size(head_time, cfg.H, 64, 0.2 * run_s)
+    runs = [step_estimate(n, h) for _ in range(5)]
+    full = float(np.median([r[0] for r in runs]))
+    oracle.set_threads(1)
+    try:
+        n1 = size(tail_time, ng, 2, 0.8 * run_s)
+        h1 = size(head_time, cfg.H, 8, 0.2 * run_s)
+        one, tt1, th1 = step_estimate(n1, h1)
+    finally:
+        oracle.set_threads(nth)
     cpu = "unknown"
     try:
         with open("/proc/cpuinfo") as f:
@@ -188,9 +215,13 @@ def cpu_baseline(inp, seconds):
         pass
     return {"value": B / full, "unit": "samples/s", "cores": nth, "kind": "oracle",
             "cpu_model": cpu, "host_cpus": os.cpu_count(),
-            "sample": f"fp64 oracle training step on the first {n} of {ng} tail groups "
-                      f"({tt:.1f} s) and the first {h} of {cfg.H} head labels ({th:.1f} s), "
-                      f"scaled by group/label count to the full step ({full:.1f} s per step)"}
+            "sample": f"fp64 oracle training step on the first {n} of {ng} tail groups and the "
+                      f"first {h} of {cfg.H} head labels, scaled by group/label count to the "
+                      f"full step; median of 5 runs ({', '.join(f'{r[0]:.1f}' for r in runs)} s per "
+                      f"step) on {nth} threads",
+            "one_thread": {"value": B / one, "cores": 1,
+                           "sample": f"first {n1} tail groups ({tt1:.2f} s) and {h1} head labels "
+                                     f"({th1:.2f} s), scaled to {one:.1f} s per step"}}
 
 
 def run_infer(args, cfg, inp, t_gen):
@@ -588,6 +619,8 @@ def main():
                        device=dev)
     ws_h = torch.empty(max(256, H.haste_head_workspace_bytes(X, Wh, bce_h)), dtype=torch.uint8,
                        device=dev)
+    # idx does not change between steps: its feature order is formed once
+    H.haste_tail_prepare_layout(X, idx, L, G, ws_t)
     names = ["head_step", "tail_prepare", "tail_step_dw", "tail_step_dx"] + (["topk_merge"] if K else [])
     side = torch.cuda.Stream()   # default priority, like every stream here
 
@@ -607,10 +640,10 @@ def main():
             H.haste_head_step(X, Wh, bce_h, dWh, dX, accumulate_dX=True, workspace=ws_h)
         H.haste_tail_prepare(X, idx, L, G, bce_t, ws_t)
         if dom_dx:
-            H.haste_tail_step_dw(X, idx, W, L, G, bce_t, dW, ws_t)
+            H.haste_tail_step_dw(X, idx, W, L, G, bce_t, dW, ws_t, layout_ready=True)
         ev[0].record(main)
         if not dom_dx:
-            H.haste_tail_step_dw(X, idx, W, L, G, bce_t, dW, ws_t)
+            H.haste_tail_step_dw(X, idx, W, L, G, bce_t, dW, ws_t, layout_ready=True)
         else:
             H.haste_tail_step_dx(X, idx, W, L, G, bce_t, dX, ws_t, accumulate_dX=True)
         ev[1].record(main)
@@ -629,7 +662,7 @@ def main():
         ev[1].record()
         H.haste_tail_prepare(X, idx, L, G, bce_t, ws_t)
         ev[2].record()
-        H.haste_tail_step_dw(X, idx, W, L, G, bce_t, dW, ws_t)
+        H.haste_tail_step_dw(X, idx, W, L, G, bce_t, dW, ws_t, layout_ready=True)
         ev[3].record()
         H.haste_tail_step_dx(X, idx, W, L, G, bce_t, dX, ws_t, accumulate_dX=True)
         ev[4].record()
@@ -680,8 +713,7 @@ def main():
 
     peaks = measured_peaks(H, torch)
     alg = algorithmic(cfg)
-    tot_flops = sum(v["flops"] for v in alg.values())
-    tot_bytes = sum(v["bytes"] for v in alg.values())
+    tot_flops, tot_bytes = step_algorithmic(cfg)
     a_tf = alg[dom]["flops"] / (live_dom * 1e-6) / 1e12
     kernels = {n: {"avg_us": round(per[n], 2),
                    "tflops": round(alg[n]["flops"] / (per[n] * 1e-6) / 1e12, 1),

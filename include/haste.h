@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define HASTE_ABI_VERSION 3
+#define HASTE_ABI_VERSION 4
 
 typedef enum {
     HASTE_OK = 0,
@@ -87,7 +87,7 @@ typedef struct {
     int32_t G;      /* labels per group                     */
     int32_t F;      /* fan-in indices per group             */
     int32_t dtype;  /* haste_dtype of X, W, Z, dZ, dW       */
-    int32_t flags;  /* 0 or HASTE_TAIL_LEAN                 */
+    int32_t flags;  /* HASTE_TAIL_LEAN | HASTE_TAIL_LAYOUT_READY, or 0 */
 } haste_tail_desc;
 
 /* Tail flag.  By default the bf16 training calls that form dz from the
@@ -101,6 +101,16 @@ typedef struct {
  * dZ in place), and nothing of size B x L is stored.  Both forms give the
  * same results up to the summation order of Z. */
 #define HASTE_TAIL_LEAN 1
+
+/* Tail flag.  The bf16 calls that form logits read every group's features in
+ * an order chosen for the LDS banks (a permutation of idx[g], formed from idx
+ * alone, kept in the workspace at an offset that depends on the shape only).
+ * Without this flag every such call forms it first.  With it the call takes
+ * it from the workspace as haste_tail_prepare_layout (or an earlier call on
+ * the same workspace and idx) left it: for training with a fixed idx, form it
+ * once.  Calling with the flag on a workspace that does not hold the order
+ * of this idx gives wrong results. */
+#define HASTE_TAIL_LAYOUT_READY 2
 
 /* Head shape (dense classifier).  bf16 needs D a multiple of 32. */
 typedef struct {
@@ -155,7 +165,8 @@ typedef struct {
  * haste_topk_merge.  The workspace then also holds the call's fp32 logits
  * (B x labels x 4 bytes) and the bucket lists (B x buckets x K' x 8 bytes).
  * haste_tail_bwd and haste_head_bwd reject topk > 0; the other calls ignore
- * it. */
+ * it.  Ids are int32: a call whose label_offset + labels - 1 exceeds
+ * 2^31 - 1 returns HASTE_ERR_UNSUPPORTED when topk > 0. */
 
 /* Expected recall of the two-stage top-K (top-K page, "Theoretical
  * analysis": the K largest of n items fall into the buckets as a uniformly
@@ -189,9 +200,21 @@ haste_status haste_tail_layout(const haste_tail_desc *d, int64_t *out);
 
 /* Workspace bytes needed by the tail / head calls for this shape and BCE
  * setup (bce may be NULL).  Pass a 256-byte aligned device buffer at least
- * this large as `ws`. */
+ * this large as `ws`.  haste_tail_fwd needs only
+ * haste_tail_fwd_workspace_bytes (the training calls' dz tiles excluded; the
+ * regions they share sit at the same offsets). */
 size_t haste_tail_workspace_bytes(const haste_tail_desc *d, const haste_bce *bce);
+size_t haste_tail_fwd_workspace_bytes(const haste_tail_desc *d, const haste_bce *bce);
 size_t haste_head_workspace_bytes(const haste_head_desc *d, const haste_bce *bce);
+
+/* Forms in ws the feature order of idx that the logits calls read with
+ * HASTE_TAIL_LAYOUT_READY (see there).  ws: at least
+ * haste_tail_fwd_workspace_bytes(d, NULL) bytes, the workspace the later
+ * calls use.  Nothing to do for fp32 or G = 1 (returns HASTE_OK).  Errors as
+ * for the compute calls; the order depends on idx alone, so it stays valid
+ * until idx changes. */
+haste_status haste_tail_prepare_layout(const haste_tail_desc *d, const int32_t *idx, void *ws,
+                                       size_t ws_bytes, void *stream);
 
 /* Tail forward (Method item 1: gather X[:, idx[g]] once per group into LDS,
  * then a dense per-group contraction).  Writes Z (B x L) if Z != NULL;
@@ -202,8 +225,12 @@ haste_status haste_tail_fwd(const haste_tail_desc *d, const void *X,
                             const haste_bce *bce, void *ws, size_t ws_bytes,
                             void *stream);
 
-/* Tail backward: dW (same shape/dtype as W, padded rows zeroed) and dX
- * (B x D fp32; overwritten, or added to when accumulate_dX != 0).
+/* Tail backward (HASTE page, "Method" item 1: the exact gradients of the
+ * group-shared layer; the pages print no formulas, the reading is that the
+ * backward is the exact gradient of the forward: dW_g = dZ_g^T X_g, dX the
+ * scatter-add of dZ_g W_g through idx[g]).  dW (same shape/dtype as W,
+ * padded rows zeroed) and dX (B x D fp32; overwritten, or added to when
+ * accumulate_dX != 0).
  * dZ != NULL: use the given B x L gradient.  dZ == NULL: recompute z and
  * dz = s*(sigmoid(z)-y) from bce (dz kept in ws between the dW and dX
  * passes unless HASTE_TAIL_LEAN; bce->loss is NOT added here, so a separate
@@ -214,8 +241,10 @@ haste_status haste_tail_bwd(const haste_tail_desc *d, const void *X,
                             int accumulate_dX, void *ws, size_t ws_bytes,
                             void *stream);
 
-/* Fused tail training step: loss (+= into bce->loss), dW and dX in one
- * call; no logits are stored, and with HASTE_TAIL_LEAN no B x L buffer of
+/* Fused tail training step (HASTE page, "Method" item 1; the loss is the
+ * sigmoid binary cross-entropy over the listed positives, summed over
+ * labels and scaled by s, and the gradients are its exact ones): loss
+ * (+= into bce->loss), dW and dX in one call; no logits are stored, and with HASTE_TAIL_LEAN no B x L buffer of
  * any kind (see HASTE_TAIL_LEAN). */
 haste_status haste_tail_step(const haste_tail_desc *d, const void *X,
                              const int32_t *idx, const void *W,
@@ -276,30 +305,36 @@ haste_status haste_head_fwd(const haste_head_desc *d, const void *X,
                             const void *Wh, void *Zh, const haste_bce *bce,
                             void *ws, size_t ws_bytes, void *stream);
 
-/* Head backward: dWh (H x D, dtype) and dX (B x D fp32, overwritten or
- * accumulated).  dZh != NULL uses it; NULL recomputes from bce. */
+/* Head backward (HASTE page, "Method" item 2: the dense classifier over the
+ * frequent labels; exact gradients dWh = dZh^T X, dX += dZh Wh): dWh (H x D,
+ * dtype) and dX (B x D fp32, overwritten or accumulated).  dZh != NULL uses it; NULL recomputes from bce. */
 haste_status haste_head_bwd(const haste_head_desc *d, const void *X,
                             const void *Wh, const void *dZh,
                             const haste_bce *bce, void *dWh, float *dX,
                             int accumulate_dX, void *ws, size_t ws_bytes,
                             void *stream);
 
-/* Fused head step: loss (+=), top-K (if asked), dWh, dX. */
+/* Fused head step (HASTE page, "Method" item 2, with the same loss as the
+ * tail's): loss (+=), top-K (if asked), dWh, dX. */
 haste_status haste_head_step(const haste_head_desc *d, const void *X,
                              const void *Wh, const haste_bce *bce, void *dWh,
                              float *dX, int accumulate_dX, void *ws,
                              size_t ws_bytes, void *stream);
 
 /* Group-major view of the tail positives (the list the fused epilogue
- * walks): grp_ptr (N_g + 1 entries) and entries (<= nnz), entry = b*G + j,
+ * walks; the positives are the labels y = 1 of the sigmoid-BCE, and the
+ * order is fixed so that it can be compared bit for bit): grp_ptr (N_g + 1 entries) and entries (<= nnz), entry = b*G + j,
  * ordered by group, then row b, then slot j.  Deterministic. */
 haste_status haste_tail_group_positives(const haste_tail_desc *d,
                                         const haste_bce *bce, int32_t *grp_ptr,
                                         int32_t *entries, void *ws,
                                         size_t ws_bytes, void *stream);
 
-/* Index check: writes to *first_bad_group (device int32) the smallest group
- * whose row of idx is not strictly increasing inside [0, D), or -1. */
+/* Index check (HASTE page, "Method" item 1: one set of F distinct input
+ * features per group; the reading here is that each set is stored sorted,
+ * strictly increasing, inside [0, D)): writes to *first_bad_group (a DEVICE
+ * int32, so the call stays asynchronous) the smallest group whose row of idx
+ * breaks that, or -1. */
 haste_status haste_tail_validate(const haste_tail_desc *d, const int32_t *idx,
                                  int32_t *first_bad_group, void *stream);
 

@@ -58,7 +58,7 @@ inline int pad_rows(int B) { return (B + 63) / 64 * 64; }
 
 // ----------------------------------------------------------- workspace maps
 struct TailWs {
-    size_t xt, cnt, ptr, ent, idxp, perm, sched, dz, dzt, z32, cand, total;
+    size_t xt, cnt, ptr, ent, idxp, perm, sched, dz, dzt, z32, cand, fwd_total, total;
     bool has_dzt, has_topk, tk_fused;
 };
 
@@ -77,22 +77,23 @@ TailWs tail_ws(const haste_tail_desc *d, const haste_bce *bce) {
     const int nnz = bce ? (bce->nnz > 0 ? bce->nnz : 0) : 0;
     size_t o = 0;
     if (d->dtype == HASTE_BF16) {
+        // first the dW/logits pass's feature order: idx reordered, and the
+        // order (groups of 16 and more; G = 1 gathers per label).  It depends
+        // on the shape and idx alone, so it sits at the same offset for every
+        // call and haste_tail_prepare_layout can form it once.
+        if (d->G > 1) {
+            w.idxp = o; o += al256((size_t)ng * d->F * 2);
+            w.perm = o; o += al256((size_t)ng * d->F);
+        }
         w.xt = o;  o += al256((size_t)d->D * pad_rows(d->B) * 2);
         w.cnt = o; o += al256((size_t)(nnz > 0 ? nnz : 1) * 20 + 8);  // keys, sorted, ranks, count
         w.ptr = o; o += al256((size_t)(ng + 4) * 4);   // +3: 16-byte reads of a pair
         w.ent = o; o += al256((size_t)(nnz > 0 ? nnz : 1) * 4);
         w.sched = o; o += 256;   // the dW/logits pass's run counters
-        // the dW/logits pass's feature order: idx reordered, and the order
-        // (groups of 16 and more; G = 1 gathers per label)
-        if (d->G > 1) {
-            w.idxp = o; o += al256((size_t)ng * d->F * 2);
-            w.perm = o; o += al256((size_t)ng * d->F);
-        }
         // dz of the dW pass, kept for the dX pass unless the caller asks for
         // the lean form (which recomputes it): Bp x (Ng*G) bf16 in 1 KB tiles
         // (also without bce: the backward from a given dZ forms the same tiles)
         w.has_dzt = !(d->flags & HASTE_TAIL_LEAN) && d->G > 1;
-        if (w.has_dzt) { w.dzt = o; o += al256((size_t)ng * d->G * pad_rows(d->B) * 2); }
     } else {
         // per-group counts; also the key space of haste_tail_group_positives
         const size_t keys = (size_t)(nnz > 0 ? nnz : 1) * 20 + 8;
@@ -111,6 +112,10 @@ TailWs tail_ws(const haste_tail_desc *d, const haste_bce *bce) {
         o += al256((size_t)ng * pad_rows(d->B) * 8 +
                    (size_t)d->B * topk_gm_segments(ng, d->B).nseg * bce->topk * 8);
     }
+    // the dz tiles last: the forward, which never uses them, needs only what
+    // comes before (fwd_total)
+    w.fwd_total = o;
+    if (w.has_dzt) { w.dzt = o; o += al256((size_t)ng * d->G * pad_rows(d->B) * 2); }
     w.total = o;
     return w;
 }
@@ -145,7 +150,8 @@ haste_status check_tail(const haste_tail_desc *d) {
     if (d->F > d->D) return fail(HASTE_ERR_INVALID, "F=%d exceeds D=%d", d->F, d->D);
     if (d->dtype != HASTE_F32 && d->dtype != HASTE_BF16)
         return fail(HASTE_ERR_INVALID, "unknown dtype %d", d->dtype);
-    if (d->flags & ~HASTE_TAIL_LEAN) return fail(HASTE_ERR_INVALID, "unknown tail flags 0x%x", d->flags);
+    if (d->flags & ~(HASTE_TAIL_LEAN | HASTE_TAIL_LAYOUT_READY))
+        return fail(HASTE_ERR_INVALID, "unknown tail flags 0x%x", d->flags);
     if (d->dtype == HASTE_BF16) {
         if (!tail_bf16_supported(d->G, d->F, d->D))
             return fail(HASTE_ERR_UNSUPPORTED,
@@ -170,7 +176,8 @@ haste_status check_head(const haste_head_desc *d) {
     return HASTE_OK;
 }
 
-haste_status check_bce(const haste_bce *b, int B, bool topk_ok) {
+// n: the call's label count (ids label_offset .. label_offset + n - 1)
+haste_status check_bce(const haste_bce *b, int B, bool topk_ok, int64_t n) {
     if (!b) return HASTE_OK;
     if (b->nnz < 0) return fail(HASTE_ERR_INVALID, "bce.nnz < 0");
     if (!b->row_ptr) return fail(HASTE_ERR_INVALID, "bce.row_ptr is NULL");
@@ -187,6 +194,9 @@ haste_status check_bce(const haste_bce *b, int B, bool topk_ok) {
             return fail(HASTE_ERR_INVALID, "an approximate top-K (K' < K) needs bce.topk_buckets > 0");
         if (!b->topk_val || !aligned(b->topk_val, 4)) return fail(HASTE_ERR_INVALID, "bce.topk_val NULL or misaligned");
         if (!b->topk_idx || !aligned(b->topk_idx, 4)) return fail(HASTE_ERR_INVALID, "bce.topk_idx NULL or misaligned");
+        if (b->label_offset + n - 1 > (int64_t)INT32_MAX)
+            return fail(HASTE_ERR_UNSUPPORTED, "top-K ids are int32: label_offset + labels - 1 = %lld exceeds 2^31 - 1",
+                        (long long)(b->label_offset + n - 1));
     }
     (void)B;
     return HASTE_OK;
@@ -261,6 +271,7 @@ haste_status bf16_prep(const haste_tail_desc *d, const void *X, const haste_bce 
 // depends on idx alone and is formed before every such pass.
 haste_status feature_order(const haste_tail_desc *d, const int32_t *idx, void *ws, const TailWs &m,
                            hipStream_t st) {
+    if (d->flags & HASTE_TAIL_LAYOUT_READY) return HASTE_OK;   // formed by an earlier call
     TRY_HIP(launch_feature_order(idx, n_groups(d), d->F, (unsigned short *)B8(ws, m.idxp),
                                  (unsigned char *)B8(ws, m.perm), st),
             "feature order");
@@ -377,6 +388,24 @@ size_t haste_tail_workspace_bytes(const haste_tail_desc *d, const haste_bce *bce
     return tail_ws(d, bce).total;
 }
 
+size_t haste_tail_fwd_workspace_bytes(const haste_tail_desc *d, const haste_bce *bce) {
+    if (check_tail(d) != HASTE_OK) return 0;
+    return tail_ws(d, bce).fwd_total;
+}
+
+haste_status haste_tail_prepare_layout(const haste_tail_desc *d, const int32_t *idx, void *ws,
+                                       size_t ws_bytes, void *stream) {
+    g_err.clear();
+    TRY(check_tail(d));
+    TRY(need_al(idx, 4, "idx"));
+    if (d->dtype != HASTE_BF16 || d->G == 1) return HASTE_OK;   // no feature order on these paths
+    const TailWs m = tail_ws(d, nullptr);
+    TRY(check_ws(ws, ws_bytes, m.fwd_total));
+    haste_tail_desc dd = *d;
+    dd.flags &= ~HASTE_TAIL_LAYOUT_READY;
+    return feature_order(&dd, idx, ws, m, S(stream));
+}
+
 size_t haste_head_workspace_bytes(const haste_head_desc *d, const haste_bce *bce) {
     (void)bce;
     if (check_head(d) != HASTE_OK) return 0;
@@ -388,11 +417,11 @@ haste_status haste_tail_fwd(const haste_tail_desc *d, const void *X, const int32
                             size_t ws_bytes, void *stream) {
     g_err.clear();
     TRY(tail_common(d, X, idx, W));
-    TRY(check_bce(bce, d->B, true));
+    TRY(check_bce(bce, d->B, true, d->L));
     if (!Z && !bce) return fail(HASTE_ERR_INVALID, "nothing to compute: Z and bce are both NULL");
     if (Z && !aligned(Z, d->dtype == HASTE_BF16 ? 2 : 4)) return fail(HASTE_ERR_INVALID, "Z misaligned");
     const TailWs m = tail_ws(d, bce);
-    TRY(check_ws(ws, ws_bytes, m.total));
+    TRY(check_ws(ws, ws_bytes, m.fwd_total));
     hipStream_t st = S(stream);
     if (d->dtype == HASTE_BF16 && d->G == 1) {
         if (m.has_topk) return fail(HASTE_ERR_UNSUPPORTED, "no top-K with G = 1");
@@ -435,7 +464,7 @@ haste_status haste_tail_bwd(const haste_tail_desc *d, const void *X, const int32
     TRY(tail_common(d, X, idx, W));
     TRY(not_g1(d));
     if (!dZ && !bce) return fail(HASTE_ERR_INVALID, "need dZ or bce to form the gradient");
-    if (!dZ) TRY(check_bce(bce, d->B, false));
+    if (!dZ) TRY(check_bce(bce, d->B, false, d->L));
     TRY(need_al(dW, d->dtype == HASTE_BF16 ? 8 : 4, "dW"));
     TRY(need_al(dX, 4, "dX"));
     if (dZ && !aligned(dZ, d->dtype == HASTE_BF16 ? 2 : 4)) return fail(HASTE_ERR_INVALID, "dZ misaligned");
@@ -481,7 +510,7 @@ haste_status haste_tail_step(const haste_tail_desc *d, const void *X, const int3
     TRY(tail_common(d, X, idx, W));
     TRY(not_g1(d));
     TRY(need(bce, "bce"));
-    TRY(check_bce(bce, d->B, true));
+    TRY(check_bce(bce, d->B, true, d->L));
     TRY(need_al(dW, d->dtype == HASTE_BF16 ? 8 : 4, "dW"));
     TRY(need_al(dX, 4, "dX"));
     const TailWs m = tail_ws(d, bce);
@@ -522,7 +551,7 @@ haste_status haste_tail_step_sgd(const haste_tail_desc *d, const void *X, const 
     TRY(tail_common(d, X, idx, W));
     TRY(not_g1(d));
     TRY(need(bce, "bce"));
-    TRY(check_bce(bce, d->B, true));
+    TRY(check_bce(bce, d->B, true, d->L));
     TRY(need_al(W_out, 16, "W_out"));
     TRY(need_al(dX, 4, "dX"));
     if (d->dtype != HASTE_BF16)
@@ -573,7 +602,7 @@ haste_status haste_tail_prepare(const haste_tail_desc *d, const void *X, const h
     TRY(not_g1(d));
     TRY(need_al(X, d->dtype == HASTE_BF16 ? 16 : 4, "X"));
     TRY(need(bce, "bce"));
-    TRY(check_bce(bce, d->B, true));
+    TRY(check_bce(bce, d->B, true, d->L));
     const TailWs m = tail_ws(d, bce);
     TRY(check_ws(ws, ws_bytes, m.total));
     if (d->dtype == HASTE_BF16) TRY(bf16_prep(d, X, bce, ws, m, S(stream)));
@@ -587,7 +616,7 @@ haste_status haste_tail_step_dw(const haste_tail_desc *d, const void *X, const i
     TRY(tail_common(d, X, idx, W));
     TRY(not_g1(d));
     TRY(need(bce, "bce"));
-    TRY(check_bce(bce, d->B, true));
+    TRY(check_bce(bce, d->B, true, d->L));
     TRY(need_al(dW, d->dtype == HASTE_BF16 ? 8 : 4, "dW"));
     const TailWs m = tail_ws(d, bce);
     TRY(check_ws(ws, ws_bytes, m.total));
@@ -620,7 +649,7 @@ haste_status haste_tail_step_dx(const haste_tail_desc *d, const void *X, const i
     TRY(tail_common(d, X, idx, W));
     TRY(not_g1(d));
     TRY(need(bce, "bce"));
-    TRY(check_bce(bce, d->B, true));
+    TRY(check_bce(bce, d->B, true, d->L));
     TRY(need_al(dX, 4, "dX"));
     const TailWs m = tail_ws(d, bce);
     TRY(check_ws(ws, ws_bytes, m.total));
@@ -757,7 +786,7 @@ haste_status haste_head_fwd(const haste_head_desc *d, const void *X, const void 
                             const haste_bce *bce, void *ws, size_t ws_bytes, void *stream) {
     g_err.clear();
     TRY(head_common(d, X, Wh));
-    TRY(check_bce(bce, d->B, true));
+    TRY(check_bce(bce, d->B, true, d->H));
     if (!Zh && !bce) return fail(HASTE_ERR_INVALID, "nothing to compute: Zh and bce are both NULL");
     const HeadWs m = head_ws(d, bce);
     TRY(check_ws(ws, ws_bytes, bce ? m.total : 0));
@@ -770,7 +799,7 @@ haste_status haste_head_bwd(const haste_head_desc *d, const void *X, const void 
     g_err.clear();
     TRY(head_common(d, X, Wh));
     if (!dZh && !bce) return fail(HASTE_ERR_INVALID, "need dZh or bce to form the gradient");
-    if (!dZh) TRY(check_bce(bce, d->B, false));
+    if (!dZh) TRY(check_bce(bce, d->B, false, d->H));
     TRY(need_al(dWh, d->dtype == HASTE_BF16 ? 2 : 4, "dWh"));
     TRY(need_al(dX, 4, "dX"));
     if (dZh && !aligned(dZh, 16)) return fail(HASTE_ERR_INVALID, "dZh is not 16-byte aligned");
@@ -792,7 +821,7 @@ haste_status haste_head_step(const haste_head_desc *d, const void *X, const void
     g_err.clear();
     TRY(head_common(d, X, Wh));
     TRY(need(bce, "bce"));
-    TRY(check_bce(bce, d->B, true));
+    TRY(check_bce(bce, d->B, true, d->H));
     TRY(need_al(dWh, d->dtype == HASTE_BF16 ? 2 : 4, "dWh"));
     TRY(need_al(dX, 4, "dX"));
     const HeadWs m = head_ws(d, bce);
@@ -810,7 +839,7 @@ haste_status haste_tail_group_positives(const haste_tail_desc *d, const haste_bc
     g_err.clear();
     TRY(check_tail(d));
     TRY(need(bce, "bce"));
-    TRY(check_bce(bce, d->B, true));   // top-K settings do not matter here
+    TRY(check_bce(bce, d->B, true, d->L));   // top-K settings do not matter here
     TRY(need_al(grp_ptr, 4, "grp_ptr"));
     if (bce->nnz > 0) TRY(need_al(entries, 4, "entries"));
     const TailWs m = tail_ws(d, bce);

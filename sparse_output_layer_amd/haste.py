@@ -23,6 +23,7 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "haste.h")
 HASTE_OK, HASTE_ERR_INVALID, HASTE_ERR_UNSUPPORTED, HASTE_ERR_WORKSPACE, HASTE_ERR_HIP = range(5)
 HASTE_F32, HASTE_BF16 = 0, 1
 HASTE_TAIL_LEAN = 1   # tail flag: recompute dz in the dX pass instead of keeping it in ws
+HASTE_TAIL_LAYOUT_READY = 2   # tail flag: ws already holds the feature order of idx
 
 
 class HasteError(RuntimeError):
@@ -64,6 +65,8 @@ _SIGS = {
     "haste_tail_layout": (ctypes.c_int, [_PD, ctypes.POINTER(ctypes.c_int64)]),
     "haste_tail_workspace_bytes": (_sz, [_PD, _PB]),
     "haste_head_workspace_bytes": (_sz, [_PH, _PB]),
+    "haste_tail_fwd_workspace_bytes": (_sz, [_PD, _PB]),
+    "haste_tail_prepare_layout": (ctypes.c_int, [_PD, _vp, _vp, _sz, _vp]),
     "haste_tail_fwd": (ctypes.c_int, [_PD, _vp, _vp, _vp, _vp, _PB, _vp, _sz, _vp]),
     "haste_tail_bwd": (ctypes.c_int, [_PD, _vp, _vp, _vp, _vp, _PB, _vp, _vp, ctypes.c_int,
                                       _vp, _sz, _vp]),
@@ -188,10 +191,11 @@ def _bref(bce: Optional[Bce]):
     return None if bce is None else ctypes.pointer(bce.struct())
 
 
-def tail_desc(X: torch.Tensor, idx: torch.Tensor, L: int, G: int, lean: bool = False) -> TailDesc:
+def tail_desc(X: torch.Tensor, idx: torch.Tensor, L: int, G: int, lean: bool = False,
+              layout_ready: bool = False) -> TailDesc:
     B, D = X.shape
     return TailDesc(B=B, D=D, L=int(L), G=int(G), F=int(idx.shape[1]), dtype=_dtype_code(X),
-                    flags=HASTE_TAIL_LEAN if lean else 0)
+                    flags=(HASTE_TAIL_LEAN if lean else 0) | (HASTE_TAIL_LAYOUT_READY if layout_ready else 0))
 
 
 def head_desc(X: torch.Tensor, Wh: torch.Tensor) -> HeadDesc:
@@ -225,6 +229,19 @@ def haste_tail_workspace_bytes(X, idx, L, G, bce: Optional[Bce] = None, lean=Fal
     return lib().haste_tail_workspace_bytes(ctypes.byref(tail_desc(X, idx, L, G, lean)), _bref(bce))
 
 
+def haste_tail_fwd_workspace_bytes(X, idx, L, G, bce: Optional[Bce] = None) -> int:
+    return lib().haste_tail_fwd_workspace_bytes(ctypes.byref(tail_desc(X, idx, L, G)), _bref(bce))
+
+
+def haste_tail_prepare_layout(X, idx, L, G, workspace: torch.Tensor, lean=False):
+    """Forms idx's feature order in `workspace`; later calls on it pass
+    layout_ready=True (tail flag HASTE_TAIL_LAYOUT_READY) to skip forming it."""
+    _need(idx, "idx", torch.int32)
+    d = tail_desc(X, idx, L, G, lean)
+    _check(lib().haste_tail_prepare_layout(ctypes.byref(d), _ptr(idx), _ptr(workspace),
+                                           workspace.numel(), _stream()))
+
+
 def haste_head_workspace_bytes(X, Wh, bce: Optional[Bce] = None) -> int:
     return lib().haste_head_workspace_bytes(ctypes.byref(head_desc(X, Wh)), _bref(bce))
 
@@ -235,13 +252,13 @@ def _tail_in(X, idx, W):
     _need(W, "W", X.dtype)
 
 
-def haste_tail_fwd(X, idx, W, L, G, Z=None, bce: Optional[Bce] = None, workspace=None, lean=False):
+def haste_tail_fwd(X, idx, W, L, G, Z=None, bce: Optional[Bce] = None, workspace=None, lean=False, layout_ready=False):
     _tail_in(X, idx, W)
     if Z is not None:
         _need(Z, "Z", X.dtype)
-    d = tail_desc(X, idx, L, G, lean)
+    d = tail_desc(X, idx, L, G, lean, layout_ready)
     b = _bref(bce)
-    ws, nb = _workspace(lib().haste_tail_workspace_bytes(ctypes.byref(d), b), X.device, workspace)
+    ws, nb = _workspace(lib().haste_tail_fwd_workspace_bytes(ctypes.byref(d), b), X.device, workspace)
     _check(lib().haste_tail_fwd(ctypes.byref(d), _ptr(X), _ptr(idx), _ptr(W), _ptr(Z), b,
                                 _ptr(ws), nb, _stream()))
     return Z
@@ -263,11 +280,11 @@ def haste_tail_bwd(X, idx, W, L, G, dW, dX, dZ=None, bce: Optional[Bce] = None,
 
 
 def haste_tail_step(X, idx, W, L, G, bce: Bce, dW, dX, accumulate_dX=False, workspace=None,
-                    lean=False):
+                    lean=False, layout_ready=False):
     _tail_in(X, idx, W)
     _need(dW, "dW", X.dtype)
     _need(dX, "dX", torch.float32)
-    d = tail_desc(X, idx, L, G, lean)
+    d = tail_desc(X, idx, L, G, lean, layout_ready)
     b = _bref(bce)
     ws, nb = _workspace(lib().haste_tail_workspace_bytes(ctypes.byref(d), b), X.device, workspace)
     _check(lib().haste_tail_step(ctypes.byref(d), _ptr(X), _ptr(idx), _ptr(W), b, _ptr(dW),
@@ -311,11 +328,11 @@ def haste_tail_prepare(X, idx, L, G, bce: Bce, workspace: torch.Tensor, lean=Fal
                                     workspace.numel(), _stream()))
 
 
-def haste_tail_step_dw(X, idx, W, L, G, bce: Bce, dW, workspace: torch.Tensor, lean=False):
+def haste_tail_step_dw(X, idx, W, L, G, bce: Bce, dW, workspace: torch.Tensor, lean=False, layout_ready=False):
     """Split step, part 2: loss and dW (one kernel)."""
     _tail_in(X, idx, W)
     _need(dW, "dW", X.dtype)
-    d = tail_desc(X, idx, L, G, lean)
+    d = tail_desc(X, idx, L, G, lean, layout_ready)
     b = _bref(bce)
     _check(lib().haste_tail_step_dw(ctypes.byref(d), _ptr(X), _ptr(idx), _ptr(W), b, _ptr(dW),
                                     _ptr(workspace), workspace.numel(), _stream()))

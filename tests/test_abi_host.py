@@ -20,7 +20,7 @@ def test_exports_every_declared_symbol(L):
     assert "haste_tail_fwd" in names and "haste_tail_step" in names
     missing = [n for n in names if not hasattr(L, n)]
     assert missing == []
-    assert L.haste_abi_version() == 3
+    assert L.haste_abi_version() == 4
     for s in range(5):
         assert L.haste_status_string(s)
 
@@ -53,7 +53,15 @@ def test_workspace_sizes(L):
     nl = L.haste_tail_workspace_bytes(ctypes.byref(lean), ctypes.byref(b))
     assert n1 - nl >= 64 * 1024 * 2 and nl >= n0l + 10000 * 4 - 256
     # unknown flags -> 0
-    assert L.haste_tail_workspace_bytes(ctypes.byref(_desc(flags=2)), None) == 0
+    assert L.haste_tail_workspace_bytes(ctypes.byref(_desc(flags=4)), None) == 0
+    # the forward needs no dz tiles: its workspace is the training calls' less them
+    nf = L.haste_tail_fwd_workspace_bytes(ctypes.byref(d), ctypes.byref(b))
+    assert nf > 0 and n1 - nf >= 64 * 1024 * 2
+    assert nf == L.haste_tail_fwd_workspace_bytes(ctypes.byref(lean), ctypes.byref(b))
+    # the feature order sits at offset 0 for every BCE setup: a workspace that
+    # holds it once serves every later call (HASTE_TAIL_LAYOUT_READY)
+    rd = _desc(flags=H.HASTE_TAIL_LAYOUT_READY)
+    assert L.haste_tail_workspace_bytes(ctypes.byref(rd), None) == n0
     # unsupported shape -> 0
     assert L.haste_tail_workspace_bytes(ctypes.byref(_desc(G=8)), None) == 0
     h = H.HeadDesc(B=8, D=64, H=128, dtype=H.HASTE_BF16)
@@ -103,6 +111,22 @@ def test_argument_errors_fail_before_launch(L):
     # fp32 accepts any G / F
     d = _desc(dtype=H.HASTE_F32, G=3, F=7)
     assert _status(L, d) == H.HASTE_ERR_WORKSPACE
+    # top-K ids are int32: the last label's global id must fit
+    big = _desc(L=2 ** 31 - 100)
+    for off, want in ((100, H.HASTE_ERR_WORKSPACE), (101, H.HASTE_ERR_UNSUPPORTED)):
+        b = H.BceStruct(nnz=5, row_ptr=0x1000, labels=0x1000, topk=5, topk_val=0x1000,
+                        topk_idx=0x1000, label_offset=off)
+        assert _status(L, big, bce=ctypes.byref(b)) == want, off
+    h = H.HeadDesc(B=8, D=64, H=1 << 20, dtype=H.HASTE_BF16)
+    b = H.BceStruct(nnz=5, row_ptr=0x1000, labels=0x1000, topk=5, topk_val=0x1000,
+                    topk_idx=0x1000, label_offset=2 ** 31 - (1 << 20) + 1)
+    assert L.haste_head_fwd(ctypes.byref(h), 0x1000, 0x1000, None, ctypes.byref(b), None, 0, None) == \
+        H.HASTE_ERR_UNSUPPORTED
+    # the layout call: checks as the compute calls, then the workspace
+    assert L.haste_tail_prepare_layout(ctypes.byref(_desc()), 0x1000, None, 0, None) == H.HASTE_ERR_WORKSPACE
+    assert L.haste_tail_prepare_layout(ctypes.byref(_desc()), 0, 0x1000, 1 << 30, None) == H.HASTE_ERR_INVALID
+    assert L.haste_tail_prepare_layout(ctypes.byref(_desc(G=8)), 0x1000, 0x1000, 1 << 30, None) == \
+        H.HASTE_ERR_UNSUPPORTED
 
 
 def test_head_and_step_argument_errors(L):

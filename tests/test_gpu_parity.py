@@ -109,6 +109,36 @@ def test_bf16_tail_and_head(H, case):
         check(f"split step dX (lean={lean})", to_f64(dX5) - 2.0, r.dX_tail, r.dX_tail_abs, "bf16",
               nterms=ng * c.G)
 
+    # the feature order formed once (haste_tail_prepare_layout) and taken
+    # from the workspace by every later call (HASTE_TAIL_LAYOUT_READY): the
+    # same results, bit for bit, over two steps on one workspace
+    b8 = d.bce(c.H, s)
+    ws = torch.empty(H.haste_tail_workspace_bytes(d.X, d.idx, c.L, c.G, b8), dtype=torch.uint8,
+                     device=DEV)
+    H.haste_tail_prepare_layout(d.X, d.idx, c.L, c.G, ws)
+    for rep in range(2):
+        b8 = d.bce(c.H, s)
+        dW8 = torch.empty_like(d.W)
+        dX8 = torch.zeros_like(dX)
+        H.haste_tail_prepare(d.X, d.idx, c.L, c.G, b8, ws)
+        H.haste_tail_step_dw(d.X, d.idx, d.W, c.L, c.G, b8, dW8, ws, layout_ready=True)
+        H.haste_tail_step_dx(d.X, d.idx, d.W, c.L, c.G, b8, dX8, ws, accumulate_dX=True)
+        torch.cuda.synchronize()
+        assert torch.equal(dW8, dW), f"layout-ready step {rep}: dW differs"
+        check_loss(f"layout-ready step loss {rep}", b8.loss.item(), r.loss_tail, "bf16")
+        check(f"layout-ready step dX {rep}", to_f64(dX8), r.dX_tail, r.dX_tail_abs, "bf16",
+              nterms=ng * c.G)
+    # the forward in a workspace of haste_tail_fwd_workspace_bytes (no dz tiles)
+    bf_ = d.bce(c.H, s)
+    wsf = torch.empty(H.haste_tail_fwd_workspace_bytes(d.X, d.idx, c.L, c.G, bf_), dtype=torch.uint8,
+                      device=DEV)
+    assert wsf.numel() < ws.numel()
+    Zf = torch.empty_like(Z)
+    H.haste_tail_fwd(d.X, d.idx, d.W, c.L, c.G, Z=Zf, bce=bf_, workspace=wsf)
+    torch.cuda.synchronize()
+    assert torch.equal(Zf, Z)
+    check_loss("tail fwd loss (forward workspace)", bf_.loss.item(), r.loss_tail, "bf16")
+
     # fused SGD step: W_out = W - lr * dW, bit for bit the update after the
     # step; against the oracle's W - lr * dW within one bf16 rounding plus
     # lr times the dW tolerance; dX and the loss as the plain step

@@ -72,25 +72,28 @@ def test_topk(H, case):
     results["tail split dW"] = (tv, ti)
     torch.cuda.synchronize()
     for name, (tv, ti) in results.items():
-        check_topk(name, tv.cpu().numpy(), ti.cpu().numpy(), Zt, Zta, K, dt, id0=c.H)
+        tie_free, _ = check_topk(name, tv.cpu().numpy(), ti.cpu().numpy(), Zt, Zta, K, dt, id0=c.H,
+                                 nterms=c.F)
+        assert tie_free >= c.B // 2, (name, tie_free)
 
     # head: forward and fused step
     hv, hi = outs()
     H.haste_head_fwd(d.X, d.Wh, bce=bce(0, hv, hi))
     torch.cuda.synchronize()
-    check_topk("head fwd", hv.cpu().numpy(), hi.cpu().numpy(), Zh, Zha, K, dt, id0=0)
+    check_topk("head fwd", hv.cpu().numpy(), hi.cpu().numpy(), Zh, Zha, K, dt, id0=0, nterms=c.D)
     hv, hi = outs()
     H.haste_head_step(d.X, d.Wh, bce(0, hv, hi), torch.empty_like(d.Wh),
                       torch.empty(c.B, c.D, dtype=torch.float32, device=DEV))
     torch.cuda.synchronize()
-    check_topk("head step", hv.cpu().numpy(), hi.cpu().numpy(), Zh, Zha, K, dt, id0=0)
+    check_topk("head step", hv.cpu().numpy(), hi.cpu().numpy(), Zh, Zha, K, dt, id0=0, nterms=c.D)
 
     # whole output space: head and tail lists merged
     tv, ti = results["tail step"]
     mv, mi = H.haste_topk_merge(hv, hi, tv, ti)
     torch.cuda.synchronize()
     check_topk("merged", mv.cpu().numpy(), mi.cpu().numpy(), np.concatenate([Zh, Zt], axis=1),
-               np.concatenate([Zha, Zta], axis=1), K, dt, id0=0)
+               np.concatenate([Zha, Zta], axis=1), K, dt, id0=0,
+               nterms=np.concatenate([np.full(c.H, c.D), np.full(c.L, c.F)]))
 
 
 APPROX = [

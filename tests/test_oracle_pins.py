@@ -343,6 +343,39 @@ def test_p6_expected_recall_exhaustive_and_closed_forms():
     assert abs(rec.mean() - exact) < 4 * rec.std() / np.sqrt(trials) + 1e-12, (rec.mean(), exact)
 
 
+def test_p6_plan_is_the_cheapest_pair_by_enumeration():
+    """The automatic (K', buckets) choice (reading C24: fewest stage-2
+    candidates buckets * K' among the pairs whose expected recall reaches the
+    target, ties to the smaller K', at least min_buckets buckets) equals a
+    brute-force search over every pair in which the recall of each pair is
+    found by enumerating every placement of the K largest items on the n
+    positions (buckets of ceil(n / b) consecutive positions), not by the
+    hypergeometric formula."""
+    from fractions import Fraction
+    from itertools import combinations
+
+    def recall_enum(n, K, kp, b):
+        seg = -(-n // b)
+        Kt = min(K, n)
+        tot, cnt = Fraction(0), 0
+        for pos in combinations(range(n), Kt):
+            per = {}
+            for p_ in pos:
+                per[p_ // seg] = per.get(p_ // seg, 0) + 1
+            tot += Fraction(sum(min(c, kp) for c in per.values()), Kt)
+            cnt += 1
+        return tot / cnt
+
+    for n, K in ((6, 2), (8, 3), (9, 4), (10, 3)):
+        rec = {(kp, b): recall_enum(n, K, kp, b) for kp in range(1, K + 1) for b in range(1, n + 1)}
+        for target in (Fraction(1, 2), Fraction(7, 10), Fraction(9, 10), Fraction(19, 20), Fraction(1)):
+            for bmin in (1, 2, 3):
+                ok = [(b * kp, kp, b) for (kp, b), r in rec.items() if b >= bmin and r >= target]
+                want = None if not ok else min(ok)[1:]
+                got = oracle.topk_plan(n, K, target, bmin)
+                assert got == want, (n, K, target, bmin, got, want)
+
+
 def test_sgd_step_descends_at_first_order_rate():
     """The update W - lr * dW with the oracle's tail gradient lowers the
     oracle's loss, and (L(W - lr g) - L(W)) / lr tends to -|g|^2 as lr -> 0
