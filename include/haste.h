@@ -161,9 +161,15 @@ typedef struct {
  * the buckets are exactly the tail's label groups (ceil(L / topk_buckets)
  * = G, bf16) and K' = 1, stage 1 runs inside the logits pass (the top-K
  * page's matmul-fused stage 1): the same result without the fp32 logits in
- * the workspace.  The head's and the tail's lists combine with
+ * the workspace.  The exact top-K (K' = K) of a bf16 tail with G >= 16 runs
+ * the same fused stage over the label groups, merges each row's K best
+ * groups, and recomputes those K groups' logits bit for bit as the logits
+ * pass forms them to keep the K best: the exact top-K of the kernels' fp32
+ * logits (a label of the row's top K lies in one of its K best groups),
+ * again without the fp32 logits.  The head's and the tail's lists combine with
  * haste_topk_merge.  The workspace then also holds the call's fp32 logits
- * (B x labels x 4 bytes) and the bucket lists (B x buckets x K' x 8 bytes).
+ * (B x labels x 4 bytes) and the bucket lists (B x buckets x K' x 8 bytes),
+ * or, for the fused forms, the per-group lists (N_g x B_pad x 8 bytes).
  * haste_tail_bwd and haste_head_bwd reject topk > 0; the other calls ignore
  * it.  Ids are int32: a call whose label_offset + labels - 1 exceeds
  * 2^31 - 1 returns HASTE_ERR_UNSUPPORTED when topk > 0. */

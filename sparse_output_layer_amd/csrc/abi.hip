@@ -62,10 +62,21 @@ struct TailWs {
     bool has_dzt, has_topk, tk_fused;
 };
 
+// The exact top-K (K' = K) of bf16 groups of 16 and more: the logits pass
+// keeps each (group, row)'s largest logit, a merge takes each row's K best
+// groups, and a last pass recomputes those groups' logits and keeps the K
+// best -- exact for any bucketing, without the fp32 logits.
+bool topk_exact_fused(const haste_tail_desc *d, const haste_bce *bce) {
+    if (!bce || bce->topk <= 0 || d->dtype != HASTE_BF16 || d->G < 16) return false;
+    return bce->topk_kprime == 0 || bce->topk_kprime == bce->topk;
+}
+
 // The top-K's stage 1 runs inside the logits pass when its buckets are the
 // label groups and K' = 1 (bf16, groups of 16 and more): same buckets, same
-// K', same result as the separate stage 1, without the fp32 logits.
+// K', same result as the separate stage 1, without the fp32 logits; and for
+// the exact top-K (above).
 bool topk_fused(const haste_tail_desc *d, const haste_bce *bce) {
+    if (topk_exact_fused(d, bce)) return true;
     if (!bce || bce->topk <= 0 || d->dtype != HASTE_BF16 || d->G < 16) return false;
     if (bce->topk_kprime != 1 || bce->topk_buckets <= 0) return false;
     return topk_buckets(d->L, bce->topk_buckets, d->B).seg_len == d->G;
@@ -313,8 +324,10 @@ haste_status run_topk(const haste_bce *bce, const float *z, int B, int64_t n, vo
     return HASTE_OK;
 }
 
-// the tail's top-K after its logits pass: stage 2 alone when stage 1 was fused
-haste_status tail_topk(const haste_tail_desc *d, const haste_bce *bce, const TailWs &m,
+// the tail's top-K after its logits pass: stage 2 alone when stage 1 was
+// fused (one maximum per group); for the exact top-K, then the recomputation
+// of each row's K best groups
+haste_status tail_topk(const haste_tail_desc *d, const void *X, const haste_bce *bce, const TailWs &m,
                        const TailArgs &a, void *ws, hipStream_t st) {
     if (!m.has_topk) return HASTE_OK;
     if (!m.tk_fused) return run_topk(bce, a.Z32, d->B, d->L, ws, m.cand, st);
@@ -324,6 +337,10 @@ haste_status tail_topk(const haste_tail_desc *d, const haste_bce *bce, const Tai
     TRY_HIP(launch_topk_group_major(a.tk_v, a.tk_i, pad_rows(d->B), d->B, ng, bce->topk, mid_v, mid_i,
                                     bce->topk_val, bce->topk_idx, st),
             "top-K merge");
+    if (topk_exact_fused(d, bce))
+        TRY_HIP(launch_topk_refine((const unsigned short *)X, d->B, d->D, a.W, a.idxp, a.perm, d->G, d->F,
+                                   d->L, bce->label_offset, bce->topk, bce->topk_val, bce->topk_idx, st),
+                "top-K refine");
     return HASTE_OK;
 }
 
@@ -445,7 +462,7 @@ haste_status haste_tail_fwd(const haste_tail_desc *d, const void *X, const int32
         }
         TRY(feature_order(d, idx, ws, m, st));
         TRY_HIP(launch_tail_t1(T1_FWD, d->G, a, Z != nullptr, bce && bce->loss, st), "tail fwd");
-        TRY(tail_topk(d, bce, m, a, ws, st));
+        TRY(tail_topk(d, X, bce, m, a, ws, st));
     } else {
         F32Args a = f32_tail_args(d, X, idx, W, bce);
         a.Z = Z ? (float *)Z : m.has_topk ? (float *)B8(ws, m.z32) : nullptr;
@@ -527,7 +544,7 @@ haste_status haste_tail_step(const haste_tail_desc *d, const void *X, const int3
         a.loss = bce->loss;
         TRY(feature_order(d, idx, ws, m, st));
         TRY_HIP(launch_tail_t1(T1_DW_BCE, d->G, a, false, bce->loss != nullptr, st), "tail step dW");
-        TRY(tail_topk(d, bce, m, a, ws, st));
+        TRY(tail_topk(d, X, bce, m, a, ws, st));
         TRY_HIP(launch_tail_t2(d->G, a.dzt ? 2 : 0, a, st), "tail step dX");
     } else {
         F32Args a = f32_tail_args(d, X, idx, W, bce);
@@ -576,7 +593,7 @@ haste_status haste_tail_step_sgd(const haste_tail_desc *d, const void *X, const 
     a.loss = bce->loss;
     TRY(feature_order(d, idx, ws, m, st));
     TRY_HIP(launch_tail_t1(T1_DW_BCE, d->G, a, false, bce->loss != nullptr, st), "tail SGD step dW");
-    TRY(tail_topk(d, bce, m, a, ws, st));
+    TRY(tail_topk(d, X, bce, m, a, ws, st));
     TRY_HIP(launch_tail_t2(d->G, a.dzt ? 2 : 0, a, st), "tail SGD step dX");
     return HASTE_OK;
 }
@@ -629,7 +646,7 @@ haste_status haste_tail_step_dw(const haste_tail_desc *d, const void *X, const i
         a.loss = bce->loss;
         TRY(feature_order(d, idx, ws, m, st));
         TRY_HIP(launch_tail_t1(T1_DW_BCE, d->G, a, false, bce->loss != nullptr, st), "tail step dW");
-        TRY(tail_topk(d, bce, m, a, ws, st));
+        TRY(tail_topk(d, X, bce, m, a, ws, st));
     } else {
         F32Args a = f32_tail_args(d, X, idx, W, bce);
         a.dW = (float *)dW;

@@ -97,6 +97,15 @@ hipError_t launch_topk_group_major(const float *gv, const int32_t *gi, int64_t l
                                    int64_t ngroups, int K, float *mid_v, int32_t *mid_i,
                                    float *out_v, int32_t *out_i, hipStream_t st);
 
+// Exact top-K from the K best groups of each row (out_i: their maxima's ids,
+// from launch_topk_group_major): the groups' logits recomputed bit for bit
+// as the logits pass forms them (bf16 X row-major, W, the feature order
+// idxp / perm), the K best kept, in place in out_v / out_i
+hipError_t launch_topk_refine(const unsigned short *X, int B, int D, const unsigned short *W,
+                              const unsigned short *idxp, const unsigned char *perm, int G, int F,
+                              int64_t L, int64_t tk_off, int K, float *out_v, int32_t *out_i,
+                              hipStream_t st);
+
 // A caller's dZ (B x L bf16, row-major) into the dW pass's dz tiles
 hipError_t launch_dz_tiles(const unsigned short *dZ, int B, int64_t L, int G, int Bp, int64_t Ng,
                            unsigned short *dzt, hipStream_t st);

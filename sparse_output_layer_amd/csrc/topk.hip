@@ -398,4 +398,132 @@ hipError_t launch_row_topk(const float *z, int64_t ld, int rows, int64_t n, int6
     return hipErrorInvalidValue;
 }
 
+// ------------------------------------------------ exact top-K, second step
+// With the logits pass's one-maximum-per-group lists merged into each row's
+// K best groups (value, id of the group's largest logit, ties to the smaller
+// id), the row's exact top-K lies inside those K groups: a label of the true
+// top-K has a logit at least that of every label after it, so its group's
+// maximum ranks before the maxima of all groups holding only later labels,
+// and fewer than K groups can rank before it.  This pass recomputes the K
+// groups' logits of the row exactly as the logits pass forms them -- the
+// same bf16 operands in the same feature order, the same sequence of
+// 16x16x32 MFMAs from a zero accumulator, so the same fp32 values bit for
+// bit -- and keeps the K best of the K*G.  Workgroup = one row, wave w = its
+// w-th group; A operand: the row's X values at the group's features (every
+// MFMA row the same), B operand: W_g in that order.
+template <int G, int F>
+__global__ __launch_bounds__(64 * TOPK_MAX) void k_topk_refine(const unsigned short *__restrict__ X, int D,
+                                                               const unsigned short *__restrict__ W,
+                                                               const unsigned short *__restrict__ idxp,
+                                                               const unsigned char *__restrict__ perm,
+                                                               int64_t L, int64_t tk_off, int K,
+                                                               float *out_v, int32_t *out_i) {
+    constexpr int JT = G / 16, KS = F / 32;
+    __shared__ float lv[TOPK_MAX * G];
+    __shared__ int32_t li[TOPK_MAX * G];
+    const int b = blockIdx.x;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int q = lane >> 4, m = lane & 15;
+    // the w-th group of the row (wave-uniform); -1: fewer than K candidates
+    const int32_t cid = w < K ? out_i[(int64_t)b * K + w] : -1;
+    if (cid >= 0) {
+        const int64_t g = ((int64_t)cid - tk_off) / G;
+        const unsigned short *xr = X + (int64_t)b * D;
+        bf16x8 A[KS];
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            unsigned short e8[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) e8[e] = xr[idxp[g * F + 32 * s + 8 * q + e]];
+            A[s] = __builtin_bit_cast(bf16x8, e8);
+        }
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt) {
+            const unsigned short *wr = W + (g * G + 16 * jt + m) * (int64_t)F;
+            f32x4 acc = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                unsigned short e8[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) e8[e] = wr[perm[g * F + 32 * s + 8 * q + e]];
+                acc = mfma32(A[s], __builtin_bit_cast(bf16x8, e8), acc);
+            }
+            if (q == 0) {   // lanes 0..15 hold label 16jt + m (every row is row b)
+                const int64_t t = g * G + 16 * jt + m;
+                lv[w * G + 16 * jt + m] = t < L ? acc[0] : -INFINITY;
+                li[w * G + 16 * jt + m] = t < L ? (int32_t)(tk_off + t) : -1;
+            }
+        }
+    } else if (w < TOPK_MAX) {
+        for (int j = lane; j < G; j += 64) {
+            lv[w * G + j] = -INFINITY;
+            li[w * G + j] = -1;
+        }
+    }
+    __syncthreads();
+    if (w != 0) return;
+    // wave 0: K rounds of an arg-max over the K * G entries (ties: smaller id)
+    const int n = K * G;
+    for (int k = 0; k < K; ++k) {
+        float bv = -INFINITY;
+        int32_t bi = -1;
+        int bp = -1;
+        for (int p = lane; p < n; p += 64) {
+            const int32_t id = li[p];
+            if (id >= 0 && (bi < 0 || tk_before(lv[p], id, bv, bi))) {
+                bv = lv[p];
+                bi = id;
+                bp = p;
+            }
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            const float ov = __shfl_xor(bv, off, 64);
+            const int32_t oi = __shfl_xor(bi, off, 64);
+            const int op = __shfl_xor(bp, off, 64);
+            if (oi >= 0 && (bi < 0 || tk_before(ov, oi, bv, bi))) {
+                bv = ov;
+                bi = oi;
+                bp = op;
+            }
+        }
+        if (lane == 0) {
+            out_v[(int64_t)b * K + k] = bi >= 0 ? bv : -INFINITY;
+            out_i[(int64_t)b * K + k] = bi;
+            if (bp >= 0) li[bp] = -1;   // taken
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
+template <int G, int F>
+static hipError_t topk_refine_go(const unsigned short *X, int B, int D, const unsigned short *W,
+                                 const unsigned short *idxp, const unsigned char *perm, int64_t L,
+                                 int64_t tk_off, int K, float *out_v, int32_t *out_i, hipStream_t st) {
+    hipLaunchKernelGGL((k_topk_refine<G, F>), dim3((unsigned)B), dim3(64 * TOPK_MAX), 0, st, X, D, W, idxp,
+                       perm, L, tk_off, K, out_v, out_i);
+    return hipGetLastError();
+}
+
+hipError_t launch_topk_refine(const unsigned short *X, int B, int D, const unsigned short *W,
+                              const unsigned short *idxp, const unsigned char *perm, int G, int F,
+                              int64_t L, int64_t tk_off, int K, float *out_v, int32_t *out_i,
+                              hipStream_t st) {
+    if (B <= 0) return hipSuccess;
+    if (K < 1 || K > TOPK_MAX) return hipErrorInvalidValue;
+    switch (G * 1000 + F) {
+    case 16032: return topk_refine_go<16, 32>(X, B, D, W, idxp, perm, L, tk_off, K, out_v, out_i, st);
+    case 16064: return topk_refine_go<16, 64>(X, B, D, W, idxp, perm, L, tk_off, K, out_v, out_i, st);
+    case 16128: return topk_refine_go<16, 128>(X, B, D, W, idxp, perm, L, tk_off, K, out_v, out_i, st);
+    case 32032: return topk_refine_go<32, 32>(X, B, D, W, idxp, perm, L, tk_off, K, out_v, out_i, st);
+    case 32064: return topk_refine_go<32, 64>(X, B, D, W, idxp, perm, L, tk_off, K, out_v, out_i, st);
+    case 32128: return topk_refine_go<32, 128>(X, B, D, W, idxp, perm, L, tk_off, K, out_v, out_i, st);
+    case 64032: return topk_refine_go<64, 32>(X, B, D, W, idxp, perm, L, tk_off, K, out_v, out_i, st);
+    case 64064: return topk_refine_go<64, 64>(X, B, D, W, idxp, perm, L, tk_off, K, out_v, out_i, st);
+    case 64128: return topk_refine_go<64, 128>(X, B, D, W, idxp, perm, L, tk_off, K, out_v, out_i, st);
+    }
+    return hipErrorInvalidValue;
+}
+
 }  // namespace haste
