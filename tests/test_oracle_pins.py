@@ -308,6 +308,32 @@ def test_p6_two_stage_approximate_topk_brute_force():
     assert val[0, :4].tolist() == [9.0, 8.0, 1.0, 0.5] and np.isneginf(val[0, 4])
 
 
+def test_p6_exact_topk_lies_in_the_k_best_groups():
+    """Reading C28: a row's exact top-K lies among the labels of its K best
+    groups, the groups ranked by their largest logit (value descending, ties
+    to the smaller id); so the top-K over those K * G labels is the exact
+    top-K.  Checked against the brute-force sort on random rows, on rows with
+    many exact ties, and with a ragged last group."""
+    rng = np.random.default_rng(17)
+    for trial in range(40):
+        G = int(rng.choice([1, 2, 4, 16]))
+        n = int(rng.integers(1, 200))
+        K = int(rng.integers(1, 9))
+        rows = 6
+        z = rng.standard_normal((rows, n))
+        if trial % 3 == 0:
+            z = np.round(z * 2) / 2          # many exact ties
+        want_v, want_i = oracle.topk(z, K, id_offset=11)
+        ng = -(-n // G)
+        for r in range(rows):
+            maxv = np.array([z[r, g * G:(g + 1) * G].max() for g in range(ng)])
+            maxi = np.array([g * G + int(np.argmax(z[r, g * G:(g + 1) * G])) for g in range(ng)])
+            order = np.lexsort((maxi, -maxv))[:K]
+            labs = np.concatenate([np.arange(g * G, min(n, (g + 1) * G)) for g in order])
+            v, i = oracle.topk(z[r:r + 1, labs], K, ids=labs + 11)
+            assert np.array_equal(i[0], want_i[r]) and np.array_equal(v[0], want_v[r]), (trial, r)
+
+
 def test_p6_expected_recall_exhaustive_and_closed_forms():
     """Expected recall of the two-stage top-K (top-K page, section
     "Theoretical analysis": hypergeometric placement of the top-K in the
