@@ -327,6 +327,23 @@ haste_status haste_head_step(const haste_head_desc *d, const void *X,
                              float *dX, int accumulate_dX, void *ws,
                              size_t ws_bytes, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same as
+ * haste_head_step, but its workspace is a static device array of the library,
+ * HASTE_HEAD_SCRATCH_BYTES per GPU, held by each GPU the library runs on
+ * from module load until the process ends; the call allocates nothing.  The
+ * caller still passes every input and output.  HASTE_ERR_WORKSPACE when the
+ * step needs more than the array (haste_head_workspace_bytes(d, bce) >
+ * HASTE_HEAD_SCRATCH_BYTES).  Every call on one GPU uses that GPU's one
+ * array and keeps nothing in it for the next: calls that overlap on one GPU
+ * (other streams, other host threads) race and must be serialised by the
+ * caller.  Other errors as haste_head_step. */
+#define HASTE_HEAD_SCRATCH_BYTES ((size_t)64 << 20)
+haste_status haste_head_step_noalloc(const haste_head_desc *d, const void *X,
+                                     const void *Wh, const haste_bce *bce,
+                                     void *dWh, float *dX, int accumulate_dX,
+                                     void *stream);
+
 /* Group-major view of the tail positives (the list the fused epilogue
  * walks; the positives are the labels y = 1 of the sigmoid-BCE, and the
  * order is fixed so that it can be compared bit for bit): grp_ptr (N_g + 1 entries) and entries (<= nnz), entry = b*G + j,

@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "../../include/haste.h"
@@ -830,6 +831,51 @@ haste_status haste_head_bwd(const haste_head_desc *d, const void *X, const void 
         dz = B8(ws, m.dz);
     }
     return head_grads(d, X, Wh, dz, dWh, dX, st);
+}
+
+// ------------------------------------------- the entry point that allocates nothing
+// Its workspace is this file-scope device array (each GPU holds its own
+// copy, from module load until the process ends).  In host code `scratch`
+// names a host-side stand-in, not device memory: the device address comes
+// from hipGetSymbolAddress, taken once per device with that device current,
+// and only that address is ever passed to a kernel.
+static __device__ __align__(256) unsigned char scratch[HASTE_HEAD_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+haste_status scratch_ptr(void **out) {
+    int dev = -1;
+    TRY_HIP(hipGetDevice(&dev), "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(HASTE_ERR_UNSUPPORTED, "device %d out of range", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        TRY_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+        if (!p) return fail(HASTE_ERR_HIP, "hipGetSymbolAddress(scratch) gave NULL");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return HASTE_OK;
+}
+}  // namespace
+
+haste_status haste_head_step_noalloc(const haste_head_desc *d, const void *X, const void *Wh,
+                                     const haste_bce *bce, void *dWh, float *dX, int accumulate_dX,
+                                     void *stream) {
+    g_err.clear();
+    TRY(head_common(d, X, Wh));
+    TRY(need(bce, "bce"));
+    TRY(check_bce(bce, d->B, true, d->H));
+    const size_t need_bytes = head_ws(d, bce).total;
+    if (need_bytes > HASTE_HEAD_SCRATCH_BYTES)
+        return fail(HASTE_ERR_WORKSPACE, "this head step needs %zu workspace bytes; the static scratch holds %zu",
+                    need_bytes, (size_t)HASTE_HEAD_SCRATCH_BYTES);
+    void *ws = nullptr;
+    TRY(scratch_ptr(&ws));
+    return haste_head_step(d, X, Wh, bce, dWh, dX, accumulate_dX, ws, HASTE_HEAD_SCRATCH_BYTES, stream);
 }
 
 haste_status haste_head_step(const haste_head_desc *d, const void *X, const void *Wh,

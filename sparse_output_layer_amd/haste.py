@@ -84,6 +84,7 @@ _SIGS = {
                                       _sz, _vp]),
     "haste_head_step": (ctypes.c_int, [_PH, _vp, _vp, _PB, _vp, _vp, ctypes.c_int, _vp, _sz,
                                        _vp]),
+    "haste_head_step_noalloc": (ctypes.c_int, [_PH, _vp, _vp, _PB, _vp, _vp, ctypes.c_int, _vp]),
     "haste_tail_group_positives": (ctypes.c_int, [_PD, _PB, _vp, _vp, _vp, _sz, _vp]),
     "haste_tail_validate": (ctypes.c_int, [_PD, _vp, _vp, _vp]),
     "haste_topk_merge": (ctypes.c_int, [_i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
@@ -388,6 +389,18 @@ def haste_head_step(X, Wh, bce: Bce, dWh, dX, accumulate_dX=False, workspace=Non
     ws, nb = _workspace(lib().haste_head_workspace_bytes(ctypes.byref(d), b), X.device, workspace)
     _check(lib().haste_head_step(ctypes.byref(d), _ptr(X), _ptr(Wh), b, _ptr(dWh), _ptr(dX),
                                  int(bool(accumulate_dX)), _ptr(ws), nb, _stream()))
+
+
+def haste_head_step_noalloc(X, Wh, bce: Bce, dWh, dX, accumulate_dX=False):
+    """haste_head_step with the library's static device scratch as workspace
+    (no allocation by the call or the binding); calls overlapping on one GPU race."""
+    _need(X, "X")
+    _need(Wh, "Wh", X.dtype)
+    _need(dWh, "dWh", X.dtype)
+    _need(dX, "dX", torch.float32)
+    d = head_desc(X, Wh)
+    _check(lib().haste_head_step_noalloc(ctypes.byref(d), _ptr(X), _ptr(Wh), _bref(bce), _ptr(dWh),
+                                         _ptr(dX), int(bool(accumulate_dX)), _stream()))
 
 
 def haste_tail_group_positives(B, D, L, G, F, bce: Bce, dtype=torch.bfloat16, workspace=None):

@@ -159,6 +159,17 @@ def test_head_and_step_argument_errors(L):
     assert L.haste_tail_validate(None, 0x1000, 0x1000, None) == H.HASTE_ERR_INVALID
 
 
+def test_noalloc_head_step_rejects_a_step_beyond_its_scratch(L):
+    """The allocation-free head step checks its need against the static
+    scratch before it touches the device."""
+    h = H.HeadDesc(B=4096, D=64, H=16384, dtype=H.HASTE_BF16)   # dZh alone: 128 MiB
+    b = H.BceStruct(nnz=5, row_ptr=0x1000, labels=0x1000)
+    assert L.haste_head_step_noalloc(ctypes.byref(h), 0x1000, 0x1000, ctypes.byref(b), 0x1000,
+                                     0x1000, 0, None) == H.HASTE_ERR_WORKSPACE
+    assert b"scratch" in L.haste_last_error()
+    assert L.haste_head_step_noalloc(ctypes.byref(h), 0x1000, 0x1000, None, 0x1000, 0x1000, 0,
+                                     None) == H.HASTE_ERR_INVALID          # bce required
+
 def test_topk_recall_and_plan_match_the_oracle(L):
     """The library's expected recall and parameter choice (host code) against
     the oracle's exact-fraction formula and plain search."""
