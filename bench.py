@@ -55,6 +55,9 @@ def parse():
                         "its SGD update fused into the dW pass, next to step + update; "
                         "calls: every forward, backward and step entry point on its own")
     p.add_argument("--topk", type=int, default=5, help="K of the inference mode")
+    p.add_argument("--lean", choices=["auto", "yes", "no"], default="auto",
+                   help="training step without the dz tiles (dX recomputes dz); auto: as the "
+                        "workload says")
     p.add_argument("--recall", type=float, default=0.95,
                    help="recall target of the approximate top-K in the inference mode")
     return p.parse_args()
@@ -603,6 +606,7 @@ def main():
     rp = torch.from_numpy(inp.row_ptr).to(dev)
     lab = torch.from_numpy(inp.labels).to(dev)
     B, D, L, G = cfg.B, cfg.D, cfg.L, cfg.G
+    lean = args.lean == "yes" or (args.lean == "auto" and cfg.lean)
     s = 1.0 / B
     loss = torch.zeros(1, dtype=torch.float32, device=dev)
     bce_h = H.Bce(rp, lab, 0, s, loss)
@@ -615,12 +619,12 @@ def main():
     dX = torch.empty(B, D, dtype=torch.float32, device=dev)
     dWh = torch.empty_like(Wh)
     dW = torch.empty_like(W)
-    ws_t = torch.empty(H.haste_tail_workspace_bytes(X, idx, L, G, bce_t), dtype=torch.uint8,
+    ws_t = torch.empty(H.haste_tail_workspace_bytes(X, idx, L, G, bce_t, lean=lean), dtype=torch.uint8,
                        device=dev)
     ws_h = torch.empty(max(256, H.haste_head_workspace_bytes(X, Wh, bce_h)), dtype=torch.uint8,
                        device=dev)
     # idx does not change between steps: its feature order is formed once
-    H.haste_tail_prepare_layout(X, idx, L, G, ws_t)
+    H.haste_tail_prepare_layout(X, idx, L, G, ws_t, lean=lean)
     names = ["head_step", "tail_prepare", "tail_step_dw", "tail_step_dx"] + (["topk_merge"] if K else [])
     side = torch.cuda.Stream()   # default priority, like every stream here
 
@@ -638,17 +642,17 @@ def main():
         side.wait_stream(main)
         with torch.cuda.stream(side):
             H.haste_head_step(X, Wh, bce_h, dWh, dX, accumulate_dX=True, workspace=ws_h)
-        H.haste_tail_prepare(X, idx, L, G, bce_t, ws_t)
+        H.haste_tail_prepare(X, idx, L, G, bce_t, ws_t, lean=lean)
         if dom_dx:
-            H.haste_tail_step_dw(X, idx, W, L, G, bce_t, dW, ws_t, layout_ready=True)
+            H.haste_tail_step_dw(X, idx, W, L, G, bce_t, dW, ws_t, lean=lean, layout_ready=True)
         ev[0].record(main)
         if not dom_dx:
-            H.haste_tail_step_dw(X, idx, W, L, G, bce_t, dW, ws_t, layout_ready=True)
+            H.haste_tail_step_dw(X, idx, W, L, G, bce_t, dW, ws_t, lean=lean, layout_ready=True)
         else:
-            H.haste_tail_step_dx(X, idx, W, L, G, bce_t, dX, ws_t, accumulate_dX=True)
+            H.haste_tail_step_dx(X, idx, W, L, G, bce_t, dX, ws_t, accumulate_dX=True, lean=lean)
         ev[1].record(main)
         if not dom_dx:
-            H.haste_tail_step_dx(X, idx, W, L, G, bce_t, dX, ws_t, accumulate_dX=True)
+            H.haste_tail_step_dx(X, idx, W, L, G, bce_t, dX, ws_t, accumulate_dX=True, lean=lean)
         main.wait_stream(side)
         if K:
             H.haste_topk_merge(bce_h.topk_val, bce_h.topk_idx, bce_t.topk_val, bce_t.topk_idx)
@@ -660,11 +664,11 @@ def main():
         ev[0].record()
         H.haste_head_step(X, Wh, bce_h, dWh, dX, workspace=ws_h)
         ev[1].record()
-        H.haste_tail_prepare(X, idx, L, G, bce_t, ws_t)
+        H.haste_tail_prepare(X, idx, L, G, bce_t, ws_t, lean=lean)
         ev[2].record()
-        H.haste_tail_step_dw(X, idx, W, L, G, bce_t, dW, ws_t, layout_ready=True)
+        H.haste_tail_step_dw(X, idx, W, L, G, bce_t, dW, ws_t, lean=lean, layout_ready=True)
         ev[3].record()
-        H.haste_tail_step_dx(X, idx, W, L, G, bce_t, dX, ws_t, accumulate_dX=True)
+        H.haste_tail_step_dx(X, idx, W, L, G, bce_t, dX, ws_t, accumulate_dX=True, lean=lean)
         ev[4].record()
         if K:
             H.haste_topk_merge(bce_h.topk_val, bce_h.topk_idx, bce_t.topk_val, bce_t.topk_idx)
@@ -735,7 +739,10 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: {cfg.note}; B={B} D={D} H={cfg.H} L={L} G={G} "
-                               f"F={cfg.F}, positives/row={cfg.pos_per_row} Zipf({cfg.zipf_s})",
+                               f"F={cfg.F}, positives/row={cfg.pos_per_row} Zipf({cfg.zipf_s})"
+                               + (f", exact top-{K}" if K else "")
+                               + ("; dX pass recomputes dz (no B x L array)" if lean else
+                                  "; dz kept in tiles between the passes"),
                    "global_batch": B, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(a_tf, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",

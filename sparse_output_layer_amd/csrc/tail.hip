@@ -1978,9 +1978,13 @@ hipError_t launch_tail_t2(int G, int dz_mode, const TailArgs &a, hipStream_t st)
     if (dz_mode < 0 || dz_mode > 2 || (dz_mode == 1 && !a.dZ) || (dz_mode == 2 && !a.dzt))
         return hipErrorInvalidValue;
     if (dz_mode == 2) {
-        // groups of 32 and more: the scatter form (its LDS traffic per flop
-        // falls as G grows); groups of 16: the dense form
-        if (G >= 32 && tail_dxs_supported(G, a.F, a.D)) return launch_tail_dxs(G, a, st);
+        // The dense form runs D/F times the layer's flops; the scatter form
+        // runs the layer's own but pays a fixed cost per group and row chunk.
+        // Measured on gfx950: the scatter form is ahead only where the dense
+        // form's excess is large and groups are wide (D = 16F, G = 64: 1.18
+        // against 1.79 ms); at D = 6F it is behind for G = 16, 32 and 64.
+        if (G >= 32 && a.D >= 12 * a.F && tail_dxs_supported(G, a.F, a.D))
+            return launch_tail_dxs(G, a, st);
         switch (G) {
         case 16: return t2d_pick<16>(a, st);
         case 32: return t2d_pick<32>(a, st);

@@ -27,6 +27,10 @@ CASES = [
     dict(B=40, D=1024, H=64, L=600, G=16, F=64),
     dict(B=96, D=544, H=64, L=800, G=16, F=32),
     dict(B=20, D=448, H=48, L=400, G=16, F=128),
+    # the scatter form of dX (groups of 32 and more on inputs of at least
+    # 12F features): groups of 32, and a ragged batch with groups of 64
+    dict(B=50, D=512, H=64, L=900, G=32, F=32),
+    dict(B=90, D=800, H=64, L=1300, G=64, F=64),
 ]
 
 

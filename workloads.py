@@ -54,6 +54,7 @@ class Config:
     zipf_s: float
     idx_dist: str = "uniform"
     topk: int = 0
+    lean: bool = False        # the step keeps no B x L array (the dX pass recomputes dz)
     seed: int = 0
     note: str = ""
 
@@ -83,8 +84,8 @@ CONFIGS = {
                  dtype="bf16", w_std=0.02, pos_per_row=5, zipf_s=1.1,
                  note="670K-shaped, G=64 (ragged last group: 48 live labels)"),
     "c4": Config("c4", B=256, D=768, H=16_384, L=2_984_000, G=32, F=128,
-                 dtype="bf16", w_std=0.02, pos_per_row=6, zipf_s=1.05,
-                 note="3M-shaped, fused step"),
+                 dtype="bf16", w_std=0.02, pos_per_row=6, zipf_s=1.05, lean=True,
+                 note="3M-shaped, fused step, no B x L array"),
     "c5": Config("c5", B=128, D=1024, H=32_768, L=8_600_000, G=64, F=64,
                  dtype="bf16", w_std=0.02, pos_per_row=4, zipf_s=1.0,
                  idx_dist="skew10", topk=5,
