@@ -60,7 +60,7 @@ inline int pad_rows(int B) { return (B + 63) / 64 * 64; }
 // ----------------------------------------------------------- workspace maps
 struct TailWs {
     size_t xt, cnt, ptr, ent, idxp, perm, sched, dz, dzt, z32, cand, fwd_total, total;
-    bool has_dzt, has_topk, tk_fused;
+    bool has_dzt, has_topk, tk_fused, tk_exact;
 };
 
 // The exact top-K (K' = K) of bf16 groups of 16 and more: the logits pass
@@ -116,6 +116,7 @@ TailWs tail_ws(const haste_tail_desc *d, const haste_bce *bce) {
     // the group-major lists (N_g x B_pad) and the merge's segment lists instead
     w.has_topk = bce && bce->topk > 0;
     w.tk_fused = topk_fused(d, bce);
+    w.tk_exact = topk_exact_fused(d, bce);
     if (w.has_topk && !w.tk_fused) {
         w.z32 = o;  o += al256((size_t)d->B * d->L * 4);
         w.cand = o; o += al256(topk_cand_bytes(d->B, d->L, bce));
@@ -255,6 +256,7 @@ TailArgs tail_args(const haste_tail_desc *d, const void *X, const int32_t *idx, 
     if (m.tk_fused) {   // the group-major bucket lists, written by the logits pass (K' = 1)
         a.tk_v = (float *)B8(ws, m.cand);
         a.tk_i = (int32_t *)(a.tk_v + n_groups(d) * pad_rows(d->B));
+        a.tk_max_only = m.tk_exact ? 1 : 0;
     }
     a.B = d->B;
     a.D = d->D;

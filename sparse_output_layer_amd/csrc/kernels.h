@@ -19,6 +19,8 @@ struct TailArgs {
     float *tk_v;                 // fused top-K stage 1 (one bucket per group, K' = 1): Ng x Bp
     int32_t *tk_i;               //   largest logit of each (group, row) and its id (-1: none); or null
     int64_t tk_off;              //   id of tail label 0
+    int tk_max_only;             //   1: each list entry's id is its group's first label (the exact
+                                 //   top-K needs only the groups); 0: the maximum's own id
     const unsigned short *idxp;  // Ng x F: idx in T1's bank-aware order (idxp[g][k] = idx[g][perm[g][k]])
     const unsigned char *perm;   // Ng x F: that order's feature per position
     unsigned short *dzt;         // dz tiles of the dW pass for the dX pass, or null:

@@ -477,8 +477,9 @@ __device__ __forceinline__ void t1_stage_async(const TailArgs &a, unsigned short
     }
 }
 
-// TK: the fused top-K stage 1 (one bucket per group, K' = 1) is compiled in
-template <int G, int F, int RW, int NW, int MODE, bool TK = false>
+// TK: the fused top-K stage 1 (one bucket per group, K' = 1) is compiled in:
+// 1 with the maximum's own id, 2 with the group's first label as the id
+template <int G, int F, int RW, int NW, int MODE, int TK = 0>
 __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, int store_z, int do_loss) {
     constexpr int JT = G / 16, KS = F / 32, FT = F / 16;
     constexpr int BC = T1_BC, BCP = T1_BCP;
@@ -696,7 +697,66 @@ __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, int store_z,
                             dzp[h2][jt][1] = pack_bf16x2(dzv[2], dzv[3]);
                         }
                 }
-                if (TK) {
+                if constexpr (TK == 2) {
+                    // the exact top-K needs only each (group, row)'s largest
+                    // logit: the group is its candidate, and a later pass
+                    // recomputes the K best groups of the row.  Ties between
+                    // groups go to the smaller group, as they would to the
+                    // smaller label id.  The max runs on order keys over the
+                    // lane's slots, then over the 16 lanes of the row.
+                    const bool all_live = (g + 1) * G <= a.L;   // wave-uniform
+                    unsigned ku[2][4];
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            if (all_live) {
+                                float v = zacc[h2][0][i];
+#pragma unroll
+                                for (int jt = 1; jt < JT; ++jt) v = fmaxf(v, zacc[h2][jt][i]);
+                                ku[h2][i] = f32_order_key(v);
+                            } else {
+                                unsigned u = 0u;   // key 0: no live label
+#pragma unroll
+                                for (int jt = 0; jt < JT; ++jt)
+                                    if (g * G + 16 * jt + m < a.L) u = max(u, f32_order_key(zacc[h2][jt][i]));
+                                ku[h2][i] = u;
+                            }
+                        }
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) ku[h2][i] = max(ku[h2][i], dpp_u32<0xB1>(ku[h2][i]));
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) ku[h2][i] = max(ku[h2][i], dpp_u32<0x4E>(ku[h2][i]));
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) ku[h2][i] = max(ku[h2][i], dpp_u32<0x141>(ku[h2][i]));
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) ku[h2][i] = max(ku[h2][i], dpp_u32<0x140>(ku[h2][i]));
+                    if (m == 0) {
+                        const unsigned gid = (unsigned)(a.tk_off + g * G);
+#pragma unroll
+                        for (int h2 = 0; h2 < 2; ++h2) {
+                            f32x4 cv;
+                            u32x4 ci;
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                const unsigned u = ku[h2][i];
+                                cv[i] = u == 0u ? -INFINITY : f32_from_order_key(u);
+                                ci[i] = u == 0u ? 0xffffffffu : gid;
+                            }
+                            const int64_t o = g * (int64_t)a.Bp + r0 + 16 * h2 + 4 * q;
+                            __builtin_nontemporal_store(cv, (f32x4 *)(a.tk_v + o));
+                            __builtin_nontemporal_store(ci, (u32x4 *)(a.tk_i + o));
+                        }
+                    }
+                } else if constexpr (TK == 1) {
                     // top-K stage 1 fused here, one bucket per group and K' = 1:
                     // per row, the group's largest logit (ties: smaller id), into
                     // group-major lists (Ng x Bp); lane m = 0 of each q stores rows
@@ -939,19 +999,25 @@ static hipError_t t1_launch(int mode, const TailArgs &a, bool store_z, bool do_l
     const int64_t grid = n_runs < ncu ? n_runs : ncu;
     if (grid <= 0) return hipSuccess;
     const dim3 blk(64 * NW);
-    const bool tk = a.tk_v != nullptr;
+    const int tk = a.tk_v == nullptr ? 0 : a.tk_max_only ? 2 : 1;
     switch (mode) {
     case T1_FWD:
-        if (tk)
-            hipLaunchKernelGGL((k_tail_t1<G, F, RW, NW, T1_FWD, true>), dim3((unsigned)grid), blk, lds,
+        if (tk == 2)
+            hipLaunchKernelGGL((k_tail_t1<G, F, RW, NW, T1_FWD, 2>), dim3((unsigned)grid), blk, lds,
+                               st, a, (int)store_z, (int)do_loss);
+        else if (tk == 1)
+            hipLaunchKernelGGL((k_tail_t1<G, F, RW, NW, T1_FWD, 1>), dim3((unsigned)grid), blk, lds,
                                st, a, (int)store_z, (int)do_loss);
         else
             hipLaunchKernelGGL((k_tail_t1<G, F, RW, NW, T1_FWD>), dim3((unsigned)grid), blk, lds, st,
                                a, (int)store_z, (int)do_loss);
         break;
     case T1_DW_BCE:
-        if (tk)
-            hipLaunchKernelGGL((k_tail_t1<G, F, RW, NW, T1_DW_BCE, true>), dim3((unsigned)grid), blk,
+        if (tk == 2)
+            hipLaunchKernelGGL((k_tail_t1<G, F, RW, NW, T1_DW_BCE, 2>), dim3((unsigned)grid), blk,
+                               lds, st, a, 0, (int)do_loss);
+        else if (tk == 1)
+            hipLaunchKernelGGL((k_tail_t1<G, F, RW, NW, T1_DW_BCE, 1>), dim3((unsigned)grid), blk,
                                lds, st, a, 0, (int)do_loss);
         else
             hipLaunchKernelGGL((k_tail_t1<G, F, RW, NW, T1_DW_BCE>), dim3((unsigned)grid), blk, lds,
