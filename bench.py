@@ -73,18 +73,19 @@ def source_digest(path):
 
 
 def measured_traffic(kernel, launch_key):
-    """HBM bytes per launch of `kernel` from the committed counter runs
-    (profiles/traffic.json), or None when there are none for this workload or
-    when the kernel's source changed since the counters were taken."""
+    """HBM bytes per launch of the call `kernel` (its kernels summed) from the
+    committed counter runs (profiles/traffic.json), or None when there are
+    none for this workload or when a source of its kernels changed since the
+    counters were taken."""
     try:
         with open(TRAFFIC_FILE) as f:
-            rec = json.load(f)[kernel]
+            rec = json.load(f)[kernel][launch_key]
     except (OSError, KeyError, ValueError):
         return None
-    src = os.path.join(ROOT, rec["source"])
-    if rec.get("workload") != launch_key or not os.path.exists(src) \
-            or source_digest(src) != rec["source_sha256"]:
-        return None
+    for src, digest in rec["sources"].items():
+        path = os.path.join(ROOT, src)
+        if not os.path.exists(path) or source_digest(path) != digest:
+            return None
     return rec["fetch_bytes"] + rec["write_bytes"]
 
 
