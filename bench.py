@@ -354,13 +354,13 @@ def run_infer(args, cfg, inp, t_gen):
 
 def run_dense(args, cfg, inp, t_gen):
     """The tail (group-shared fixed fan-in, F indices per group) next to its
-    two comparison points: the same layer with G = 1 (F indices per label;
-    forward: logits and loss) and a FLOPs-matched dense bottleneck, a dense
-    layer from F inputs to the same L labels, (B x F) . (F x L), with the same
-    sigmoid-BCE over the same positives, forward and training step (logits,
-    dW, dX), on the dense kernels of this library (the head's GEMMs with
-    D = F, H = L).  Inputs of the bottleneck: x ~ N(0, 1), W ~ N(0, 0.02),
-    bf16."""
+    two comparison points: the same layer with G = 1 (F indices per label),
+    forward (logits and loss) and training step (loss, dW, dX); and a
+    FLOPs-matched dense bottleneck, a dense layer from F inputs to the same L
+    labels, (B x F) . (F x L), on the dense kernels of this library (the
+    head's GEMMs with D = F, H = L): forward with the same sigmoid-BCE over
+    the same positives, forward storing the logits (no BCE), and training
+    step.  Inputs of the bottleneck: x ~ N(0, 1), W ~ N(0, 0.02), bf16."""
     import numpy as np
     import torch
 
@@ -395,10 +395,16 @@ def run_dense(args, cfg, inp, t_gen):
         idx1[c0:c0 + n] = keys.argsort(dim=1)[:, :F].sort(dim=1).values.to(torch.int32)
         del keys
     ws_1 = torch.empty(H.haste_tail_workspace_bytes(X, idx1, L, 1, bt), dtype=torch.uint8, device=dev)
+    dW1 = torch.empty(L, F, dtype=torch.bfloat16, device=dev)
+    Zs = torch.empty(B, L, dtype=torch.bfloat16, device=dev)
+    Zd = torch.empty(B, L, dtype=torch.bfloat16, device=dev)
     calls = {
         "fanin1_fwd": lambda: H.haste_tail_fwd(X, idx1, W, L, 1, bce=bt, workspace=ws_1),
+        "fanin1_step": lambda: H.haste_tail_step(X, idx1, W, L, 1, bt, dW1, dX, workspace=ws_1),
         "sparse_fwd": lambda: H.haste_tail_fwd(X, idx, W, L, G, bce=bt, workspace=ws_t),
+        "sparse_fwd_z": lambda: H.haste_tail_fwd(X, idx, W, L, G, Z=Zs, workspace=ws_t),
         "dense_fwd": lambda: H.haste_head_fwd(Xb, Wb, bce=bt, workspace=ws_d),
+        "dense_fwd_z": lambda: H.haste_head_fwd(Xb, Wb, Zh=Zd, workspace=ws_d),
         "sparse_step": lambda: (H.haste_tail_prepare(X, idx, L, G, bt, ws_t),
                                 H.haste_tail_step_dw(X, idx, W, L, G, bt, dW, ws_t),
                                 H.haste_tail_step_dx(X, idx, W, L, G, bt, dX, ws_t)),
@@ -429,8 +435,14 @@ def run_dense(args, cfg, inp, t_gen):
         "tflops": {k: round((fl_fwd if "fwd" in k else fl_step) / (v * 1e-6) / 1e12, 1)
                    for k, v in res.items()},
         "sparse_over_dense_time": {"fwd": round(res["sparse_fwd"] / res["dense_fwd"], 3),
+                                   "fwd_z": round(res["sparse_fwd_z"] / res["dense_fwd_z"], 3),
                                    "step": round(res["sparse_step"] / res["dense_step"], 3)},
-        "fanin1_over_sparse_fwd_time": round(res["fanin1_fwd"] / res["sparse_fwd"], 3),
+        "fanin1_over_sparse_time": {"fwd": round(res["fanin1_fwd"] / res["sparse_fwd"], 3),
+                                    "step": round(res["fanin1_step"] / res["sparse_step"], 3),
+                                    "bwd": round((res["fanin1_step"] - res["fanin1_fwd"])
+                                                 / (res["sparse_step"] - res["sparse_fwd"]), 3)},
+        "z_store_gbs": {k: round(B * L * 2 / (res[k] * 1e-6) / 1e9, 1)
+                        for k in ("sparse_fwd_z", "dense_fwd_z")},
         "gen_s": round(t_gen, 2),
     }
     print(json.dumps(out), flush=True)

@@ -105,7 +105,8 @@ TailWs tail_ws(const haste_tail_desc *d, const haste_bce *bce) {
         // dz of the dW pass, kept for the dX pass unless the caller asks for
         // the lean form (which recomputes it): Bp x (Ng*G) bf16 in 1 KB tiles
         // (also without bce: the backward from a given dZ forms the same tiles)
-        w.has_dzt = !(d->flags & HASTE_TAIL_LEAN) && d->G > 1;
+        // (G = 1: the step's dz, label-major, L x B_p bf16: the same size)
+        w.has_dzt = !(d->flags & HASTE_TAIL_LEAN);
     } else {
         // per-group counts; also the key space of haste_tail_group_positives
         const size_t keys = (size_t)(nnz > 0 ? nnz : 1) * 20 + 8;
@@ -353,10 +354,10 @@ haste_status zero_dx(float *dX, int B, int D, int accumulate, hipStream_t st) {
 }
 
 // common argument checks of tail compute calls
-// bf16 with G = 1 (per-label fan-in) has the forward only
+// bf16 with G = 1 (per-label fan-in) has the forward and the one-call step
 haste_status not_g1(const haste_tail_desc *d) {
     if (d->dtype == HASTE_BF16 && d->G == 1)
-        return fail(HASTE_ERR_UNSUPPORTED, "bf16 with G = 1 supports haste_tail_fwd only");
+        return fail(HASTE_ERR_UNSUPPORTED, "bf16 with G = 1 supports haste_tail_fwd and haste_tail_step only");
     return HASTE_OK;
 }
 
@@ -528,16 +529,33 @@ haste_status haste_tail_step(const haste_tail_desc *d, const void *X, const int3
                              int accumulate_dX, void *ws, size_t ws_bytes, void *stream) {
     g_err.clear();
     TRY(tail_common(d, X, idx, W));
-    TRY(not_g1(d));
+    const bool g1 = d->dtype == HASTE_BF16 && d->G == 1;
     TRY(need(bce, "bce"));
     TRY(check_bce(bce, d->B, true, d->L));
-    TRY(need_al(dW, d->dtype == HASTE_BF16 ? 8 : 4, "dW"));
+    TRY(need_al(dW, d->dtype == HASTE_BF16 ? (g1 ? 2 : 8) : 4, "dW"));
     TRY(need_al(dX, 4, "dX"));
     const TailWs m = tail_ws(d, bce);
+    if (g1) {
+        if (m.has_topk) return fail(HASTE_ERR_UNSUPPORTED, "no top-K with G = 1");
+        if (d->flags & HASTE_TAIL_LEAN)
+            return fail(HASTE_ERR_UNSUPPORTED, "the G = 1 step keeps dz; HASTE_TAIL_LEAN is not taken");
+        if (!fanin1_step_supported(d->F, d->D))
+            return fail(HASTE_ERR_UNSUPPORTED, "the G = 1 step takes F in {32,64,128} and D <= 960 (F=%d D=%d)",
+                        d->F, d->D);
+    }
     TRY(check_ws(ws, ws_bytes, m.total));
     hipStream_t st = S(stream);
     TRY(zero_dx(dX, d->B, d->D, accumulate_dX, st));
-    if (d->dtype == HASTE_BF16) {
+    if (g1) {
+        TRY(bf16_prep(d, X, bce, ws, m, st));
+        TailArgs a = tail_args(d, X, idx, W, ws, m);
+        a.tk_off = bce->label_offset;
+        a.dW = (unsigned short *)dW;
+        a.dX = dX;
+        a.s = bce->grad_scale;
+        a.loss = bce->loss;
+        TRY_HIP(launch_fanin1_step(a, bce->loss != nullptr, st), "tail step (G = 1)");
+    } else if (d->dtype == HASTE_BF16) {
         TRY(bf16_prep(d, X, bce, ws, m, st));
         TailArgs a = tail_args(d, X, idx, W, ws, m);
         a.tk_off = bce ? bce->label_offset : 0;

@@ -69,6 +69,10 @@ bool tail_dxs_supported(int G, int F, int D);
 hipError_t launch_tail_dxs(int G, const TailArgs &a, hipStream_t st);
 // G = 1 (per-label fan-in): logits and loss only
 hipError_t launch_fanin1_fwd(const TailArgs &a, bool store_z, bool do_loss, hipStream_t st);
+// G = 1 training step: logits, loss, dz (label-major into dzt, L x Bp bf16),
+// dW, then dX from dzt; shapes it takes (F in {32, 64, 128}, 16 <= D <= 960)
+bool fanin1_step_supported(int F, int D);
+hipError_t launch_fanin1_step(const TailArgs &a, bool do_loss, hipStream_t st);
 
 // Per-row top-K (K in [1, 8]) of fp32 logits z (rows x n, row stride ld,
 // column c has id id_offset + c): stage 1 keeps the top-KP (1 <= KP <= K;

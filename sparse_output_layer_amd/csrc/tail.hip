@@ -1167,6 +1167,303 @@ hipError_t launch_fanin1_fwd(const TailArgs &a, bool store_z, bool do_loss, hipS
     return hipErrorInvalidValue;
 }
 
+// Training step of the per-label layer (G = 1): the forward's logits and
+// loss, then dz = s (sigmoid(z) - y) (zero past B and L) and dW[t][f] =
+// sum_b X[b][idx[t][f]] dz[b][t] over the batch.  dz also goes to HBM
+// label-major (dzt: L x Bp bf16) for the dX pass.  Workgroup = FS_R labels
+// over the whole batch, four per wave (a quarter-wave per label, a lane per
+// two adjacent rows, as in the forward).  Per chunk the wave's four labels'
+// dz pass through LDS (fp32, 4 x 32); then each lane takes one label
+// (lane / 16) and every sixteenth of its features (lane % 16 + 16j): 32 FMAs
+// per feature over the chunk's rows, read as four 16-byte pieces of the
+// feature's X^T row.  A row's pieces fall in four bank groups that depend on
+// the feature, so the lanes of a label start at different pieces (the same
+// rotation picks the dz they multiply, which keeps every register index
+// static).  The chunk buffers are 60 KB (D <= 960).
+constexpr int FS_BUF_BYTES = 60 * 1024;
+constexpr int FS_R = 32;                   // labels per workgroup (four per wave)
+
+template <int F>
+__global__ __launch_bounds__(64 * FF_NW, 1) void k_fanin1_step(TailArgs a, int do_loss) {
+    constexpr int FJ = F / 16;   // features per lane
+    __shared__ __attribute__((aligned(16))) unsigned short fbuf0[FS_BUF_BYTES / 2];
+    __shared__ __attribute__((aligned(16))) unsigned short fbuf1[FS_BUF_BYTES / 2];
+    __shared__ __attribute__((aligned(16))) unsigned tab[FS_R][F];  // row offset | bf16 weight << 16
+    __shared__ __attribute__((aligned(16))) float dzl[FF_NW][4][32];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    const int qd = lane >> 4, rp = lane & 15;      // the label of the quarter-wave, row pair / first feature
+    const int rot = rp & 3;                        // phase B: first 16-byte piece
+    const unsigned voff = (unsigned)((lane >> 2) * a.Bp + 8 * (lane & 3)) * 2u;
+    const int nch = a.Bp / 32;
+    const int64_t t_begin = (int64_t)blockIdx.x * FS_R;
+    const int lt = 4 * wu + qd;                    // this lane's label in the workgroup
+    const int64_t t = t_begin + lt;
+    float lsum = 0.f;
+
+    ff_stage_async(a, fbuf0, 0, wu, voff);
+    for (int e = threadIdx.x; e < FS_R * F; e += 64 * FF_NW) {
+        const int64_t te = t_begin + e / F;
+        unsigned v = 0;
+        if (te < a.L) v = (unsigned)a.idx[te * F + e % F] * 64u | (unsigned)a.W[te * F + e % F] << 16;
+        tab[e / F][e % F] = v;
+    }
+    int p0 = 0, p1 = 0;
+    if (t < a.L) {
+        p0 = a.grp_ptr[t];
+        p1 = a.grp_ptr[t + 1];
+    }
+    float acc[FJ];
+#pragma unroll
+    for (int j = 0; j < FJ; ++j) acc[j] = 0.f;
+    unsigned offs[FJ];   // phase B: byte offsets of this lane's feature rows (after the first barrier)
+
+    auto chunk = [&](const unsigned short *tile, const int ch) {
+        const int row0 = ch * 32 + 2 * rp;
+        const unsigned char *tb = (const unsigned char *)tile + 4 * rp;
+        float z0 = 0.f, z1 = 0.f;
+#pragma unroll 4
+        for (int f4 = 0; f4 < F; f4 += 4) {
+            const u32x4 v4 = *(const u32x4 *)&tab[lt][f4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const unsigned x2 = *(const unsigned *)(tb + (v4[j] & 0xffffu));
+                const float wf = __uint_as_float(v4[j] & 0xffff0000u);
+                z0 = __builtin_fmaf(__uint_as_float(x2 << 16), wf, z0);
+                z1 = __builtin_fmaf(__uint_as_float(x2 & 0xffff0000u), wf, z1);
+            }
+        }
+        // phase A: dz and the loss; dz to LDS (this wave's labels) and to HBM
+        float dz[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const float z = i ? z1 : z0;
+            const int row = row0 + i;
+            dz[i] = 0.f;
+            if (t < a.L && row < a.B) {
+                float y = 0.f;
+                for (int e = p0; e < p1; ++e) y = a.grp_ent[e] == row ? 1.f : y;
+                const float ex = fast_exp_neg_abs(z);
+                float den;
+                dz[i] = a.s * (fast_sigmoid(z, ex, den) - y);
+                if (do_loss) lsum += a.s * ((fmaxf(z, 0.f) - y * z) + fast_log(den));
+            }
+        }
+        *(float2 *)&dzl[wu][qd][2 * rp] = make_float2(dz[0], dz[1]);
+        if (t < a.L) *(unsigned *)(a.dzt + t * a.Bp + row0) = pack_bf16x2(dz[0], dz[1]);
+        // the wave's own LDS writes are in order before its reads below
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        // phase B: dW over the chunk's rows, one 16-byte piece (8 rows) of
+        // every feature row at a time, the pieces in the lane's rotated order
+        const unsigned char *tt = (const unsigned char *)tile;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int pp = (p + rot) & 3;
+            const f32x4 lo = *(const f32x4 *)&dzl[wu][qd][8 * pp];
+            const f32x4 hi = *(const f32x4 *)&dzl[wu][qd][8 * pp + 4];
+            const float dr[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+            for (int j = 0; j < FJ; ++j) {
+                const u32x4 x = *(const u32x4 *)(tt + offs[j] + 16 * pp);
+                float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    s0 = __builtin_fmaf(__uint_as_float(x[e] << 16), dr[2 * e], s0);
+                    s1 = __builtin_fmaf(__uint_as_float(x[e] & 0xffff0000u), dr[2 * e + 1], s1);
+                }
+                acc[j] += s0 + s1;
+            }
+        }
+    };
+    for (int ch = 0; ch < nch; ch += 2) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (ch == 0) {   // the tables are complete after the first barrier
+#pragma unroll
+            for (int j = 0; j < FJ; ++j) offs[j] = tab[lt][rp + 16 * j] & 0xffffu;
+        }
+        ff_stage_async(a, fbuf1, ch + 1, wu, voff);
+        chunk(fbuf0, ch);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (ch + 2 < nch) ff_stage_async(a, fbuf0, ch + 2, wu, voff);
+        chunk(fbuf1, ch + 1);
+    }
+    if (t < a.L) {
+#pragma unroll
+        for (int j = 0; j < FJ; ++j) a.dW[t * F + rp + 16 * j] = f32_to_bf16(acc[j]);
+    }
+    if (do_loss && a.loss) {
+        const float v = wave_sum(lsum);
+        if (lane == 0) atomicAdd(a.loss, v);
+    }
+}
+
+// dX of the per-label layer from the step's label-major dz: dX[b][d] +=
+// dz[b][t] W[t][f] for every (t, f) with idx[t][f] = d.  Workgroup = 32 rows
+// x a range of labels; its dX^T tile (D x 32 fp32) stays in LDS, the four
+// rows 4w..4w+3 of feature d in the 16 bytes at d*128 + 16 (w ^ (d & 7)) (so
+// that the lanes' 16-byte pieces spread over the banks).  The range's labels
+// come through LDS in batches of FX_NB (idx, W, dz), loaded into registers
+// one batch ahead.  Wave w owns rows 4w..4w+3; per label a lane takes a
+// feature (lane, lane + 64) and adds dz[rows][t] W[t][f] to its four rows of
+// feature idx[t][f]: one 16-byte read, four FMAs, one 16-byte write.  The
+// features of a label are distinct and the waves' rows are, so no two lanes
+// touch one element at once.  The tile is flushed once with coalesced fp32
+// atomics.
+constexpr int FX_NW = 8, FX_NB = 16;
+
+template <int F>
+struct FxBatch {
+    static constexpr int IDX = FX_NB * F * 4 / 16;      // 16-byte pieces of idx
+    static constexpr int WP = FX_NB * F * 2 / 16;       // of W
+    static constexpr int DZ = FX_NB * 32 * 2 / 16;      // of dz
+    static constexpr int N = IDX + WP + DZ;
+    static constexpr int PPT = (N + 64 * FX_NW - 1) / (64 * FX_NW);   // pieces per thread
+    static constexpr int BYTES = N * 16;
+};
+
+__host__ __device__ inline size_t fx_lds_bytes(int D, int F) {
+    return (size_t)D * 128 + (size_t)FX_NB * (F * 6 + 64);
+}
+
+template <int F>
+__global__ __launch_bounds__(64 * FX_NW, 1) void k_fanin1_dx(TailArgs a, int nrc, int64_t per) {
+    using Bt = FxBatch<F>;
+    extern __shared__ __attribute__((aligned(16))) unsigned char fx_lds[];
+    float *const dxt = (float *)fx_lds;
+    unsigned char *const bat = fx_lds + (size_t)a.D * 128;   // idx, then W, then dz
+    const int32_t *const bidx = (const int32_t *)bat;
+    const unsigned short *const bw = (const unsigned short *)(bat + Bt::IDX * 16);
+    const unsigned short *const bdz = (const unsigned short *)(bat + (Bt::IDX + Bt::WP) * 16);
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, tid = threadIdx.x;
+    // blocks: the row chunks of one label range run on one XCD (block b on XCD b % 8)
+    const int k8 = blockIdx.x >> 3, xcd = blockIdx.x & 7;
+    const int rc = k8 % nrc;
+    const int64_t rg = (int64_t)(k8 / nrc) * 8 + xcd;
+    const int r0 = rc * 32;
+    const int64_t t0 = rg * per;
+    const int64_t t1 = t0 + per < a.L ? t0 + per : a.L;
+    if (t0 >= t1) return;   // an empty range (workgroup-uniform)
+    for (int i = tid; i < a.D * 32; i += 64 * FX_NW) dxt[i] = 0.f;
+
+    auto load = [&](int64_t tb, u32x4 (&r)[Bt::PPT]) {
+#pragma unroll
+        for (int n = 0; n < Bt::PPT; ++n) {
+            const int pc = tid + 64 * FX_NW * n;
+            const char *src;
+            if (pc < Bt::IDX) {
+                const int64_t e = tb * F + 4 * (int64_t)pc;    // F ints a label, contiguous
+                src = (const char *)(a.idx + (e < a.L * F ? e : a.L * F - 4));
+            } else if (pc < Bt::IDX + Bt::WP) {
+                const int64_t e = tb * F + 8 * (int64_t)(pc - Bt::IDX);
+                src = (const char *)(a.W + (e < a.L * F ? e : a.L * F - 8));
+            } else {
+                const int q = pc - Bt::IDX - Bt::WP, l = q >> 2;   // four pieces a label
+                const int64_t t = tb + l < a.L ? tb + l : a.L - 1;
+                src = (const char *)(a.dzt + t * a.Bp + r0 + 8 * (q & 3));
+            }
+            r[n] = pc < Bt::N ? *(const u32x4 *)src : (u32x4){0u, 0u, 0u, 0u};
+        }
+    };
+    auto store = [&](const u32x4 (&r)[Bt::PPT]) {
+#pragma unroll
+        for (int n = 0; n < Bt::PPT; ++n) {
+            const int pc = tid + 64 * FX_NW * n;
+            if (pc < Bt::N) *(u32x4 *)(bat + 16 * pc) = r[n];
+        }
+    };
+    u32x4 pf[Bt::PPT];
+    load(t0, pf);
+    for (int64_t tb = t0; tb < t1; tb += FX_NB) {
+        __syncthreads();           // the previous batch is consumed (and the tile zeroed)
+        store(pf);
+        if (tb + FX_NB < t1) load(tb + FX_NB, pf);
+        __syncthreads();
+        const int nl = t1 - tb < FX_NB ? (int)(t1 - tb) : FX_NB;
+        // a label's operands are read one label ahead; its two features'
+        // read-modify-writes are issued together (the features of a label
+        // are distinct, so their pieces are too)
+        constexpr int KF = (F + 63) / 64;
+        struct Ops {
+            int d[KF];
+            float wt[KF];
+            u32x2 dz2;
+        };
+        auto ops = [&](int l) {
+            Ops o;
+            o.dz2 = *(const u32x2 *)(bdz + l * 32 + 4 * w);   // rows 4w..4w+3 (broadcast)
+#pragma unroll
+            for (int k = 0; k < KF; ++k) {
+                const int f = lane + 64 * k < F ? lane + 64 * k : F - 1;
+                o.d[k] = bidx[l * F + f];
+                o.wt[k] = __uint_as_float((unsigned)bw[l * F + f] << 16);
+            }
+            return o;
+        };
+        Ops nx = ops(0);
+        for (int l = 0; l < nl; ++l) {
+            const Ops o = nx;
+            if (l + 1 < nl) nx = ops(l + 1);
+            const float dz[4] = {__uint_as_float(o.dz2.x << 16), __uint_as_float(o.dz2.x & 0xffff0000u),
+                                 __uint_as_float(o.dz2.y << 16), __uint_as_float(o.dz2.y & 0xffff0000u)};
+            f32x4 *e[KF];
+            f32x4 v[KF];
+#pragma unroll
+            for (int k = 0; k < KF; ++k) {
+                e[k] = (f32x4 *)(dxt + o.d[k] * 32 + 4 * (w ^ (o.d[k] & 7)));
+                v[k] = *e[k];
+            }
+#pragma unroll
+            for (int k = 0; k < KF; ++k) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) v[k][i] = __builtin_fmaf(dz[i], o.wt[k], v[k][i]);
+                if (lane + 64 * k < F) *e[k] = v[k];
+            }
+        }
+    }
+    __syncthreads();
+    // flush: lanes over consecutive features of one row
+    for (int i = tid; i < a.D * 32; i += 64 * FX_NW) {
+        const int rr = i / a.D, d = i - rr * a.D;
+        if (r0 + rr < a.B)
+            atomicAdd(a.dX + (int64_t)(r0 + rr) * a.D + d, dxt[d * 32 + 4 * ((rr >> 2) ^ (d & 7)) + (rr & 3)]);
+    }
+}
+
+bool fanin1_step_supported(int F, int D) {
+    return (F == 32 || F == 64 || F == 128) && D >= 16 && D <= FS_BUF_BYTES / 64 &&
+           fx_lds_bytes(D, F) <= 160 * 1024;
+}
+
+hipError_t launch_fanin1_step(const TailArgs &a, bool do_loss, hipStream_t st) {
+    if (!fanin1_step_supported(a.F, a.D) || !a.dzt || !a.dW || !a.dX || a.Bp % 64) return hipErrorInvalidValue;
+    const int64_t grid = (a.L + FS_R - 1) / FS_R;
+    if (grid <= 0) return hipSuccess;
+    int dev = 0, ncu = 256;
+    if (hipGetDevice(&dev) == hipSuccess)
+        (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    const int nrc = a.Bp / 32;
+    int ngr = (ncu + nrc - 1) / nrc;
+    ngr = (ngr + 7) / 8 * 8;
+    const int64_t per = ((a.L + ngr - 1) / ngr + FX_NB - 1) / FX_NB * FX_NB;
+    const size_t lds = fx_lds_bytes(a.D, a.F);
+#define FSCASE(FF)                                                                                 \
+    if (a.F == FF) {                                                                               \
+        hipLaunchKernelGGL((k_fanin1_step<FF>), dim3((unsigned)grid), dim3(64 * FF_NW), 0, st, a,  \
+                           (int)do_loss);                                                          \
+        allow_lds((const void *)k_fanin1_dx<FF>, lds);                                             \
+        hipLaunchKernelGGL((k_fanin1_dx<FF>), dim3((unsigned)(nrc * ngr)), dim3(64 * FX_NW), lds,  \
+                           st, a, nrc, per);                                                       \
+        return hipGetLastError();                                                                  \
+    }
+    FSCASE(32)
+    FSCASE(64)
+    FSCASE(128)
+#undef FSCASE
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_tail_t1(int mode, int G, const TailArgs &a, bool store_z, bool do_loss,
                           hipStream_t st) {
 #define T1CASE(GG, FF, RR, NN) \

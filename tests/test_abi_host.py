@@ -139,12 +139,21 @@ def test_head_and_step_argument_errors(L):
     d = _desc()
     assert L.haste_tail_step(ctypes.byref(d), 0x1000, 0x1000, 0x1000, None, 0x1000, 0x1000, 0,
                              None, 0, None) == H.HASTE_ERR_INVALID       # bce required
-    # bf16 with G = 1 (per-label fan-in): the forward only
+    # bf16 with G = 1 (per-label fan-in): the forward and the one-call step
+    # (it keeps dz: no lean form; no top-K; D <= 960); the split calls are not taken
     g1 = _desc(G=1)
     b = H.BceStruct(nnz=5, row_ptr=0x1000, labels=0x1000)
     assert _status(L, g1) == H.HASTE_ERR_WORKSPACE                       # forward: accepted
-    assert L.haste_tail_step(ctypes.byref(g1), 0x1000, 0x1000, 0x1000, ctypes.byref(b), 0x1000,
-                             0x1000, 0, 0x1000, 1 << 30, None) == H.HASTE_ERR_UNSUPPORTED
+
+    def g1_step(d, bce, nb=0):
+        return L.haste_tail_step(ctypes.byref(d), 0x1000, 0x1000, 0x1000, ctypes.byref(bce), 0x1000,
+                                 0x1000, 0, 0x1000 if nb else None, nb, None)
+    assert g1_step(g1, b) == H.HASTE_ERR_WORKSPACE                        # step: accepted
+    assert L.haste_tail_workspace_bytes(ctypes.byref(g1), ctypes.byref(b)) >= 1024 * 64 * 2
+    assert g1_step(_desc(G=1, flags=H.HASTE_TAIL_LEAN), b, 1 << 30) == H.HASTE_ERR_UNSUPPORTED
+    assert g1_step(_desc(G=1, D=1024), b, 1 << 30) == H.HASTE_ERR_UNSUPPORTED
+    bk = H.BceStruct(nnz=5, row_ptr=0x1000, labels=0x1000, topk=5, topk_val=0x1000, topk_idx=0x1000)
+    assert g1_step(g1, bk, 1 << 30) == H.HASTE_ERR_UNSUPPORTED
     assert L.haste_tail_prepare(ctypes.byref(g1), 0x1000, ctypes.byref(b), 0x1000, 1 << 30,
                                 None) == H.HASTE_ERR_UNSUPPORTED
     assert L.haste_topk_merge(4, 0, 1, 1, 1, 1, 1, 1, None) == H.HASTE_ERR_INVALID

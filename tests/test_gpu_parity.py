@@ -386,6 +386,44 @@ def test_bf16_fixed_fan_in_forward(H, case):
     check_loss("G=1 loss (no Z)", b2.loss.item(), float(lt.sum()), "bf16")
 
 
+FANIN1_STEP = [
+    dict(B=40, D=96, H=48, L=300, G=1, F=32),
+    dict(B=70, D=768, H=64, L=1500, G=1, F=128),
+    dict(B=33, D=960, H=64, L=700, G=1, F=64, idx_dist="skew10"),
+    dict(B=130, D=200, H=64, L=77, G=1, F=64, pos_per_row=6),
+]
+
+
+@pytest.mark.parametrize("case", FANIN1_STEP, ids=[_ids(c) for c in FANIN1_STEP])
+def test_bf16_fixed_fan_in_step(H, case):
+    """G = 1 training step (haste_tail_step): loss, dW and dX against the
+    oracle at G = 1; dW twice, bit for bit (no atomics on it)."""
+    print("case", case, flush=True)
+    inp = wl.make_inputs(wl.tiny("g1s", **case))
+    c = inp.cfg
+    s = 1.0 / c.B
+    X, Wt = inp.X_f64(), inp.W_f64()
+    Zr, _ = oracle.tail_logits(X, inp.idx, Wt, c.L, c.G, want_abs=False)
+    Y = oracle.positive_mask(inp.row_ptr, inp.labels, c.H, c.L)
+    dZ, lt = oracle.bce(Zr, Y, s)
+    rW, rWa = oracle.tail_dW(X, inp.idx, dZ, c.L, c.G)
+    rX, rXa = oracle.tail_dX(inp.idx, Wt, dZ, c.D, c.L, c.G)
+    d = Dev(inp)
+    outs = []
+    for _ in range(2):
+        dW = torch.full_like(d.W, 3.0)
+        dX = torch.full((c.B, c.D), 5.0, dtype=torch.float32, device=DEV)
+        b = d.bce(c.H, s)
+        H.haste_tail_step(d.X, d.idx, d.W, c.L, c.G, b, dW, dX)
+        torch.cuda.synchronize()
+        outs.append((dW, dX, b.loss.item()))
+    dW, dX, loss = outs[0]
+    check_loss("G=1 step loss", loss, float(lt.sum()), "bf16")
+    check("G=1 step dW", to_f64(dW[:c.L]), rW, rWa, "bf16", nterms=c.B)
+    check("G=1 step dX", to_f64(dX), rX, rXa, "bf16", nterms=c.L)
+    assert torch.equal(outs[0][0], outs[1][0]), "G=1 dW differs between calls"
+
+
 def test_mfma_probe_runs(H):
     """The measurement probe (not a step of the layer) launches and completes;
     its flop count is blocks x 4 waves x iters x 16 MFMAs of 16x16x32x2."""
