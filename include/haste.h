@@ -76,10 +76,12 @@ typedef enum { HASTE_F32 = 0, HASTE_BF16 = 1 } haste_dtype;
  * bf16 kernels additionally need G in {16, 32, 64}, F a multiple of 32 with
  * F <= 128 (F in {32, 64, 128}), D <= 1024; other shapes
  * return HASTE_ERR_UNSUPPORTED.  G = 1 (every label its own F indices: the
- * per-label fixed fan-in layout the HASTE page compares against) is taken
- * in bf16 by haste_tail_fwd only (logits and loss, no top-K, D >= 16); the
- * other bf16 tail calls return HASTE_ERR_UNSUPPORTED for it.  fp32 accepts
- * any G and F. */
+ * per-label fixed fan-in layout the HASTE page compares against, section
+ * "Results") is taken in bf16 by haste_tail_fwd (logits and loss, no top-K,
+ * D >= 16) and by haste_tail_step (loss, dW, dX; no top-K, not
+ * HASTE_TAIL_LEAN, 16 <= D <= 960: its dz is kept label-major in the
+ * workspace, L x B_pad bf16); the other bf16 tail calls return
+ * HASTE_ERR_UNSUPPORTED for it.  fp32 accepts any G and F. */
 typedef struct {
     int32_t B;      /* rows in the batch                    */
     int32_t D;      /* input feature width                  */
