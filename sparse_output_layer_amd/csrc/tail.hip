@@ -2056,6 +2056,19 @@ __global__ __launch_bounds__(64 * T2D_NW, 1) void k_tail_t2d(TailArgs a, int n_g
 #pragma unroll
             for (int nt = 0; nt < NTW32; ++nt) ivn[nt] = iv[32 * nt];
         };
+        // A (dz: row 32rt + lane%32, labels 16jt + 8(lane/32) .. + 7) from the
+        // tile as the dW pass wrote it, by two transposing reads of four
+        // labels each: in a block of 16 lanes (rows 16h .. 16h + 15, labels
+        // 8lh ..), lane 4k + j points at the four rows 16h + 4j .. of label
+        // 8lh + 4t + k, which the dW pass's lane (j, label) holds at bytes
+        // 8h .. 8h + 7 of its piece (slot 16j + (label ^ 4j))
+        const int tr_k = (lane & 15) >> 2, tr_j = lane & 3, tr_h = (lane >> 4) & 1, tr_lh = lane >> 5;
+        unsigned tr_off[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int lab = 8 * tr_lh + 4 * t + tr_k;
+            tr_off[t] = 16 * (16 * tr_j + (lab ^ (4 * tr_j))) + 8 * tr_h;
+        }
         auto load = [&](int k, int q) {
             const unsigned char *wt = wts0 + ((k % 3) * GPI + q) * LY.wts_grp + 16 * (lane >> 5);
             const unsigned char *ex = exch0 + ((k % 3) * GPI + q) * LY.exch_grp;
@@ -2063,8 +2076,13 @@ __global__ __launch_bounds__(64 * T2D_NW, 1) void k_tail_t2d(TailArgs a, int n_g
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-                for (int jt = 0; jt < JT; ++jt)
-                    R[q % NS].A[rt][jt] = *(const bf16x8 *)(ex + ((rt * JT + jt) * 64 + lane) * 16);
+                for (int jt = 0; jt < JT; ++jt) {
+                    const unsigned char *tb = ex + (rt * JT + jt) * 1024;
+                    const i16x4 a0 = lds_read_tr(tb + tr_off[0]);
+                    const i16x4 a1 = lds_read_tr(tb + tr_off[1]);
+                    R[q % NS].A[rt][jt] =
+                        __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+                }
 #pragma unroll
             for (int nt = 0; nt < NTW32; ++nt) {
                 const unsigned char *br = wt + ivn[nt] * WTS;
@@ -2208,15 +2226,11 @@ __global__ __launch_bounds__(64 * T2D_NW, 1) void k_tail_t2d(TailArgs a, int n_g
             for (int t = 0; t < TPB; ++t) {
                 int q, rt, jt;
                 if (!tile_of(t, q, rt, jt) || !live(k, q)) continue;
-                // (row rho, label mm) -> lane rho + 32(mm/8), K slot mm%8 of block (rt, jt)
-                unsigned char *ex = exch0 + ((k % 3) * GPI + q) * LY.exch_grp + (rt * JT + jt) * 1024 +
-                                    (32 * (mm >> 3)) * 16 + 2 * (mm & 7);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int rho = 16 * (e >> 2) + 4 * qq + (e & 3);
-                    const unsigned wv = o.dz[t][e >> 1];
-                    *(unsigned short *)(ex + rho * 16) = (unsigned short)((e & 1) ? (wv >> 16) : (wv & 0xffffu));
-                }
+                // the tile as the dW pass wrote it, lane (qq, mm)'s piece at
+                // slot 16qq + (mm ^ 4qq): the consumers' transposing reads of
+                // one 16-lane block then fall on distinct banks
+                unsigned char *ex = exch0 + ((k % 3) * GPI + q) * LY.exch_grp + (rt * JT + jt) * 1024;
+                *(u32x4 *)(ex + 16 * (16 * qq + (mm ^ (4 * qq)))) = o.dz[t];
             }
         };
         // operand sets: step s in set s mod 4, loaded four iterations ahead
