@@ -31,6 +31,11 @@ CASES = [
     # 12F features): groups of 32, and a ragged batch with groups of 64
     dict(B=50, D=512, H=64, L=900, G=32, F=32),
     dict(B=90, D=800, H=64, L=1300, G=64, F=64),
+    # degenerate shapes: one row and fewer labels than a group; full fan-in
+    # (F = D); exactly one group of 64 at F = D = 128
+    dict(B=1, D=64, H=16, L=10, G=16, F=32),
+    dict(B=3, D=32, H=8, L=100, G=32, F=32),
+    dict(B=64, D=128, H=64, L=64, G=64, F=128),
 ]
 
 
