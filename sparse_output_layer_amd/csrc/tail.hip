@@ -477,10 +477,35 @@ __device__ __forceinline__ void t1_stage_async(const TailArgs &a, unsigned short
     }
 }
 
+// How T1's groups are dealt out.  A run gives each of the NW waves RW
+// groups.  Whole runs fill `n_full` tickets, a whole number of rounds of the
+// grid; the groups left over are spread over the grid in smaller tickets of
+// `k` waves each (the other waves of the workgroup idle), so the last round
+// is not a few full runs on a few CUs while the others wait.  A ticket's time
+// is set by its chunk loop, which is shorter with fewer waves at work.
+struct T1Tickets {
+    int64_t n_full;     // tickets of whole runs
+    int64_t n_tickets;  // all tickets
+    int k;              // waves at work in a ticket past n_full
+};
+
+__host__ inline T1Tickets t1_tickets(int64_t Ng, int RW, int NW, int ncu) {
+    T1Tickets t{};
+    const int64_t slots = (Ng + RW - 1) / RW, runs = (slots + NW - 1) / NW;
+    t.n_full = runs / ncu * ncu;
+    const int64_t left = slots - t.n_full * NW;
+    int64_t k = (left + ncu - 1) / ncu;
+    k = k < 1 ? 1 : k > NW ? NW : k;
+    t.k = (int)k;
+    t.n_tickets = t.n_full + (left + k - 1) / k;
+    return t;
+}
+
 // TK: the fused top-K stage 1 (one bucket per group, K' = 1) is compiled in:
 // 1 with the maximum's own id, 2 with the group's first label as the id
 template <int G, int F, int RW, int NW, int MODE, int TK = 0>
-__global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, int store_z, int do_loss) {
+__global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, T1Tickets tix, int store_z,
+                                                        int do_loss) {
     constexpr int JT = G / 16, KS = F / 32, FT = F / 16;
     constexpr int BC = T1_BC, BCP = T1_BCP;
     // a group's W / dW slab (G x F) passes through LDS, one row per WSP
@@ -503,7 +528,6 @@ __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, int store_z,
     const unsigned voff = t1_copy_voff(lane, a.Bp);
     const int q = lane >> 4, m = lane & 15;
     const int nch = a.Bp / BC;
-    const int64_t n_runs = (a.Ng + NW * RW - 1) / (NW * RW);
     const bool need_pos = MODE != T1_DW_MEM && (do_loss || DO_DW);
     float lsum = 0.f;
 
@@ -515,8 +539,11 @@ __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, int store_z,
     // of a run no copy into buffer 1 is pending and the next run's W staging
     // comes after its first barrier).
     int *const s_ticket = (int *)(buf1 + 32);
-    for (int64_t run = blockIdx.x; run < n_runs;) {
-        const int64_t gw = run * (NW * RW) + (int64_t)w * RW;
+    for (int64_t run = blockIdx.x; run < tix.n_tickets;) {
+        // first group of this wave; a.Ng (no group) for the idle waves of a small ticket
+        const int64_t gw = run < tix.n_full ? (run * NW + w) * RW
+                           : w < tix.k      ? (tix.n_full * NW + (run - tix.n_full) * tix.k + w) * RW
+                                            : a.Ng;
         bf16x8 wreg[RW][KS][JT];
         u32x2 pwz[DO_Z ? RW : 1][KS];     // perm bytes of positions 32s + 8q .. + 7
         unsigned zrow[RW][KS];            // tr-gather rows: lo16 = h 0, hi16 = h 1
@@ -992,11 +1019,11 @@ static hipError_t t1_launch(int mode, const TailArgs &a, bool store_z, bool do_l
                             hipStream_t st) {
     if (t1_buf_bytes(a.D, NW) > (size_t)T1_BUF_BYTES) return hipErrorInvalidValue;
     const size_t lds = 0;
-    const int64_t n_runs = (a.Ng + NW * RW - 1) / (NW * RW);
     int dev = 0, ncu = 256;
     if (hipGetDevice(&dev) == hipSuccess)
         (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
-    const int64_t grid = n_runs < ncu ? n_runs : ncu;
+    const T1Tickets tix = t1_tickets(a.Ng, RW, NW, ncu);
+    const int64_t grid = tix.n_tickets < ncu ? tix.n_tickets : ncu;
     if (grid <= 0) return hipSuccess;
     const dim3 blk(64 * NW);
     const int tk = a.tk_v == nullptr ? 0 : a.tk_max_only ? 2 : 1;
@@ -1004,29 +1031,29 @@ static hipError_t t1_launch(int mode, const TailArgs &a, bool store_z, bool do_l
     case T1_FWD:
         if (tk == 2)
             hipLaunchKernelGGL((k_tail_t1<G, F, RW, NW, T1_FWD, 2>), dim3((unsigned)grid), blk, lds,
-                               st, a, (int)store_z, (int)do_loss);
+                               st, a, tix, (int)store_z, (int)do_loss);
         else if (tk == 1)
             hipLaunchKernelGGL((k_tail_t1<G, F, RW, NW, T1_FWD, 1>), dim3((unsigned)grid), blk, lds,
-                               st, a, (int)store_z, (int)do_loss);
+                               st, a, tix, (int)store_z, (int)do_loss);
         else
             hipLaunchKernelGGL((k_tail_t1<G, F, RW, NW, T1_FWD>), dim3((unsigned)grid), blk, lds, st,
-                               a, (int)store_z, (int)do_loss);
+                               a, tix, (int)store_z, (int)do_loss);
         break;
     case T1_DW_BCE:
         if (tk == 2)
             hipLaunchKernelGGL((k_tail_t1<G, F, RW, NW, T1_DW_BCE, 2>), dim3((unsigned)grid), blk,
-                               lds, st, a, 0, (int)do_loss);
+                               lds, st, a, tix, 0, (int)do_loss);
         else if (tk == 1)
             hipLaunchKernelGGL((k_tail_t1<G, F, RW, NW, T1_DW_BCE, 1>), dim3((unsigned)grid), blk,
-                               lds, st, a, 0, (int)do_loss);
+                               lds, st, a, tix, 0, (int)do_loss);
         else
             hipLaunchKernelGGL((k_tail_t1<G, F, RW, NW, T1_DW_BCE>), dim3((unsigned)grid), blk, lds,
-                               st, a, 0, (int)do_loss);
+                               st, a, tix, 0, (int)do_loss);
         break;
     default:
         if (tk) return hipErrorInvalidValue;
         hipLaunchKernelGGL((k_tail_t1<G, F, RW, NW, T1_DW_MEM>), dim3((unsigned)grid), blk, lds,
-                           st, a, 0, 0);
+                           st, a, tix, 0, 0);
         break;
     }
     return hipGetLastError();
