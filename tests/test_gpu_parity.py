@@ -328,6 +328,7 @@ def test_topk_merge_exact(H):
     (3, 40, 16, 0, False, torch.bfloat16),       # no positives at all
     (70, 300, 64, 4, True, torch.bfloat16),      # duplicates, ragged last group
     (1100, 5000, 16, 5, True, torch.bfloat16),   # more keys than one LDS chunk
+    (2000, 9000, 32, 6, True, torch.bfloat16),   # 7,557 keys: a 30 x 30 grid of rank tiles
     (600, 777, 3, 7, True, torch.float32),       # fp32 desc, groups of three
 ])
 def test_group_positives_edges(H, B, L, G, per_row, dup, dtype):
