@@ -880,8 +880,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, T1Tickets ti
                         if (MODE == T1_DW_BCE && a.dzt)
                             __builtin_nontemporal_store(v, (u32x4 *)(a.dzt + ((((int64_t)g * nch + ch) * JT + jt) << 9) + lane * 8));
                     }
-#pragma unroll
-                    for (int ft = 0; ft < FT; ++ft) {
+                    auto dw_read = [&](int ft) {
                         const unsigned row =
                             (ft & 1) ? (frow[r][ft >> 1] >> 16) : (frow[r][ft >> 1] & 0xffffu);
                         // two separate 8-byte reads: fused into one paired read
@@ -892,10 +891,20 @@ __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, T1Tickets ti
                         u32x2 lo = *(const u32x2 *)(tile + o_lo);
                         u32x2 hi = *(const u32x2 *)(tile + o_hi);
                         u32x4 v = {lo.x, lo.y, hi.x, hi.y};
-                        bf16x8 A = __builtin_bit_cast(bf16x8, v);
+                        return __builtin_bit_cast(bf16x8, v);
+                    };
+                    // the reads of step ft+1 are issued before the products of
+                    // step ft, so a step waits for its own reads only
+                    bf16x8 Acur = dw_read(0);
+#pragma unroll
+                    for (int ft = 0; ft < FT; ++ft) {
+                        bf16x8 Anext = Acur;
+                        if (ft + 1 < FT) Anext = dw_read(ft + 1);
+                        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                         for (int jt = 0; jt < JT; ++jt)
-                            dwacc[r][ft][jt] = mfma32(A, Bj[jt], dwacc[r][ft][jt]);
+                            dwacc[r][ft][jt] = mfma32(Acur, Bj[jt], dwacc[r][ft][jt]);
+                        Acur = Anext;
                     }
                 }
             }
