@@ -44,8 +44,8 @@ __global__ void k_f32_tail_logits(F32Args a, int store_z, int bce, int loss) {
         }
     }
     if (loss && a.loss) {
-        float v = wave_sum(l);
-        if ((threadIdx.x & 63) == 0) atomicAdd(a.loss, v);
+        __shared__ float s_loss[16];
+        block_loss_add(l, s_loss, a.loss);
     }
 }
 
@@ -98,8 +98,8 @@ __global__ void k_f32_head_logits(F32Args a, int store_z, int bce, int loss) {
         }
     }
     if (loss && a.loss) {
-        float v = wave_sum(l);
-        if ((threadIdx.x & 63) == 0) atomicAdd(a.loss, v);
+        __shared__ float s_loss[16];
+        block_loss_add(l, s_loss, a.loss);
     }
 }
 

@@ -177,8 +177,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g) {
             }
         }
     if (EPI == EPI_BCE && g.loss) {
-        float v = wave_sum(lsum);
-        if (lane == 0) atomicAdd(g.loss, v);
+        __shared__ float s_loss[4];
+        block_loss_add(lsum, s_loss, g.loss);
     }
 }
 
@@ -453,8 +453,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm2(GemmArgs g) {
         }
     }
     if (EPI == EPI_BCE && g.loss) {
-        float v = wave_sum(g.s * (lin + lsum));
-        if (lane == 0) atomicAdd(g.loss, v);
+        __shared__ float s_loss[4];
+        block_loss_add(g.s * (lin + lsum), s_loss, g.loss);
     }
 }
 

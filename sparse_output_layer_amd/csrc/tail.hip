@@ -1012,10 +1012,9 @@ __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, T1Tickets ti
             atomicExch(a.sched + 1, 0u);
         }
     }
-    if (do_loss && a.loss) {
-        float v = wave_sum(lsum);
-        if (lane == 0) atomicAdd(a.loss, v);
-    }
+    // one add per workgroup; the waves' sums meet in buffer 0, where no copy
+    // is pending after the last run
+    if (do_loss && a.loss) block_loss_add(lsum, (float *)buf0, a.loss);
 }
 
 // Dynamic LDS above the default per-kernel limit must be allowed per kernel.
@@ -1180,10 +1179,8 @@ __global__ __launch_bounds__(64 * FF_NW, 1) void k_fanin1_fwd(TailArgs a, int st
         if (ch + 2 < nch) ff_stage_async(a, fbuf0, ch + 2, wu, voff);
         chunk(fbuf1, ch + 1);
     }
-    if (do_loss && a.loss) {
-        const float v = wave_sum(lsum);
-        if (lane == 0) atomicAdd(a.loss, v);
-    }
+    // no copy into buffer 0 is pending after the last chunk pair
+    if (do_loss && a.loss) block_loss_add(lsum, (float *)fbuf0, a.loss);
 }
 
 hipError_t launch_fanin1_fwd(const TailArgs &a, bool store_z, bool do_loss, hipStream_t st) {
@@ -1329,10 +1326,8 @@ __global__ __launch_bounds__(64 * FF_NW, 1) void k_fanin1_step(TailArgs a, int d
 #pragma unroll
         for (int j = 0; j < FJ; ++j) a.dW[t * F + rp + 16 * j] = f32_to_bf16(acc[j]);
     }
-    if (do_loss && a.loss) {
-        const float v = wave_sum(lsum);
-        if (lane == 0) atomicAdd(a.loss, v);
-    }
+    // no copy into buffer 0 is pending after the last chunk pair
+    if (do_loss && a.loss) block_loss_add(lsum, (float *)fbuf0, a.loss);
 }
 
 // dX of the per-label layer from the step's label-major dz: dX[b][d] +=
