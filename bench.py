@@ -621,7 +621,9 @@ def main():
     B, D, L, G = cfg.B, cfg.D, cfg.L, cfg.G
     lean = args.lean == "yes" or (args.lean == "auto" and cfg.lean)
     s = 1.0 / B
-    loss = torch.zeros(1, dtype=torch.float32, device=dev)
+    # dX and the loss share one buffer, so one fill clears both each step
+    acc = torch.zeros(B * D + 64, dtype=torch.float32, device=dev)
+    dX, loss = acc[:B * D].view(B, D), acc[B * D:B * D + 1]
     bce_h = H.Bce(rp, lab, 0, s, loss)
     bce_t = H.Bce(rp, lab, cfg.H, s, loss)
     K = cfg.topk
@@ -629,7 +631,6 @@ def main():
         for b_ in (bce_h, bce_t):
             b_.topk_val = torch.empty(B, K, dtype=torch.float32, device=dev)
             b_.topk_idx = torch.empty(B, K, dtype=torch.int32, device=dev)
-    dX = torch.empty(B, D, dtype=torch.float32, device=dev)
     dWh = torch.empty_like(Wh)
     dW = torch.empty_like(W)
     ws_t = torch.empty(H.haste_tail_workspace_bytes(X, idx, L, G, bce_t, lean=lean), dtype=torch.uint8,
@@ -650,8 +651,7 @@ def main():
         loss atomically, so both are zeroed first.  ev: two events on the
         main stream around the dW pass (around the dX pass when dom_dx)."""
         main = torch.cuda.current_stream()
-        loss.zero_()
-        dX.zero_()
+        acc.zero_()                      # dX and the loss
         side.wait_stream(main)
         with torch.cuda.stream(side):
             H.haste_head_step(X, Wh, bce_h, dWh, dX, accumulate_dX=True, workspace=ws_h)

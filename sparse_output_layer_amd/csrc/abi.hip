@@ -735,10 +735,18 @@ haste_status head_logits(const haste_head_desc *d, const void *X, const void *Wh
         g.k_split = d->D;
         g.Zout = (unsigned short *)Zh;
         if (bce) {
-            TRY_HIP(launch_head_bitmap(bce->row_ptr, bce->labels, bce->nnz, d->B, bce->label_offset,
-                                       d->H, (uint32_t *)B8(ws, m.bm), m.words, st), "head bitmap");
-            g.bitmap = (const uint32_t *)B8(ws, m.bm);
-            g.bm_words = m.words;
+            if (gemm2_shape(g)) {   // the GEMM reads the positives per tile
+                g.pos_ptr = bce->row_ptr;
+                g.pos_lab = bce->labels;
+                g.pos_off = bce->label_offset;
+                g.pos_nnz = bce->nnz;
+            } else {
+                TRY_HIP(launch_head_bitmap(bce->row_ptr, bce->labels, bce->nnz, d->B, bce->label_offset,
+                                           d->H, (uint32_t *)B8(ws, m.bm), m.words, st),
+                        "head bitmap");
+                g.bitmap = (const uint32_t *)B8(ws, m.bm);
+                g.bm_words = m.words;
+            }
             g.s = bce->grad_scale;
             g.loss = want_loss ? bce->loss : nullptr;
             g.dZout = (unsigned short *)dz_out;

@@ -285,9 +285,31 @@ __global__ __launch_bounds__(256, 2) void k_gemm2(GemmArgs g) {
     if (kend > g.K) kend = g.K;
     const int nk = (kend - kbeg + TK2 - 1) / TK2;
     // BCE: the positives of the tile (TMT rows x 4 bitmap words) go to LDS
-    // first, so the epilogue reads them there instead of once per logit
-    __shared__ uint32_t bm_tile[EPI == EPI_BCE ? TMT * 4 : 1];
-    if (EPI == EPI_BCE) {
+    // first, so the epilogue reads them there instead of once per logit.
+    // From the row CSR: a thread per row builds the row's four words (no two
+    // threads share a word); the K loop's barriers publish them.
+    __shared__ __attribute__((aligned(16))) uint32_t bm_tile[EPI == EPI_BCE ? TMT * 4 : 1];
+    const bool has_pos = g.bitmap || g.pos_ptr;
+    if (EPI == EPI_BCE && g.pos_ptr) {
+        for (int r = threadIdx.x; r < TMT; r += 256) {
+            const int row = m0 + r;
+            uint32_t w0 = 0u, w1 = 0u, w2 = 0u, w3 = 0u;
+            if (row < g.M) {
+                const int e1 = min(g.pos_ptr[row + 1], g.pos_nnz);
+                for (int e = max(g.pos_ptr[row], 0); e < e1; ++e) {
+                    const int64_t c = (int64_t)g.pos_lab[e] - g.pos_off - n0;
+                    if (c < 0 || c >= TN || n0 + c >= g.N) continue;
+                    const uint32_t bit = 1u << (c & 31);
+                    const int wd = (int)(c >> 5);
+                    w0 |= wd == 0 ? bit : 0u;
+                    w1 |= wd == 1 ? bit : 0u;
+                    w2 |= wd == 2 ? bit : 0u;
+                    w3 |= wd == 3 ? bit : 0u;
+                }
+            }
+            *(u32x4 *)(bm_tile + 4 * r) = (u32x4){w0, w1, w2, w3};
+        }
+    } else if (EPI == EPI_BCE) {
         for (int i = threadIdx.x; i < TMT * 4; i += 256) {
             const int row = m0 + (i >> 2), wd = (n0 >> 5) + (i & 3);
             bm_tile[i] = g.bitmap && row < g.M && wd < g.bm_words
@@ -380,7 +402,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm2(GemmArgs g) {
                     bw[i][e][h] = bm_tile[(wm + 16 * i + 4 * q + e) * 4 + (wn >> 5) + h];
     }
     const bool whole = m0 + TMT <= g.M && n0 + TN <= g.N;
-    if (EPI == EPI_BCE && whole && g.bitmap && g.dZout && !g.Zout && !g.Z32) {
+    if (EPI == EPI_BCE && whole && has_pos && g.dZout && !g.Zout && !g.Z32) {
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
 #pragma unroll
@@ -428,7 +450,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm2(GemmArgs g) {
                     const float v = acc[i][j][e];
                     const int64_t o = (int64_t)row * g.N + col;
                     if (EPI == EPI_BCE) {
-                        if (g.bitmap) {
+                        if (has_pos) {
                             const float y = (float)((bw[i][e][j >> 1] >> ((16 * j + m) & 31)) & 1u);
                             const float ex = fast_exp_neg_abs(v);
                             float den;
@@ -458,11 +480,15 @@ __global__ __launch_bounds__(256, 2) void k_gemm2(GemmArgs g) {
     }
 }
 
+bool gemm2_shape(const GemmArgs &g) {
+    return g.M % 8 == 0 && g.N % 8 == 0 && g.K % 8 == 0 && g.k_split % 8 == 0;
+}
+
 hipError_t launch_gemm(bool a_kmaj, bool b_kmaj, int epi, const GemmArgs &g, hipStream_t st) {
     if (g.M <= 0 || g.N <= 0 || g.K <= 0) return hipSuccess;
     const int splits = (g.K + g.k_split - 1) / g.k_split;
     dim3 grid((g.N + TN - 1) / TN, (g.M + TM - 1) / TM, splits);
-    if (g.M % 8 == 0 && g.N % 8 == 0 && g.K % 8 == 0 && g.k_split % 8 == 0) {
+    if (gemm2_shape(g)) {
         // 64-row M tiles (4 waves of 32 x 64, LDS-bound) only when 128-row
         // tiles (4 waves of 64 x 64) would leave CUs idle
         const int t128 = ((g.N + TN - 1) / TN) * ((g.M + 127) / 128) * splits;
@@ -480,6 +506,7 @@ hipError_t launch_gemm(bool a_kmaj, bool b_kmaj, int epi, const GemmArgs &g, hip
     }
 #define GL(AK, BK, E) \
     hipLaunchKernelGGL((k_gemm<AK, BK, E>), grid, dim3(256), 0, st, g)
+    if (epi == EPI_BCE && g.pos_ptr) return hipErrorInvalidValue;   // k_gemm reads the bitmap
     if (epi == EPI_BCE && a_kmaj && b_kmaj) GL(true, true, EPI_BCE);
     else if (epi == EPI_STORE16 && !a_kmaj && !b_kmaj) GL(false, false, EPI_STORE16);
     else if (epi == EPI_ATOMIC32 && a_kmaj && !b_kmaj) GL(true, false, EPI_ATOMIC32);

@@ -134,6 +134,10 @@ struct GemmArgs {
     float *Z32;                // BCE: optional fp32 logits (for the top-K), ld N
     const uint32_t *bitmap;    // BCE: positives bitmap, row stride bm_words
     int bm_words;
+    const int32_t *pos_ptr;    // BCE on the pipelined GEMM (gemm2_shape): the positives as
+    const int32_t *pos_lab;    //   row CSR, global ids, column c = id - pos_off (instead of
+    int64_t pos_off;           //   the bitmap; read per tile in the GEMM's prologue)
+    int pos_nnz;               //   entries of pos_lab (reads stay below it)
     float *loss;
     float s;
     int k_split;               // K elements per split (multiple of 32)
@@ -142,6 +146,8 @@ enum GemmEpi { EPI_BCE = 0, EPI_STORE16 = 1, EPI_ATOMIC32 = 2 };
 // a_kmaj: A stored [m][k]; else [k][m].  b_kmaj: B stored [n][k]; else [k][n].
 hipError_t launch_gemm(bool a_kmaj, bool b_kmaj, int epi, const GemmArgs &g,
                        hipStream_t st);
+// the pipelined GEMM takes the shape (M, N, K and the split multiples of 8)
+bool gemm2_shape(const GemmArgs &g);
 hipError_t launch_head_bitmap(const int32_t *row_ptr, const int32_t *labels,
                               int nnz, int B, int64_t label_offset, int H,
                               uint32_t *bm, int bm_words, hipStream_t st);
