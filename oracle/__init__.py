@@ -377,3 +377,65 @@ def sgd(W, dW, lr):
     pages name no optimizer; this is the textbook step the fused update
     implements."""
     return _c(W, np.float64) - lr * _c(dW, np.float64)
+
+
+# ------------------------------------------------------ dynamic rewiring
+def rewire_scores(Wg, live):
+    """Magnitude of each position of one group: the L1 norm of its weight
+    column over the group's live labels, summed in float32 in ascending
+    label order (the precision and order in which the rewiring decides which
+    positions to prune; the inputs are exact in float32)."""
+    Wg = np.asarray(Wg, np.float32)
+    s = np.zeros(Wg.shape[1], np.float32)
+    for j in range(live):
+        s = (s + np.abs(Wg[j])).astype(np.float32)
+    return s
+
+
+def tail_rewire(idx, W, L, G, D, k, cand):
+    """One prune-and-regrow step of every group's fan-in set (dynamic sparse
+    training at group granularity; HASTE page title, and "Method" item 1:
+    one index set per group).  The pages give no rule; the reading here:
+
+    1. score every position f of group g by `rewire_scores`;
+    2. prune the k positions that come first in (score, feature) order;
+    3. regrow k features outside the kept ones: the caller's candidates
+       cand[g] in list order, skipping values outside [0, D), kept features
+       and repeats; if the list runs out, the smallest features left;
+    4. the new set, sorted ascending, replaces idx[g]; a kept feature's
+       weight column moves with it (every row of the group, padded rows
+       too), a regrown feature's column is zero.
+
+    idx: N_g x F int; W: (N_g*G) x F float32 (exact bf16 or fp32 values);
+    cand: N_g x R int.  Returns (idx', W') as new arrays."""
+    idx = np.asarray(idx, np.int64)
+    W = np.asarray(W, np.float32)
+    cand = np.asarray(cand, np.int64)
+    ng, F = idx.shape
+    idx_new = np.empty_like(idx)
+    W_new = np.zeros_like(W)
+    for g in range(ng):
+        live = min(G, L - g * G)
+        rows = slice(g * G, (g + 1) * G)
+        score = rewire_scores(W[rows], live)
+        order = sorted(range(F), key=lambda f: (float(score[f]), int(idx[g, f])))
+        pruned = set(order[:k])
+        src = {int(idx[g, f]): f for f in range(F) if f not in pruned}
+        taken = []
+        for c in cand[g]:
+            if len(taken) == k:
+                break
+            c = int(c)
+            if 0 <= c < D and c not in src and c not in taken:
+                taken.append(c)
+        d = 0
+        while len(taken) < k:
+            if d not in src and d not in taken:
+                taken.append(d)
+            d += 1
+        new = sorted(list(src) + taken)
+        idx_new[g] = new
+        for p, feat in enumerate(new):
+            if feat in src:
+                W_new[rows, p] = W[rows, src[feat]]
+    return idx_new.astype(np.int32), W_new

@@ -482,3 +482,105 @@ def test_generator_is_deterministic_and_shaped():
     bits = wl.bf16_bits_from_f32(np.array([1.0, 1.00390625, 1.005859375,
                                            -2.5], np.float32))
     assert list(wl.f64_from_bf16_bits(bits)) == [1.0, 1.0, 1.0078125, -2.5]
+
+
+# ------------------------------------------------------- F4: rewiring
+def test_rewire_golden_example():
+    """Hand-derived worked example (tests/golden/rewire_example.json): two
+    groups, a ragged last group whose padded row must not count towards the
+    scores, a tie between two columns, candidates that are out of range,
+    kept, repeated or pruned a moment ago, and a group whose candidates run
+    out."""
+    ex = json.load(open(os.path.join(GOLD, "rewire_example.json")))
+    i2, W2 = oracle.tail_rewire(np.array(ex["idx"]), np.array(ex["W"], np.float32),
+                                ex["L"], ex["G"], ex["D"], ex["k"], np.array(ex["cand"]))
+    assert i2.tolist() == ex["expected_idx"]
+    assert np.array_equal(W2, np.array(ex["expected_W"], np.float32))
+
+
+def _grid_weights(rng, rows, F, zero_cols=0):
+    # multiples of 1/16 in [-0.5, 0.5]: every float32 sum of up to 64 of them
+    # is exact, so the float64 column sums below order the positions exactly
+    W = (rng.integers(-8, 9, size=(rows, F)) / 16.0).astype(np.float32)
+    if zero_cols:
+        W[:, rng.choice(F, zero_cols, replace=False)] = 0.0
+    return W
+
+
+@pytest.mark.parametrize("G,F,D,L,k", [(16, 32, 96, 200, 8), (1, 16, 40, 30, 5),
+                                       (64, 16, 16, 100, 6), (32, 64, 300, 90, 64),
+                                       (16, 128, 768, 48, 0)])
+def test_rewire_invariants_and_function(G, F, D, L, k):
+    """Checks the rewiring step against properties that fix it, each by a
+    route of its own: (a) every pruned position comes before every kept one
+    in (score, feature) order, with scores summed in float64 over the live
+    rows (exact on this weight grid); (b) the regrown set is the first k
+    distinct admissible candidates in list order (found with np.unique), then
+    the smallest features left (np.setdiff1d); (c) the layer's function: the
+    rewired layer's logits equal those of the old layer with the pruned
+    columns zeroed (the pinned tail_logits oracle); (d) k = 0 changes nothing."""
+    rng = np.random.default_rng(G * 1000 + F + k)
+    ng = (L + G - 1) // G
+    idx = np.sort(np.stack([rng.choice(D, F, replace=False) for _ in range(ng)]), axis=1)
+    W = _grid_weights(rng, ng * G, F, zero_cols=min(3, F // 4))
+    R = 12
+    cand = rng.integers(-3, D + 3, size=(ng, R))
+    cand[:, 1] = idx[:, 0]                      # a kept-or-pruned feature
+    cand[:, 3] = cand[:, 2]                     # a repeat
+    i2, W2 = oracle.tail_rewire(idx, W, L, G, D, k, cand)
+    assert np.all(np.diff(i2, axis=1) > 0) and i2.min() >= 0 and i2.max() < D
+    for g in range(ng):
+        live = min(G, L - g * G)
+        rows = slice(g * G, (g + 1) * G)
+        s64 = np.abs(W[g * G:g * G + live].astype(np.float64)).sum(axis=0)
+        keys = sorted((s64[f], idx[g, f], f) for f in range(F))
+        pruned = {f for _, _, f in keys[:k]}
+        kept = [f for f in range(F) if f not in pruned]
+        kept_feats = set(idx[g, kept].tolist())
+        # (a) the oracle kept exactly these features
+        assert kept_feats <= set(i2[g].tolist())
+        # (b) regrown features
+        c = cand[g]
+        ok = (c >= 0) & (c < D) & ~np.isin(c, list(kept_feats))
+        vals, first = np.unique(c[ok], return_index=True)
+        taken = vals[np.argsort(first)][:k].tolist()
+        if len(taken) < k:
+            rest = np.setdiff1d(np.arange(D), list(kept_feats) + taken)
+            taken += rest[:k - len(taken)].tolist()
+        assert set(i2[g].tolist()) == kept_feats | set(taken)
+        # regrown columns are zero, kept ones carry their weights unchanged
+        for p, feat in enumerate(i2[g]):
+            if feat in kept_feats:
+                f = int(np.nonzero(idx[g] == feat)[0][0])
+                assert np.array_equal(W2[rows, p], W[rows, f])
+            else:
+                assert np.all(W2[rows, p] == 0.0)
+    # (c) function
+    X = rng.standard_normal((5, D))
+    Wz = W.astype(np.float64).copy()
+    for g in range(ng):
+        live = min(G, L - g * G)
+        s64 = np.abs(W[g * G:g * G + live].astype(np.float64)).sum(axis=0)
+        keys = sorted((s64[f], idx[g, f], f) for f in range(F))
+        for _, _, f in keys[:k]:
+            Wz[g * G:(g + 1) * G, f] = 0.0
+    Z_old, A = oracle.tail_logits(X, idx, Wz, L, G)
+    Z_new, _ = oracle.tail_logits(X, i2, W2.astype(np.float64), L, G)
+    assert np.all(np.abs(Z_new - Z_old) <= 1e-12 * A + 1e-300)
+    # (d) identity at k = 0
+    i0, W0 = oracle.tail_rewire(idx, W, L, G, D, 0, cand)
+    assert np.array_equal(i0, idx) and np.array_equal(W0, W)
+
+
+def test_rewire_prune_all_takes_the_candidates():
+    """k = F: every position goes, the new set is the first F distinct
+    admissible candidates (here all of them, already distinct), sorted, and
+    every weight is zero."""
+    rng = np.random.default_rng(5)
+    G, F, D, L = 4, 8, 50, 8
+    idx = np.sort(np.stack([rng.choice(D, F, replace=False) for _ in range(2)]), axis=1)
+    W = _grid_weights(rng, 2 * G, F)
+    cand = np.stack([rng.choice(D, F, replace=False) for _ in range(2)])
+    i2, W2 = oracle.tail_rewire(idx, W, L, G, D, F, cand)
+    assert np.array_equal(i2, np.sort(cand, axis=1))
+    assert np.all(W2 == 0.0)

@@ -220,6 +220,14 @@ def make_inputs(cfg: Config | str, **overrides) -> Inputs:
     return Inputs(cfg, X, Wh, idx, W, row_ptr, labels)
 
 
+def rewire_candidates(cfg: Config, n_cand: int, seed: int = 1) -> np.ndarray:
+    """Regrowth candidates for the rewiring step: N_g x n_cand features drawn
+    uniformly from [0, D) with repeats (the random draws a training loop
+    makes and passes to the layer), deterministically from ``seed``."""
+    rng = np.random.default_rng(np.random.SeedSequence([seed, cfg.seed]))
+    return rng.integers(0, cfg.D, size=(cfg.n_groups, n_cand), dtype=np.int32)
+
+
 def tiny(name="t", **kw) -> Config:
     """Small configs for parity tests (several tiles plus ragged tails)."""
     base = dict(name=name, B=40, D=96, H=48, L=200, G=16, F=32, dtype="bf16",
