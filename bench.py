@@ -48,13 +48,15 @@ def parse():
     p.add_argument("--calib-mib", type=int, default=0,
                    help="after timing, one device-to-device copy of this many MiB: the "
                         "known-size reference for the FETCH_SIZE / WRITE_SIZE counters")
-    p.add_argument("--mode", choices=["train", "infer", "dense", "sgd", "calls"], default="train",
+    p.add_argument("--mode", choices=["train", "infer", "dense", "sgd", "calls", "rewire"], default="train",
                    help="train: the training step (default); infer: head + tail forward "
                         "with a per-row top-K, exact and approximate; dense: the tail next "
                         "to a FLOPs-matched dense bottleneck layer; sgd: the tail step with "
                         "its SGD update fused into the dW pass, next to step + update; "
                         "calls: every forward, backward and step entry point on its own")
     p.add_argument("--topk", type=int, default=5, help="K of the inference mode")
+    p.add_argument("--rewire-k", type=int, default=-1, help="positions pruned per group (rewire mode; default F/4)")
+    p.add_argument("--rewire-cand", type=int, default=64, help="regrowth candidates per group (rewire mode)")
     p.add_argument("--lean", choices=["auto", "yes", "no"], default="auto",
                    help="training step without the dz tiles (dX recomputes dz); auto: as the "
                         "workload says")
@@ -580,6 +582,61 @@ def run_sgd(args, cfg, inp, t_gen):
     print(json.dumps(out), flush=True)
 
 
+def run_rewire(args, cfg, inp, t_gen):
+    """One prune-and-regrow step of every group's fan-in set
+    (haste_tail_rewire), out of place between two buffer pairs that swap
+    every call, with the same seeded candidates.  HBM-bound: algorithmic
+    bytes per call = W read and written, idx read and written, the
+    candidates read."""
+    import numpy as np
+    import torch
+
+    import workloads as wl
+    from sparse_output_layer_amd import haste as H
+    dev = "cuda:0"
+    k = cfg.F // 4 if args.rewire_k < 0 else args.rewire_k
+    R = args.rewire_cand
+    W = torch.from_numpy(np.ascontiguousarray(inp.W).view(np.int16)).view(torch.bfloat16).to(dev)
+    idx = torch.from_numpy(inp.idx).to(dev)
+    cand = torch.from_numpy(wl.rewire_candidates(cfg, R)).to(dev) if R > 0 else None
+    bufs = [(idx.clone(), W.clone()), (torch.empty_like(idx), torch.empty_like(W))]
+    state = {"k": 0}
+
+    def call():
+        a, b = bufs[state["k"]], bufs[1 - state["k"]]
+        H.haste_tail_rewire(a[0], a[1], cfg.D, cfg.L, cfg.G, k, cand, idx_out=b[0], W_out=b[1])
+        state["k"] = 1 - state["k"]
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.steps):
+        call()
+    t1.record()
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) / args.steps * 1e3
+    ng = cfg.n_groups
+    nbytes = 2 * ng * cfg.G * cfg.F * 2 + 2 * ng * cfg.F * 4 + ng * R * 4
+    gbs = nbytes / (us * 1e-6) / 1e9
+    peaks = measured_peaks(H, torch)
+    out = {
+        "metric": "tail rewiring step (prune and regrow every group's fan-in set) at %s" % cfg.name,
+        "value": round(us, 2), "unit": "us", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "higher_is_better": False, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: D={cfg.D} L={cfg.L} G={cfg.G} F={cfg.F}, "
+                               f"k={k} pruned per group, {R} uniform candidates per group",
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
+                     "frac": round(gbs / 8000.0, 4), "algorithmic_bytes_per_launch": nbytes,
+                     "peak_measured": peaks["hbm_copy_gbs"],
+                     "frac_measured": round(gbs / peaks["hbm_copy_gbs"], 4)},
+        "gen_s": round(t_gen, 2),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -610,6 +667,8 @@ def main():
         return run_sgd(args, cfg, inp, t_gen)
     if args.mode == "calls":
         return run_calls(args, cfg, inp, t_gen)
+    if args.mode == "rewire":
+        return run_rewire(args, cfg, inp, t_gen)
 
     def bf(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)

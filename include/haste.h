@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define HASTE_ABI_VERSION 4
+#define HASTE_ABI_VERSION 5
 
 typedef enum {
     HASTE_OK = 0,
@@ -362,6 +362,37 @@ haste_status haste_tail_group_positives(const haste_tail_desc *d,
  * breaks that, or -1. */
 haste_status haste_tail_validate(const haste_tail_desc *d, const int32_t *idx,
                                  int32_t *first_bad_group, void *stream);
+
+/* Dynamic rewiring of the tail's fan-in sets: one prune-and-regrow step of
+ * every group (HASTE page: the title's dynamic sparse training; "Method"
+ * item 1, "Structure": one fan-in set per group, own weights per label).
+ * The page gives no rule; this call applies the plainest one at group
+ * granularity:
+ *   - position f of group g scores the L1 norm of its weight column over the
+ *     group's live labels, sum_{j < min(G, L - gG)} |W[gG+j][f]|, added in
+ *     fp32 in ascending j;
+ *   - the k_prune positions first in (score, feature id) order are pruned;
+ *   - k_prune features outside the kept set are regrown: cand[g][0..n_cand)
+ *     in order (the caller's random draws; values outside [0, D), kept
+ *     features and repeats are skipped, a feature pruned by this call may
+ *     come back), then the smallest features left;
+ *   - idx_out[g] is the new set, ascending; in W_out a kept feature's column
+ *     is its column of W (every row of the group, padded rows too) and a
+ *     regrown feature's column is zero.
+ * idx: N_g x F int32, each row valid (strictly increasing in [0, D); see
+ * haste_tail_validate); W, W_out: (N_g*G) x F of d->dtype; cand: N_g x n_cand
+ * int32 (may be NULL when n_cand = 0); idx_out: N_g x F int32.  idx_out and
+ * W_out may be idx and W (in place) but must not overlap them otherwise.
+ * d->B and d->flags are not used.  After a rewiring, a feature order formed
+ * for HASTE_TAIL_LAYOUT_READY belongs to the old idx: form it again.
+ * Supported: G <= 64, F <= 256, D <= 65536.  Errors: HASTE_ERR_INVALID
+ * (NULL or misaligned pointers, sizes < 1, F > D, k_prune outside [0, F],
+ * n_cand < 0, partial overlap), HASTE_ERR_UNSUPPORTED (G > 64, F > 256,
+ * D > 65536), HASTE_ERR_HIP.  Asynchronous on `stream`. */
+haste_status haste_tail_rewire(const haste_tail_desc *d, const int32_t *idx,
+                               const void *W, int32_t k_prune,
+                               const int32_t *cand, int32_t n_cand,
+                               int32_t *idx_out, void *W_out, void *stream);
 
 /* Merge two per-row top-K lists (e.g. head and tail) into one: B x K each,
  * descending, ties broken toward the smaller id (second stage of the

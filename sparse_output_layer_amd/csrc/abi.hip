@@ -633,6 +633,42 @@ haste_status haste_sgd_update(int64_t n, int32_t dtype, const void *W, const voi
     return HASTE_OK;
 }
 
+haste_status haste_tail_rewire(const haste_tail_desc *d, const int32_t *idx, const void *W,
+                               int32_t k_prune, const int32_t *cand, int32_t n_cand,
+                               int32_t *idx_out, void *W_out, void *stream) {
+    g_err.clear();
+    if (!d) return fail(HASTE_ERR_INVALID, "tail descriptor is NULL");
+    if (d->D < 1 || d->L < 1 || d->G < 1 || d->F < 1)
+        return fail(HASTE_ERR_INVALID, "tail sizes must be >= 1 (D=%d L=%lld G=%d F=%d)", d->D,
+                    (long long)d->L, d->G, d->F);
+    if (d->F > d->D) return fail(HASTE_ERR_INVALID, "F=%d exceeds D=%d", d->F, d->D);
+    if (d->dtype != HASTE_BF16 && d->dtype != HASTE_F32) return fail(HASTE_ERR_INVALID, "unknown dtype %d", d->dtype);
+    if (!rewire_supported(d->G, d->F, d->D))
+        return fail(HASTE_ERR_UNSUPPORTED, "rewiring takes G <= 64, F <= 256 and D <= 65536 (G=%d F=%d D=%d)",
+                    d->G, d->F, d->D);
+    if (k_prune < 0 || k_prune > d->F) return fail(HASTE_ERR_INVALID, "k_prune=%d outside [0, F=%d]", k_prune, d->F);
+    if (n_cand < 0) return fail(HASTE_ERR_INVALID, "n_cand < 0");
+    const int64_t ng = n_groups(d);
+    if (ng > 0x7fffffffLL) return fail(HASTE_ERR_UNSUPPORTED, "more than 2^31 - 1 groups");
+    const size_t es = d->dtype == HASTE_BF16 ? 2 : 4;
+    TRY(need_al(idx, 4, "idx"));
+    TRY(need_al(W, es, "W"));
+    TRY(need_al(idx_out, 4, "idx_out"));
+    TRY(need_al(W_out, es, "W_out"));
+    if (n_cand > 0) TRY(need_al(cand, 4, "cand"));
+    const size_t ibytes = (size_t)ng * d->F * 4, wbytes = (size_t)ng * d->G * d->F * es;
+    const char *i0 = (const char *)idx, *io = (const char *)idx_out;
+    const char *w0 = (const char *)W, *wo = (const char *)W_out;
+    if (io != i0 && io < i0 + ibytes && i0 < io + ibytes)
+        return fail(HASTE_ERR_INVALID, "idx_out overlaps idx without being it");
+    if (wo != w0 && wo < w0 + wbytes && w0 < wo + wbytes)
+        return fail(HASTE_ERR_INVALID, "W_out overlaps W without being it");
+    TRY_HIP(launch_rewire(idx, W, d->dtype == HASTE_BF16, ng, d->G, d->F, d->D, d->L, k_prune, cand,
+                          n_cand, idx_out, W_out, S(stream)),
+            "rewire");
+    return HASTE_OK;
+}
+
 haste_status haste_tail_prepare(const haste_tail_desc *d, const void *X, const haste_bce *bce,
                                 void *ws, size_t ws_bytes, void *stream) {
     g_err.clear();

@@ -112,6 +112,13 @@ hipError_t launch_topk_refine(const unsigned short *X, int B, int D, const unsig
                               int64_t L, int64_t tk_off, int K, float *out_v, int32_t *out_i,
                               hipStream_t st);
 
+// One prune-and-regrow step of every group's fan-in set: shapes it takes
+// (G <= 64, F <= 256, F <= D <= 65536); idx_out / W_out may be idx / W
+bool rewire_supported(int G, int F, int D);
+hipError_t launch_rewire(const int32_t *idx, const void *W, bool bf16, int64_t Ng, int G, int F,
+                         int D, int64_t L, int k, const int32_t *cand, int R, int32_t *idx_out,
+                         void *W_out, hipStream_t st);
+
 // A caller's dZ (B x L bf16, row-major) into the dW pass's dz tiles
 hipError_t launch_dz_tiles(const unsigned short *dZ, int B, int64_t L, int G, int Bp, int64_t Ng,
                            unsigned short *dzt, hipStream_t st);

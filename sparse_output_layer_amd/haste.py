@@ -91,6 +91,7 @@ _SIGS = {
     "haste_topk_expected_recall": (ctypes.c_double, [_i64, ctypes.c_int, ctypes.c_int, _i64]),
     "haste_topk_plan": (ctypes.c_int, [_i64, ctypes.c_int, ctypes.c_double, _i64, ctypes.POINTER(_i32)]),
     "haste_probe_mfma": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _vp, _vp]),
+    "haste_tail_rewire": (ctypes.c_int, [_PD, _vp, _vp, _i32, _vp, _i32, _vp, _vp, _vp]),
 }
 
 
@@ -432,6 +433,27 @@ def haste_tail_validate(idx, D, L, G) -> torch.Tensor:
     out = torch.empty(1, dtype=torch.int32, device=idx.device)
     _check(lib().haste_tail_validate(ctypes.byref(d), _ptr(idx), _ptr(out), _stream()))
     return out
+
+
+def haste_tail_rewire(idx, W, D, L, G, k_prune, cand=None, idx_out=None, W_out=None):
+    """One prune-and-regrow step of every group's fan-in set; returns
+    (idx_out, W_out).  cand: N_g x n_cand int32 regrowth candidates (or None);
+    idx_out / W_out default to new tensors and may be idx / W (in place)."""
+    _need(idx, "idx", torch.int32)
+    _need(W, "W")
+    F = int(idx.shape[1])
+    dt = HASTE_BF16 if W.dtype == torch.bfloat16 else HASTE_F32
+    d = TailDesc(B=1, D=D, L=L, G=G, F=F, dtype=dt)
+    idx_out = torch.empty_like(idx) if idx_out is None else idx_out
+    W_out = torch.empty_like(W) if W_out is None else W_out
+    n_cand = 0
+    if cand is not None:
+        _need(cand, "cand", torch.int32)
+        n_cand = int(cand.shape[1]) if cand.dim() == 2 else 0
+    _check(lib().haste_tail_rewire(ctypes.byref(d), _ptr(idx), _ptr(W), int(k_prune),
+                                   _ptr(cand) if cand is not None else None, n_cand,
+                                   _ptr(idx_out), _ptr(W_out), _stream()))
+    return idx_out, W_out
 
 
 def haste_topk_expected_recall(n: int, K: int, kprime: int, buckets: int = 0) -> float:

@@ -20,7 +20,7 @@ def test_exports_every_declared_symbol(L):
     assert "haste_tail_fwd" in names and "haste_tail_step" in names
     missing = [n for n in names if not hasattr(L, n)]
     assert missing == []
-    assert L.haste_abi_version() == 4
+    assert L.haste_abi_version() == 5
     for s in range(5):
         assert L.haste_status_string(s)
 
@@ -235,3 +235,26 @@ def test_probe_argument_checks(L):
     assert L.haste_probe_mfma(4, 10, None, None) == H.HASTE_ERR_INVALID
     assert L.haste_probe_mfma(4, 10, 0x1002, None) == H.HASTE_ERR_INVALID
 
+
+
+def test_rewire_argument_errors_fail_before_launch(L):
+    """haste_tail_rewire rejects bad arguments before it enqueues anything."""
+    def rw(d, k=2, cand=0x1000, R=4, idx=0x1000, W=0x2000, io=0x100000, Wo=0x200000):
+        return L.haste_tail_rewire(ctypes.byref(d) if d is not None else None, idx, W, k, cand, R,
+                                   io, Wo, None)
+    d = _desc(D=64, L=1024, G=16, F=32)
+    assert rw(None) == H.HASTE_ERR_INVALID
+    assert rw(d, k=-1) == H.HASTE_ERR_INVALID
+    assert rw(d, k=33) == H.HASTE_ERR_INVALID                  # k > F
+    assert rw(d, R=-1) == H.HASTE_ERR_INVALID
+    assert rw(d, cand=0) == H.HASTE_ERR_INVALID                # n_cand > 0 needs a list
+    assert rw(d, idx=0) == H.HASTE_ERR_INVALID
+    assert rw(d, W=0x2001) == H.HASTE_ERR_INVALID              # misaligned bf16
+    assert rw(_desc(D=64, F=128)) == H.HASTE_ERR_INVALID        # F > D
+    assert rw(_desc(D=70000, F=32)) == H.HASTE_ERR_UNSUPPORTED
+    assert rw(_desc(D=1024, F=512)) == H.HASTE_ERR_UNSUPPORTED
+    assert rw(_desc(D=1024, F=32, G=65, dtype=H.HASTE_F32)) == H.HASTE_ERR_UNSUPPORTED
+    # partial overlaps (in place, the same pointer, is allowed)
+    assert rw(d, io=0x1000 + 64) == H.HASTE_ERR_INVALID
+    assert rw(d, Wo=0x2000 + 64) == H.HASTE_ERR_INVALID
+    assert b"overlaps" in L.haste_last_error()
