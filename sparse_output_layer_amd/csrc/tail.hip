@@ -502,11 +502,19 @@ __host__ inline T1Tickets t1_tickets(int64_t Ng, int RW, int NW, int ncu) {
 }
 
 // TK: the fused top-K stage 1 (one bucket per group, K' = 1) is compiled in:
-// 1 with the maximum's own id, 2 with the group's first label as the id
-template <int G, int F, int RW, int NW, int MODE, int TK = 0>
+// 1 with the maximum's own id, 2 with the group's first label as the id.
+// GS: the layer's group size when a wave owns a slice of G labels of a
+// larger group (GS = G: a wave owns whole groups).  The GS / G slices of a
+// group share its index set and feature order and go to different waves, so
+// a wave of a wide group needs no more registers than one of a group of G.
+template <int G, int F, int RW, int NW, int MODE, int TK = 0, int GS = G>
 __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, T1Tickets tix, int store_z,
                                                         int do_loss) {
     constexpr int JT = G / 16, KS = F / 32, FT = F / 16;
+    constexpr int NSL = GS / G;            // label slices per group
+    constexpr int JTS = GS / 16;           // 16-label tiles per group (dz tile index)
+    static_assert(GS % G == 0 && (NSL == 1 || (RW == 1 && TK == 0)), "slices: one per wave, no top-K");
+    const int64_t Nu = a.Ng * NSL;         // work units: (group, slice)
     constexpr int BC = T1_BC, BCP = T1_BCP;
     // a group's W / dW slab (G x F) passes through LDS, one row per WSP
     // elements (16 bytes of padding: rows 4 banks apart), to turn the feature
@@ -543,7 +551,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, T1Tickets ti
         // first group of this wave; a.Ng (no group) for the idle waves of a small ticket
         const int64_t gw = run < tix.n_full ? (run * NW + w) * RW
                            : w < tix.k      ? (tix.n_full * NW + (run - tix.n_full) * tix.k + w) * RW
-                                            : a.Ng;
+                                            : Nu;
         bf16x8 wreg[RW][KS][JT];
         u32x2 pwz[DO_Z ? RW : 1][KS];     // perm bytes of positions 32s + 8q .. + 7
         unsigned zrow[RW][KS];            // tr-gather rows: lo16 = h 0, hi16 = h 1
@@ -553,8 +561,8 @@ __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, T1Tickets ti
         f32x4 dwacc[RW][FT][JT];
 #pragma unroll
         for (int r = 0; r < RW; ++r) {
-            const int64_t g = gw + r;
-            const bool ok = g < a.Ng;
+            const bool ok = gw + r < Nu;
+            const int64_t g = (gw + r) / NSL;
             // features in the bank-aware order: position k reads feature
             // perm[g][k] (row idxp[g][k] of the chunk, column perm[g][k] of W)
             const int64_t gs = ok ? g : 0;
@@ -587,14 +595,16 @@ __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, T1Tickets ti
 
 #pragma unroll
             for (int r = 0; r < RW; ++r) {
-                const int64_t g = gw + r;
-                if (g >= a.Ng) continue;  // wave-uniform
+                if (gw + r >= Nu) continue;  // wave-uniform
+                const int64_t g = (gw + r) / NSL;
+                const int sl = (int)((gw + r) % NSL);
+                const int64_t t0 = g * GS + G * sl;   // this wave's first label
                 // positives of group g in rows [r0, r0+32): lane owns rows r0+16h2+4q+i, slot 16jt+m
                 uint64_t ymask = 0;
                 bool has_pos = false;             // wave-uniform
                 auto add_pos = [&](const int v) {
-                    const int lb = v / G - r0, j = v % G;
-                    if (lb < 0 || lb >= BC) return;
+                    const int lb = v / GS - r0, j = v % GS - G * sl;
+                    if (lb < 0 || lb >= BC || j < 0 || j >= G) return;
                     has_pos = true;
                     if (((lb >> 2) & 3) == q && (j & 15) == m)
                         ymask |= 1ull << (((lb >> 4) * JT + (j >> 4)) * 4 + (lb & 3));
@@ -610,13 +620,13 @@ __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, T1Tickets ti
                     const int n1 = pn[r] < 64 ? pn[r] : 64;
                     for (; e < n1; ++e) {
                         const int v = __builtin_amdgcn_readlane(pe[r], e);
-                        if (v / G >= r0 + BC) break;
+                        if (v / GS >= r0 + BC) break;
                         add_pos(v);
                     }
                     if (e >= 64)
                         for (; e < pn[r]; ++e) {
                             const int v = a.grp_ent[gp0[r] + e];
-                            if (v / G >= r0 + BC) break;
+                            if (v / GS >= r0 + BC) break;
                             add_pos(v);
                         }
                     pc[r] = e;
@@ -645,13 +655,13 @@ __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, T1Tickets ti
                 }
                 // ---- epilogue: lane owns (row r0+16h2+4q+i, slot 16jt+m)
                 unsigned dzp[2][JT][2];
-                const bool tile_live = (r0 + BC <= a.B) && ((g + 1) * G <= a.L);
+                const bool tile_live = (r0 + BC <= a.B) && (t0 + G <= a.L);
                 if (MODE == T1_DW_MEM && a.dzt) {
                     // the caller's dZ, already in the tile layout (zero past B and L)
 #pragma unroll
                     for (int jt = 0; jt < JT; ++jt) {
                         const u32x4 v =
-                            *(const u32x4 *)(a.dzt + ((((int64_t)g * nch + ch) * JT + jt) << 9) + lane * 8);
+                            *(const u32x4 *)(a.dzt + ((((int64_t)g * nch + ch) * JTS + JT * sl + jt) << 9) + lane * 8);
                         dzp[0][jt][0] = v[0];
                         dzp[0][jt][1] = v[1];
                         dzp[1][jt][0] = v[2];
@@ -681,7 +691,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, T1Tickets ti
                             dzp[h2][jt][0] = pack_bf16x2(dzv[0], dzv[1]);
                             dzp[h2][jt][1] = pack_bf16x2(dzv[2], dzv[3]);
                             if (a.Z32) {   // fp32 logits for the top-K
-                                const int64_t t = g * G + 16 * jt + m;
+                                const int64_t t = t0 + 16 * jt + m;
 #pragma unroll
                                 for (int i = 0; i < 4; ++i)
                                     a.Z32[(int64_t)(r0 + 16 * h2 + 4 * q + i) * a.L + t] = zacc[h2][jt][i];
@@ -695,7 +705,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, T1Tickets ti
 #pragma unroll
                         for (int jt = 0; jt < JT; ++jt) {
                             float dzv[4];
-                            const int64_t t = g * G + 16 * jt + m;
+                            const int64_t t = t0 + 16 * jt + m;
 #pragma unroll
                             for (int i = 0; i < 4; ++i) {
                                 const int row = r0 + 16 * h2 + 4 * q + i;
@@ -878,7 +888,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, T1Tickets ti
                         // which leaves the cache to the chunks of X^T (measured: 6% less
                         // time for this pass on the 670K workload)
                         if (MODE == T1_DW_BCE && a.dzt)
-                            __builtin_nontemporal_store(v, (u32x4 *)(a.dzt + ((((int64_t)g * nch + ch) * JT + jt) << 9) + lane * 8));
+                            __builtin_nontemporal_store(v, (u32x4 *)(a.dzt + ((((int64_t)g * nch + ch) * JTS + JT * sl + jt) << 9) + lane * 8));
                     }
                     auto dw_read = [&](int ft) {
                         const unsigned row =
@@ -918,11 +928,12 @@ __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, T1Tickets ti
             unsigned short *ws = buf1 + w * (G * WSP);
 #pragma unroll
             for (int r = 0; r < RW; ++r) {
-                const int64_t gs = gw + r < a.Ng ? gw + r : 0;
+                // this wave's G label rows (slice of its group), or group 0's
+                const int64_t ls = gw + r < Nu ? ((gw + r) / NSL) * GS + G * ((gw + r) % NSL) : 0;
                 u32x4 wraw[WPL];
 #pragma unroll
                 for (int i = 0; i < WPL; ++i)
-                    wraw[i] = __builtin_nontemporal_load((const u32x4 *)(a.W + gs * G * (int64_t)F + 8 * (64 * i + lane)));
+                    wraw[i] = __builtin_nontemporal_load((const u32x4 *)(a.W + ls * (int64_t)F + 8 * (64 * i + lane)));
 #pragma unroll
                 for (int i = 0; i < WPL; ++i) {
                     const int pc16 = 64 * i + lane;
@@ -958,8 +969,9 @@ __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, T1Tickets ti
             unsigned short *ws = buf0 + w * (G * WSP);
 #pragma unroll
             for (int r = 0; r < RW; ++r) {
-                const int64_t g = gw + r;
-                if (g >= a.Ng) continue;   // wave-uniform
+                if (gw + r >= Nu) continue;   // wave-uniform
+                const int64_t g = (gw + r) / NSL;
+                const int64_t t0 = g * GS + G * ((gw + r) % NSL);
                 unsigned pw[FT];           // perm bytes of positions 16ft + 4q .. + 3
 #pragma unroll
                 for (int ft = 0; ft < FT; ++ft) pw[ft] = *(const unsigned *)(a.perm + g * F + 16 * ft + 4 * q);
@@ -976,7 +988,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, T1Tickets ti
                 for (int i = 0; i < WPL; ++i) {
                     const int pc16 = 64 * i + lane;
                     const u32x4 v = *(const u32x4 *)(ws + (pc16 / (F / 8)) * WSP + 8 * (pc16 % (F / 8)));
-                    const int64_t o = g * G * (int64_t)F + 8 * pc16;
+                    const int64_t o = t0 * (int64_t)F + 8 * pc16;
                     if (!a.Wout) {
                         __builtin_nontemporal_store(v, (u32x4 *)(a.dW + o));
                     } else {
@@ -1022,7 +1034,7 @@ static void allow_lds(const void *fn, size_t bytes) {
     (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
-template <int G, int F, int RW, int NW>
+template <int G, int F, int RW, int NW, int GS = G>
 static hipError_t t1_launch(int mode, const TailArgs &a, bool store_z, bool do_loss,
                             hipStream_t st) {
     if (t1_buf_bytes(a.D, NW) > (size_t)T1_BUF_BYTES) return hipErrorInvalidValue;
@@ -1030,11 +1042,30 @@ static hipError_t t1_launch(int mode, const TailArgs &a, bool store_z, bool do_l
     int dev = 0, ncu = 256;
     if (hipGetDevice(&dev) == hipSuccess)
         (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
-    const T1Tickets tix = t1_tickets(a.Ng, RW, NW, ncu);
+    const T1Tickets tix = t1_tickets(a.Ng * (GS / G), RW, NW, ncu);
     const int64_t grid = tix.n_tickets < ncu ? tix.n_tickets : ncu;
     if (grid <= 0) return hipSuccess;
     const dim3 blk(64 * NW);
     const int tk = a.tk_v == nullptr ? 0 : a.tk_max_only ? 2 : 1;
+    if constexpr (GS != G) {
+        // label slices: no fused top-K
+        if (tk) return hipErrorInvalidValue;
+        switch (mode) {
+        case T1_FWD:
+            hipLaunchKernelGGL((k_tail_t1<G, F, RW, NW, T1_FWD, 0, GS>), dim3((unsigned)grid), blk, lds,
+                               st, a, tix, (int)store_z, (int)do_loss);
+            break;
+        case T1_DW_BCE:
+            hipLaunchKernelGGL((k_tail_t1<G, F, RW, NW, T1_DW_BCE, 0, GS>), dim3((unsigned)grid), blk,
+                               lds, st, a, tix, 0, (int)do_loss);
+            break;
+        default:
+            hipLaunchKernelGGL((k_tail_t1<G, F, RW, NW, T1_DW_MEM, 0, GS>), dim3((unsigned)grid), blk,
+                               lds, st, a, tix, 0, 0);
+            break;
+        }
+        return hipGetLastError();
+    }
     switch (mode) {
     case T1_FWD:
         if (tk == 2)
@@ -1497,6 +1528,15 @@ hipError_t launch_fanin1_step(const TailArgs &a, bool do_loss, hipStream_t st) {
 
 hipError_t launch_tail_t1(int mode, int G, const TailArgs &a, bool store_z, bool do_loss,
                           hipStream_t st) {
+    // Groups of 64 at F = 128 without a fused top-K: each wave takes a
+    // 32-label slice of a group (8 waves of 256 registers, as for groups of
+    // 32); a whole group per wave needs 512 registers, four waves per
+    // workgroup, too few to hide the chunk loop's latencies.  Measured on the
+    // 670K-label workload (c3 shape): 433 us against 562 us whole-group and
+    // 451 us with 16-label slices (16 waves); groups of 32 kept whole ran
+    // 1,019 us against 1,105 us in 16-label slices on the 3M-label workload.
+    if (a.tk_v == nullptr && G == 64 && a.F == 128)
+        return t1_launch<32, 128, 1, 8, 64>(mode, a, store_z, do_loss, st);
 #define T1CASE(GG, FF, RR, NN) \
     if (G == GG && a.F == FF) return t1_launch<GG, FF, RR, NN>(mode, a, store_z, do_loss, st);
     T1CASE(16, 32, 2, 16)
@@ -2016,9 +2056,15 @@ __host__ __device__ inline T2dLds t2d_layout(int F, int G, int BC2, int NTW32) {
     return L;
 }
 
-template <int G, int BC2, int NTW32>
+// GS: the layer's group size when each unit of work is a slice of G labels of
+// a larger group (GS = G: whole groups).  Unit u is slice u % (GS/G) of group
+// u / (GS/G); its weight rows start at u * G, its index row is its group's.
+template <int G, int BC2, int NTW32, int GS = G>
 __global__ __launch_bounds__(64 * T2D_NW, 1) void k_tail_t2d(TailArgs a, int n_granges) {
     constexpr int NT = 64 * T2D_NW;
+    constexpr int NSL = GS / G, JTS = GS / 16;
+    static_assert(GS % G == 0, "slices of whole label tiles");
+    const int64_t Nu = a.Ng * NSL;
     constexpr int GPI = t2d_gpi(G, BC2, NTW32);
     constexpr int JT = G / 16, RT = BC2 / 32;
     constexpr int GPR = G / 4, LGPR = G == 16 ? 2 : G == 32 ? 3 : 4;
@@ -2042,7 +2088,7 @@ __global__ __launch_bounds__(64 * T2D_NW, 1) void k_tail_t2d(TailArgs a, int n_g
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int gr = blockIdx.x % n_granges, bch = blockIdx.x / n_granges;
-    const int64_t gA = (int64_t)gr * a.Ng / n_granges, gB = (int64_t)(gr + 1) * a.Ng / n_granges;
+    const int64_t gA = (int64_t)gr * Nu / n_granges, gB = (int64_t)(gr + 1) * Nu / n_granges;
     const int ng = (int)(gB - gA);
     const int nsteps = (ng + GPI - 1) / GPI;
     // iterations: a multiple of four, so the builders' loop body (unrolled
@@ -2200,9 +2246,9 @@ __global__ __launch_bounds__(64 * T2D_NW, 1) void k_tail_t2d(TailArgs a, int n_g
         // the group, unit or tile does not exist (the value is then unused):
         // with no load skipped, the compiler can wait for exactly the set it
         // needs instead of for all loads in flight.
-        auto gsafe = [&](int k, int q) {
+        auto gsafe = [&](int k, int q) {   // unit (group slice), clamped
             const int64_t g = gA + (int64_t)k * GPI + q;
-            return g < a.Ng ? g : a.Ng - 1;
+            return g < Nu ? g : Nu - 1;
         };
         auto fetch = [&](int k, Ops &o) {
 #pragma unroll
@@ -2219,13 +2265,14 @@ __global__ __launch_bounds__(64 * T2D_NW, 1) void k_tail_t2d(TailArgs a, int n_g
                 const int e = bth + NB_T * i;
                 const int q = e < GPI * F ? e / F : 0;
                 const int f = e < GPI * F ? e - q * F : 0;
-                o.fi[i] = a.idx[gsafe(k, q) * F + f];
+                o.fi[i] = a.idx[gsafe(k, q) / NSL * F + f];
             }
 #pragma unroll
             for (int t = 0; t < TPB; ++t) {
                 int q, rt, jt;
                 if (!tile_of(t, q, rt, jt)) q = rt = jt = 0;
-                o.dz[t] = *(const u32x4 *)(a.dzt + (((gsafe(k, q) * nch32 + (r0 >> 5) + rt) * JT + jt) << 9) +
+                const int64_t u = gsafe(k, q);
+                o.dz[t] = *(const u32x4 *)(a.dzt + (((u / NSL * nch32 + (r0 >> 5) + rt) * JTS + u % NSL * JT + jt) << 9) +
                                            lane * 8);
             }
         };
@@ -2338,28 +2385,28 @@ static hipError_t t2_pick_ntw(int dz_mode, const TailArgs &a, hipStream_t st) {
     return hipErrorInvalidValue;
 }
 
-template <int G, int BC2, int NTW32>
+template <int G, int BC2, int NTW32, int GS = G>
 static hipError_t t2d_go(const TailArgs &a, hipStream_t st) {
     const int nbch = a.Bp / BC2;
-    const int64_t ngr = t2_granges(nbch, a.Ng);
+    const int64_t ngr = t2_granges(nbch, a.Ng * (GS / G));
     if (ngr < 1) return hipSuccess;
     const T2dLds L = t2d_layout(a.F, G, BC2, NTW32);
     if (L.total > 160 * 1024) return hipErrorInvalidValue;
-    allow_lds((const void *)k_tail_t2d<G, BC2, NTW32>, L.total);
-    hipLaunchKernelGGL((k_tail_t2d<G, BC2, NTW32>), dim3((unsigned)(ngr * nbch)), dim3(64 * T2D_NW),
+    allow_lds((const void *)k_tail_t2d<G, BC2, NTW32, GS>, L.total);
+    hipLaunchKernelGGL((k_tail_t2d<G, BC2, NTW32, GS>), dim3((unsigned)(ngr * nbch)), dim3(64 * T2D_NW),
                        L.total, st, a, (int)ngr);
     return hipGetLastError();
 }
 
-template <int G, int BC2>
+template <int G, int BC2, int GS = G>
 static hipError_t t2d_pick_ntw(const TailArgs &a, hipStream_t st) {
     switch (t2_ntw(a.D, BC2)) {
-    case 1: return t2d_go<G, BC2, 1>(a, st);
-    case 2: return t2d_go<G, BC2, 2>(a, st);
-    case 3: return t2d_go<G, BC2, 3>(a, st);
+    case 1: return t2d_go<G, BC2, 1, GS>(a, st);
+    case 2: return t2d_go<G, BC2, 2, GS>(a, st);
+    case 3: return t2d_go<G, BC2, 3, GS>(a, st);
     }
     if constexpr (BC2 == 32)
-        if (t2_ntw(a.D, BC2) == 4) return t2d_go<G, BC2, 4>(a, st);
+        if (t2_ntw(a.D, BC2) == 4) return t2d_go<G, BC2, 4, GS>(a, st);
     return hipErrorInvalidValue;
 }
 
@@ -2370,6 +2417,14 @@ static hipError_t t2d_pick(const TailArgs &a, hipStream_t st) {
     if constexpr (G < 64)
         if (a.B > 32 && t2_ntw(a.D, 64) <= 3) return t2d_pick_ntw<G, 64>(a, st);
     return t2d_pick_ntw<G, 32>(a, st);
+}
+
+// Groups of GS > 16 as GS/16 slices of 16 labels (each slice its own unit of
+// the dense product, with the operand sets and 64-row chunks of groups of 16)
+template <int GS>
+static hipError_t t2d_pick_sliced(const TailArgs &a, hipStream_t st) {
+    if (a.B > 32 && t2_ntw(a.D, 64) <= 3) return t2d_pick_ntw<16, 64, GS>(a, st);
+    return t2d_pick_ntw<16, 32, GS>(a, st);
 }
 
 // 64-row chunks when they fit in LDS, the batch is larger than 32 rows and
@@ -2397,6 +2452,11 @@ hipError_t launch_tail_t2(int G, int dz_mode, const TailArgs &a, hipStream_t st)
         // against 1.79 ms); at D = 6F it is behind for G = 16, 32 and 64.
         if (G >= 32 && a.D >= 12 * a.F && tail_dxs_supported(G, a.F, a.D))
             return launch_tail_dxs(G, a, st);
+        // Groups of 64 as four slices of 16 labels (measured on the 670K-label
+        // workload with groups of 64: 435-440 us against 479-486 us with whole
+        // groups in 32-row chunks); groups of 32 stay whole (the same either
+        // way on the 3M-label workload)
+        if (G == 64) return t2d_pick_sliced<64>(a, st);
         switch (G) {
         case 16: return t2d_pick<16>(a, st);
         case 32: return t2d_pick<32>(a, st);
