@@ -15,6 +15,7 @@ CASES = [
     dict(B=40, D=96, H=48, L=200, G=16, F=32, K=5),
     dict(B=33, D=128, H=64, L=70000, G=64, F=64, K=5),     # three buckets of the tail
     dict(B=70, D=200, H=56, L=300, G=32, F=128, K=8),
+    dict(B=50, D=256, H=64, L=5000, G=64, F=128, K=5),     # groups of 64 in two label slices
     dict(B=17, D=64, H=40, L=3, G=16, F=32, K=5),           # fewer tail labels than K
     dict(B=9, D=64, H=64, L=1024, G=16, F=16, K=1, dtype="f32"),
 ]
