@@ -2020,12 +2020,20 @@ __global__ __launch_bounds__(64 * T2_NW, 1) void k_tail_t2(TailArgs a, int dz_mo
                 unit(i, q, fc, ja);
                 if (bth + NB_T * i >= (GPI << lnq) || !live(k, q)) continue;
                 unsigned char *wt = wts + q * LY.wts_grp + (4 * fc) * WTS + 8 * ja;
+                // rows of labels past L (a ragged last group) go in as zeros:
+                // their dz is zero, and 0 times whatever the caller left in
+                // those rows (NaN included) must not reach dX.  Masks on the
+                // permuted words (label 4ja + e in half e % 2 of word e / 2),
+                // so no loaded register is rewritten before its use
+                const int64_t lab0 = (gA + (int64_t)k * GPI + q) * G + 4 * ja;
+                const unsigned m01 = (lab0 < a.L ? 0x0000ffffu : 0u) | (lab0 + 1 < a.L ? 0xffff0000u : 0u);
+                const unsigned m23 = (lab0 + 2 < a.L ? 0x0000ffffu : 0u) | (lab0 + 3 < a.L ? 0xffff0000u : 0u);
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {   // feature 4fc+kk: element kk of each row
                     const unsigned sel = (kk & 1) ? 0x07060302u : 0x05040100u;
                     const int wd = kk >> 1;
-                    const u32x2 v = {__builtin_amdgcn_perm(o.r[i][1][wd], o.r[i][0][wd], sel),
-                                     __builtin_amdgcn_perm(o.r[i][3][wd], o.r[i][2][wd], sel)};
+                    const u32x2 v = {__builtin_amdgcn_perm(o.r[i][1][wd], o.r[i][0][wd], sel) & m01,
+                                     __builtin_amdgcn_perm(o.r[i][3][wd], o.r[i][2][wd], sel) & m23};
                     *(u32x2 *)(wt + kk * WTS) = v;
                 }
             }
@@ -2330,12 +2338,20 @@ __global__ __launch_bounds__(64 * T2D_NW, 1) void k_tail_t2d(TailArgs a, int n_g
                 unit(i, q, fc, ja);
                 if (bth + NB_T * i >= (GPI << lnq) || !live(k, q)) continue;
                 unsigned char *wt = wts + q * LY.wts_grp + (4 * fc) * WTS + 8 * ja;
+                // rows of labels past L (a ragged last group) go in as zeros:
+                // their dz is zero, and 0 times whatever the caller left in
+                // those rows (NaN included) must not reach dX.  Masks on the
+                // permuted words (label 4ja + e in half e % 2 of word e / 2),
+                // so no loaded register is rewritten before its use
+                const int64_t lab0 = (gA + (int64_t)k * GPI + q) * G + 4 * ja;
+                const unsigned m01 = (lab0 < a.L ? 0x0000ffffu : 0u) | (lab0 + 1 < a.L ? 0xffff0000u : 0u);
+                const unsigned m23 = (lab0 + 2 < a.L ? 0x0000ffffu : 0u) | (lab0 + 3 < a.L ? 0xffff0000u : 0u);
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {   // feature 4fc+kk: element kk of each row
                     const unsigned sel = (kk & 1) ? 0x07060302u : 0x05040100u;
                     const int wd = kk >> 1;
-                    const u32x2 v = {__builtin_amdgcn_perm(o.r[i][1][wd], o.r[i][0][wd], sel),
-                                     __builtin_amdgcn_perm(o.r[i][3][wd], o.r[i][2][wd], sel)};
+                    const u32x2 v = {__builtin_amdgcn_perm(o.r[i][1][wd], o.r[i][0][wd], sel) & m01,
+                                     __builtin_amdgcn_perm(o.r[i][3][wd], o.r[i][2][wd], sel) & m23};
                     *(u32x2 *)(wt + kk * WTS) = v;
                 }
             }

@@ -439,3 +439,43 @@ def test_mfma_probe_runs(H):
     torch.cuda.synchronize()
     assert flops == 8 * 4 * 4 * 16 * (16 * 16 * 32 * 2)
     assert sink.item() == 0.0
+
+
+@pytest.mark.parametrize("case", [dict(B=70, D=200, H=56, L=300, G=64, F=128),
+                                  dict(B=40, D=96, H=48, L=200, G=16, F=32),
+                                  dict(B=33, D=1024, H=96, L=700, G=64, F=64)],
+                         ids=["G64-F128-dense", "G16-F32-dense", "G64-F64-scatter"])
+def test_padded_weight_rows_never_reach_a_result(H, case):
+    """Rows of W past L (the padding of a ragged last group) are never read
+    for a result: filled with NaN, they must leave the loss, logits, dW of
+    the live rows and dX as the oracle has them, in every form of the dX pass
+    (dense from the tiles, lean, scatter) and through the exact top-K."""
+    print("case", case, flush=True)
+    inp = wl.make_inputs(wl.tiny("pad", **case))
+    c = inp.cfg
+    assert c.L % c.G != 0
+    s = 1.0 / c.B
+    r = _ref(inp)
+    d = Dev(inp)
+    d.W[c.L:] = float("nan")
+    ng = c.n_groups
+    for lean in (False, True):
+        dW = torch.empty_like(d.W)
+        dX = torch.empty(c.B, c.D, dtype=torch.float32, device=DEV)
+        b = d.bce(c.H, s)
+        H.haste_tail_step(d.X, d.idx, d.W, c.L, c.G, b, dW, dX, lean=lean)
+        torch.cuda.synchronize()
+        check_loss(f"padded-NaN step loss (lean={lean})", b.loss.item(), r.loss_tail, "bf16")
+        check(f"padded-NaN dW (lean={lean})", to_f64(dW[:c.L]), r.dWt, r.dWt_abs, "bf16", nterms=c.B)
+        assert torch.all(dW[c.L:] == 0)
+        check(f"padded-NaN dX (lean={lean})", to_f64(dX), r.dX_tail, r.dX_tail_abs, "bf16",
+              nterms=ng * c.G)
+    Z = torch.empty(c.B, c.L, dtype=torch.bfloat16, device=DEV)
+    b = d.bce(c.H, s)
+    b.topk_val = torch.empty(c.B, 5, dtype=torch.float32, device=DEV)
+    b.topk_idx = torch.empty(c.B, 5, dtype=torch.int32, device=DEV)
+    H.haste_tail_fwd(d.X, d.idx, d.W, c.L, c.G, Z=Z, bce=b)
+    torch.cuda.synchronize()
+    check("padded-NaN Z", to_f64(Z), r.Zt, r.Zt_abs, "bf16", nterms=c.F)
+    assert torch.all(torch.isfinite(b.topk_val))
+    assert int(b.topk_idx.min()) >= c.H and int(b.topk_idx.max()) < c.H + c.L
