@@ -362,7 +362,11 @@ def run_dense(args, cfg, inp, t_gen):
     labels, (B x F) . (F x L), on the dense kernels of this library (the
     head's GEMMs with D = F, H = L): forward with the same sigmoid-BCE over
     the same positives, forward storing the logits (no BCE), and training
-    step.  Inputs of the bottleneck: x ~ N(0, 1), W ~ N(0, 0.02), bf16."""
+    step.  The bottleneck also runs on this layer's own tail kernels with
+    D = F and every group's index set the identity (the layer reduces to the
+    dense (B x F)(F x L) product there): the same sigmoid-BCE, logits and
+    training step.  Inputs of the bottleneck: x ~ N(0, 1), W ~ N(0, 0.02),
+    bf16."""
     import numpy as np
     import torch
 
@@ -400,6 +404,13 @@ def run_dense(args, cfg, inp, t_gen):
     dW1 = torch.empty(L, F, dtype=torch.bfloat16, device=dev)
     Zs = torch.empty(B, L, dtype=torch.bfloat16, device=dev)
     Zd = torch.empty(B, L, dtype=torch.bfloat16, device=dev)
+    # the bottleneck through the tail's kernels: D = F, identity index sets
+    ngb = (L + G - 1) // G
+    idx_id = torch.arange(F, dtype=torch.int32, device=dev).repeat(ngb, 1).contiguous()
+    Wbt = torch.zeros(ngb * G, F, dtype=torch.bfloat16, device=dev)
+    Wbt[:L] = Wb
+    ws_dt = torch.empty(H.haste_tail_workspace_bytes(Xb, idx_id, L, G, bt), dtype=torch.uint8, device=dev)
+    dWbt = torch.empty_like(Wbt)
     calls = {
         "fanin1_fwd": lambda: H.haste_tail_fwd(X, idx1, W, L, 1, bce=bt, workspace=ws_1),
         "fanin1_step": lambda: H.haste_tail_step(X, idx1, W, L, 1, bt, dW1, dX, workspace=ws_1),
@@ -411,6 +422,11 @@ def run_dense(args, cfg, inp, t_gen):
                                 H.haste_tail_step_dw(X, idx, W, L, G, bt, dW, ws_t),
                                 H.haste_tail_step_dx(X, idx, W, L, G, bt, dX, ws_t)),
         "dense_step": lambda: H.haste_head_step(Xb, Wb, bt, dWb, dXb, workspace=ws_d),
+        "dense_tail_fwd": lambda: H.haste_tail_fwd(Xb, idx_id, Wbt, L, G, bce=bt, workspace=ws_dt),
+        "dense_tail_fwd_z": lambda: H.haste_tail_fwd(Xb, idx_id, Wbt, L, G, Z=Zd, workspace=ws_dt),
+        "dense_tail_step": lambda: (H.haste_tail_prepare(Xb, idx_id, L, G, bt, ws_dt),
+                                    H.haste_tail_step_dw(Xb, idx_id, Wbt, L, G, bt, dWbt, ws_dt),
+                                    H.haste_tail_step_dx(Xb, idx_id, Wbt, L, G, bt, dXb, ws_dt)),
     }
     res = {}
     for name, fn in calls.items():
@@ -439,12 +455,16 @@ def run_dense(args, cfg, inp, t_gen):
         "sparse_over_dense_time": {"fwd": round(res["sparse_fwd"] / res["dense_fwd"], 3),
                                    "fwd_z": round(res["sparse_fwd_z"] / res["dense_fwd_z"], 3),
                                    "step": round(res["sparse_step"] / res["dense_step"], 3)},
+        "sparse_over_dense_tail_kernels_time": {
+            "fwd": round(res["sparse_fwd"] / res["dense_tail_fwd"], 3),
+            "fwd_z": round(res["sparse_fwd_z"] / res["dense_tail_fwd_z"], 3),
+            "step": round(res["sparse_step"] / res["dense_tail_step"], 3)},
         "fanin1_over_sparse_time": {"fwd": round(res["fanin1_fwd"] / res["sparse_fwd"], 3),
                                     "step": round(res["fanin1_step"] / res["sparse_step"], 3),
                                     "bwd": round((res["fanin1_step"] - res["fanin1_fwd"])
                                                  / (res["sparse_step"] - res["sparse_fwd"]), 3)},
         "z_store_gbs": {k: round(B * L * 2 / (res[k] * 1e-6) / 1e9, 1)
-                        for k in ("sparse_fwd_z", "dense_fwd_z")},
+                        for k in ("sparse_fwd_z", "dense_fwd_z", "dense_tail_fwd_z")},
         "gen_s": round(t_gen, 2),
     }
     print(json.dumps(out), flush=True)
