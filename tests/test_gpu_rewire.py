@@ -54,6 +54,7 @@ def _run(idx, W32, cand, D, L, G, k, dtype, inplace=False):
     (64, 32, 200, 130, 32, 10, "f32"),     # prune everything
     (3, 20, 50, 17, 0, 5, "f32"),          # k = 0: unchanged
     (16, 48, 70000 // 1000, 64, 7, 70, "f32"),
+    (3, 20, 50, 17, 4, 9, "bf16"),         # rows of 40 bytes: weights moved element by element
 ])
 def test_rewire_matches_oracle_bit_exact(G, F, D, L, k, R, dtype):
     idx, W32, cand = _case(G, F, D, L, k, R, dtype, seed=G + F + k)
