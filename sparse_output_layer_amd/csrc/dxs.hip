@@ -16,9 +16,9 @@
 // labels, lane (q, m) of that pass holding label m, rows 4q..4q+3 and
 // 16+4q..16+4q+3).
 //
-// Workgroup: 4 waves, one per SIMD.  Wave w = 2t + h takes rows 16t..16t+15 of
-// the chunk and the feature half h of every group, so within a group the four
-// waves touch disjoint (row, feature) cells; one barrier per group keeps the
+// Workgroup: 4 waves (F = 32) or 8 (F >= 64: two per SIMD).  Wave w = P t + h,
+// P = waves / 2, takes rows 16t..16t+15 of the chunk and the feature part h of
+// every group, so within a group the waves touch disjoint (row, feature) cells; one barrier per group keeps the
 // groups apart (two groups may share features).  The barrier also hands over
 // a two-stage ring of operands that direct global->LDS copies fill one group
 // ahead: the group's dz tiles and W_g (16-byte pieces permuted on the way so
@@ -32,10 +32,12 @@
 
 namespace haste {
 
-constexpr int DXS_NW = 4;      // waves per workgroup
 constexpr int DXS_R = 32;      // rows per chunk (one dz tile row block)
 
-template <int G, int F>
+// waves per workgroup: two row halves x NW/2 feature parts of 16-feature tiles
+__host__ __device__ constexpr int dxs_nw(int F) { return F >= 64 ? 8 : 4; }
+
+template <int G, int F, int NW = dxs_nw(F)>
 struct DxsShape {
     static constexpr int JT = G / 16;                // dz tiles per group and chunk
     static constexpr int DZB = JT * 1024;            // their bytes
@@ -43,11 +45,12 @@ struct DxsShape {
     static constexpr int IXB = F * 4;                // idx_g bytes
     static constexpr int STAGE = DZB + WB + IXB;     // one stage: dz tiles, W_g, idx_g
     static constexpr int NP = STAGE / 16;            // its 16-byte pieces
-    static constexpr int NPW = (NP + 255) / 256;     // pieces per lane (4 waves of 64 lanes)
+    static constexpr int NPW = (NP + 64 * NW - 1) / (64 * NW);   // pieces per lane
     // groups in flight from global memory: a register ring of DPF * NPW * 4
     // VGPRs, at most 128 of a wave's 256
     static constexpr int DPF = 32 / NPW > 8 ? 8 : 32 / NPW;
-    static constexpr int FTW = F / 32;               // 16-feature tiles per wave
+    static constexpr int NFP = NW / 2;               // feature parts
+    static constexpr int FTW = F / 16 / NFP;         // 16-feature tiles per wave
     static constexpr int KS = G >= 32 ? G / 32 : 1;  // K steps of 32 labels (G = 16: one K = 16 step)
     static constexpr int QB = G >= 32 ? 3 : 2;       // label bit that tells the paired lane blocks apart
     static constexpr int P = F / 8;                  // 16-byte pieces per W_g row
@@ -82,8 +85,9 @@ __device__ __forceinline__ int dxs_tile_off(int d, int slot) {
 }
 
 template <int G, int F>
-__global__ __launch_bounds__(64 * DXS_NW, 1) void k_tail_dxs(TailArgs a, int nrc, int ngr) {
+__global__ __launch_bounds__(64 * dxs_nw(F), 1) void k_tail_dxs(TailArgs a, int nrc, int ngr) {
     using S = DxsShape<G, F>;
+    constexpr int DXS_NW = dxs_nw(F);
     constexpr int FTW = S::FTW, KS = S::KS, QB = S::QB, NPW = S::NPW;
     constexpr int DPF = S::DPF;
     // the two stages are distinct LDS objects, each named statically in every
@@ -95,7 +99,7 @@ __global__ __launch_bounds__(64 * DXS_NW, 1) void k_tail_dxs(TailArgs a, int nrc
     const int lane = threadIdx.x & 63;
     const int wu = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int q = lane >> 4, m = lane & 15;
-    const int t = wu >> 1, hf = wu & 1;
+    const int t = wu / S::NFP, hf = wu % S::NFP;
     // block -> (row chunk, group range); blocks b, b + 8, ... share an XCD, and
     // the nrc row chunks of one group range are among them, so W_g comes from
     // HBM once and from that XCD's L2 for the others
@@ -306,7 +310,7 @@ static hipError_t dxs_go(const TailArgs &a, hipStream_t st) {
     ngr = (ngr + 7) / 8 * 8;
     const size_t dyn = (size_t)a.D * DXS_R * 4;
     dxs_allow_lds((const void *)k_tail_dxs<G, F>, dyn);
-    hipLaunchKernelGGL((k_tail_dxs<G, F>), dim3((unsigned)(nrc * ngr)), dim3(64 * DXS_NW), dyn, st, a, nrc, ngr);
+    hipLaunchKernelGGL((k_tail_dxs<G, F>), dim3((unsigned)(nrc * ngr)), dim3(64 * dxs_nw(F)), dyn, st, a, nrc, ngr);
     return hipGetLastError();
 }
 
