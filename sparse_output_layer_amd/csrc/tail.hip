@@ -567,8 +567,14 @@ __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, T1Tickets ti
                                             : Nu;
         bf16x8 wreg[RW][KS][JT];
         u32x2 pwz[DO_Z ? RW : 1][KS];     // perm bytes of positions 32s + 8q .. + 7
-        unsigned zrow[RW][KS];            // tr-gather rows: lo16 = h 0, hi16 = h 1
-        unsigned frow[RW][FT / 2];        // dW rows, two f-tiles per word
+        // LDS byte offsets within a chunk buffer, fixed for a run: the two
+        // transposing gathers of each K step (this lane's column included),
+        // and the two 8-byte halves of each dW operand row.  The second half's
+        // offset is made opaque here, so the compiler neither fuses the two
+        // reads into one paired read (about twice the LDS cycles) nor spends
+        // instructions per chunk on keeping them apart.
+        unsigned zoff[RW][KS][2];
+        unsigned dwo[RW][FT][2];
         int gp0[RW], pn[RW], pe[RW];      // positives per group: first, count, entry per lane
         int pc[RW];                       // next positive of the group not yet below the chunk
         f32x4 dwacc[RW][FT][JT];
@@ -584,12 +590,16 @@ __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, T1Tickets ti
             for (int s = 0; s < KS; ++s) {
                 const unsigned lo = (unsigned)ix[32 * s + 8 * q + (m >> 2)];
                 const unsigned hi = (unsigned)ix[32 * s + 8 * q + 4 + (m >> 2)];
-                zrow[r][s] = lo | (hi << 16);
+                zoff[r][s][0] = (lo * BCP + 4 * (m & 3)) * 2u;
+                zoff[r][s][1] = (hi * BCP + 4 * (m & 3)) * 2u;
                 if (DO_Z) pwz[r][s] = *(const u32x2 *)(a.perm + gs * F + 32 * s + 8 * q);
             }
 #pragma unroll
-            for (int p = 0; p < FT / 2; ++p)
-                frow[r][p] = (unsigned)ix[32 * p + m] | ((unsigned)ix[32 * p + 16 + m] << 16);
+            for (int ft = 0; ft < FT; ++ft) {
+                dwo[r][ft][0] = ((unsigned)ix[16 * ft + m] * BCP + 4 * q) * 2u;
+                dwo[r][ft][1] = dwo[r][ft][0] + 32u;
+                asm volatile("" : "+v"(dwo[r][ft][1]));
+            }
             gp0[r] = pn[r] = pe[r] = pc[r] = 0;
             if (need_pos && ok) {
                 gp0[r] = __builtin_amdgcn_readfirstlane(a.grp_ptr[g]);
@@ -652,12 +662,11 @@ __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, T1Tickets ti
                 if (DO_Z) {
 #pragma unroll
                     for (int s = 0; s < KS; ++s) {
-                        const unsigned rlo = zrow[r][s] & 0xffffu, rhi = zrow[r][s] >> 16;
 #pragma unroll
                         for (int h2 = 0; h2 < 2; ++h2) {
-                            const int col = 16 * h2 + 4 * (m & 3);
-                            i16x4 a0 = lds_read_tr(tile + rlo * BCP + col);
-                            i16x4 a1 = lds_read_tr(tile + rhi * BCP + col);
+                            const char *tb = (const char *)tile + 32 * h2;
+                            i16x4 a0 = lds_read_tr(tb + zoff[r][s][0]);
+                            i16x4 a1 = lds_read_tr(tb + zoff[r][s][1]);
                             bf16x8 A = __builtin_bit_cast(
                                 bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
@@ -937,15 +946,8 @@ __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, T1Tickets ti
                             __builtin_nontemporal_store(v, (u32x4 *)(a.dzt + ((((int64_t)g * nch + ch) * JTS + JT * sl + jt) << 9) + lane * 8));
                     }
                     auto dw_read = [&](int ft) {
-                        const unsigned row =
-                            (ft & 1) ? (frow[r][ft >> 1] >> 16) : (frow[r][ft >> 1] & 0xffffu);
-                        // two separate 8-byte reads: fused into one paired read
-                        // (ds_read2_b64) they take about twice the LDS cycles
-                        const unsigned o_lo = row * BCP + 4 * q;
-                        unsigned o_hi = o_lo + 16;
-                        asm volatile("" : "+v"(o_hi));
-                        u32x2 lo = *(const u32x2 *)(tile + o_lo);
-                        u32x2 hi = *(const u32x2 *)(tile + o_hi);
+                        u32x2 lo = *(const u32x2 *)((const char *)tile + dwo[r][ft][0]);
+                        u32x2 hi = *(const u32x2 *)((const char *)tile + dwo[r][ft][1]);
                         u32x4 v = {lo.x, lo.y, hi.x, hi.y};
                         return __builtin_bit_cast(bf16x8, v);
                     };
