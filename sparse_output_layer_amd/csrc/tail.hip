@@ -562,8 +562,10 @@ __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, T1Tickets ti
     int *const s_ticket = (int *)(buf1 + 32);
     for (int64_t run = blockIdx.x; run < tix.n_tickets;) {
         // first group of this wave; a.Ng (no group) for the idle waves of a small ticket
-        const int64_t gw = run < tix.n_full ? (run * NW + w) * RW
-                           : w < tix.k      ? (tix.n_full * NW + (run - tix.n_full) * tix.k + w) * RW
+        // (wave-uniform: from the scalar wave index, so the group's
+        // addresses are formed in scalar registers)
+        const int64_t gw = run < tix.n_full ? (run * NW + wu) * RW
+                           : wu < tix.k     ? (tix.n_full * NW + (run - tix.n_full) * tix.k + wu) * RW
                                             : Nu;
         bf16x8 wreg[RW][KS][JT];
         u32x2 pwz[DO_Z ? RW : 1][KS];     // perm bytes of positions 32s + 8q .. + 7
@@ -1058,7 +1060,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, T1Tickets ti
         if (a.sched) {
             if (threadIdx.x == 0) *s_ticket = (int)gridDim.x + (int)atomicAdd(a.sched, 1u);
             __syncthreads();
-            run = *s_ticket;
+            run = __builtin_amdgcn_readfirstlane(*s_ticket);
         } else {
             run += gridDim.x;
         }
