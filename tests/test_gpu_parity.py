@@ -441,6 +441,48 @@ def test_mfma_probe_runs(H):
     assert sink.item() == 0.0
 
 
+@pytest.mark.parametrize("case", [dict(B=37, D=100, H=40, L=300, G=16, F=32),
+                                  dict(B=70, D=203, H=40, L=500, G=64, F=64)],
+                         ids=["D100-G16", "D203-G64"])
+def test_feature_count_not_a_multiple_of_eight(H, case):
+    """The tail alone (the bf16 head takes D in multiples of 8 only) on rows of
+    X that are not whole 16-byte pieces, and a feature count that is not a
+    whole number of the dX kernels' feature tiles.  Forward, one-call step
+    and the split step."""
+    print("case odd D", case, flush=True)
+    inp = wl.make_inputs(wl.tiny("odd", **case))
+    c = inp.cfg
+    s = 1.0 / c.B
+    r = _ref(inp)
+    d = Dev(inp)
+    ng = c.n_groups
+    Z = torch.empty(c.B, c.L, dtype=torch.bfloat16, device=DEV)
+    b = d.bce(c.H, s)
+    H.haste_tail_fwd(d.X, d.idx, d.W, c.L, c.G, Z=Z, bce=b)
+    torch.cuda.synchronize()
+    check("odd-D tail Z", to_f64(Z), r.Zt, r.Zt_abs, "bf16", nterms=c.F)
+    check_loss("odd-D tail fwd loss", b.loss.item(), r.loss_tail, "bf16")
+    dW = torch.empty_like(d.W)
+    dX = torch.empty((c.B, c.D), dtype=torch.float32, device=DEV)
+    b = d.bce(c.H, s)
+    H.haste_tail_step(d.X, d.idx, d.W, c.L, c.G, b, dW, dX)
+    torch.cuda.synchronize()
+    check_loss("odd-D step loss", b.loss.item(), r.loss_tail, "bf16")
+    check("odd-D dW", to_f64(dW[:c.L]), r.dWt, r.dWt_abs, "bf16", nterms=c.B)
+    check("odd-D dX", to_f64(dX), r.dX_tail, r.dX_tail_abs, "bf16", nterms=ng * c.G)
+    b5 = d.bce(c.H, s)
+    ws = torch.empty(H.haste_tail_workspace_bytes(d.X, d.idx, c.L, c.G, b5), dtype=torch.uint8,
+                     device=DEV)
+    dW5 = torch.empty_like(d.W)
+    dX5 = torch.zeros_like(dX)
+    H.haste_tail_prepare(d.X, d.idx, c.L, c.G, b5, ws)
+    H.haste_tail_step_dw(d.X, d.idx, d.W, c.L, c.G, b5, dW5, ws)
+    H.haste_tail_step_dx(d.X, d.idx, d.W, c.L, c.G, b5, dX5, ws, accumulate_dX=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dW5, dW)
+    check("odd-D split dX", to_f64(dX5), r.dX_tail, r.dX_tail_abs, "bf16", nterms=ng * c.G)
+
+
 @pytest.mark.parametrize("case", [dict(B=70, D=200, H=56, L=300, G=64, F=128),
                                   dict(B=40, D=96, H=48, L=200, G=16, F=32),
                                   dict(B=33, D=1024, H=96, L=700, G=64, F=64)],
