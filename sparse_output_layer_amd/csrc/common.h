@@ -89,7 +89,7 @@ __device__ __forceinline__ BceOut bce_both(float z, float y, float s) {
 // v_log_f32, about 1 ulp each).  sigmoid(z) from e = exp(-|z|):
 // r = 1/(1+e) is sigmoid(|z|); sigmoid(z) = r for z >= 0, 1 - r otherwise.
 // softplus(z) = max(z,0) + log(1+e); the log of a product of (1+e) factors
-// (each in [1, 2]) replaces one log per logit.
+// (each in [1, 2]) replaces one log per logit (prod1p, log1p_pos below).
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -103,6 +103,18 @@ __device__ __forceinline__ float fast_sigmoid(float z, float e, float &den) {
 }
 __device__ __forceinline__ float fast_log(float x) {
     return __builtin_amdgcn_logf(x) * kLn2;
+}
+// Products of (1 + e) factors are kept as q = product - 1: the small e of a
+// large |z| would otherwise be rounded away against the 1 (an absolute error
+// of 2^-24 on a term of size e), which dominates the loss when most logits
+// are far below zero.  (1 + q)(1 + t) - 1 = q + t + q*t:
+__device__ __forceinline__ float prod1p(float q, float t) { return __builtin_fmaf(q, t, q + t); }
+// log(1 + q) for q >= 0 within a few ulps: with u = 1 + q rounded,
+// log(u) * q / (u - 1) cancels the rounding of u (exact q when u = 1)
+__device__ __forceinline__ float log1p_pos(float q) {
+    const float u = 1.0f + q;
+    const float d = u - 1.0f;
+    return d == 0.f ? q : fast_log(u) * (q * __builtin_amdgcn_rcpf(d));
 }
 
 // Workgroup barrier that waits only for this wave's LDS operations.  Global

@@ -388,9 +388,9 @@ __global__ __launch_bounds__(256, 2) void k_gemm2(GemmArgs g) {
     // epilogue: lane owns C[m0+wm+16i+4q+e][n0+wn+16j+m].  BCE with the
     // hardware exp / rcp / log: sigmoid(z) from e = exp(-|z|), and
     // softplus(z) = max(z, 0) + log(1 + e), the logs taken of products of
-    // sixteen (1 + e) factors (each in [1, 2]).  Whole tiles take a path with
-    // no per-element branches.
-    float lsum = 0.f, lin = 0.f, prod = 1.f;
+    // sixteen (1 + e) factors (each in [1, 2]), kept as product - 1.  Whole
+    // tiles take a path with no per-element branches.
+    float lsum = 0.f, lin = 0.f, prod = 0.f;
     uint32_t bw[MI][4][2];   // bitmap words of the lane's rows: columns wn .. wn+31, wn+32 .. wn+63
     if (EPI == EPI_BCE) {
 #pragma unroll
@@ -416,13 +416,13 @@ __global__ __launch_bounds__(256, 2) void k_gemm2(GemmArgs g) {
                     const float ex = fast_exp_neg_abs(v);
                     float den;
                     const float sg = fast_sigmoid(v, ex, den);
-                    prod *= den;
+                    prod = prod1p(prod, ex);
                     lin += fmaxf(v, 0.f) - y * v;
                     g.dZout[(int64_t)row * g.N + col] = f32_to_bf16(g.s * (sg - y));
                 }
             }
-            lsum += fast_log(prod);
-            prod = 1.f;
+            lsum += log1p_pos(prod);
+            prod = 0.f;
         }
     } else if (EPI != EPI_BCE && whole) {
 #pragma unroll
@@ -455,7 +455,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm2(GemmArgs g) {
                             const float ex = fast_exp_neg_abs(v);
                             float den;
                             const float sg = fast_sigmoid(v, ex, den);
-                            prod *= den;
+                            prod = prod1p(prod, ex);
                             lin += fmaxf(v, 0.f) - y * v;
                             if (g.dZout) g.dZout[o] = f32_to_bf16(g.s * (sg - y));
                         }
@@ -469,8 +469,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm2(GemmArgs g) {
                 }
             }
             if (EPI == EPI_BCE) {   // sixteen factors per i
-                lsum += fast_log(prod);
-                prod = 1.f;
+                lsum += log1p_pos(prod);
+                prod = 0.f;
             }
         }
     }

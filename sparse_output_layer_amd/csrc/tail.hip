@@ -501,7 +501,7 @@ __host__ inline T1Tickets t1_tickets(int64_t Ng, int RW, int NW, int ncu) {
     return t;
 }
 
-// Whether every logit of the wave's chunk tile has |z| <= 10 (wave-uniform)
+// Whether every logit of the wave's chunk tile has |z| <= 2 (wave-uniform)
 template <int JT>
 __device__ __forceinline__ bool t1_small_logits(const f32x4 (&zacc)[2][JT]) {
     float mz = 0.f;
@@ -511,7 +511,7 @@ __device__ __forceinline__ bool t1_small_logits(const f32x4 (&zacc)[2][JT]) {
         for (int jt = 0; jt < JT; ++jt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) mz = fmaxf(mz, fabsf(zacc[h2][jt][i]));
-    return __all(mz <= 10.0f);
+    return __all(mz <= 2.0f);
 }
 
 // TK: the fused top-K stage 1 (one bucket per group, K' = 1) is compiled in:
@@ -693,10 +693,11 @@ __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, T1Tickets ti
                     }
                 } else if (MODE != T1_DW_MEM && tile_live && !has_pos && !(MODE == T1_FWD && store_z) &&
                            t1_small_logits<JT>(zacc)) {
-                    // fastest path: as below, and every |z| <= 10 in the wave, so
+                    // fastest path: as below, and every |z| <= 2 in the wave, so
                     // t = e^-z needs no sign split: s*sigmoid(z) = s / (1 + t), and
-                    // softplus(z) = z + log(1 + t) with eight factors 1 + t <= e^10.03
-                    // a product (below 2^116)
+                    // softplus(z) = z + log(1 + t) with eight factors 1 + t <= 8.4
+                    // a product (below 2^25); the sum of z and the log cancel to
+                    // at most 2e-6 of the terms' value at |z| <= 2
                     float sumz = 0.f, logs = 0.f;
 #pragma unroll
                     for (int jt = 0; jt < JT; ++jt) {
@@ -726,8 +727,9 @@ __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, T1Tickets ti
                     if (do_loss) lsum += a.s * (sumz + logs);
                 } else if (MODE != T1_DW_MEM && tile_live && !has_pos && !(MODE == T1_FWD && store_z)) {
                     // fast path: every element live, no positive, no logits to store;
-                    // lin2 = sum of z + |z| = twice the sum of max(z, 0), exactly
-                    float lin2 = 0.f, prod = 1.f;
+                    // lin2 = sum of z + |z| = twice the sum of max(z, 0), exactly;
+                    // the (1 + e) factors' product kept as product - 1
+                    float lin2 = 0.f, prod = 0.f;
                     const float hs = 0.5f * a.s;
 #pragma unroll
                     for (int h2 = 0; h2 < 2; ++h2)
@@ -739,10 +741,10 @@ __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, T1Tickets ti
                                 // r = 1/(1 + exp(-|z|)) is sigmoid(|z|); s*sigmoid(z)
                                 // = s/2 + sign(z) * (s*r - s/2)
                                 const float z = zacc[h2][jt][i];
-                                const float den = 1.0f + fast_exp_neg_abs(z);
-                                const float r = __builtin_amdgcn_rcpf(den);
+                                const float e = fast_exp_neg_abs(z);
+                                const float r = __builtin_amdgcn_rcpf(1.0f + e);
                                 dzv[i] = hs + __builtin_copysignf(__builtin_fmaf(a.s, r, -hs), z);
-                                prod *= den;
+                                prod = prod1p(prod, e);
                                 lin2 += z + fabsf(z);
                             }
                             dzp[h2][jt][0] = pack_bf16x2(dzv[0], dzv[1]);
@@ -755,7 +757,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, T1Tickets ti
                             }
                         }
                     // at most 8*JT <= 32 factors in [1, 2]: the product stays below 2^32
-                    if (do_loss) lsum += a.s * (0.5f * lin2 + fast_log(prod));
+                    if (do_loss) lsum += a.s * (0.5f * lin2 + log1p_pos(prod));
                 } else {
 #pragma unroll
                     for (int h2 = 0; h2 < 2; ++h2)
@@ -779,7 +781,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_tail_t1(TailArgs a, T1Tickets ti
                                         float den;
                                         dz = a.s * (fast_sigmoid(z, e, den) - y);
                                         if (do_loss)
-                                            lsum += a.s * ((fmaxf(z, 0.f) - y * z) + fast_log(den));
+                                            lsum += a.s * ((fmaxf(z, 0.f) - y * z) + log1p_pos(e));
                                     }
                                     if (MODE == T1_FWD && store_z && live)
                                         a.Z[(int64_t)row * a.L + t] = f32_to_bf16(z);
@@ -1243,8 +1245,7 @@ __global__ __launch_bounds__(64 * FF_NW, 1) void k_fanin1_fwd(TailArgs a, int st
                 if (do_loss) {
                     float y = 0.f;
                     for (int e = p0[k]; e < p1[k]; ++e) y = a.grp_ent[e] == row ? 1.f : y;
-                    const float den = 1.0f + fast_exp_neg_abs(z[k][i]);
-                    lsum += a.s * ((fmaxf(z[k][i], 0.f) - y * z[k][i]) + fast_log(den));
+                    lsum += a.s * ((fmaxf(z[k][i], 0.f) - y * z[k][i]) + log1p_pos(fast_exp_neg_abs(z[k][i])));
                 }
             }
         }
@@ -1360,7 +1361,7 @@ __global__ __launch_bounds__(64 * FF_NW, 1) void k_fanin1_step(TailArgs a, int d
                 const float ex = fast_exp_neg_abs(z);
                 float den;
                 dz[i] = a.s * (fast_sigmoid(z, ex, den) - y);
-                if (do_loss) lsum += a.s * ((fmaxf(z, 0.f) - y * z) + fast_log(den));
+                if (do_loss) lsum += a.s * ((fmaxf(z, 0.f) - y * z) + log1p_pos(ex));
             }
         }
         *(float2 *)&dzl[wu][qd][2 * rp] = make_float2(dz[0], dz[1]);

@@ -441,6 +441,60 @@ def test_mfma_probe_runs(H):
     assert sink.item() == 0.0
 
 
+def _far_below_zero(case, zmean=-15.0):
+    """A workload whose every logit lies far below zero (about zmean): X
+    shifted positive, all weights negative.  No positives, so the loss is a
+    sum of tiny softplus terms, each about e^zmean."""
+    inp = wl.make_inputs(wl.tiny("neg", pos_per_row=0, **case))
+    c = inp.cfg
+    x = np.abs(wl.f64_from_bf16_bits(inp.X)) + 0.5
+    inp.X = wl.bf16_bits_from_f32(x.astype(np.float32))
+    ex = float(np.mean(wl.f64_from_bf16_bits(inp.X)))
+    for name, n in (("W", c.F), ("Wh", c.D)):
+        w = wl.f64_from_bf16_bits(getattr(inp, name))
+        w = -(1.0 + np.abs(w) / c.w_std) * (-zmean / (n * ex * (1.0 + np.sqrt(2.0 / np.pi))))
+        setattr(inp, name, wl.bf16_bits_from_f32(w.astype(np.float32)))
+    return inp
+
+
+@pytest.mark.parametrize("case", [dict(B=64, D=128, H=64, L=500, G=16, F=32),
+                                  dict(B=48, D=256, H=64, L=700, G=64, F=64)],
+                         ids=["G16", "G64"])
+def test_loss_with_logits_far_below_zero(H, case):
+    """Each softplus term is about 3e-7 here, below the spacing of floats
+    near 1: the loss must not round the (1 + e^-|z|) factors against 1.
+    Tail forward, tail step and head step, within reading C16's relative
+    bound alone (the losses are far below its absolute slack of 1e-6)."""
+    print("case far below zero", case, flush=True)
+    inp = _far_below_zero(case)
+    c = inp.cfg
+    s = 1.0 / c.B
+    r = _ref(inp)
+    assert np.max(r.Zt) < -5.0 and np.max(r.Zh) < -5.0
+    d = Dev(inp)
+
+    def _rel(name, got, ref):
+        err = abs(got - ref) / ref
+        print(f"  far below zero, {name}: relative error {err:.2e}", flush=True)
+        assert err <= 1e-4, f"{name}: got {got} ref {ref}"
+
+    b = d.bce(c.H, s)
+    H.haste_tail_fwd(d.X, d.idx, d.W, c.L, c.G, bce=b)
+    torch.cuda.synchronize()
+    _rel("tail fwd loss", b.loss.item(), r.loss_tail)
+    dW = torch.empty_like(d.W)
+    dX = torch.empty((c.B, c.D), dtype=torch.float32, device=DEV)
+    b = d.bce(c.H, s)
+    H.haste_tail_step(d.X, d.idx, d.W, c.L, c.G, b, dW, dX)
+    torch.cuda.synchronize()
+    _rel("tail step loss", b.loss.item(), r.loss_tail)
+    bh = d.bce(0, s)
+    dWh = torch.empty_like(d.Wh)
+    H.haste_head_step(d.X, d.Wh, bh, dWh, dX, accumulate_dX=True)
+    torch.cuda.synchronize()
+    _rel("head step loss", bh.loss.item(), r.loss_head)
+
+
 @pytest.mark.parametrize("case", [dict(B=37, D=100, H=40, L=300, G=16, F=32),
                                   dict(B=70, D=203, H=40, L=500, G=64, F=64)],
                          ids=["D100-G16", "D203-G64"])
