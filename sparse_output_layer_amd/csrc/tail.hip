@@ -1700,7 +1700,7 @@ __global__ __launch_bounds__(64 * T2_NW, 1) void k_tail_t2(TailArgs a, int dz_mo
     const int r0 = bch * BC2;
     // wave roles (uniform): consumers 0..7, Z^T waves 8..11, builders 12..15
     const int role = w < T2_NC ? 0 : w < T2_NC + T2_NZ ? 1 : 2;
-    auto live = [&](int k, int q) { return gA + (int64_t)k * GPI + q < gB; };
+    auto live = [&](int k, int q) { return k * GPI + q < ng; };   // 32-bit, scalar
 
     const int dz_mem = dz_mode;             // dz not recomputed (modes 1, 2)
     {   // stage the chunk (units rotated by row), reset the inverse maps, zero rows
@@ -2154,7 +2154,7 @@ __global__ __launch_bounds__(64 * T2D_NW, 1) void k_tail_t2d(TailArgs a, int n_g
     // by four) has no exits; the extra iterations only pass the barrier
     const int niter = (nsteps + 3) & ~3;
     const int r0 = bch * BC2;
-    auto live = [&](int k, int q) { return gA + (int64_t)k * GPI + q < gB; };
+    auto live = [&](int k, int q) { return k * GPI + q < ng; };   // 32-bit, scalar
     const unsigned fill = (unsigned)F * 0x01010101u;
 
     // inverse maps to "no feature" (row F), zero rows of the W^T buffers
