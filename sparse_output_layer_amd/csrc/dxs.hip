@@ -234,33 +234,36 @@ __global__ __launch_bounds__(64 * dxs_nw(F), 1) void k_tail_dxs(TailArgs a, int 
     u32x4 pf[DPF][NPW];
     f32x4 ycur[FTW], ynext[FTW] = {};
     int icur[FTW], inext[FTW] = {};
-    auto clampg = [&](int64_t g) { return g < g1 ? g : g1 - 1; };
+    // groups counted from g0 in 32-bit scalar arithmetic (64-bit compares
+    // would be vector instructions)
+    const int nrg = (int)(g1 - g0);
+    auto clampg = [&](int r) { return g0 + (r < nrg ? r : nrg - 1); };
 #pragma unroll
-    for (int k = 0; k < DPF; ++k) gload(clampg(g0 + k), pf[k]);
+    for (int k = 0; k < DPF; ++k) gload(clampg(k), pf[k]);
     lwrite(g0, pf[0], st0);
-    lwrite(clampg(g0 + 1), pf[1], st1);
-    gload(clampg(g0 + DPF), pf[0]);
-    gload(clampg(g0 + DPF + 1), pf[1]);
+    lwrite(clampg(1), pf[1], st1);
+    gload(clampg(DPF), pf[0]);
+    gload(clampg(DPF + 1), pf[1]);
     lds_barrier();                    // stages of g0, g0 + 1 written; tile zeroed
     read_idx(st0, icur);
     product(st0, ycur);
 
-    auto iter = [&](auto kslot, int64_t g) {
-        constexpr int K = decltype(kslot)::value;   // (g - g0) mod DPF
-        constexpr int K2 = (K + 2) % DPF;           // slot of g + 2
-        // stage of g (and g + 2) and of g + 1: parity of g - g0 (DPF is even
-        // or the parity is taken from g itself)
-        const bool odd = (DPF % 2 == 0) ? (K & 1) : ((g - g0) & 1);
+    auto iter = [&](auto kslot, int r) {          // group g0 + r
+        constexpr int K = decltype(kslot)::value;   // r mod DPF
+        constexpr int K2 = (K + 2) % DPF;           // slot of r + 2
+        // stage of r (and r + 2) and of r + 1: parity of r (DPF is even or
+        // the parity is taken from r itself)
+        const bool odd = (DPF % 2 == 0) ? (K & 1) : (r & 1);
         unsigned char *const sa = odd ? st1 : st0;
         unsigned char *const sb = odd ? st0 : st1;
         lds_barrier();
         scatter(ycur, icur);
-        if (g + 1 < g1) {
+        if (r + 1 < nrg) {
             read_idx(sb, inext);
             product(sb, ynext);
         }
-        if (g + 2 < g1) lwrite(g + 2, pf[K2], sa);
-        gload(clampg(g + 2 + DPF), pf[K2]);
+        if (r + 2 < nrg) lwrite(g0 + r + 2, pf[K2], sa);
+        gload(clampg(r + 2 + DPF), pf[K2]);
 #pragma unroll
         for (int u = 0; u < FTW; ++u) {
             ycur[u] = ynext[u];
@@ -268,9 +271,9 @@ __global__ __launch_bounds__(64 * dxs_nw(F), 1) void k_tail_dxs(TailArgs a, int 
         }
     };
     // unrolled DPF times, so that every register slot is named statically
-    for (int64_t g = g0; g < g1; g += DPF)
+    for (int r = 0; r < nrg; r += DPF)
         dxs_unroll([&](auto k) {
-            if (g + decltype(k)::value < g1) iter(k, g + decltype(k)::value);
+            if (r + decltype(k)::value < nrg) iter(k, r + decltype(k)::value);
         }, std::make_integer_sequence<int, DPF>{});
 
     // ---- flush: one fp32 atomic per live element; lanes run over consecutive
@@ -308,6 +311,7 @@ static hipError_t dxs_go(const TailArgs &a, hipStream_t st) {
     // about one workgroup per CU in all (the tile fills most of a CU's LDS)
     int ngr = (ncu + nrc - 1) / nrc;
     ngr = (ngr + 7) / 8 * 8;
+    if (a.Ng / ngr + 1 > 0x7fffffff) return hipErrorInvalidValue;   // groups of a range: 32-bit
     const size_t dyn = (size_t)a.D * DXS_R * 4;
     dxs_allow_lds((const void *)k_tail_dxs<G, F>, dyn);
     hipLaunchKernelGGL((k_tail_dxs<G, F>), dim3((unsigned)(nrc * ngr)), dim3(64 * dxs_nw(F)), dyn, st, a, nrc, ngr);
