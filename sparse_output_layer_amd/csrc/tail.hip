@@ -2305,9 +2305,12 @@ __global__ __launch_bounds__(64 * T2D_NW, 1) void k_tail_t2d(TailArgs a, int n_g
         // the group, unit or tile does not exist (the value is then unused):
         // with no load skipped, the compiler can wait for exactly the set it
         // needs instead of for all loads in flight.
-        auto gsafe = [&](int k, int q) {   // unit (group slice), clamped
-            const int64_t g = gA + (int64_t)k * GPI + q;
-            return g < Nu ? g : Nu - 1;
+        // unit (group slice) of step k's slot q, clamped to the last one; the
+        // clamp in 32-bit arithmetic (gA < Nu, so the bound is >= 0)
+        const int ulast = (int)(Nu - 1 - gA < 0x7fffffff ? Nu - 1 - gA : 0x7fffffff);
+        auto gsafe = [&](int k, int q) {
+            const int r = k * GPI + q;
+            return gA + (int64_t)(r < ulast ? r : ulast);
         };
         auto fetch = [&](int k, Ops &o) {
 #pragma unroll
