@@ -2107,7 +2107,7 @@ __host__ __device__ inline T2dLds t2d_layout(int F, int G, int BC2, int NTW32) {
     L.wts_grp = (F + 1) * (G * 2 + 16);                // W_g^T (padded rows) + zero row F
     o += 3 * GPI * L.wts_grp;
     L.inv = o;
-    o += (4 * GPI * L.ndp + 15) & ~15;                // u8 inverse index
+    o += (4 * GPI * L.ndp * 2 + 15) & ~15;            // u16 inverse index (byte offsets)
     L.exch = o;
     L.exch_grp = BC2 * G * 2;                          // dz of one group, MFMA A layout
     o += 3 * GPI * L.exch_grp;
@@ -2142,7 +2142,9 @@ __global__ __launch_bounds__(64 * T2D_NW, 1) void k_tail_t2d(TailArgs a, int n_g
     const T2dLds LY = t2d_layout(F, G, BC2, NTW32);
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     unsigned char *wts0 = lds + LY.wts;
-    unsigned char *inv0 = lds + LY.inv;
+    // inverse index: per feature the byte offset of its W^T row (f * WTS),
+    // F * WTS (the zero row) for a feature the group lacks
+    unsigned short *inv0 = (unsigned short *)(lds + LY.inv);
     unsigned char *exch0 = lds + LY.exch;
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -2155,10 +2157,10 @@ __global__ __launch_bounds__(64 * T2D_NW, 1) void k_tail_t2d(TailArgs a, int n_g
     const int niter = (nsteps + 3) & ~3;
     const int r0 = bch * BC2;
     auto live = [&](int k, int q) { return k * GPI + q < ng; };   // 32-bit, scalar
-    const unsigned fill = (unsigned)F * 0x01010101u;
+    const unsigned fill = (unsigned)(F * WTS) * 0x00010001u;
 
     // inverse maps to "no feature" (row F), zero rows of the W^T buffers
-    for (int i = tid; i < 4 * GPI * NDP / 4; i += NT) ((unsigned *)inv0)[i] = fill;
+    for (int i = tid; i < 4 * GPI * NDP / 2; i += NT) ((unsigned *)inv0)[i] = fill;
     for (int i = tid; i < 3 * GPI * (G / 2); i += NT)
         ((unsigned *)(wts0 + (i / (G / 2)) * LY.wts_grp + F * WTS))[i % (G / 2)] = 0u;
     __syncthreads();
@@ -2180,7 +2182,7 @@ __global__ __launch_bounds__(64 * T2D_NW, 1) void k_tail_t2d(TailArgs a, int n_g
         // first two of the next, complete since the previous iteration); with
         // one group per step, one set taking the next step's group.
         constexpr int NS = GPI >= 2 ? 2 : 1;
-        // With at least NS + 2 groups per step, the inverse-index bytes of a
+        // With at least NS + 2 groups per step, the inverse-index entries of a
         // load's group are read one load earlier (that group is then at most
         // in step k+1, whose index is complete), so the W~ row reads do not
         // wait for them.  Steps with fewer groups look them up in the load.
@@ -2188,7 +2190,7 @@ __global__ __launch_bounds__(64 * T2D_NW, 1) void k_tail_t2d(TailArgs a, int n_g
         Opd R[NS];
         unsigned ivn[NTW32];
         auto load_iv = [&](int k, int q) {
-            const unsigned char *iv = inv0 + ((k & 3) * GPI + q) * NDP + dbase + (lane & 31);
+            const unsigned short *iv = inv0 + ((k & 3) * GPI + q) * NDP + dbase + (lane & 31);
 #pragma unroll
             for (int nt = 0; nt < NTW32; ++nt) ivn[nt] = iv[32 * nt];
         };
@@ -2221,7 +2223,7 @@ __global__ __launch_bounds__(64 * T2D_NW, 1) void k_tail_t2d(TailArgs a, int n_g
                 }
 #pragma unroll
             for (int nt = 0; nt < NTW32; ++nt) {
-                const unsigned char *br = wt + ivn[nt] * WTS;
+                const unsigned char *br = wt + ivn[nt];
 #pragma unroll
                 for (int jt = 0; jt < JT; ++jt) R[q % NS].Bv[jt][nt] = *(const bf16x8 *)(br + 32 * jt);
             }
@@ -2247,7 +2249,7 @@ __global__ __launch_bounds__(64 * T2D_NW, 1) void k_tail_t2d(TailArgs a, int n_g
                                 acc[rt][nt] = mfma32x32(R[q % NS].A[rt][jt], R[q % NS].Bv[jt][nt], acc[rt][nt]);
                 }
                 // operands of group q + NS (this step or the next), then the
-                // inverse-index bytes of the group after it
+                // inverse-index entries of the group after it
                 if (q + NS < GPI) {
                     if (live(k, q + NS)) load(k, q + NS);
                 } else if (live(k + 1, q + NS - GPI)) {
@@ -2368,7 +2370,7 @@ __global__ __launch_bounds__(64 * T2D_NW, 1) void k_tail_t2d(TailArgs a, int n_g
                 const int e = bth + NB_T * i;
                 if (e >= GPI * F) break;
                 const int q = e / F;
-                if (live(k, q)) inv0[((k & 3) * GPI + q) * NDP + o.fi[i]] = (unsigned char)(e - q * F);
+                if (live(k, q)) inv0[((k & 3) * GPI + q) * NDP + o.fi[i]] = (unsigned short)((e - q * F) * WTS);
             }
 #pragma unroll
             for (int t = 0; t < TPB; ++t) {
@@ -2395,7 +2397,7 @@ __global__ __launch_bounds__(64 * T2D_NW, 1) void k_tail_t2d(TailArgs a, int n_g
         __syncthreads();
         auto iter = [&](int k, Ops &o) {
             unsigned *ivp = (unsigned *)(inv0 + ((k + 3) & 3) * GPI * NDP);   // step k-1
-            for (int i = bth; i < GPI * NDP / 4; i += NB_T) ivp[i] = fill;
+            for (int i = bth; i < GPI * NDP / 2; i += NB_T) ivp[i] = fill;
             build(k + 2, o);
             fetch(k + 6, o);
             __syncthreads();
