@@ -1696,6 +1696,9 @@ __global__ __launch_bounds__(64 * T2_NW, 1) void k_tail_t2(TailArgs a, int dz_mo
     const int gr = blockIdx.x % n_granges, bch = blockIdx.x / n_granges;
     const int64_t gA = (int64_t)gr * a.Ng / n_granges, gB = (int64_t)(gr + 1) * a.Ng / n_granges;
     const int ng = (int)(gB - gA);
+    // labels from the range's first one on, at most INT_MAX: bounds in 32-bit
+    // arithmetic (gA is below the unit count, so this is positive)
+    const int lrem = (int)(a.L - gA * G < 0x7fffffff ? a.L - gA * G : 0x7fffffff);
     const int nsteps = (ng + GPI - 1) / GPI;
     const int r0 = bch * BC2;
     // wave roles (uniform): consumers 0..7, Z^T waves 8..11, builders 12..15
@@ -2030,9 +2033,9 @@ __global__ __launch_bounds__(64 * T2_NW, 1) void k_tail_t2(TailArgs a, int dz_mo
                 // those rows (NaN included) must not reach dX.  Masks on the
                 // permuted words (label 4ja + e in half e % 2 of word e / 2),
                 // so no loaded register is rewritten before its use
-                const int64_t lab0 = (gA + (int64_t)k * GPI + q) * G + 4 * ja;
-                const unsigned m01 = (lab0 < a.L ? 0x0000ffffu : 0u) | (lab0 + 1 < a.L ? 0xffff0000u : 0u);
-                const unsigned m23 = (lab0 + 2 < a.L ? 0x0000ffffu : 0u) | (lab0 + 3 < a.L ? 0xffff0000u : 0u);
+                const int lab0 = (k * GPI + q) * G + 4 * ja;   // from the range's first label
+                const unsigned m01 = (lab0 < lrem ? 0x0000ffffu : 0u) | (lab0 + 1 < lrem ? 0xffff0000u : 0u);
+                const unsigned m23 = (lab0 + 2 < lrem ? 0x0000ffffu : 0u) | (lab0 + 3 < lrem ? 0xffff0000u : 0u);
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {   // feature 4fc+kk: element kk of each row
                     const unsigned sel = (kk & 1) ? 0x07060302u : 0x05040100u;
@@ -2151,6 +2154,9 @@ __global__ __launch_bounds__(64 * T2D_NW, 1) void k_tail_t2d(TailArgs a, int n_g
     const int gr = blockIdx.x % n_granges, bch = blockIdx.x / n_granges;
     const int64_t gA = (int64_t)gr * Nu / n_granges, gB = (int64_t)(gr + 1) * Nu / n_granges;
     const int ng = (int)(gB - gA);
+    // labels from the range's first one on, at most INT_MAX: bounds in 32-bit
+    // arithmetic (gA is below the unit count, so this is positive)
+    const int lrem = (int)(a.L - gA * G < 0x7fffffff ? a.L - gA * G : 0x7fffffff);
     const int nsteps = (ng + GPI - 1) / GPI;
     // iterations: a multiple of four, so the builders' loop body (unrolled
     // by four) has no exits; the extra iterations only pass the barrier
@@ -2353,9 +2359,9 @@ __global__ __launch_bounds__(64 * T2D_NW, 1) void k_tail_t2d(TailArgs a, int n_g
                 // those rows (NaN included) must not reach dX.  Masks on the
                 // permuted words (label 4ja + e in half e % 2 of word e / 2),
                 // so no loaded register is rewritten before its use
-                const int64_t lab0 = (gA + (int64_t)k * GPI + q) * G + 4 * ja;
-                const unsigned m01 = (lab0 < a.L ? 0x0000ffffu : 0u) | (lab0 + 1 < a.L ? 0xffff0000u : 0u);
-                const unsigned m23 = (lab0 + 2 < a.L ? 0x0000ffffu : 0u) | (lab0 + 3 < a.L ? 0xffff0000u : 0u);
+                const int lab0 = (k * GPI + q) * G + 4 * ja;   // from the range's first label
+                const unsigned m01 = (lab0 < lrem ? 0x0000ffffu : 0u) | (lab0 + 1 < lrem ? 0xffff0000u : 0u);
+                const unsigned m23 = (lab0 + 2 < lrem ? 0x0000ffffu : 0u) | (lab0 + 3 < lrem ? 0xffff0000u : 0u);
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {   // feature 4fc+kk: element kk of each row
                     const unsigned sel = (kk & 1) ? 0x07060302u : 0x05040100u;
